@@ -1,0 +1,161 @@
+"""Pins of oracle/attention.py: textbook special case, split invariance, per-token loops,
+underflow closed form, and the logit formula."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import codecs as C
+from oracle import kvquant as KQ
+from oracle.query import quantize_query
+
+F32 = np.float32
+
+
+def _rand_case(rng, L, d=128, fmt=KQ.NVFP4, g=4):
+    K = rng.standard_normal((L, d)).astype(F32)
+    V = rng.standard_normal((L, d)).astype(F32)
+    Q = rng.standard_normal((g, d)).astype(F32)
+    return Q, K, V
+
+
+def test_identity_codec_is_textbook_softmax():
+    rng = np.random.default_rng(30)
+    for L in (1, 100, 128, 1000):
+        s = (rng.standard_normal((3, L)) * 3).astype(F32)
+        v = rng.standard_normal((L, 64))
+        got = A.attend(s, v, L, KQ.NVFP4, p_mode="exact")["out"]
+        z = s.astype(np.float64) * math.log(2.0)
+        p = np.exp(z - z.max(-1, keepdims=True))
+        ref = (p / p.sum(-1, keepdims=True)) @ v
+        # p~ is rounded to fp32 (as in the kernel): relative error per weight <= 2^-24
+        assert np.all(A.row_rel_err(got, ref) < 1e-6)
+
+
+def _online_split(o_t, m_t, l_t, bounds):
+    """Running-max accumulation of tiles inside each split, then the split merge."""
+    R, T, d = o_t.shape
+    os_, ms, ls = [], [], []
+    for a, b in bounds:
+        m = np.full(R, -np.inf)
+        o = np.zeros((R, d))
+        l = np.zeros(R)
+        for t in range(a, b):
+            mn = np.maximum(m, m_t[:, t])
+            al = np.where(np.isfinite(m), np.exp2(m - mn), 0.0)
+            be = np.exp2(m_t[:, t] - mn)
+            o = o * al[:, None] + o_t[:, t] * be[:, None]
+            l = l * al + l_t[:, t] * be
+            m = mn
+        os_.append(o)
+        ms.append(m)
+        ls.append(l)
+    return A.merge_partials(np.stack(os_, 1), np.stack(ms, 1), np.stack(ls, 1))
+
+
+def test_split_merge_invariance():
+    rng = np.random.default_rng(31)
+    L = 1500
+    s = (rng.standard_normal((4, L)) * 4).astype(F32)
+    v = rng.standard_normal((L, 32))
+    res = A.attend(s, v, L, KQ.NVFP4, partials=True)
+    T = res["m_tiles"].shape[1]
+    for bounds in ([(0, T)], [(0, 3), (3, 7), (7, T)], [(i, i + 1) for i in range(T)],
+                   [(0, 5), (5, 5), (5, T)]):
+        got = _online_split(res["o_tiles"], res["m_tiles"].astype(np.float64), res["l_tiles"], bounds)
+        assert np.allclose(got, res["out"], rtol=1e-12, atol=1e-14)
+
+
+def _loop_reference(s, vhat, L, fmt):
+    """Per-token, per-block loops written from the definitions (no vectorised helpers)."""
+    R = s.shape[0]
+    d = vhat.shape[1]
+    B = 16 if fmt == KQ.NVFP4 else 32
+    out = np.zeros((R, d))
+    for r in range(R):
+        ms, os_, ls = [], [], []
+        for t0 in range(0, L, 128):
+            toks = range(t0, min(L, t0 + 128))
+            m = max(F32(s[r, t]) for t in toks)
+            p = {t: F32(2.0 ** float(F32(F32(s[r, t]) - m))) for t in toks}
+            o = np.zeros(d)
+            l = 0.0
+            for b0 in range(t0, min(L, t0 + 128), B):
+                bt = [t for t in range(b0, b0 + B) if t < L]
+                amax = max(p[t] for t in bt)
+                if fmt == KQ.NVFP4:
+                    tq = F32(amax * F32(F32(1.0) / F32(F32(6.0) * F32(2.0 ** -10))))
+                    e = int(math.ceil(math.log2(float(tq)))) if tq > 0 else -9
+                    if tq > 0 and 2.0 ** (e - 1) >= float(tq):     # guard log2 rounding
+                        e -= 1
+                    e = min(8, max(-9, e))
+                    r_ = F32(F32(1.0) / F32(F32(2.0 ** e) * F32(2.0 ** -10)))
+                    scale = 2.0 ** (e - 10)
+                else:
+                    e = max(-127, math.frexp(float(amax))[1] - 1 - 2) if amax > 0 else -127
+                    r_ = F32(2.0 ** -e)
+                    scale = 2.0 ** e
+                for t in bt:
+                    code = C.e2m1_encode(np.array([F32(p[t] * r_)], F32))[0]
+                    ph = float(C.e2m1_decode(np.array([code]))[0]) * scale
+                    o += ph * vhat[t]
+                for t in bt:
+                    l += float(p[t])
+            ms.append(float(m))
+            os_.append(o)
+            ls.append(l)
+        M = max(ms)
+        w = [2.0 ** (x - M) for x in ms]
+        out[r] = sum(wi * oi for wi, oi in zip(w, os_)) / sum(wi * li for wi, li in zip(w, ls))
+    return out
+
+
+@pytest.mark.parametrize("fmt", [KQ.NVFP4, KQ.MXFP4])
+def test_tiny_contexts_match_explicit_loops(fmt):
+    rng = np.random.default_rng(32)
+    for L in (1, 2, 15, 16, 17, 127, 128, 129, 300):
+        s = (rng.standard_normal((2, L)) * 3).astype(F32)
+        v = rng.standard_normal((L, 16))
+        got = A.attend(s, v, L, fmt)["out"]
+        ref = _loop_reference(s, v, L, fmt)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-13), L
+
+
+def test_underflow_closed_form():
+    """Flat logits at long context: tile-relative P keeps every block, vanilla P loses all.
+
+    Closed form: vanilla p ~ 1/L, its E4M3 scale amax/6 <= 2^-10 once L > 6*2^10/e^{max gap}.
+    The tile-relative p~ >= 2^(-gap) with gap << 19, so no block falls to zero.
+    """
+    rng = np.random.default_rng(33)
+    L, d = 16384, 128
+    Q = rng.standard_normal((4, d)).astype(F32)
+    K = (rng.standard_normal((L, d)) * 0.05).astype(F32)
+    V = rng.standard_normal((L, d)).astype(F32)
+    ones = np.ones(d, F32)
+    args = (Q, K, V, ones, ones, F32(0.05 * 8 * math.sqrt(d) / 2688), F32(8 / 2688), KQ.NVFP4,
+            1 / math.sqrt(d))
+    tile = A.gqa_head(*args)
+    van = A.gqa_head(*args, opts=dict(p_mode="vanilla"))
+    nblk = 4 * (L // 16)
+    assert tile["zero_blocks"] == 0
+    assert van["zero_blocks"] == nblk
+    smax = np.max(np.abs(tile["s"]))
+    assert smax < 2.0                       # the logits are indeed nearly flat (base 2)
+
+
+def test_logit_formula_closed_form():
+    rng = np.random.default_rng(34)
+    L, d = 50, 128
+    Q, K, V = _rand_case(rng, L)
+    ones = np.ones(d, F32)
+    G_K = F32(0.02)
+    kc, ks = KQ.quantize_keys(K, ones, G_K, KQ.NVFP4)
+    qq = quantize_query(Q, ones, KQ.NVFP4)
+    cs = A.logit_coeff(0.125, d)
+    s = A.logits(qq, A.key_dequant_exact(kc, ks, KQ.NVFP4), G_K, cs, KQ.NVFP4)
+    q_full = qq.approx()                                       # (Q1 + Q2) with G, float64
+    k_full = A.key_dequant_exact(kc, ks, KQ.NVFP4) * float(G_K)
+    ref = (q_full @ k_full.T) * 0.125 * math.log2(math.e) / d
+    assert np.allclose(s, ref, rtol=3e-6, atol=1e-6 * np.abs(ref).max())
