@@ -1,0 +1,55 @@
+"""Build libfp4kv.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
+
+Usage: ``python -m fp4_kv_cache_amd.build`` or ``fp4_kv_cache_amd.build.build()``.
+Objects go to ``fp4_kv_cache_amd/_build/``; the library to ``fp4_kv_cache_amd/libfp4kv.so``.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libfp4kv.so")
+SOURCES = ["api.hip", "append.hip", "decode_gqa.hip", "stream.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
+    # every quantization decision is a single rounded fp32 operation: no contraction
+    "-ffp-contract=off",
+    # no packed fp32 arithmetic in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("command failed: %s\n%s" % (" ".join(cmd), err))
+    return err
+
+
+def build(verbose=False):
+    """Compile every source for gfx950 and link libfp4kv.so (always rebuilds)."""
+    os.makedirs(OUT, exist_ok=True)
+
+    def compile_one(src):
+        obj = os.path.join(OUT, src + ".o")
+        err = _run([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

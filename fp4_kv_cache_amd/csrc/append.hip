@@ -1,0 +1,440 @@
+// KV-append quantizer kernels for gfx950.
+//
+// Keys follow Outlier-Aware Key Quantization ("BitDecoding-FP4: Native FP4 KV
+// Cache Decoding via Algorithm-System Co-Design", Article Summary; "FP4 KV
+// Cache Done Right", section "What is actually new in BitDecoding-FP4?"):
+// static per-channel smoothing, a Hadamard rotation over head_dim, then a
+// scale search per block under token-wise scaling ("BitDecoding-FP4 :
+// décodage natif du KV cache FP4", Analyse approfondie: the search picks a
+// better-fitted factor for each group).  The search window, objective and
+// tie rule, the value blocking and the tail re-quantization are this
+// library's readings of what the pages leave open:
+//   * search: NVFP4 scale codes c0, c0+1, c0-1, c0-2, c0-3 (MXFP4 exponents
+//     e0, e0+1, e0-1), objective sum of squared fp32 errors accumulated in
+//     element order, first strictly smaller objective wins;
+//   * values: channel-wise scales over page-aligned blocks of B tokens (the
+//     P.V contraction runs over tokens), default scale, no search;
+//   * the last, partly filled value block (MLA: latent tile) of a sequence is
+//     re-quantized from the fp32 stage with absent tokens as +0.0.
+// Every decision uses single fp32 operations in a fixed order (built with
+// -ffp-contract=off), so codes and scales are reproducible bit for bit.
+#include "fp4kv_device.h"
+#include "fp4kv_internal.h"
+
+namespace fp4kv {
+
+// ---------------------------------------------------------------------------------------------
+// Block encoders and scale search on arrays held in registers.
+
+// Objective and codes of an NVFP4 block under scale code c and tensor scale G.
+template <int N>
+__device__ __forceinline__ float nv_block_err(const float *x, uint32_t c, float G) {
+  float S = e4m3_dec(c);
+  float sg = S * G;
+  float r = (sg != 0.0f) ? 1.0f / sg : 0.0f;
+  float err = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i++) {
+    uint32_t q = e2m1_enc(x[i] * r);
+    float xh = (e2m1_dec(q) * S) * G;
+    float d = x[i] - xh;
+    err = err + d * d;
+  }
+  return err;
+}
+
+template <int N>
+__device__ __forceinline__ void nv_block_codes(const float *x, uint32_t c, float G, uint8_t *codes) {
+  float S = e4m3_dec(c);
+  float sg = S * G;
+  float r = (sg != 0.0f) ? 1.0f / sg : 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i += 2)
+    codes[i / 2] = (uint8_t)(e2m1_enc(x[i] * r) | (e2m1_enc(x[i + 1] * r) << 4));
+}
+
+__device__ __forceinline__ uint32_t nv_default_scale(float amax, float G) {
+  if (G == 0.0f) return 0u;
+  float sixg = 6.0f * G;
+  if (sixg == 0.0f) return 0u;
+  return e4m3_enc_sat(amax / sixg);
+}
+
+// NVFP4 scale search (window of five codes around the default).
+template <int N>
+__device__ __forceinline__ uint32_t nv_search(const float *x, float G, bool search) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i++) amax = fmaxf(amax, fabsf(x[i]));
+  uint32_t c0 = nv_default_scale(amax, G);
+  uint32_t best = c0;
+  if (!search) return best;
+  float best_err = nv_block_err<N>(x, c0, G);
+  const int deltas[4] = {1, -1, -2, -3};
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    int c = (int)c0 + deltas[k];
+    if (c < 0 || c > 0x7E) continue;
+    float e = nv_block_err<N>(x, (uint32_t)c, G);
+    if (e < best_err) { best_err = e; best = (uint32_t)c; }
+  }
+  return best;
+}
+
+template <int N>
+__device__ __forceinline__ float mx_block_err(const float *x, int e) {
+  float err = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i++) {
+    uint32_t q = e2m1_enc(ldexpf(x[i], -e));
+    float xh = ldexpf(e2m1_dec(q), e);
+    float d = x[i] - xh;
+    err = err + d * d;
+  }
+  return err;
+}
+
+template <int N>
+__device__ __forceinline__ void mx_block_codes(const float *x, int e, uint8_t *codes) {
+#pragma unroll
+  for (int i = 0; i < N; i += 2)
+    codes[i / 2] = (uint8_t)(e2m1_enc(ldexpf(x[i], -e)) | (e2m1_enc(ldexpf(x[i + 1], -e)) << 4));
+}
+
+// MXFP4 exponent search (e0, e0+1, e0-1).
+template <int N>
+__device__ __forceinline__ int mx_search(const float *x, bool search) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i++) amax = fmaxf(amax, fabsf(x[i]));
+  int e0 = mx_exp(amax);
+  if (!search) return e0;
+  int best = e0;
+  float best_err = mx_block_err<N>(x, e0);
+  const int deltas[2] = {1, -1};
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    int e = e0 + deltas[k];
+    if (e < -127 || e > 127) continue;
+    float er = mx_block_err<N>(x, e);
+    if (er < best_err) { best_err = er; best = e; }
+  }
+  return best;
+}
+
+// Unnormalised Walsh-Hadamard transform of 128 values in registers; stages h = 1, 2, ..., 64.
+__device__ __forceinline__ void fwht128(float *x) {
+#pragma unroll
+  for (int h = 1; h < 128; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 128; i++) {
+      if (!(i & h)) {
+        float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// 8 consecutive elements (fp32 or bf16) starting at element index i (multiple of 8).
+__device__ __forceinline__ void load8(const void *p, long i, int bf16, float *o) {
+  if (bf16) {
+    uint4 v = *(const uint4 *)((const uint16_t *)p + i);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      o[2 * k] = __uint_as_float(w[k] << 16);
+      o[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  } else {
+    float4 a = *(const float4 *)((const float *)p + i);
+    float4 b = *(const float4 *)((const float *)p + i + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// GQA keys: one thread per (new token, KV head); head_dim 128.
+
+template <int FMT>
+__global__ __launch_bounds__(128) void k_append_gqa(AppendArgs a) {
+  constexpr int B = FMT == kFmtNV ? 16 : 32;
+  constexpr int NB = 128 / B;
+  long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long)a.num_tokens * a.hkv) return;
+  int tok = (int)(gid / a.hkv), h = (int)(gid % a.hkv);
+  int slot = a.slots[tok];
+  if (slot < 0 || slot >= a.num_pages * a.page_size) return;
+  int page = slot / a.page_size, off = slot % a.page_size;
+
+  float x[128];
+  const long base = ((long)tok * a.hkv + h) * 128;
+  const float *ksi = a.ksi + (long)h * 128;
+#pragma unroll
+  for (int c = 0; c < 128; c += 8) load8(a.k_new, base + c, a.bf16, x + c);
+#pragma unroll
+  for (int c = 0; c < 128; c++) x[c] = x[c] * ksi[c];
+  fwht128(x);
+
+  const float G = FMT == kFmtNV ? a.gk[h] : 1.0f;
+  uint8_t codes[64];
+  uint8_t sc[NB];
+#pragma unroll
+  for (int blk = 0; blk < NB; blk++) {
+    if (FMT == kFmtNV) {
+      uint32_t c = nv_search<B>(x + blk * B, G, true);
+      nv_block_codes<B>(x + blk * B, c, G, codes + blk * B / 2);
+      sc[blk] = (uint8_t)c;
+    } else {
+      int e = mx_search<B>(x + blk * B, true);
+      mx_block_codes<B>(x + blk * B, e, codes + blk * B / 2);
+      sc[blk] = (uint8_t)(e + 127);
+    }
+  }
+  const long row = ((long)page * a.hkv + h) * a.page_size + off;
+  uint4 *dst = (uint4 *)(a.k_codes + row * 64);
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    uint4 v;
+    v.x = codes[16 * k + 0] | (codes[16 * k + 1] << 8) | (codes[16 * k + 2] << 16) | ((uint32_t)codes[16 * k + 3] << 24);
+    v.y = codes[16 * k + 4] | (codes[16 * k + 5] << 8) | (codes[16 * k + 6] << 16) | ((uint32_t)codes[16 * k + 7] << 24);
+    v.z = codes[16 * k + 8] | (codes[16 * k + 9] << 8) | (codes[16 * k + 10] << 16) | ((uint32_t)codes[16 * k + 11] << 24);
+    v.w = codes[16 * k + 12] | (codes[16 * k + 13] << 8) | (codes[16 * k + 14] << 16) | ((uint32_t)codes[16 * k + 15] << 24);
+    dst[k] = v;
+  }
+  if (NB == 8) {
+    uint2 v;
+    v.x = sc[0] | (sc[1] << 8) | (sc[2] << 16) | ((uint32_t)sc[3] << 24);
+    v.y = sc[4 % NB] | (sc[5 % NB] << 8) | (sc[6 % NB] << 16) | ((uint32_t)sc[7 % NB] << 24);
+    *(uint2 *)(a.k_scales + row * NB) = v;
+  } else {
+    *(uint32_t *)(a.k_scales + row * NB) = sc[0] | (sc[1] << 8) | (sc[2 % NB] << 16) | ((uint32_t)sc[3 % NB] << 24);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Token-block bookkeeping shared by the value and latent kernels.  Token i leads a
+// block when it is the first token of its sequence in this batch or its position
+// starts a block; the block's new tokens are i .. i + n_new - 1 and its first
+// `first` positions were appended by earlier calls (their values are in the stage).
+
+struct BlockSpan {
+  int seq, bstart, first, n_new, page, off0;
+  bool ok;
+};
+
+template <int B>
+__device__ __forceinline__ BlockSpan block_span(const AppendArgs &a, int i) {
+  BlockSpan sp;
+  sp.ok = false;
+  int s = a.seq_ids[i], pos = a.positions[i];
+  bool leader = (i == 0) || (a.seq_ids[i - 1] != s) || (pos % B == 0);
+  int slot = a.slots[i];
+  if (!leader || s < 0 || s >= a.max_seqs || pos < 0 || slot < 0 || slot >= a.num_pages * a.page_size)
+    return sp;
+  sp.seq = s;
+  sp.bstart = pos - pos % B;
+  sp.first = pos - sp.bstart;
+  int n = 1;
+  while (i + n < a.num_tokens && a.seq_ids[i + n] == s && a.positions[i + n] < sp.bstart + B) n++;
+  sp.n_new = n;
+  sp.page = slot / a.page_size;
+  sp.off0 = (slot % a.page_size) - sp.first;
+  // the block must sit inside the slot's page (slot and position disagree otherwise)
+  sp.ok = sp.off0 >= 0 && (sp.off0 % B) == 0 && sp.off0 + B <= a.page_size;
+  return sp;
+}
+
+// ---------------------------------------------------------------------------------------------
+// GQA values: one workgroup per (leading token, KV head), one thread per channel.
+
+template <int FMT>
+__global__ __launch_bounds__(128) void v_append_gqa(AppendArgs a) {
+  constexpr int B = FMT == kFmtNV ? 16 : 32;
+  const int i = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
+  BlockSpan sp = block_span<B>(a, i);
+  if (!sp.ok) return;
+  const int d = 128;
+  float *stage = a.stage + ((long)sp.seq * a.hkv + h) * B * d;
+  float v[B];
+#pragma unroll
+  for (int k = 0; k < B; k++) {
+    float x = 0.0f;
+    if (k < sp.first) x = stage[k * d + c];
+    else if (k < sp.first + sp.n_new) x = load_elem(a.v_new, ((long)(i + k - sp.first) * a.hkv + h) * d + c, a.bf16);
+    v[k] = x;
+  }
+  uint8_t codes[B / 2];
+  uint32_t sbyte;
+  if (FMT == kFmtNV) {
+    const float G = a.gv[h];
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < B; k++) amax = fmaxf(amax, fabsf(v[k]));
+    uint32_t sc = nv_default_scale(amax, G);
+    nv_block_codes<B>(v, sc, G, codes);
+    sbyte = sc;
+  } else {
+    int e = mx_search<B>(v, false);
+    mx_block_codes<B>(v, e, codes);
+    sbyte = (uint32_t)(e + 127);
+  }
+  const long row = ((long)sp.page * a.hkv + h) * d + c;
+  uint8_t *cdst = a.v_codes + row * (a.page_size / 2) + sp.off0 / 2;
+#pragma unroll
+  for (int k = 0; k < B / 2; k += 4)
+    *(uint32_t *)(cdst + k) = codes[k] | (codes[k + 1] << 8) | (codes[k + 2] << 16) | ((uint32_t)codes[k + 3] << 24);
+  a.v_scales[row * (a.page_size / B) + sp.off0 / B] = (uint8_t)sbyte;
+  if (sp.first + sp.n_new < B) {
+#pragma unroll
+    for (int k = 0; k < B; k++)
+      if (k >= sp.first && k < sp.first + sp.n_new) stage[k * d + c] = v[k];
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// MLA latent: one workgroup (256 threads) per (leading token) = one B-token tile row of
+// the sequence.  The new tokens are smoothed and rotated over 512 channels in LDS, the
+// earlier tokens of the tile come from the stage, then one thread per B x B tile runs
+// the scale search with the objective in (token, channel) order.
+
+template <int FMT>
+__global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
+  constexpr int B = FMT == kFmtNV ? 16 : 32;
+  constexpr int D = 512;
+  constexpr int NT = D / B;
+  __shared__ float xs[B][D];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  BlockSpan sp = block_span<B>(a, i);
+  if (!sp.ok) return;
+  float *stage = a.stage + (long)sp.seq * B * D;
+  const float *ksi = a.ksi;
+  for (int e = tid; e < B * D; e += 256) {
+    int k = e / D, ch = e % D;
+    float x = 0.0f;
+    if (k < sp.first) x = stage[k * D + ch];
+    else if (k < sp.first + sp.n_new) x = load_elem(a.k_new, (long)(i + k - sp.first) * D + ch, a.bf16) * ksi[ch];
+    xs[k][ch] = x;
+  }
+  __syncthreads();
+  // FWHT over the rows of the new tokens (stages h = 1, 2, ..., 256)
+  for (int h = 1; h < D; h <<= 1) {
+    for (int e = tid; e < B * (D / 2); e += 256) {
+      int k = e / (D / 2), w = e % (D / 2);
+      if (k < sp.first || k >= sp.first + sp.n_new) continue;
+      int idx = (w / h) * 2 * h + (w % h);
+      float p = xs[k][idx], q = xs[k][idx + h];
+      xs[k][idx] = p + q;
+      xs[k][idx + h] = p - q;
+    }
+    __syncthreads();
+  }
+  // stage the rotated new tokens when the tile stays incomplete
+  if (sp.first + sp.n_new < B) {
+    for (int e = tid; e < B * D; e += 256) {
+      int k = e / D, ch = e % D;
+      if (k >= sp.first && k < sp.first + sp.n_new) stage[k * D + ch] = xs[k][ch];
+    }
+  }
+  // rope keys of the new tokens, copied unquantized
+  for (int e = tid; e < sp.n_new * a.rope_dim; e += 256) {
+    int k = e / a.rope_dim, r = e % a.rope_dim;
+    a.k_rope[((long)sp.page * a.page_size + sp.off0 + sp.first + k) * a.rope_dim + r] =
+        ((const uint16_t *)a.k_rope_new)[(long)(i + k) * a.rope_dim + r];
+  }
+  if (tid >= NT) return;
+  const int ct = tid;
+  // amax over the tile, then the search with the objective in (token, channel) order
+  float amax = 0.0f;
+  for (int k = 0; k < B; k++)
+#pragma unroll
+    for (int cc = 0; cc < B; cc++) amax = fmaxf(amax, fabsf(xs[k][ct * B + cc]));
+  uint32_t sbyte;
+  float G = 1.0f, r = 1.0f;
+  int eb = 0;
+  if (FMT == kFmtNV) {
+    G = a.gk[0];
+    uint32_t c0 = nv_default_scale(amax, G), best = c0;
+    float best_err = 0.0f;
+    const int deltas[5] = {0, 1, -1, -2, -3};
+    for (int kk = 0; kk < 5; kk++) {
+      int c = (int)c0 + deltas[kk];
+      if (c < 0 || c > 0x7E) continue;
+      float S = e4m3_dec((uint32_t)c), sg = S * G, rr = (sg != 0.0f) ? 1.0f / sg : 0.0f;
+      float err = 0.0f;
+      for (int k = 0; k < B; k++)
+#pragma unroll
+        for (int cc = 0; cc < B; cc++) {
+          float x = xs[k][ct * B + cc];
+          float xh = (e2m1_dec(e2m1_enc(x * rr)) * S) * G;
+          float dd = x - xh;
+          err = err + dd * dd;
+        }
+      if (kk == 0 || err < best_err) { best_err = err; best = (uint32_t)c; }
+    }
+    sbyte = best;
+    float S = e4m3_dec(best), sg = S * G;
+    r = (sg != 0.0f) ? 1.0f / sg : 0.0f;
+  } else {
+    int e0 = mx_exp(amax), best = e0;
+    float best_err = 0.0f;
+    const int deltas[3] = {0, 1, -1};
+    for (int kk = 0; kk < 3; kk++) {
+      int e = e0 + deltas[kk];
+      if (e < -127 || e > 127) continue;
+      float err = 0.0f;
+      for (int k = 0; k < B; k++)
+#pragma unroll
+        for (int cc = 0; cc < B; cc++) {
+          float x = xs[k][ct * B + cc];
+          float xh = ldexpf(e2m1_dec(e2m1_enc(ldexpf(x, -e))), e);
+          float dd = x - xh;
+          err = err + dd * dd;
+        }
+      if (kk == 0 || err < best_err) { best_err = err; best = e; }
+    }
+    sbyte = (uint32_t)(best + 127);
+    eb = best;
+  }
+  const long pbase = (long)sp.page * a.page_size;
+  for (int k = 0; k < B; k++) {
+    uint8_t *dst = a.k_codes + (pbase + sp.off0 + k) * (D / 2) + ct * (B / 2);
+#pragma unroll
+    for (int j = 0; j < B / 2; j += 4) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        float x = xs[k][ct * B + 2 * j + u];
+        uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
+        w |= q << (4 * u);
+      }
+      *(uint32_t *)(dst + j) = w;
+    }
+  }
+  a.k_scales[((long)sp.page * (a.page_size / B) + sp.off0 / B) * NT + ct] = (uint8_t)sbyte;
+}
+
+// ---------------------------------------------------------------------------------------------
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  if (a.attn == FP4KV_GQA) {
+    long n = (long)a.num_tokens * a.hkv;
+    dim3 gk((unsigned)((n + 127) / 128)), gv((unsigned)a.num_tokens, (unsigned)a.hkv);
+    if (a.fmt == kFmtNV) {
+      k_append_gqa<kFmtNV><<<gk, 128, 0, s>>>(a);
+      v_append_gqa<kFmtNV><<<gv, 128, 0, s>>>(a);
+    } else {
+      k_append_gqa<kFmtMX><<<gk, 128, 0, s>>>(a);
+      v_append_gqa<kFmtMX><<<gv, 128, 0, s>>>(a);
+    }
+  } else {
+    if (a.fmt == kFmtNV) latent_append<kFmtNV><<<a.num_tokens, 256, 0, s>>>(a);
+    else latent_append<kFmtMX><<<a.num_tokens, 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp4kv

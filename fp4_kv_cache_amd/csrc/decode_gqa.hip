@@ -1,0 +1,554 @@
+// Paged FP4 decode attention for GQA on gfx950: split-K partial kernel and merge kernel.
+//
+// Method ("BitDecoding-FP4: Native FP4 KV Cache Decoding via Algorithm-System
+// Co-Design", Article Summary; "BitDecoding-FP4 : décodage natif du KV cache
+// FP4", Analyse approfondie): the query is split into two FP4 tensors (the
+// second holds the residual of the first); the query rows of one KV head are
+// stacked so that one K/V tile load feeds all of them; the softmax is computed
+// transposed and its probabilities are quantized to FP4 in registers, scaled so
+// that E4M3 block scales keep long-context probabilities away from zero.
+//
+// Mapping onto CDNA4 (one wave = one workgroup = one (sequence, KV head, split)):
+//  * v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 operands: A = 16 tokens x 128
+//    channels of K (lane l: token row l%16, channels 32*(l/16)..+31), B = the
+//    stacked query rows, D lane l = column l%16, token rows 4*(l/16)..+3.
+//    Token row 4q+r of token group i is tile token 32q + 4i + r, so after the 8
+//    groups of a 128-token tile lane l holds 32 consecutive tokens
+//    (32*(l/16)..+31) of its column -- exactly the K-slice the P.V MFMA takes
+//    as its B operand.  The softmax works on this transposed layout and the
+//    probabilities never leave registers.
+//  * NVFP4 keys carry E4M3 block scales (16 channels) whose mantissa the
+//    E8M0-scaled MFMA cannot take.  Each MFMA therefore sees one 16-channel
+//    block per output column (query rows masked to one block), giving the exact
+//    block dot 2^eQ * sum(code_q * code_k); the key scale multiplies it in fp32
+//    and the 8 block terms are added in the fixed order ((T0+T2)+T4)+T6 +
+//    (((T1+T3)+T5)+T7) -- every term is exact, so the logit is reproducible bit
+//    for bit.  Columns: 8 * parity + stacked row (row = 2*head + {Q1, Q2}).
+//  * MXFP4 keys (32-channel E8M0 blocks = one lane group) use one native MFMA
+//    per 16 tokens with both scales in hardware.
+//  * Probabilities: NVFP4 with power-of-two block scales and tensor scale 2^-10
+//    over the tile-relative p = 2^(s - m_tile) (<= 1), converted with
+//    v_cvt_scalef32_pk_fp4_f32 (exact power-of-two scaling, RNE); MXFP4 with
+//    the MX exponent rule.
+//  * NVFP4 values: the E4M3 block scale S_V = sum_j bit_j 2^(E-j) is applied
+//    as up to four E8M0 passes (one per set bit; absent bits use scale byte 0,
+//    2^-127, which contributes nothing) and two parity passes (16-token
+//    blocks inside a 32-token lane group), accumulated in the MFMA.
+#include "fp4kv_device.h"
+#include "fp4kv_internal.h"
+
+namespace fp4kv {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int OPA, int OPB>
+__device__ __forceinline__ v4f mfma4(const v8i &a, const v8i &b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, OPA, sa, OPB, sb);
+}
+
+// lane l <- lane (l ^ 8) inside each row of 16 (row_ror:8)
+__device__ __forceinline__ float xlane8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+// lane l <- lane (l ^ 1) (quad_perm [1,0,3,2])
+__device__ __forceinline__ float xlane1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+// {x(l), x(l^16)} and {x(l), x(l^32)} pairs
+__device__ __forceinline__ float max_x16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Four E2M1 conversions of consecutive token pairs into one dword:
+// nibbles (x0[0..3], x1[0..3]) = tokens 4i..4i+3, 4i+4..4i+7, divided by the power of two `sc`.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_pk(uint32_t old, float a, float b, float sc) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, sc, SEL);
+}
+__device__ __forceinline__ uint32_t pack8(const float *x0, const float *x1, float sc) {
+  uint32_t w = 0u;
+  w = cvt_pk<0>(w, x0[0], x0[1], sc);
+  w = cvt_pk<1>(w, x0[2], x0[3], sc);
+  w = cvt_pk<2>(w, x1[0], x1[1], sc);
+  w = cvt_pk<3>(w, x1[2], x1[3], sc);
+  return w;
+}
+
+// Physical page of logical page lp of sequence b, clamped to the sequence's last page
+// (tokens past the end are masked, but their loads must stay inside the pool); a page
+// id outside the pool is clamped into it, so a bad table reads wrong data, not memory
+// outside the cache.
+__device__ __forceinline__ int phys_page(const DecodeArgs &a, int b, int lp, int last_lp) {
+  int pg = a.block_table[(long)b * a.max_pages + (lp < last_lp ? lp : last_lp)];
+  return pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+}
+
+template <int FMT, int G, int P>
+__global__ __launch_bounds__(64) void gqa_partials(DecodeArgs a) {
+  constexpr int D = 128;
+  constexpr int NR = 2 * G;                    // stacked rows: (head, Q1/Q2)
+  constexpr int B = FMT == kFmtNV ? 16 : 32;   // scale block
+  constexpr int NBLK = D / B;
+  static_assert(FMT == kFmtNV ? G <= 4 : G <= 8, "group too large for one 16-column MFMA");
+  static_assert(P >= 16 && (P % B) == 0, "page size");
+
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int L = a.seq_lens[b];
+  const int ntiles = (L + 127) >> 7;
+  const int tb = split * a.tiles_per_split;
+  const int te = min(ntiles, tb + a.tiles_per_split);
+  if (tb >= te) return;
+  const int last_lp = min((L - 1) / P, a.max_pages - 1);
+
+  __shared__ float qy[G][D];
+  __shared__ uint32_t qc[2][G][D / 8];
+  __shared__ int qe[2][G][NBLK];
+  __shared__ float qg[2][G];
+  __shared__ uint32_t lut[256];
+  __shared__ float4 sk[128 * 2];               // NVFP4 key scales of the tile: [token][parity] x 4 blocks
+
+  // ---------------- prologue: smoothing, rotation, dual-residual FP4 query ----------------
+  for (int e = lane; e < G * D; e += 64) {
+    int r = e / D, c = e % D;
+    long qi = ((long)b * a.hq + kvh * G + r) * D + c;
+    qy[r][c] = load_elem(a.q, qi, a.q_bf16) * a.qs[kvh * D + c];
+  }
+  __syncthreads();
+  for (int h = 1; h < D; h <<= 1) {
+    for (int e = lane; e < G * D / 2; e += 64) {
+      int r = e / (D / 2), w = e % (D / 2);
+      int i = (w / h) * 2 * h + (w % h);
+      float x0 = qy[r][i], x1 = qy[r][i + h];
+      qy[r][i] = x0 + x1;
+      qy[r][i + h] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  {
+    const bool act = lane < G * NBLK;
+    const int ur = act ? lane / NBLK : 0, ub = lane % NBLK;
+    float y[B];
+#pragma unroll
+    for (int i = 0; i < B; i++) y[i] = act ? qy[ur][ub * B + i] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      float bmax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < B; i++) bmax = fmaxf(bmax, fabsf(y[i]));
+      uint32_t w[B / 8];
+#pragma unroll
+      for (int i = 0; i < B / 8; i++) w[i] = 0u;
+      int e;
+      float gq = 1.0f;
+      if (FMT == kFmtNV) {
+        float rmax = bmax;
+#pragma unroll
+        for (int o = 1; o < NBLK; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
+        gq = rmax / 1536.0f;
+        const bool valid = bmax > 0.0f && gq > 0.0f;
+        const float sixg = 6.0f * gq;
+        const float inv6g = sixg != 0.0f ? 1.0f / sixg : 0.0f;
+        e = ceil_log2_clamp(bmax * inv6g, -9, 8);
+        const float S = pow2f(e);
+        const float sg = S * gq;
+        const float r = (valid && sg != 0.0f) ? 1.0f / sg : 0.0f;
+#pragma unroll
+        for (int i = 0; i < B; i++) {
+          uint32_t c = e2m1_enc(y[i] * r);
+          w[i / 8] |= c << (4 * (i % 8));
+          y[i] = y[i] - (e2m1_dec(c) * S) * gq;
+        }
+        if (!valid) e = -128;
+      } else {
+        e = mx_exp(bmax);
+#pragma unroll
+        for (int i = 0; i < B; i++) {
+          uint32_t c = e2m1_enc(ldexpf(y[i], -e));
+          w[i / 8] |= c << (4 * (i % 8));
+          y[i] = y[i] - ldexpf(e2m1_dec(c), e);
+        }
+      }
+      if (act) {
+#pragma unroll
+        for (int i = 0; i < B / 8; i++) qc[k][ur][ub * (B / 8) + i] = w[i];
+        qe[k][ur][ub] = e;
+        if (ub == 0) qg[k][ur] = gq;
+      }
+    }
+  }
+  // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale), for NVFP4 values
+  for (int c = lane; c < 256; c += 64) {
+    uint32_t w = 0u;
+    if (c < 0x7F) {
+      int ef = (c >> 3) & 15, m = c & 7;
+      int E = (ef ? ef : 1) - 7;
+      int bits[4] = {ef ? 1 : 0, (m >> 2) & 1, (m >> 1) & 1, m & 1};
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (bits[j]) w |= (uint32_t)(E - j + 127) << (8 * j);
+    }
+    lut[c] = w;
+  }
+  __syncthreads();
+
+  const int q4 = lane >> 4;        // lane group: channel block (A/B operands) or token group (D)
+  const int n = lane & 15;         // operand row / output column
+  // B operands (stacked query rows) and per-lane logit coefficients
+  v8i bq[FMT == kFmtNV ? 4 : 1];
+  int qsb = 127;
+  float a_own = 0.0f, a_nb = 0.0f;
+  {
+    const float gk = FMT == kFmtNV ? a.gk[kvh] : 1.0f;
+    const int r = FMT == kFmtNV ? (n & 7) : n;       // stacked row of this column
+    const int h = r >> 1, k = r & 1;
+    const bool live = r < NR;
+    if constexpr (FMT == kFmtNV) {
+      const int par = n >> 3;
+      const int blk = 2 * q4 + par;
+      uint32_t c0 = live ? qc[k][h][2 * blk] : 0u, c1 = live ? qc[k][h][2 * blk + 1] : 0u;
+      int e = live ? qe[k][h][blk] : -128;
+      qsb = e == -128 ? 127 : e + 127;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (j == q4) {
+          if (par == 0) { v[0] = (int)c0; v[1] = (int)c1; }
+          else { v[2] = (int)c0; v[3] = (int)c1; }
+        }
+        bq[j] = v;
+      }
+    } else {
+      v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) v[i] = (int)qc[k][h][4 * q4 + i];
+        qsb = qe[k][h][q4] + 127;
+      }
+      bq[0] = v;
+    }
+    if (live) {
+      a_own = (qg[k][h] * gk) * a.coef;
+      a_nb = (qg[1 - k][h] * gk) * a.coef;
+    }
+  }
+
+  // ---------------- main loop over 128-token tiles ----------------
+  const long head_pages = (long)a.hkv;          // pages are [page][hkv][...]
+  float m_run = -INFINITY, l_run = 0.0f;
+  v4f o_run[8];
+#pragma unroll
+  for (int cg = 0; cg < 8; cg++) o_run[cg] = v4f{0.f, 0.f, 0.f, 0.f};
+  int nzero = 0;
+  const float inv6gp = 1.0f / (6.0f * 0.0009765625f);   // fl32(1 / fl32(6 * 2^-10))
+
+  for (int tile = tb; tile < te; ++tile) {
+    const int tok0 = tile * 128;
+    // ---- key codes: lane row n -> tokens 32*(n/4) + 4i + n%4, channel block q4
+    uint4 kc[8];
+    int ksc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int t = tok0 + 32 * (n >> 2) + 4 * i + (n & 3);
+      const int pg = phys_page(a, b, t / P, last_lp);
+      const long row = ((long)pg * head_pages + kvh) * P + (t % P);
+      kc[i] = *(const uint4 *)(a.k_codes + row * 64 + 16 * q4);
+      if (FMT == kFmtMX) ksc[i] = a.k_scales[row * 4 + q4];
+    }
+    if (FMT == kFmtNV) {
+      // stage the tile's key scales, decoded, as [token][parity][j] = S(block 2j + parity)
+      const int t = tok0 + 2 * lane;
+      const int pg = phys_page(a, b, t / P, last_lp);
+      const long row = ((long)pg * head_pages + kvh) * P + (t % P);
+      uint4 raw = *(const uint4 *)(a.k_scales + row * 8);
+      uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        uint32_t lo = wv[2 * u], hi = wv[2 * u + 1];   // blocks 0..3 and 4..7 of token 2*lane+u
+        float4 ev, od;
+        ev.x = e4m3_dec(lo & 0xFF);          od.x = e4m3_dec((lo >> 8) & 0xFF);
+        ev.y = e4m3_dec((lo >> 16) & 0xFF);  od.y = e4m3_dec(lo >> 24);
+        ev.z = e4m3_dec(hi & 0xFF);          od.z = e4m3_dec((hi >> 8) & 0xFF);
+        ev.w = e4m3_dec((hi >> 16) & 0xFF);  od.w = e4m3_dec(hi >> 24);
+        sk[(2 * lane + u) * 2 + 0] = ev;
+        sk[(2 * lane + u) * 2 + 1] = od;
+      }
+    }
+    // ---- value codes and scales: lane row n -> channel 16*cg + n, tokens 32*q4 .. +31
+    uint4 vc[8];
+    uint32_t vsc[8];
+    {
+      const int t = tok0 + 32 * q4;
+#pragma unroll
+      for (int cg = 0; cg < 8; cg++) {
+        const int ch = 16 * cg + n;
+        if constexpr (P >= 32) {
+          const int pg = phys_page(a, b, t / P, last_lp);
+          const long row = ((long)pg * head_pages + kvh) * D + ch;
+          vc[cg] = *(const uint4 *)(a.v_codes + row * (P / 2) + (t % P) / 2);
+          if (FMT == kFmtNV) vsc[cg] = *(const uint16_t *)(a.v_scales + row * (P / 16) + (t % P) / 16);
+          else vsc[cg] = a.v_scales[row * (P / 32) + (t % P) / 32];
+        } else {  // P == 16: the 32 tokens span two pages
+          const int pg0 = phys_page(a, b, t / P, last_lp), pg1 = phys_page(a, b, t / P + 1, last_lp);
+          const long r0 = ((long)pg0 * head_pages + kvh) * D + ch, r1 = ((long)pg1 * head_pages + kvh) * D + ch;
+          uint2 c0 = *(const uint2 *)(a.v_codes + r0 * 8), c1 = *(const uint2 *)(a.v_codes + r1 * 8);
+          vc[cg] = uint4{c0.x, c0.y, c1.x, c1.y};
+          vsc[cg] = (uint32_t)a.v_scales[r0] | ((uint32_t)a.v_scales[r1] << 8);
+        }
+      }
+    }
+    if (FMT == kFmtNV) __syncthreads();
+
+    // ---- Q.K^T: raw logits for (column n, tokens 32*q4 + 4i + rr)
+    float s[8][4];
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const v8i av = {(int)kc[i].x, (int)kc[i].y, (int)kc[i].z, (int)kc[i].w, 0, 0, 0, 0};
+      if constexpr (FMT == kFmtNV) {
+        v4f o0 = mfma4<0, 0>(av, bq[0], zero, 127, qsb);
+        v4f o1 = mfma4<0, 0>(av, bq[1], zero, 127, qsb);
+        v4f o2 = mfma4<0, 0>(av, bq[2], zero, 127, qsb);
+        v4f o3 = mfma4<0, 0>(av, bq[3], zero, 127, qsb);
+        const int par = n >> 3;
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) {
+          const float4 S = sk[(32 * q4 + 4 * i + rr) * 2 + par];
+          float acc = o0[rr] * S.x;
+          acc = acc + o1[rr] * S.y;
+          acc = acc + o2[rr] * S.z;
+          acc = acc + o3[rr] * S.w;
+          s[i][rr] = acc;
+        }
+      } else {
+        v4f o = mfma4<0, 0>(av, bq[0], zero, ksc[i], qsb);
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) s[i][rr] = o[rr];
+      }
+    }
+    // combine parities (NVFP4), then Q1/Q2 rows: s = a1*raw1 + a2*raw2
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) {
+        float raw = s[i][rr];
+        if (FMT == kFmtNV) raw = raw + xlane8(raw);
+        float t1 = a_own * raw;
+        float t2 = a_nb * xlane1(raw);
+        s[i][rr] = t1 + t2;
+      }
+    // mask tokens past the end
+    if (tok0 + 128 > L) {
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++)
+          if (tok0 + 32 * q4 + 4 * i + rr >= L) s[i][rr] = -INFINITY;
+    }
+    // ---- transposed softmax over the tile
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) mt = fmaxf(mt, s[i][rr]);
+    mt = max_x32(max_x16(mt));
+    float lt = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) {
+        float p = __builtin_amdgcn_exp2f(s[i][rr] - mt);
+        s[i][rr] = p;
+        lt = lt + p;
+      }
+    // ---- fused probability quantization into the P.V B operand
+    uint32_t pk[4] = {0u, 0u, 0u, 0u};
+    int pbyte[2];
+    if (FMT == kFmtNV) {
+#pragma unroll
+      for (int pb = 0; pb < 2; pb++) {
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 4 * pb; i < 4 * pb + 4; i++)
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) am = fmaxf(am, s[i][rr]);
+        const int e = ceil_log2_clamp(am * inv6gp, -9, 8);
+        const float ps = pow2f(e - 10);
+        pbyte[pb] = e - 10 + 127;
+        pk[2 * pb] = pack8(s[4 * pb], s[4 * pb + 1], ps);
+        pk[2 * pb + 1] = pack8(s[4 * pb + 2], s[4 * pb + 3], ps);
+      }
+    } else {
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) am = fmaxf(am, s[i][rr]);
+      const int e = mx_exp(am);
+      const float ps = ldexpf(1.0f, e);
+      pbyte[0] = pbyte[1] = e + 127;
+#pragma unroll
+      for (int w = 0; w < 4; w++) pk[w] = pack8(s[2 * w], s[2 * w + 1], ps);
+    }
+    if (a.zero_blocks) {
+      const int r = FMT == kFmtNV ? (n & 7) : n;
+      const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (r & 1) == 0 && r < NR;
+      if (rep) {
+        if (FMT == kFmtNV) {
+#pragma unroll
+          for (int pb = 0; pb < 2; pb++)
+            if (tok0 + 32 * q4 + 16 * pb < L && ((pk[2 * pb] | pk[2 * pb + 1]) & 0x77777777u) == 0u) nzero++;
+        } else if (tok0 + 32 * q4 < L && ((pk[0] | pk[1] | pk[2] | pk[3]) & 0x77777777u) == 0u) {
+          nzero++;
+        }
+      }
+    }
+    // ---- online rescale
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float beta = __builtin_amdgcn_exp2f(mt - m_new);
+    l_run = l_run * alpha + lt * beta;
+    m_run = m_new;
+    // ---- P.V
+    v4f acc[8];
+#pragma unroll
+    for (int cg = 0; cg < 8; cg++) acc[cg] = zero;
+    if constexpr (FMT == kFmtNV) {
+      uint32_t vl[8][2];
+#pragma unroll
+      for (int cg = 0; cg < 8; cg++) {
+        vl[cg][0] = lut[vsc[cg] & 0xFF];
+        vl[cg][1] = lut[(vsc[cg] >> 8) & 0xFF];
+      }
+      const v8i p0 = {(int)pk[0], (int)pk[1], 0, 0, 0, 0, 0, 0};
+      const v8i p1 = {0, 0, (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+#pragma unroll
+      for (int cg = 0; cg < 8; cg++) {
+        const v8i av = {(int)vc[cg].x, (int)vc[cg].y, (int)vc[cg].z, (int)vc[cg].w, 0, 0, 0, 0};
+        acc[cg] = mfma4<0, 0>(av, p0, acc[cg], (int)vl[cg][0], pbyte[0]);
+        acc[cg] = mfma4<1, 0>(av, p0, acc[cg], (int)vl[cg][0], pbyte[0]);
+        acc[cg] = mfma4<2, 0>(av, p0, acc[cg], (int)vl[cg][0], pbyte[0]);
+        acc[cg] = mfma4<3, 0>(av, p0, acc[cg], (int)vl[cg][0], pbyte[0]);
+        acc[cg] = mfma4<0, 0>(av, p1, acc[cg], (int)vl[cg][1], pbyte[1]);
+        acc[cg] = mfma4<1, 0>(av, p1, acc[cg], (int)vl[cg][1], pbyte[1]);
+        acc[cg] = mfma4<2, 0>(av, p1, acc[cg], (int)vl[cg][1], pbyte[1]);
+        acc[cg] = mfma4<3, 0>(av, p1, acc[cg], (int)vl[cg][1], pbyte[1]);
+      }
+    } else {
+      const v8i pv = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+#pragma unroll
+      for (int cg = 0; cg < 8; cg++) {
+        const v8i av = {(int)vc[cg].x, (int)vc[cg].y, (int)vc[cg].z, (int)vc[cg].w, 0, 0, 0, 0};
+        acc[cg] = mfma4<0, 0>(av, pv, acc[cg], (int)vsc[cg], pbyte[0]);
+      }
+    }
+#pragma unroll
+    for (int cg = 0; cg < 8; cg++)
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = fmaf(o_run[cg][rr], alpha, acc[cg][rr] * beta);
+    if (FMT == kFmtNV) __syncthreads();   // key-scale stage is rewritten by the next tile
+  }
+
+  // ---------------- epilogue: split partials ----------------
+  const float l_tot = sum_x32(sum_x16(l_run));
+  const int r = FMT == kFmtNV ? (n & 7) : n;
+  const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (r & 1) == 0 && r < NR;
+  if (rep) {
+    const int head = kvh * G + (r >> 1);
+    const long rowi = ((long)b * a.hq + head) * a.n_split + split;
+    const float gv = FMT == kFmtNV ? a.gv[kvh] : 1.0f;
+#pragma unroll
+    for (int cg = 0; cg < 8; cg++) {
+      float4 v = {o_run[cg][0] * gv, o_run[cg][1] * gv, o_run[cg][2] * gv, o_run[cg][3] * gv};
+      *(float4 *)(a.ws_o + rowi * D + 16 * cg + 4 * q4) = v;
+    }
+    if (q4 == 0) *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run, l_tot};
+  }
+  if (a.zero_blocks) {
+    int z = nzero;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
+    if (lane == 0 && z) atomicAdd(a.zero_blocks, z);
+  }
+}
+
+// One wave per (sequence, query head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+__global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const int b = row / a.hq;
+  const int L = a.seq_lens[b];
+  const int ntiles = (L + 127) >> 7;
+  const int nv = min((ntiles + a.tiles_per_split - 1) / a.tiles_per_split, a.n_split);
+  float2 *dst = (float2 *)(a.out + (long)row * 128) + lane;
+  if (nv == 0) { *dst = float2{0.f, 0.f}; return; }
+  const float *ml = a.ws_ml + (long)row * a.n_split * 2;
+  const float *o = a.ws_o + (long)row * a.n_split * 128;
+  float M = -INFINITY;
+  for (int s = 0; s < nv; s++) M = fmaxf(M, ml[2 * s]);
+  float den = 0.f, n0 = 0.f, n1 = 0.f;
+  for (int s = 0; s < nv; s++) {
+    const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+    const float2 v = *((const float2 *)(o + (long)s * 128) + lane);
+    den = fmaf(w, ml[2 * s + 1], den);
+    n0 = fmaf(w, v.x, n0);
+    n1 = fmaf(w, v.y, n1);
+  }
+  *dst = float2{n0 / den, n1 / den};
+}
+
+template <int FMT, int G>
+static hipError_t launch_g(const DecodeArgs &a, dim3 grid, hipStream_t s) {
+  switch (a.page_size) {
+    case 16:
+      if constexpr (FMT == kFmtNV) { gqa_partials<FMT, G, 16><<<grid, 64, 0, s>>>(a); break; }
+      return hipErrorInvalidValue;
+    case 32: gqa_partials<FMT, G, 32><<<grid, 64, 0, s>>>(a); break;
+    case 64: gqa_partials<FMT, G, 64><<<grid, 64, 0, s>>>(a); break;
+    case 128: gqa_partials<FMT, G, 128><<<grid, 64, 0, s>>>(a); break;
+    case 256: gqa_partials<FMT, G, 256><<<grid, 64, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  dim3 grid((unsigned)a.n_split, (unsigned)a.hkv, (unsigned)a.batch);
+  if (a.fmt == kFmtNV) {
+    switch (a.group) {
+      case 1: return launch_g<kFmtNV, 1>(a, grid, s);
+      case 2: return launch_g<kFmtNV, 2>(a, grid, s);
+      case 4: return launch_g<kFmtNV, 4>(a, grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (a.group) {
+    case 1: return launch_g<kFmtMX, 1>(a, grid, s);
+    case 2: return launch_g<kFmtMX, 2>(a, grid, s);
+    case 4: return launch_g<kFmtMX, 4>(a, grid, s);
+    case 8: return launch_g<kFmtMX, 8>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  gqa_merge<<<(unsigned)(a.batch * a.hq), 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace fp4kv

@@ -1,0 +1,91 @@
+// Device-side scalar codecs and helpers shared by the gfx950 kernels.
+//
+// Formats: E2M1 elements and E8M0 scales as in the OCP Microscaling (MX) v1.0
+// specification, E4M3 ("FN") scales as in the OCP 8-bit floating point
+// specification; NVFP4 = 16-element blocks with an E4M3 scale and an fp32
+// tensor scale.  Every quantization decision below is taken with single IEEE
+// binary32 operations in a fixed order (the library is built with
+// -ffp-contract=off), so that codes and scales are reproducible bit for bit.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4kv {
+
+constexpr int kFmtNV = 0;
+constexpr int kFmtMX = 1;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Load element i of an fp32 or bf16 array as fp32 (bf16 -> fp32 is exact).
+__device__ __forceinline__ float load_elem(const void *p, long i, int bf16) {
+  return bf16 ? bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
+}
+
+// E2M1 code of y: round to nearest, ties to the even code, saturating at 6; the
+// sign is y's sign bit (so -0.0 gives 8).  Each threshold is a midpoint of two
+// neighbouring grid points; '>' sends a tie down, '>=' sends it up, chosen so the
+// tie lands on the even code.
+__device__ __forceinline__ uint32_t e2m1_enc(float y) {
+  float a = fabsf(y);
+  uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+  return idx | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// Value of an E2M1 code (exact).
+__device__ __forceinline__ float e2m1_dec(uint32_t c) {
+  uint32_t m = c & 7u;
+  // magnitude bits: m >= 2 -> (1 + (m&1)/2) * 2^((m>>1)-1); m == 1 -> 0.5; m == 0 -> 0
+  uint32_t bits = (m >= 2u) ? (((126u + (m >> 1)) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
+  return __uint_as_float(bits | ((c & 8u) << 28));
+}
+
+// E4M3 byte -> fp32 (exact).  0x7F / 0xFF decode to NaN.
+__device__ __forceinline__ float e4m3_dec(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);
+  return (c & 0x80u) ? -v : v;
+}
+
+// Non-negative fp32 -> E4M3 byte, round to nearest with ties to the even code,
+// saturating at 448 (code 0x7E, so the NaN pattern is never produced).
+__device__ __forceinline__ uint32_t e4m3_enc_sat(float t) {
+  if (!(t < 448.0f)) return 0x7Eu;
+  if (t < 0.015625f) return (uint32_t)rintf(t * 512.0f);  // multiples of 2^-9; 8 is code 0x08
+  int e = (int)((__float_as_uint(t) >> 23) & 0xFFu) - 127;
+  uint32_t q = (uint32_t)rintf(ldexpf(t, 3 - e));           // in [8, 16]
+  if (q == 16u) { e += 1; q = 8u; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | (q - 8u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E4M3 byte of 2^e for e in [-9, 8].
+__device__ __forceinline__ uint32_t e4m3_pow2_code(int e) {
+  return e >= -6 ? (uint32_t)(e + 7) << 3 : (1u << (e + 9));
+}
+
+// ceil(log2 t) for t > 0 finite or +inf, clamped to [lo, hi]; t == 0 gives lo.
+__device__ __forceinline__ int ceil_log2_clamp(float t, int lo, int hi) {
+  uint32_t b = __float_as_uint(t);
+  uint32_t ef = (b >> 23) & 0xFFu;
+  if (ef == 0u) return lo;                       // zero or subnormal: below 2^-126
+  int e = (int)ef - 127 + ((b & 0x7FFFFFu) ? 1 : 0);
+  return e < lo ? lo : (e > hi ? hi : e);
+}
+
+// MX shared exponent floor(log2 amax) - 2, clamped to [-127, 127]; amax == 0 (or
+// subnormal, whose floor(log2) is below -126) gives -127.
+__device__ __forceinline__ int mx_exp(float amax) {
+  uint32_t ef = (__float_as_uint(amax) >> 23) & 0xFFu;
+  if (ef == 0u) return -127;
+  int e = (int)ef - 127 - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^e as fp32 for e in [-126, 127].
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+}  // namespace fp4kv

@@ -1,0 +1,87 @@
+"""Build a prefilled paged FP4 cache for a synthetic workload on the GPU.
+
+Host plumbing only: draws the workload's inputs (``workloads``), moves them to
+the device with torch and feeds them through the library's ``kv_quant_append``;
+all quantization happens in the HIP kernels.
+"""
+import numpy as np
+
+from . import workloads as W
+from .lib import PagedFP4Cache, GQA, MLA
+
+
+def _dev(x, w, torch, device):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if w["dtype"] == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.to(device)
+
+
+class Built:
+    """A prefilled cache with the workload's page table, lengths and calibration."""
+
+    def __init__(self, w, cache, bt, lens, calib, device):
+        import torch
+        self.w, self.cache, self.lens, self.calib = w, cache, lens, calib
+        self.bt_np = bt
+        self.bt = torch.from_numpy(bt).to(device)
+        self.seq_lens = torch.from_numpy(lens.astype(np.int32)).to(device)
+        self.device = device
+
+    def queries(self):
+        import torch
+        q = np.stack([W.queries(self.w, b) for b in range(self.w["batch"])])
+        if self.w["attn"] == MLA:
+            qr = np.stack([W.rope_queries(self.w, b) for b in range(self.w["batch"])])
+            q = np.concatenate([q, qr], axis=-1)
+        return _dev(q, self.w, torch, self.device)
+
+
+def slots_for(bt_row, positions, P):
+    positions = np.asarray(positions, np.int64)
+    return (bt_row[positions // P].astype(np.int64) * P + positions % P).astype(np.int32)
+
+
+def build(w, lens=None, copy=0, device="cuda", seqs_per_call=None, stop=None, workers=8):
+    """Allocate the cache for workload ``w`` and append every sequence's context.
+
+    ``stop`` (optional int array) appends only the first stop[b] tokens of each
+    sequence; the rest can be appended later with ``append_range``.
+    """
+    import torch
+    lens = W.seq_lens(w) if lens is None else np.asarray(lens, np.int32)
+    bt, num_pages = W.page_table(w, lens, copy)
+    ksi, qs, gk, gv = W.calibration(w)
+    attn = w["attn"]
+    cache = PagedFP4Cache(w["fmt"], attn, num_pages, w["page"], w["hkv"], w["d"], w["batch"],
+                          ksi, qs, gk if w["fmt"] == 0 else None,
+                          gv if (w["fmt"] == 0 and attn == GQA) else None,
+                          rope_dim=w["rope"], device=device)
+    built = Built(w, cache, bt, lens, (ksi, qs, gk, gv), device)
+    stop = lens if stop is None else np.asarray(stop)
+    for b in range(w["batch"]):
+        append_range(built, b, 0, int(stop[b]), workers=workers)
+    return built
+
+
+def append_range(built, b, start, end, workers=8):
+    """Append positions [start, end) of sequence b in one kv_quant_append call."""
+    import torch
+    w, cache, dev = built.w, built.cache, built.device
+    n = end - start
+    if n <= 0:
+        return
+    pos = np.arange(start, end, dtype=np.int32)
+    slots = slots_for(built.bt_np[b], pos, w["page"])
+    if w["attn"] == GQA:
+        ks = W.parallel_map(lambda h: W.keys(w, b, h, end)[start:end], range(w["hkv"]), workers)
+        vs = W.parallel_map(lambda h: W.values(w, b, h, end)[start:end], range(w["hkv"]), workers)
+        k = _dev(np.stack(ks, axis=1), w, torch, dev)
+        v = _dev(np.stack(vs, axis=1), w, torch, dev)
+        kr = None
+    else:
+        k = _dev(W.keys(w, b, 0, end)[start:end][:, None, :], w, torch, dev)
+        v = None
+        kr = torch.from_numpy(W.bf16_bits(W.rope_keys(w, b, end)[start:end]).view(np.int16)).to(dev)
+    cache.append(k, v, torch.from_numpy(slots).to(dev), torch.full((n,), b, dtype=torch.int32, device=dev),
+                 torch.from_numpy(pos).to(dev), kr)

@@ -7,7 +7,8 @@ attention arithmetic.  It needs numpy, not torch.
 
 Every tensor chunk is drawn from its own counter-based stream,
 ``Philox(SeedSequence([workload id, tensor id, seq, head]))``, so any
-(sequence, head) slice can be regenerated on its own, in any order.
+(sequence, head) slice can be regenerated on its own, in any order, and the
+first n tokens of a sequence do not depend on how many tokens are drawn.
 
 Workloads (shapes of Qwen3-4B, Qwen3-30B-A3B and an MLA model; the pages'
 serving runs used those models, and their evaluation data is not available,
@@ -53,7 +54,7 @@ WORKLOADS = {
                 n_outliers=10, k_std=1.0, lognormal=0.0),
 }
 
-T_Q, T_K, T_V, T_KROPE, T_QROPE, T_LEN, T_PAGES, T_OUTL = range(1, 9)
+T_Q, T_K, T_V, T_KROPE, T_QROPE, T_LEN, T_PAGES, T_OUTL, T_KMAG, T_VMAG = range(1, 11)
 
 
 def workload(name, **over):
@@ -124,10 +125,9 @@ def outlier_channels(w, h):
 
 def keys(w, b, h, L):
     """K[b, :L, h, :] as float32 (bf16-rounded for bf16 workloads).  For MLA: the latent."""
-    r = _rng(w, T_K, b, h)
-    k = r.standard_normal((L, w["d"]), dtype=np.float32) * np.float32(w["k_std"])
+    k = _rng(w, T_K, b, h).standard_normal((L, w["d"]), dtype=np.float32) * np.float32(w["k_std"])
     if w["lognormal"]:
-        k *= np.exp(r.normal(0.0, w["lognormal"], size=(L, 1))).astype(np.float32)
+        k *= np.exp(_rng(w, T_KMAG, b, h).normal(0.0, w["lognormal"], size=(L, 1))).astype(np.float32)
     ch = outlier_channels(w, h)
     if len(ch):
         k[:, ch] *= np.float32(w["outlier_scale"])
@@ -135,10 +135,9 @@ def keys(w, b, h, L):
 
 
 def values(w, b, h, L):
-    r = _rng(w, T_V, b, h)
-    v = r.standard_normal((L, w["d"]), dtype=np.float32)
+    v = _rng(w, T_V, b, h).standard_normal((L, w["d"]), dtype=np.float32)
     if w["lognormal"]:
-        v *= np.exp(r.normal(0.0, w["lognormal"], size=(L, 1))).astype(np.float32)
+        v *= np.exp(_rng(w, T_VMAG, b, h).normal(0.0, w["lognormal"], size=(L, 1))).astype(np.float32)
     return _cast(w, v)
 
 

@@ -1,0 +1,198 @@
+/*
+ * fp4kv.h -- C ABI of libfp4kv.so: a paged 4-bit microscaling KV cache and
+ * decode attention over it, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is the hot path of BitDecoding-FP4 as described in
+ * "BitDecoding-FP4: Native FP4 KV Cache Decoding via Algorithm-System Co-Design"
+ * (section "Article Summary", the arXiv abstract):
+ *   - keys are stored after static per-channel smoothing, a Hadamard rotation
+ *     over head_dim and a per-block scale search under token-wise scaling
+ *     (Outlier-Aware Key Quantization);
+ *   - the query is split into two FP4 tensors, the second encoding the
+ *     residual of the first (Dual-Residual Query Quantization);
+ *   - probabilities are quantized to FP4 inside a transposed softmax, scaled so
+ *     that their E4M3 block scales do not round long-context probabilities to
+ *     zero (Underflow-Aware Probability Scaling);
+ *   - the query rows that share a KV head are stacked into one matrix-core
+ *     operation over the paged cache ("stacked query MMA").
+ * The cache formats are NVFP4 (16-element blocks, E4M3 block scale, fp32
+ * tensor scale) and MXFP4 (32-element blocks, E8M0 block scale).
+ *
+ * Conventions for every entry point
+ *   - All pointers are DEVICE pointers unless a parameter says "host".  The
+ *     caller owns every buffer; the library never allocates, frees or
+ *     synchronizes.  Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and runs asynchronously.
+ *   - Return value: FP4KV_OK (0) or an FP4KV_ERR_* code.  Arguments are checked
+ *     on the host before anything is launched; on an error nothing is enqueued.
+ *     fp4kv_status_string() describes a code.
+ *   - Device-side contents that break a documented precondition (page ids out
+ *     of range, unsorted append batches) are not detected: the result is
+ *     undefined, except that append slots and sequence ids outside their
+ *     ranges are skipped.
+ *
+ * Cache layout (P = page_size tokens, B = 16 for NVFP4 and 32 for MXFP4, a
+ * physical page holds P consecutive tokens of one sequence; sequence s's
+ * logical page i is block_table[s * max_pages_per_seq + i]; a token's slot is
+ * page * P + (position % P)):
+ *   GQA (attn = FP4KV_GQA, head_dim d = 128):
+ *     k_codes  u8 [num_pages][Hkv][P][d/2]  token-major; byte j holds channel 2j
+ *                                            (low nibble) and 2j+1 (high nibble)
+ *     k_scales u8 [num_pages][Hkv][P][d/B]  per (token, B-channel block)
+ *     v_codes  u8 [num_pages][Hkv][d][P/2]  channel-major; byte j holds tokens
+ *                                            2j (low) and 2j+1 (high) of the page
+ *     v_scales u8 [num_pages][Hkv][d][P/B]  per (channel, B-token block)
+ *     stage    f32 [max_seqs][Hkv][B][d]    unquantized values of each sequence's
+ *                                            last, partly filled value block
+ *   MLA (attn = FP4KV_MLA, one latent head, head_dim = 512, rope_dim = 64):
+ *     k_codes  u8 [num_pages][1][P][256]    rotated latent, token-major
+ *     k_scales u8 [num_pages][1][P/B][512/B] one scale per B-token x B-channel tile
+ *     k_rope   bf16 [num_pages][1][P][64]   rope key, unquantized
+ *     stage    f32 [max_seqs][1][B][512]    rotated latent of the partial tile
+ *     v_codes, v_scales unused (the latent serves as key and value).
+ *   Codes are E2M1 (bit 3 sign, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6); NVFP4
+ *   scales are E4M3 (OCP "FN"), MXFP4 scales E8M0.  A partially filled value
+ *   block (or MLA tile) is stored as if its absent tokens were +0.0.
+ */
+#ifndef FP4KV_H
+#define FP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fp4kv_format { FP4KV_NVFP4 = 0, FP4KV_MXFP4 = 1 };
+enum fp4kv_dtype { FP4KV_F32 = 0, FP4KV_BF16 = 1 };
+enum fp4kv_attn { FP4KV_GQA = 0, FP4KV_MLA = 1 };
+
+enum fp4kv_status {
+  FP4KV_OK = 0,
+  FP4KV_ERR_INVALID_ARG = 1,      /* null pointer, bad size, bad enum value         */
+  FP4KV_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head_dim, GQA group) */
+  FP4KV_ERR_WORKSPACE = 3,        /* workspace smaller than fp4_decode_workspace_bytes */
+  FP4KV_ERR_HIP = 4               /* a HIP launch failed                              */
+};
+
+/* Cache descriptor.  Plain data; the library keeps no reference to it after a
+ * call returns.  Pointers are device pointers owned by the caller and sized as
+ * fp4kv_cache_layout() reports.
+ *   format        FP4KV_NVFP4 or FP4KV_MXFP4
+ *   attn          FP4KV_GQA or FP4KV_MLA
+ *   num_pages     physical pages in the pool (> 0)
+ *   page_size     tokens per page; a multiple of 16 (NVFP4) or 32 (MXFP4), <= 256
+ *   num_kv_heads  Hkv (GQA); must be 1 for MLA
+ *   head_dim      128 (GQA) or 512 (MLA latent)
+ *   rope_dim      0 (GQA) or 64 (MLA)
+ *   max_seqs      rows of the stage buffer; append seq_ids are < max_seqs
+ *   k_tensor_scale, v_tensor_scale  f32 [Hkv]: NVFP4 per-KV-head tensor scales G
+ *                 (decoded value = code * block_scale * G); ignored for MXFP4
+ *                 (may be NULL); v_tensor_scale unused for MLA
+ *   k_smooth_inv  f32 [Hkv][head_dim]: static smoothing applied to keys
+ *   q_smooth      f32 [Hkv][head_dim]: the matching factors applied to queries;
+ *                 the caller keeps q_smooth * k_smooth_inv == 1 per channel   */
+typedef struct fp4kv_cache {
+  int32_t format;
+  int32_t attn;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t rope_dim;
+  int32_t max_seqs;
+  uint8_t *k_codes;
+  uint8_t *k_scales;
+  uint8_t *v_codes;
+  uint8_t *v_scales;
+  float *stage;
+  uint16_t *k_rope;
+  const float *k_tensor_scale;
+  const float *v_tensor_scale;
+  const float *k_smooth_inv;
+  const float *q_smooth;
+} fp4kv_cache;
+
+/* Byte sizes of the six cache buffers for descriptor `c` (host pointer), in the
+ * order k_codes, k_scales, v_codes, v_scales, stage, k_rope (0 for unused ones).
+ * Only the scalar fields of `c` are read.  bytes_out is a host array of 6. */
+int fp4kv_cache_layout(const fp4kv_cache *c, size_t bytes_out[6]);
+
+/* Append new tokens to the cache: the KV-append quantizer.
+ *   k_new   [num_tokens][Hkv][head_dim] keys (MLA: the latent), dtype F32 or BF16
+ *   v_new   [num_tokens][Hkv][head_dim] values (GQA); NULL for MLA
+ *   k_rope_new  bf16 [num_tokens][rope_dim] (MLA), NULL for GQA
+ *   slot_mapping, seq_ids, positions  i32 [num_tokens]: destination slot,
+ *           sequence (stage row) and position of every new token.
+ * Preconditions (not checked on the device): inside one call the tokens of a
+ * sequence are contiguous in the batch, in increasing and consecutive
+ * positions, and the first of them continues that sequence (its position is
+ * the number of tokens the cache already holds for it); a token's slot lies in
+ * the page that block_table assigns to its position.  Calls on one stream are
+ * applied in order.  Keys: smoothing, FWHT over head_dim, per-block scale
+ * search, E2M1 packing.  Values: channel-wise scales over page-aligned blocks
+ * of B tokens; the block holding the last new token of a sequence is
+ * re-quantized from the stage on every call, so the bytes equal those of
+ * quantizing the whole sequence at once.  num_tokens == 0 is a no-op. */
+int kv_quant_append(const fp4kv_cache *c, const void *k_new, const void *v_new, int dtype,
+                    int num_tokens, const int32_t *slot_mapping, const int32_t *seq_ids,
+                    const int32_t *positions, const void *k_rope_new, void *stream);
+
+/* Workspace bytes fp4_decode_attention / fp4_decode_partials need for this
+ * batch shape (host function; reads only scalar fields of `c`).  max_seq_len is
+ * an upper bound of seq_lens (max_pages_per_seq * page_size is always valid).
+ * Returns 0 on invalid arguments. */
+size_t fp4_decode_workspace_bytes(const fp4kv_cache *c, int batch, int num_q_heads,
+                                  int max_seq_len);
+
+/* Decode attention: one query token per sequence against its whole cached context.
+ *   q          [batch][num_q_heads][head_dim (+ rope_dim for MLA)], dtype q_dtype
+ *   block_table i32 [batch][max_pages_per_seq]; seq_lens i32 [batch] (0 allowed,
+ *              giving a zero output row); entries past a sequence's pages are
+ *              never read
+ *   softmax_scale  multiplies q.k (the 1/head_dim of the unnormalized Hadamard
+ *              rotation is applied internally)
+ *   out        f32 [batch][num_q_heads][head_dim] (MLA: the 512-d latent
+ *              output, un-rotated and un-smoothed)
+ *   workspace  device scratch of at least fp4_decode_workspace_bytes(); its
+ *              contents need no initialisation and are overwritten
+ *   zero_block_count  nullable i32 counter; when given, the number of
+ *              probability blocks that held a valid token and quantized to all
+ *              zeros is ADDED to it (the caller zeroes it)
+ * GQA needs num_q_heads == group * Hkv with group <= 4 (NVFP4) or <= 8 (MXFP4).
+ * Launches the split-K partial kernel and the merge kernel on `stream`. */
+int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int batch,
+                         int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
+                         const int32_t *seq_lens, float softmax_scale, float *out,
+                         void *workspace, size_t workspace_bytes, int32_t *zero_block_count,
+                         void *stream);
+
+/* The two halves of fp4_decode_attention, for callers that merge split-K
+ * partials themselves (e.g. across devices holding different pages of one
+ * sequence) or time the stages separately.  fp4_decode_partials writes, for
+ * every (sequence, query head, split), the unnormalized output o, the running
+ * base-2 maximum m and the denominator l into the workspace; fp4_decode_merge
+ * combines them: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  Both
+ * take the same arguments as fp4_decode_attention and must see the same batch
+ * shape and seq_lens. */
+int fp4_decode_partials(const fp4kv_cache *c, const void *q, int q_dtype, int batch,
+                        int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
+                        const int32_t *seq_lens, float softmax_scale, void *workspace,
+                        size_t workspace_bytes, int32_t *zero_block_count, void *stream);
+int fp4_decode_merge(const fp4kv_cache *c, int batch, int num_q_heads, int max_pages_per_seq,
+                     const int32_t *seq_lens, float *out, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Measurement helper: reads `bytes` (a multiple of 4096) from `src` and writes
+ * one word per workgroup to `sink` (>= 4096 words), to measure the achievable
+ * HBM read bandwidth next to the decode kernel. */
+int fp4kv_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *fp4kv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4KV_H */

@@ -23,8 +23,14 @@ Readings:
          scale when all its p~ are below 2^-19 of the tile maximum.
 * R3     The softmax denominator sums the unquantized fp32 p~.
 * R11    Logits work in base 2: s = fl32(fl32(a1*raw1) + fl32(a2*raw2)) with
-         raw_k = fl32(<q^_k, k^>) (exact dot of the block-scaled values,
-         rounded once), a_k = fl32(fl32(G_Qk * G_K) * c), and
+         a_k = fl32(fl32(G_Qk * G_K) * c) and raw_k the block-scaled dot
+         <q^_k, k^> formed as follows.  NVFP4: each 16-channel block b gives the
+         exact term T_b = S_K[b] * 2^eQ[b] * sum_i code_q * code_k (at most 17
+         significant bits), and the 8 terms of a 128-channel chunk are added in
+         fp32 in the order E = ((T0 + T2) + T4) + T6, O = ((T1 + T3) + T5) + T7,
+         raw = E + O; several chunks (MLA) are added in chunk order.  MXFP4: the
+         exact sum over the 32-channel blocks rounded once to fp32.  The order
+         is the kernel's; each term is exact, so only those adds round.
          c = fl32(softmax_scale * fl32(log2(e) / n)), n = head_dim when the
          rotation is on (1 otherwise).  MLA adds fl32(c_r * raw_rope) with
          c_r = fl32(softmax_scale * fl32(log2 e)).
@@ -97,8 +103,12 @@ def logits(qq, khat, G_K, cs, fmt, rope=None):
     ``rope`` = (q_rope [R, r], k_rope [L, r], c_r) adds the unquantized MLA rope term.
     """
     gk = F32(G_K) if fmt == NVFP4 else F32(1.0)
-    raw1 = (qq.dequant_exact(1) @ khat.T).astype(F32)
-    raw2 = (qq.dequant_exact(2) @ khat.T).astype(F32)
+    if fmt == NVFP4:
+        raw1 = _nv_block_ordered_dot(qq.dequant_exact(1), khat)
+        raw2 = _nv_block_ordered_dot(qq.dequant_exact(2), khat)
+    else:
+        raw1 = (qq.dequant_exact(1) @ khat.T).astype(F32)
+        raw2 = (qq.dequant_exact(2) @ khat.T).astype(F32)
     a1 = ((qq.G1.astype(F32) * gk).astype(F32) * cs).astype(F32)
     a2 = ((qq.G2.astype(F32) * gk).astype(F32) * cs).astype(F32)
     s = ((a1[:, None] * raw1).astype(F32) + (a2[:, None] * raw2).astype(F32)).astype(F32)
@@ -107,6 +117,25 @@ def logits(qq, khat, G_K, cs, fmt, rope=None):
         rawr = (np.asarray(qr, np.float64) @ np.asarray(kr, np.float64).T).astype(F32)
         s = (s + (F32(cr) * rawr).astype(F32)).astype(F32)
     return s
+
+
+def _nv_block_ordered_dot(qhat, khat):
+    """raw [R, L] for NVFP4: exact per-16-channel-block terms summed in the fixed order of R11.
+
+    qhat [R, D], khat [L, D] are exact block-scaled values (float64); every
+    block term is exact in float32, so it is formed in float64 and cast.
+    """
+    R, D = qhat.shape
+    nb = D // 16
+    T = np.einsum("rbi,lbi->rlb", qhat.reshape(R, nb, 16), khat.reshape(-1, nb, 16)).astype(F32)
+    raw = None
+    for c in range(nb // 8):
+        t = T[..., 8 * c: 8 * c + 8]
+        even = (((t[..., 0] + t[..., 2]).astype(F32) + t[..., 4]).astype(F32) + t[..., 6]).astype(F32)
+        odd = (((t[..., 1] + t[..., 3]).astype(F32) + t[..., 5]).astype(F32) + t[..., 7]).astype(F32)
+        chunk = (even + odd).astype(F32)
+        raw = chunk if raw is None else (raw + chunk).astype(F32)
+    return raw
 
 
 def quantize_probs(pt, fmt, mode="tile"):

@@ -1,0 +1,100 @@
+"""Helpers shared by the GPU parity tests: run the HIP path, run the oracle, compare."""
+import sys
+
+import numpy as np
+
+from fp4_kv_cache_amd import workloads as W
+from fp4_kv_cache_amd import harness
+from oracle import attention as A
+from oracle import kvquant as KQ
+from oracle import layout as LY
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def cache_np(built):
+    return {k: v.cpu().numpy() for k, v in built.cache.views().items()}
+
+
+def check_gqa_cache(built, seqs=None):
+    """Cache bytes of the given sequences == the oracle's one-shot quantization (bit exact)."""
+    w = built.w
+    ksi, qs, gk, gv = built.calib
+    views = cache_np(built)
+    seqs = range(w["batch"]) if seqs is None else seqs
+    for b in seqs:
+        L = int(built.lens[b])
+        for h in range(w["hkv"]):
+            kc, ks, vc, vs = LY.gather_gqa(views, h, built.bt_np[b], L, w["fmt"])
+            okc, oks = KQ.quantize_keys(W.keys(w, b, h, L), ksi[h], gk[h], w["fmt"])
+            ovc, ovs = KQ.quantize_values(W.values(w, b, h, L), gv[h], w["fmt"])
+            for name, got, exp in (("k_codes", kc, okc), ("k_scales", ks, oks),
+                                   ("v_codes", vc, ovc), ("v_scales", vs, ovs)):
+                if not np.array_equal(got, exp):
+                    bad = np.argwhere(got != exp)
+                    raise AssertionError("seq %d head %d %s: %d mismatches, first at %s (got %s want %s)"
+                                         % (b, h, name, len(bad), bad[0].tolist(), got[tuple(bad[0])],
+                                            exp[tuple(bad[0])]))
+
+
+def check_mla_cache(built, seqs=None):
+    w = built.w
+    ksi, qs, gk, gv = built.calib
+    views = cache_np(built)
+    seqs = range(w["batch"]) if seqs is None else seqs
+    for b in seqs:
+        L = int(built.lens[b])
+        lc, ls, kr = LY.gather_mla(views, built.bt_np[b], L, w["fmt"])
+        olc, ols, _ = KQ.quantize_latent(W.keys(w, b, 0, L), ksi[0], gk[0], w["fmt"])
+        okr = W.bf16_bits(W.rope_keys(w, b, L))
+        for name, got, exp in (("latent codes", lc, olc), ("tile scales", ls, ols),
+                               ("rope", kr.view(np.uint16), okr)):
+            if not np.array_equal(got, exp):
+                bad = np.argwhere(got != exp)
+                raise AssertionError("seq %d %s: %d mismatches, first at %s" % (b, name, len(bad),
+                                                                               bad[0].tolist()))
+
+
+def gqa_oracle(built, b, kvh, qn, opts=None):
+    w = built.w
+    ksi, qs, gk, gv = built.calib
+    g = w["hq"] // w["hkv"]
+    L = int(built.lens[b])
+    rows = qn[b, kvh * g:(kvh + 1) * g]
+    K = W.keys(w, b, kvh, L)
+    V = W.values(w, b, kvh, L)
+    res = A.gqa_head(rows, K, V, ksi[kvh], qs[kvh], gk[kvh], gv[kvh], w["fmt"], W.softmax_scale(w),
+                     L=L, opts=opts)
+    res["ref"] = A.reference_attention(rows, K, V, W.softmax_scale(w)) if L else np.zeros_like(res["out"])
+    return res
+
+
+def run_decode(built, zero=True):
+    import torch
+    q = built.queries()
+    zc = torch.zeros(1, dtype=torch.int32, device=built.device) if zero else None
+    out = built.cache.decode(q, built.bt, built.seq_lens, W.softmax_scale(built.w), zero_block_count=zc)
+    torch.cuda.synchronize()
+    return q.float().cpu().numpy(), out.cpu().numpy(), (int(zc.item()) if zero else None)
+
+
+def compare_gqa(built, pairs=None, tol=1e-3):
+    """GPU decode vs oracle on (seq, kv-head) pairs; returns (max err, max err vs fp64, zero counts)."""
+    w = built.w
+    g = w["hq"] // w["hkv"]
+    qn, out, zgpu = run_decode(built)
+    pairs = [(b, h) for b in range(w["batch"]) for h in range(w["hkv"])] if pairs is None else pairs
+    worst, worst_ref, zor = 0.0, 0.0, 0
+    for b, h in pairs:
+        res = gqa_oracle(built, b, h, qn)
+        got = out[b, h * g:(h + 1) * g]
+        e = float(np.max(A.row_rel_err(got, res["out"]))) if built.lens[b] else float(np.abs(got).max())
+        er = float(np.max(A.row_rel_err(got, res["ref"]))) if built.lens[b] else 0.0
+        worst, worst_ref = max(worst, e), max(worst_ref, er)
+        zor += res["zero_blocks"]
+        assert np.all(np.isfinite(got)), (b, h)
+        assert e <= tol, "seq %d kv head %d: max row error %.3g > %.1g" % (b, h, e, tol)
+    return worst, worst_ref, zgpu, zor

@@ -1,0 +1,103 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/fp4kv.h declares, and rejects bad arguments on the host (nothing launched)."""
+import os
+import re
+
+import pytest
+
+from fp4_kv_cache_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4kv.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from fp4_kv_cache_amd import build
+        build.build()
+    return L.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("kv_quant_append", "fp4_decode_attention", "fp4_decode_partials", "fp4_decode_merge",
+              "fp4_decode_workspace_bytes", "fp4kv_cache_layout", "fp4kv_status_string",
+              "fp4kv_stream_read"):
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared():
+        assert hasattr(lib, n), "libfp4kv.so does not export %s" % n
+        assert n in L._SIGS, "binding lacks %s" % n
+
+
+def _desc(**kw):
+    d = dict(format=0, attn=0, num_pages=8, page_size=64, num_kv_heads=2, head_dim=128, rope_dim=0,
+             max_seqs=4)
+    d.update(kw)
+    return L.FP4KVCache(d["format"], d["attn"], d["num_pages"], d["page_size"], d["num_kv_heads"],
+                        d["head_dim"], d["rope_dim"], d["max_seqs"])
+
+
+def test_layout_sizes(lib):
+    st, b = L.fp4kv_cache_layout(_desc())
+    assert st == L.OK
+    assert b == [8 * 2 * 64 * 64, 8 * 2 * 64 * 8, 8 * 2 * 128 * 32, 8 * 2 * 128 * 4, 4 * 2 * 16 * 128 * 4, 0]
+    st, b = L.fp4kv_cache_layout(_desc(format=1, attn=1, num_kv_heads=1, head_dim=512, rope_dim=64))
+    assert st == L.OK
+    assert b == [8 * 64 * 256, 8 * 2 * 16, 0, 0, 4 * 32 * 512 * 4, 8 * 64 * 64 * 2]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(format=2), L.ERR_INVALID_ARG),
+    (dict(page_size=24), L.ERR_INVALID_ARG),
+    (dict(page_size=48), L.ERR_UNSUPPORTED),
+    (dict(format=1, page_size=16), L.ERR_INVALID_ARG),
+    (dict(head_dim=64), L.ERR_UNSUPPORTED),
+    (dict(num_pages=0), L.ERR_INVALID_ARG),
+    (dict(attn=1, head_dim=512, rope_dim=64), L.ERR_INVALID_ARG),     # MLA needs one KV head
+])
+def test_bad_descriptors_rejected(lib, kw, code):
+    st, _ = L.fp4kv_cache_layout(_desc(**kw))
+    assert st == code
+
+
+def test_null_pointers_rejected_before_launch(lib):
+    c = _desc()                     # scalars valid, all buffers NULL
+    assert L.kv_quant_append(c, 1, 1, 0, 4, 1, 1, 1, None, None) == L.ERR_INVALID_ARG
+    assert L.fp4_decode_attention(c, 1, 0, 1, 4, 1, 4, 1, 0.1, 1, 1, 1 << 20, None, None) == L.ERR_INVALID_ARG
+    assert L.kv_quant_append(None, 1, 1, 0, 4, 1, 1, 1, None, None) == L.ERR_INVALID_ARG
+
+
+def test_workspace_and_group_checks(lib):
+    c = _desc()
+    # fake non-null device pointers: validation fails before anything dereferences them
+    for f in ("k_codes", "k_scales", "v_codes", "v_scales", "stage", "k_tensor_scale", "v_tensor_scale",
+              "k_smooth_inv", "q_smooth"):
+        setattr(c, f, 0x1000)
+    need = L.fp4_decode_workspace_bytes(c, 3, 8, 1000)
+    assert need > 0
+    assert L.fp4_decode_attention(c, 1, 0, 3, 8, 1, 16, 1, 0.1, 1, 1, need - 1, None, None) == L.ERR_WORKSPACE
+    assert L.fp4_decode_attention(c, 1, 0, 3, 7, 1, 16, 1, 0.1, 1, 1, need, None, None) == L.ERR_INVALID_ARG
+    assert L.fp4_decode_attention(c, 1, 0, 3, 16, 1, 16, 1, 0.1, 1, 1, 1 << 30, None, None) == L.ERR_UNSUPPORTED
+    assert L.fp4_decode_attention(c, 1, 7, 3, 8, 1, 16, 1, 0.1, 1, 1, need, None, None) == L.ERR_INVALID_ARG
+    assert L.kv_quant_append(c, 1, 1, 5, 4, 1, 1, 1, None, None) == L.ERR_INVALID_ARG
+    assert L.kv_quant_append(c, 1, None, 0, 4, 1, 1, 1, None, None) == L.ERR_INVALID_ARG
+    assert L.kv_quant_append(c, 1, 1, 0, 0, 1, 1, 1, None, None) == L.OK        # empty batch: no-op
+    assert L.fp4kv_stream_read(1, 1000, 1, None) == L.ERR_INVALID_ARG
+    assert L.fp4kv_status_string(3) == "workspace too small"
+
+
+def test_split_plan_sizes(lib):
+    c = _desc(num_kv_heads=8)
+    # Qwen3-4B shape: 16 x 8 units, 256 tiles -> 16 splits of 16 tiles
+    assert L.fp4_decode_workspace_bytes(c, 16, 32, 32768) == 16 * 32 * 16 * 130 * 4

@@ -1,0 +1,106 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Append: cache bytes bit-exact.  Decode: max |out - oracle| / ||oracle row||_2 <= 1e-3
+per row; the error against unquantized fp64 attention is printed.
+"""
+import numpy as np
+import pytest
+
+from fp4_kv_cache_amd import workloads as W
+from fp4_kv_cache_amd import harness
+from _gpu import say, check_gqa_cache, check_mla_cache, compare_gqa
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    from fp4_kv_cache_amd import lib
+    lib.load()
+    return torch
+
+
+def test_append_tiny_nvfp4_bitexact(torch_dev):
+    w = W.workload("tiny")
+    say("append tiny nvfp4 page16 L=4096")
+    built = harness.build(w)
+    check_gqa_cache(built)
+
+
+def test_append_mxfp4_ragged_bitexact(torch_dev):
+    w = W.workload("qwen3_30b_a3b", batch=3)
+    lens = np.array([100, 33, 700], np.int32)
+    say("append mxfp4 ragged", lens.tolist())
+    built = harness.build(w, lens=lens)
+    check_gqa_cache(built)
+
+
+def test_append_incremental_tail_requant(torch_dev):
+    """Prefill part of each sequence, then append in uneven chunks (1, 5, 17, ... tokens);
+    the cache must equal the one-shot quantization of the final sequences."""
+    for name in ("qwen3_4b", "qwen3_30b_a3b"):
+        w = W.workload(name, batch=2)
+        lens = np.array([300, 97], np.int32)
+        stop = np.array([150, 37], np.int32)
+        say("append incremental", name, lens.tolist(), stop.tolist())
+        built = harness.build(w, lens=lens, stop=stop)
+        rng = np.random.default_rng(5)
+        for b in range(2):
+            p = int(stop[b])
+            while p < lens[b]:
+                n = int(min(lens[b] - p, rng.choice([1, 1, 2, 5, 17, 40])))
+                harness.append_range(built, b, p, p + n)
+                p += n
+        check_gqa_cache(built)
+
+
+def test_append_mla_latent_tiles(torch_dev):
+    w = W.workload("mla", batch=2)
+    lens = np.array([100, 48], np.int32)
+    say("append mla", lens.tolist())
+    built = harness.build(w, lens=lens, stop=np.array([60, 48]))
+    harness.append_range(built, 0, 60, 61)
+    harness.append_range(built, 0, 61, 100)
+    check_mla_cache(built)
+
+
+def test_decode_tiny_nvfp4(torch_dev):
+    w = W.workload("tiny")
+    say("decode tiny")
+    built = harness.build(w)
+    worst, worst_ref, zg, zo = compare_gqa(built, tol=TOL)
+    say("tiny: max err vs oracle %.3g, vs fp64 attention %.3g, zero blocks gpu %d oracle %d"
+        % (worst, worst_ref, zg, zo))
+
+
+@pytest.mark.parametrize("hq", [32, 16, 8])
+def test_decode_nvfp4_ragged(torch_dev, hq):
+    w = W.workload("qwen3_4b", batch=5, hq=hq)
+    lens = np.array([1, 129, 1000, 2500, 0], np.int32)
+    say("decode nvfp4 ragged hq=%d" % hq, lens.tolist())
+    built = harness.build(w, lens=lens)
+    worst, worst_ref, zg, zo = compare_gqa(built, tol=TOL)
+    say("max err vs oracle %.3g, vs fp64 %.3g, zero blocks %d/%d" % (worst, worst_ref, zg, zo))
+
+
+@pytest.mark.parametrize("hq", [32, 16])
+def test_decode_mxfp4_ragged(torch_dev, hq):
+    w = W.workload("qwen3_30b_a3b", batch=4, hq=hq)
+    lens = np.array([33, 128, 777, 3000], np.int32)
+    say("decode mxfp4 ragged hq=%d" % hq, lens.tolist())
+    built = harness.build(w, lens=lens)
+    worst, worst_ref, zg, zo = compare_gqa(built, tol=TOL)
+    say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
+
+
+def test_decode_underflow_no_zero_blocks(torch_dev):
+    w = W.workload("long_underflow", batch=1)
+    lens = np.array([16384], np.int32)
+    say("decode underflow", lens.tolist())
+    built = harness.build(w, lens=lens)
+    worst, worst_ref, zg, zo = compare_gqa(built, pairs=[(0, 0), (0, 5)], tol=TOL)
+    say("underflow: err %.3g, zero blocks gpu %d oracle %d" % (worst, zg, zo))
+    assert zg == 0 and zo == 0
