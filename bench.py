@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP4 paged-KV decode hot path on one MI355X.
+
+One step = the whole hot path for one decode token of every sequence: the
+KV-append quantizer on the new token (kv_quant_append) and paged FP4 decode
+attention over the full context (fp4_decode_attention: fused dual-residual
+query prologue, FP4 QK^T, transposed softmax with fused P quantization, FP4
+P.V, split-K merge).  Default workload: the Qwen3-4B-shaped batch
+(16 sequences x 32768 tokens, 32 query / 8 KV heads, head_dim 128, page 64,
+shuffled page table, NVFP4), inputs synthetic and resident in HBM.
+
+Prints one JSON line on stdout.  `value` is KV-cache bytes read per step
+divided by the step time (GB/s); `roofline` is the decode-attention kernel's
+algorithmic KV bytes over its own average duration (HIP events on the stream
+it runs on) against the 8 TB/s HBM peak; `cpu_baseline` is the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "FP4 paged decode attention: µs/step + KV HBM GB/s (% of 8 TB/s peak)"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_token_head(w):
+    """Packed codes + scales one decode step must read per (token, KV head)."""
+    d = w["d"]
+    B = 16 if w["fmt"] == 0 else 32
+    if w["attn"] == 0:
+        return 2 * (d // 2 + d // B)
+    return d // 2 + (d // B) / B + 2 * w["rope"]
+
+
+def decode_kernel_hash():
+    h = hashlib.sha256()
+    for f in ("decode_gqa.hip", "fp4kv_device.h", "fp4kv_internal.h"):
+        h.update(open(os.path.join(ROOT, "fp4_kv_cache_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM traffic per decode launch from the committed counter summary, if it matches this kernel."""
+    path = os.path.join(PROFILES, "decode_gqa_%s_traffic.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_hash") != decode_kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, n_units, budget_s):
+    """The oracle's decode step (query prep, logits, FP4 softmax, P.V, merge) on a sample of
+    (sequence, KV head) units at full context; cache quantization is done beforehand, untimed."""
+    from threadpoolctl import threadpool_limits
+    from fp4_kv_cache_amd import workloads as W
+    from oracle import attention as A
+    from oracle import kvquant as KQ
+    from oracle.query import quantize_query
+    cores = len(os.sched_getaffinity(0))
+    ksi, qs, gk, gv = W.calibration(w)
+    g = w["hq"] // w["hkv"]
+    lens = W.seq_lens(w)
+    units = [(b, h) for b in range(w["batch"]) for h in range(w["hkv"])][:n_units]
+    done_bytes, t_total, used = 0.0, 0.0, 0
+    with threadpool_limits(limits=cores):
+        for b, h in units:
+            L = int(lens[b])
+            kc, ks = KQ.quantize_keys(W.keys(w, b, h, L), ksi[h], gk[h], w["fmt"])
+            vc, vs = KQ.quantize_values(W.values(w, b, h, L), gv[h], w["fmt"])
+            q = W.queries(w, b)[h * g:(h + 1) * g]
+            t0 = time.perf_counter()
+            qq = quantize_query(q, qs[h], w["fmt"])
+            s = A.logits(qq, A.key_dequant_exact(kc, ks, w["fmt"]), gk[h],
+                         A.logit_coeff(W.softmax_scale(w), w["d"]), w["fmt"])
+            A.attend(s, A.value_dequant_exact(vc, vs, w["fmt"], gv[h] if w["fmt"] == 0 else 1.0), L, w["fmt"])
+            t_total += time.perf_counter() - t0
+            done_bytes += L * kv_bytes_per_token_head(w)
+            used += 1
+            if t_total > budget_s:
+                break
+    return {"value": round(done_bytes / t_total / 1e9, 5), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d of %d (sequence, KV head) units at full context (%d tokens each), "
+                      "decode step only (cache quantized beforehand, untimed); %.1f s of CPU time"
+                      % (used, w["batch"] * w["hkv"], int(lens[0]), t_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_4b")
+    ap.add_argument("--copies", type=int, default=2, help="cache copies rotated between steps")
+    ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the design notes describe how it would shard); got --gpus %d" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fp4_kv_cache_amd import workloads as W
+    from fp4_kv_cache_amd import harness
+    from fp4_kv_cache_amd import lib as L
+    L.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.workload(args.workload)
+    assert w["attn"] == 0, "bench covers the GQA workloads"
+    lens = W.seq_lens(w)
+    B, hq, hkv, d, P = w["batch"], w["hq"], w["hkv"], w["d"], w["page"]
+    log("workload", args.workload, "batch", B, "ctx", int(lens.max()), "fmt", "NVFP4" if w["fmt"] == 0 else "MXFP4")
+
+    # prefill all but the last token of every sequence; each step appends the last one
+    t0 = time.time()
+    built = harness.build(w, lens=lens, stop=lens - 1, device=dev, workers=16)
+    copies = [built.cache]
+    for _ in range(1, args.copies):
+        c2 = L.PagedFP4Cache(w["fmt"], 0, built.cache.desc.num_pages, P, hkv, d, B, *built.calib[:2],
+                             built.calib[2] if w["fmt"] == 0 else None,
+                             built.calib[3] if w["fmt"] == 0 else None, device=dev)
+        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "stage"):
+            getattr(c2, name).copy_(getattr(built.cache, name))
+        copies.append(c2)
+    torch.cuda.synchronize()
+    log("prefill + %d cache copies: %.1f s" % (len(copies), time.time() - t0))
+
+    # the step's inputs: the last token of every sequence and the decode query
+    last = (lens - 1).astype(np.int32)
+    k_new = torch.from_numpy(np.stack([built.tail[b][0][0] for b in range(B)]))
+    v_new = torch.from_numpy(np.stack([built.tail[b][1][0] for b in range(B)]))
+    tdt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
+    k_new, v_new = k_new.to(tdt).to(dev).contiguous(), v_new.to(tdt).to(dev).contiguous()
+    slots = torch.from_numpy(np.array([harness.slots_for(built.bt_np[b], [last[b]], P)[0] for b in range(B)],
+                                      np.int32)).to(dev)
+    seq_ids = torch.arange(B, dtype=torch.int32, device=dev)
+    pos = torch.from_numpy(last).to(dev)
+    q = built.queries()
+    scale = W.softmax_scale(w)
+    maxp = built.bt.shape[1]
+    ws_bytes = copies[0].workspace_bytes(B, hq, maxp * P)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    qdt = L.BF16 if q.dtype == torch.bfloat16 else L.F32
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        c = copies[i % len(copies)]
+        c.append(k_new, v_new, slots, seq_ids, pos)
+        L.check(L.fp4_decode_attention(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
+                                       built.seq_lens.data_ptr(), scale, out.data_ptr(), ws.data_ptr(),
+                                       ws_bytes, None, stream), "fp4_decode_attention")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(out).all().item(), "non-finite decode output"
+
+    kv_bytes = float(np.sum(lens.astype(np.float64)) * hkv * kv_bytes_per_token_head(w))
+
+    # the decode-attention kernel alone (split-K partials), timed launch by launch on this stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    mevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        c = copies[i % len(copies)]
+        evs[i][0].record()
+        L.check(L.fp4_decode_partials(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
+                                      built.seq_lens.data_ptr(), scale, ws.data_ptr(), ws_bytes, None, stream),
+                "fp4_decode_partials")
+        evs[i][1].record()
+        mevs[i][0].record()
+        L.check(L.fp4_decode_merge(c.desc, B, hq, maxp, built.seq_lens.data_ptr(), out.data_ptr(),
+                                   ws.data_ptr(), ws_bytes, stream), "fp4_decode_merge")
+        mevs[i][1].record()
+    torch.cuda.synchronize()
+    k_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    m_us = float(np.mean([a.elapsed_time(b) for a, b in mevs])) * 1e3
+
+    # append alone (one token per sequence)
+    aev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    aev[0].record()
+    for i in range(args.steps):
+        copies[i % len(copies)].append(k_new, v_new, slots, seq_ids, pos)
+    aev[1].record()
+    torch.cuda.synchronize()
+    a_us = aev[0].elapsed_time(aev[1]) / args.steps * 1e3
+
+    # measured streaming-read ceiling of this device (2 GiB, 16-byte loads)
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(8192, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        L.check(L.fp4kv_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream), "stream_read")
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(10):
+        L.check(L.fp4kv_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream), "stream_read")
+    s1.record()
+    torch.cuda.synchronize()
+    stream_gbps = nbytes * 10 / (s0.elapsed_time(s1) * 1e-3) / 1e9
+    del buf
+
+    achieved = kv_bytes / (k_us * 1e-6) / 1e9
+    traffic = read_traffic(args.workload)
+    res = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4(e2m1) x fp4 -> f32",
+        "data": "synthetic",
+        "config": {"workload": "%s: batch %d, %d query / %d KV heads, head_dim %d, context %d, page %d, %s K/V, "
+                               "shuffled page table, 1 new token per sequence per step"
+                               % (args.workload, B, hq, hkv, d, int(lens.max()), P,
+                                  "NVFP4" if w["fmt"] == 0 else "MXFP4"),
+                   "global_batch": B, "seq_len": int(lens.max()), "kv_bytes_per_step": int(kv_bytes),
+                   "cache_copies_rotated": len(copies)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "breakdown_us": {"decode_partials_kernel": round(k_us, 2), "split_merge_kernel": round(m_us, 2),
+                         "kv_append_1_token": round(a_us, 2)},
+        "stream_read_ceiling_GBps": round(stream_gbps, 1),
+        "decode_kernel_hash": decode_kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_units, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

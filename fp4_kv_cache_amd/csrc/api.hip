@@ -55,7 +55,7 @@ struct SplitPlan {
   int n_split, tiles_per_split;
 };
 
-SplitPlan plan_splits(int batch, int hkv, int max_len) {
+SplitPlan plan_splits(int batch, int hkv, int max_len, int page_size) {
   int max_tiles = (max_len + kTile - 1) / kTile;
   if (max_tiles < 1) max_tiles = 1;
   long units = (long)(batch > 0 ? batch : 1) * hkv;
@@ -64,6 +64,9 @@ SplitPlan plan_splits(int batch, int hkv, int max_len) {
   if (ns < 1) ns = 1;
   int tps = (int)((max_tiles + ns - 1) / ns);
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit < max_tiles ? kMinTilesPerSplit : max_tiles;
+  // a split's page ids are staged in LDS by the decode kernel
+  const int pages_per_tile = page_size >= kTile ? 1 : kTile / page_size;
+  if (tps * pages_per_tile > kMaxSplitPages) tps = kMaxSplitPages / pages_per_tile;
   SplitPlan p;
   p.tiles_per_split = tps;
   p.n_split = (max_tiles + tps - 1) / tps;
@@ -71,7 +74,7 @@ SplitPlan plan_splits(int batch, int hkv, int max_len) {
 }
 
 size_t workspace_for(const fp4kv_cache *c, int batch, int hq, int max_len, SplitPlan *out) {
-  SplitPlan p = plan_splits(batch, c->num_kv_heads, max_len);
+  SplitPlan p = plan_splits(batch, c->num_kv_heads, max_len, c->page_size);
   if (out) *out = p;
   size_t rows = (size_t)batch * hq * p.n_split;
   return rows * ((size_t)c->head_dim + 2) * sizeof(float);
@@ -269,6 +272,11 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
 int fp4kv_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
   if (!src || !sink || bytes == 0 || bytes % 4096 != 0) return FP4KV_ERR_INVALID_ARG;
   return to_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream));
+}
+
+int fp4kv_stream_copy(const void *src, void *dst, size_t bytes, void *stream) {
+  if (!src || !dst || bytes == 0 || bytes % 4096 != 0) return FP4KV_ERR_INVALID_ARG;
+  return to_status(launch_stream_copy(src, dst, bytes, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -215,6 +215,98 @@ __global__ __launch_bounds__(128) void k_append_gqa(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// GQA keys, one wave per (new token, KV head): lane l holds channels 2l, 2l+1; the
+// rotation's stages h >= 2 pair lane l with lane l ^ (h/2); then every (block,
+// candidate) pair of the scale search gets its own lane (objective accumulated in
+// element order), and one lane per block picks the first strictly smallest
+// objective in candidate order.  Same arithmetic as k_append_gqa, at a fraction of
+// its latency for decode-sized batches.
+
+template <int FMT>
+__global__ __launch_bounds__(64) void k_append_wave(AppendArgs a) {
+  constexpr int B = FMT == kFmtNV ? 16 : 32;
+  constexpr int NB = 128 / B;
+  constexpr int NC = FMT == kFmtNV ? 5 : 3;
+  __shared__ float xs[128];
+  __shared__ float errs[NB][NC];
+  __shared__ int cands[NB][NC];
+  const int lane = threadIdx.x;
+  const int tok = blockIdx.x, h = blockIdx.y;
+  const int slot = a.slots[tok];
+  if (slot < 0 || slot >= a.num_pages * a.page_size) return;
+  const int page = slot / a.page_size, off = slot % a.page_size;
+  const long base = ((long)tok * a.hkv + h) * 128 + 2 * lane;
+  const float *ksi = a.ksi + (long)h * 128 + 2 * lane;
+  float x0 = load_elem(a.k_new, base, a.bf16) * ksi[0];
+  float x1 = load_elem(a.k_new, base + 1, a.bf16) * ksi[1];
+  {
+    const float p = x0 + x1, m = x0 - x1;
+    x0 = p;
+    x1 = m;
+  }
+#pragma unroll
+  for (int hh = 2; hh < 128; hh <<= 1) {
+    const int lb = hh >> 1;
+    const float y0 = __shfl_xor(x0, lb), y1 = __shfl_xor(x1, lb);
+    if (lane & lb) { x0 = y0 - x0; x1 = y1 - x1; }
+    else { x0 = x0 + y0; x1 = x1 + y1; }
+  }
+  xs[2 * lane] = x0;
+  xs[2 * lane + 1] = x1;
+  __syncthreads();
+  const float G = FMT == kFmtNV ? a.gk[h] : 1.0f;
+  if (lane < NB * NC) {
+    const int blk = lane / NC, k = lane % NC;
+    float x[B];
+#pragma unroll
+    for (int i = 0; i < B; i++) x[i] = xs[blk * B + i];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < B; i++) amax = fmaxf(amax, fabsf(x[i]));
+    float err = INFINITY;
+    int cand;
+    if constexpr (FMT == kFmtNV) {
+      const int deltas[5] = {0, 1, -1, -2, -3};
+      cand = (int)nv_default_scale(amax, G) + deltas[k];
+      if (cand >= 0 && cand <= 0x7E) err = nv_block_err<B>(x, (uint32_t)cand, G);
+    } else {
+      const int deltas[3] = {0, 1, -1};
+      cand = mx_exp(amax) + deltas[k];
+      if (cand >= -127 && cand <= 127) err = mx_block_err<B>(x, cand);
+    }
+    errs[blk][k] = err;
+    cands[blk][k] = cand;
+  }
+  __syncthreads();
+  if (lane < NB) {
+    const int blk = lane;
+    int best = cands[blk][0];
+    float be = errs[blk][0];
+#pragma unroll
+    for (int k = 1; k < NC; k++)
+      if (errs[blk][k] < be) { be = errs[blk][k]; best = cands[blk][k]; }
+    float x[B];
+#pragma unroll
+    for (int i = 0; i < B; i++) x[i] = xs[blk * B + i];
+    uint8_t codes[B / 2];
+    uint8_t sbyte;
+    if constexpr (FMT == kFmtNV) {
+      nv_block_codes<B>(x, (uint32_t)best, G, codes);
+      sbyte = (uint8_t)best;
+    } else {
+      mx_block_codes<B>(x, best, codes);
+      sbyte = (uint8_t)(best + 127);
+    }
+    const long row = ((long)page * a.hkv + h) * a.page_size + off;
+    uint8_t *dst = a.k_codes + row * 64 + blk * (B / 2);
+#pragma unroll
+    for (int j = 0; j < B / 2; j += 4)
+      *(uint32_t *)(dst + j) = codes[j] | (codes[j + 1] << 8) | (codes[j + 2] << 16) | ((uint32_t)codes[j + 3] << 24);
+    a.k_scales[row * NB + blk] = sbyte;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Token-block bookkeeping shared by the value and latent kernels.  Token i leads a
 // block when it is the first token of its sequence in this batch or its position
 // starts a block; the block's new tokens are i .. i + n_new - 1 and its first
@@ -422,12 +514,18 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   if (a.attn == FP4KV_GQA) {
     long n = (long)a.num_tokens * a.hkv;
-    dim3 gk((unsigned)((n + 127) / 128)), gv((unsigned)a.num_tokens, (unsigned)a.hkv);
+    dim3 gk((unsigned)((n + 127) / 128)), gw((unsigned)a.num_tokens, (unsigned)a.hkv),
+        gv((unsigned)a.num_tokens, (unsigned)a.hkv);
+    // small batches (decode): one wave per (token, head) for latency; large ones
+    // (prefill): one thread per (token, head) for throughput.  Identical results.
+    const bool wave = n <= 65536;
     if (a.fmt == kFmtNV) {
-      k_append_gqa<kFmtNV><<<gk, 128, 0, s>>>(a);
+      if (wave) k_append_wave<kFmtNV><<<gw, 64, 0, s>>>(a);
+      else k_append_gqa<kFmtNV><<<gk, 128, 0, s>>>(a);
       v_append_gqa<kFmtNV><<<gv, 128, 0, s>>>(a);
     } else {
-      k_append_gqa<kFmtMX><<<gk, 128, 0, s>>>(a);
+      if (wave) k_append_wave<kFmtMX><<<gw, 64, 0, s>>>(a);
+      else k_append_gqa<kFmtMX><<<gk, 128, 0, s>>>(a);
       v_append_gqa<kFmtMX><<<gv, 128, 0, s>>>(a);
     }
   } else {

@@ -97,8 +97,96 @@ __device__ __forceinline__ int phys_page(const DecodeArgs &a, int b, int lp, int
   return pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load of streamed cache data (read once per step).
+__device__ __forceinline__ uint4 ld16(const uint8_t *p) {
+  u32x4 v = *(const u32x4 *)p;
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+
+// Register tiles of one 128-token tile, loaded ahead of use.
+struct KTile {
+  uint4 kc[8];      // key codes: lane row n -> token 32*(n/4) + 4i + n%4, channels 32*q4..+31
+  uint4 ksraw;      // NVFP4: scale bytes of tokens 2*lane, 2*lane+1 (staged through LDS)
+  int ksc[8];       // MXFP4: E8M0 scale of (token of group i, channel block q4)
+};
+struct VTile {
+  uint4 vc[8];      // value codes: lane row n -> channel 16*cg + n, tokens 32*q4..+31
+  uint32_t vsc[8];  // value scale bytes of the lane's (channel, token block(s))
+};
+
+// Key tile: lane row n takes tokens tok0 + 32*(n/4) + 4i + n%4 (i = 0..7), i.e. 8 rows of one
+// 32-token group; for P >= 32 they sit in one page 4 rows apart, so the 8 loads share a
+// base address and differ by constant offsets.
+template <int FMT, int P>
+__device__ __forceinline__ void load_k(const DecodeArgs &a, KTile &k, const int *pgt, int kvh, int tok0,
+                                       int lane) {
+  constexpr int NPT = P >= 128 ? 1 : 128 / P;   // pages touched by a 128-token tile
+  const int n = lane & 15, q4 = lane >> 4;
+  const int tin = 32 * (n >> 2) + (n & 3);      // tile-relative token of row n, group 0
+  const int t = tok0 + tin;
+  if constexpr (P >= 32) {
+    const int pg = pgt[NPT == 1 ? 0 : tin / P];
+    const long row = ((long)pg * a.hkv + kvh) * P + (t % P);
+    const uint8_t *kb = a.k_codes + row * 64 + 16 * q4;
+#pragma unroll
+    for (int i = 0; i < 8; i++) k.kc[i] = ld16(kb + 256 * i);
+    if constexpr (FMT == kFmtMX) {
+      const uint8_t *sb = a.k_scales + row * 4 + q4;
+#pragma unroll
+      for (int i = 0; i < 8; i++) k.ksc[i] = sb[16 * i];
+    }
+  } else {  // P == 16 (NVFP4 only): rows i < 4 in one page, i >= 4 in the next
+    const int pg0 = pgt[tin / P], pg1 = pgt[tin / P + 1];
+    const uint8_t *k0 = a.k_codes + (((long)pg0 * a.hkv + kvh) * P + (t % P)) * 64 + 16 * q4;
+    const uint8_t *k1 = a.k_codes + (((long)pg1 * a.hkv + kvh) * P + (t % P)) * 64 + 16 * q4;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      k.kc[i] = ld16(k0 + 256 * i);
+      k.kc[i + 4] = ld16(k1 + 256 * i);
+    }
+  }
+  if constexpr (FMT == kFmtNV) {
+    const int ts = tok0 + 2 * lane;
+    const int pg = pgt[NPT == 1 ? 0 : (2 * lane) / P];
+    k.ksraw = ld16(a.k_scales + (((long)pg * a.hkv + kvh) * P + (ts % P)) * 8);
+  }
+}
+
+// Value tile: lane row n takes channels 16*cg + n (cg = 0..7) and tokens tok0 + 32*q4 .. +31.
+template <int FMT, int P>
+__device__ __forceinline__ void load_v(const DecodeArgs &a, VTile &v, const int *pgt, int kvh, int tok0,
+                                       int lane) {
+  constexpr int D = 128;
+  constexpr int NPT = P >= 128 ? 1 : 128 / P;
+  const int n = lane & 15, q4 = lane >> 4;
+  const int t = tok0 + 32 * q4;
+  if constexpr (P >= 32) {
+    const int pg = pgt[NPT == 1 ? 0 : (32 * q4) / P];
+    const long row = ((long)pg * a.hkv + kvh) * D + n;
+    const uint8_t *cb = a.v_codes + row * (P / 2) + (t % P) / 2;
+    const uint8_t *sb = a.v_scales + row * (P / (FMT == kFmtNV ? 16 : 32)) + (t % P) / (FMT == kFmtNV ? 16 : 32);
+#pragma unroll
+    for (int cg = 0; cg < 8; cg++) {
+      v.vc[cg] = ld16(cb + cg * 16 * (P / 2));
+      if constexpr (FMT == kFmtNV) v.vsc[cg] = *(const uint16_t *)(sb + cg * 16 * (P / 16));
+      else v.vsc[cg] = sb[cg * 16 * (P / 32)];
+    }
+  } else {  // P == 16: the lane's 32 tokens span two pages
+    const int pg0 = pgt[2 * q4], pg1 = pgt[2 * q4 + 1];
+    const long r0 = ((long)pg0 * a.hkv + kvh) * D + n, r1 = ((long)pg1 * a.hkv + kvh) * D + n;
+#pragma unroll
+    for (int cg = 0; cg < 8; cg++) {
+      uint2 c0 = *(const uint2 *)(a.v_codes + (r0 + 16 * cg) * 8), c1 = *(const uint2 *)(a.v_codes + (r1 + 16 * cg) * 8);
+      v.vc[cg] = uint4{c0.x, c0.y, c1.x, c1.y};
+      v.vsc[cg] = (uint32_t)a.v_scales[r0 + 16 * cg] | ((uint32_t)a.v_scales[r1 + 16 * cg] << 8);
+    }
+  }
+}
+
 template <int FMT, int G, int P>
-__global__ __launch_bounds__(64) void gqa_partials(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_partials(DecodeArgs a) {
   constexpr int D = 128;
   constexpr int NR = 2 * G;                    // stacked rows: (head, Q1/Q2)
   constexpr int B = FMT == kFmtNV ? 16 : 32;   // scale block
@@ -119,8 +207,21 @@ __global__ __launch_bounds__(64) void gqa_partials(DecodeArgs a) {
   __shared__ uint32_t qc[2][G][D / 8];
   __shared__ int qe[2][G][NBLK];
   __shared__ float qg[2][G];
-  __shared__ uint32_t lut[256];
+  __shared__ uint32_t lut[256];                // E4M3 value scale -> four E8M0 pass bytes
+  __shared__ float lutf[256];                  // E4M3 key scale -> fp32
   __shared__ float4 sk[128 * 2];               // NVFP4 key scales of the tile: [token][parity] x 4 blocks
+
+  // physical page ids of the split's tiles: entry (tile - tb) * NPT + j is logical page
+  // tile * 128 / P + j (clamped to the sequence), so per-tile lookups are LDS reads
+  constexpr int NPT = P >= 128 ? 1 : 128 / P;
+  __shared__ int pgl[kMaxSplitPages];
+  for (int e = lane; e < (te - tb) * NPT; e += 64)
+    pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
+  __syncthreads();
+
+  // the first tile's keys are in flight while the query is prepared
+  KTile kt;
+  load_k<FMT, P>(a, kt, pgl, kvh, tb * 128, lane);
 
   // ---------------- prologue: smoothing, rotation, dual-residual FP4 query ----------------
   for (int e = lane; e < G * D; e += 64) {
@@ -155,7 +256,7 @@ __global__ __launch_bounds__(64) void gqa_partials(DecodeArgs a) {
       for (int i = 0; i < B / 8; i++) w[i] = 0u;
       int e;
       float gq = 1.0f;
-      if (FMT == kFmtNV) {
+      if constexpr (FMT == kFmtNV) {
         float rmax = bmax;
 #pragma unroll
         for (int o = 1; o < NBLK; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
@@ -203,15 +304,20 @@ __global__ __launch_bounds__(64) void gqa_partials(DecodeArgs a) {
         if (bits[j]) w |= (uint32_t)(E - j + 127) << (8 * j);
     }
     lut[c] = w;
+    lutf[c] = e4m3_dec((uint32_t)c);
   }
   __syncthreads();
 
   const int q4 = lane >> 4;        // lane group: channel block (A/B operands) or token group (D)
   const int n = lane & 15;         // operand row / output column
-  // B operands (stacked query rows) and per-lane logit coefficients
-  v8i bq[FMT == kFmtNV ? 4 : 1];
+  // B operand (stacked query rows) and per-lane logit coefficients.  NVFP4: the lane
+  // holds its (row, block 2*q4 + parity) half of the 32 channels; MFMA j keeps only lane
+  // group j by giving every other lane group the E8M0 scale byte 0 (2^-127), whose
+  // products vanish below fp32 resolution.
+  v8i bq = {0, 0, 0, 0, 0, 0, 0, 0};
   int qsb = 127;
-  float a_own = 0.0f, a_nb = 0.0f;
+  int qsj[4] = {0, 0, 0, 0};
+  float a_own = 0.0f;
   {
     const float gk = FMT == kFmtNV ? a.gk[kvh] : 1.0f;
     const int r = FMT == kFmtNV ? (n & 7) : n;       // stacked row of this column
@@ -223,135 +329,94 @@ __global__ __launch_bounds__(64) void gqa_partials(DecodeArgs a) {
       uint32_t c0 = live ? qc[k][h][2 * blk] : 0u, c1 = live ? qc[k][h][2 * blk + 1] : 0u;
       int e = live ? qe[k][h][blk] : -128;
       qsb = e == -128 ? 127 : e + 127;
+      if (par == 0) { bq[0] = (int)c0; bq[1] = (int)c1; }
+      else { bq[2] = (int)c0; bq[3] = (int)c1; }
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (j == q4) {
-          if (par == 0) { v[0] = (int)c0; v[1] = (int)c1; }
-          else { v[2] = (int)c0; v[3] = (int)c1; }
-        }
-        bq[j] = v;
-      }
+      for (int j = 0; j < 4; j++) qsj[j] = (j == q4) ? qsb : 0;
     } else {
-      v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
       if (live) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) v[i] = (int)qc[k][h][4 * q4 + i];
+        for (int i = 0; i < 4; i++) bq[i] = (int)qc[k][h][4 * q4 + i];
         qsb = qe[k][h][q4] + 127;
       }
-      bq[0] = v;
     }
-    if (live) {
-      a_own = (qg[k][h] * gk) * a.coef;
-      a_nb = (qg[1 - k][h] * gk) * a.coef;
-    }
+    if (live) a_own = (qg[k][h] * gk) * a.coef;
   }
 
   // ---------------- main loop over 128-token tiles ----------------
-  const long head_pages = (long)a.hkv;          // pages are [page][hkv][...]
   float m_run = -INFINITY, l_run = 0.0f;
   v4f o_run[8];
 #pragma unroll
   for (int cg = 0; cg < 8; cg++) o_run[cg] = v4f{0.f, 0.f, 0.f, 0.f};
   int nzero = 0;
   const float inv6gp = 1.0f / (6.0f * 0.0009765625f);   // fl32(1 / fl32(6 * 2^-10))
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  const bool count_zero = a.zero_blocks != nullptr;
 
-  for (int tile = tb; tile < te; ++tile) {
+  // One tile with its keys in `kt`; the next tile's keys are loaded into `kn` meanwhile.
+  auto body = [&](KTile &kt, KTile &kn, int tile) {
     const int tok0 = tile * 128;
-    // ---- key codes: lane row n -> tokens 32*(n/4) + 4i + n%4, channel block q4
-    uint4 kc[8];
-    int ksc[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int t = tok0 + 32 * (n >> 2) + 4 * i + (n & 3);
-      const int pg = phys_page(a, b, t / P, last_lp);
-      const long row = ((long)pg * head_pages + kvh) * P + (t % P);
-      kc[i] = *(const uint4 *)(a.k_codes + row * 64 + 16 * q4);
-      if (FMT == kFmtMX) ksc[i] = a.k_scales[row * 4 + q4];
+    // issue order matters: loads complete in order, so this tile's values must be
+    // ahead of the next tile's keys for the P.V wait not to drain the key prefetch
+    VTile vt;
+    load_v<FMT, P>(a, vt, pgl + (tile - tb) * NPT, kvh, tok0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      // unconditional, so the wait counts stay static (the last tile re-reads itself)
+      const int tn = tile + 1 < te ? tile + 1 : tile;
+      load_k<FMT, P>(a, kn, pgl + (tn - tb) * NPT, kvh, tn * 128, lane);
     }
-    if (FMT == kFmtNV) {
-      // stage the tile's key scales, decoded, as [token][parity][j] = S(block 2j + parity)
-      const int t = tok0 + 2 * lane;
-      const int pg = phys_page(a, b, t / P, last_lp);
-      const long row = ((long)pg * head_pages + kvh) * P + (t % P);
-      uint4 raw = *(const uint4 *)(a.k_scales + row * 8);
-      uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+    __builtin_amdgcn_sched_barrier(0);
+
+    if constexpr (FMT == kFmtNV) {
+      // stage the tile's key scales as fp32 [token][parity][j] = S(block 2j + parity)
+      const uint32_t wv[4] = {kt.ksraw.x, kt.ksraw.y, kt.ksraw.z, kt.ksraw.w};
 #pragma unroll
       for (int u = 0; u < 2; u++) {
-        uint32_t lo = wv[2 * u], hi = wv[2 * u + 1];   // blocks 0..3 and 4..7 of token 2*lane+u
-        float4 ev, od;
-        ev.x = e4m3_dec(lo & 0xFF);          od.x = e4m3_dec((lo >> 8) & 0xFF);
-        ev.y = e4m3_dec((lo >> 16) & 0xFF);  od.y = e4m3_dec(lo >> 24);
-        ev.z = e4m3_dec(hi & 0xFF);          od.z = e4m3_dec((hi >> 8) & 0xFF);
-        ev.w = e4m3_dec((hi >> 16) & 0xFF);  od.w = e4m3_dec(hi >> 24);
-        sk[(2 * lane + u) * 2 + 0] = ev;
-        sk[(2 * lane + u) * 2 + 1] = od;
+        const uint32_t lo = wv[2 * u], hi = wv[2 * u + 1];
+        sk[(2 * lane + u) * 2 + 0] = float4{lutf[lo & 0xFF], lutf[(lo >> 16) & 0xFF], lutf[hi & 0xFF],
+                                            lutf[(hi >> 16) & 0xFF]};
+        sk[(2 * lane + u) * 2 + 1] = float4{lutf[(lo >> 8) & 0xFF], lutf[lo >> 24], lutf[(hi >> 8) & 0xFF],
+                                            lutf[hi >> 24]};
       }
+      __syncthreads();
     }
-    // ---- value codes and scales: lane row n -> channel 16*cg + n, tokens 32*q4 .. +31
-    uint4 vc[8];
-    uint32_t vsc[8];
-    {
-      const int t = tok0 + 32 * q4;
-#pragma unroll
-      for (int cg = 0; cg < 8; cg++) {
-        const int ch = 16 * cg + n;
-        if constexpr (P >= 32) {
-          const int pg = phys_page(a, b, t / P, last_lp);
-          const long row = ((long)pg * head_pages + kvh) * D + ch;
-          vc[cg] = *(const uint4 *)(a.v_codes + row * (P / 2) + (t % P) / 2);
-          if (FMT == kFmtNV) vsc[cg] = *(const uint16_t *)(a.v_scales + row * (P / 16) + (t % P) / 16);
-          else vsc[cg] = a.v_scales[row * (P / 32) + (t % P) / 32];
-        } else {  // P == 16: the 32 tokens span two pages
-          const int pg0 = phys_page(a, b, t / P, last_lp), pg1 = phys_page(a, b, t / P + 1, last_lp);
-          const long r0 = ((long)pg0 * head_pages + kvh) * D + ch, r1 = ((long)pg1 * head_pages + kvh) * D + ch;
-          uint2 c0 = *(const uint2 *)(a.v_codes + r0 * 8), c1 = *(const uint2 *)(a.v_codes + r1 * 8);
-          vc[cg] = uint4{c0.x, c0.y, c1.x, c1.y};
-          vsc[cg] = (uint32_t)a.v_scales[r0] | ((uint32_t)a.v_scales[r1] << 8);
-        }
-      }
-    }
-    if (FMT == kFmtNV) __syncthreads();
 
-    // ---- Q.K^T: raw logits for (column n, tokens 32*q4 + 4i + rr)
+    // ---- Q.K^T: logits for (column n, tokens 32*q4 + 4i + rr)
     float s[8][4];
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const v8i av = {(int)kc[i].x, (int)kc[i].y, (int)kc[i].z, (int)kc[i].w, 0, 0, 0, 0};
+      const v8i av = {(int)kt.kc[i].x, (int)kt.kc[i].y, (int)kt.kc[i].z, (int)kt.kc[i].w, 0, 0, 0, 0};
       if constexpr (FMT == kFmtNV) {
-        v4f o0 = mfma4<0, 0>(av, bq[0], zero, 127, qsb);
-        v4f o1 = mfma4<0, 0>(av, bq[1], zero, 127, qsb);
-        v4f o2 = mfma4<0, 0>(av, bq[2], zero, 127, qsb);
-        v4f o3 = mfma4<0, 0>(av, bq[3], zero, 127, qsb);
+        const v4f o0 = mfma4<0, 0>(av, bq, zero, 127, qsj[0]);
+        const v4f o1 = mfma4<0, 0>(av, bq, zero, 127, qsj[1]);
+        const v4f o2 = mfma4<0, 0>(av, bq, zero, 127, qsj[2]);
+        const v4f o3 = mfma4<0, 0>(av, bq, zero, 127, qsj[3]);
         const int par = n >> 3;
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) {
+          // each block term o_j * S_j is exact in fp32, so fma(o, S, acc) == acc + o*S
           const float4 S = sk[(32 * q4 + 4 * i + rr) * 2 + par];
           float acc = o0[rr] * S.x;
-          acc = acc + o1[rr] * S.y;
-          acc = acc + o2[rr] * S.z;
-          acc = acc + o3[rr] * S.w;
-          s[i][rr] = acc;
+          acc = fmaf(o1[rr], S.y, acc);
+          acc = fmaf(o2[rr], S.z, acc);
+          acc = fmaf(o3[rr], S.w, acc);
+          s[i][rr] = acc + xlane8(acc);                  // even-block sum + odd-block sum
         }
       } else {
-        v4f o = mfma4<0, 0>(av, bq[0], zero, ksc[i], qsb);
+        const v4f o = mfma4<0, 0>(av, bq, zero, kt.ksc[i], qsb);
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) s[i][rr] = o[rr];
       }
     }
-    // combine parities (NVFP4), then Q1/Q2 rows: s = a1*raw1 + a2*raw2
+    // Q1/Q2 rows: s = fl32(a1*raw1) + fl32(a2*raw2); the neighbour column holds the other product
 #pragma unroll
     for (int i = 0; i < 8; i++)
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
-        float raw = s[i][rr];
-        if (FMT == kFmtNV) raw = raw + xlane8(raw);
-        float t1 = a_own * raw;
-        float t2 = a_nb * xlane1(raw);
-        s[i][rr] = t1 + t2;
+        const float t1 = a_own * s[i][rr];
+        s[i][rr] = t1 + xlane1(t1);
       }
-    // mask tokens past the end
     if (tok0 + 128 > L) {
 #pragma unroll
       for (int i = 0; i < 8; i++)
@@ -359,61 +424,57 @@ __global__ __launch_bounds__(64) void gqa_partials(DecodeArgs a) {
         for (int rr = 0; rr < 4; rr++)
           if (tok0 + 32 * q4 + 4 * i + rr >= L) s[i][rr] = -INFINITY;
     }
-    // ---- transposed softmax over the tile
-    float mt = -INFINITY;
+    // ---- transposed softmax over the tile; block maxima of the logits give the
+    // probability block maxima (exp2 is monotone)
+    float bm0 = -INFINITY, bm1 = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++) mt = fmaxf(mt, s[i][rr]);
-    mt = max_x32(max_x16(mt));
+      for (int rr = 0; rr < 4; rr++) {
+        bm0 = fmaxf(bm0, s[i][rr]);
+        bm1 = fmaxf(bm1, s[i + 4][rr]);
+      }
+    const float mt = max_x32(max_x16(fmaxf(bm0, bm1)));
     float lt = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++)
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
-        float p = __builtin_amdgcn_exp2f(s[i][rr] - mt);
+        const float p = __builtin_amdgcn_exp2f(s[i][rr] - mt);
         s[i][rr] = p;
         lt = lt + p;
       }
     // ---- fused probability quantization into the P.V B operand
-    uint32_t pk[4] = {0u, 0u, 0u, 0u};
+    uint32_t pk[4];
     int pbyte[2];
-    if (FMT == kFmtNV) {
+    if constexpr (FMT == kFmtNV) {
+      const float am[2] = {__builtin_amdgcn_exp2f(bm0 - mt), __builtin_amdgcn_exp2f(bm1 - mt)};
 #pragma unroll
       for (int pb = 0; pb < 2; pb++) {
-        float am = 0.0f;
-#pragma unroll
-        for (int i = 4 * pb; i < 4 * pb + 4; i++)
-#pragma unroll
-          for (int rr = 0; rr < 4; rr++) am = fmaxf(am, s[i][rr]);
-        const int e = ceil_log2_clamp(am * inv6gp, -9, 8);
+        const int e = ceil_log2_clamp(am[pb] * inv6gp, -9, 8);
         const float ps = pow2f(e - 10);
         pbyte[pb] = e - 10 + 127;
         pk[2 * pb] = pack8(s[4 * pb], s[4 * pb + 1], ps);
         pk[2 * pb + 1] = pack8(s[4 * pb + 2], s[4 * pb + 3], ps);
       }
     } else {
-      float am = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; i++)
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++) am = fmaxf(am, s[i][rr]);
+      const float am = __builtin_amdgcn_exp2f(fmaxf(bm0, bm1) - mt);
       const int e = mx_exp(am);
       const float ps = ldexpf(1.0f, e);
       pbyte[0] = pbyte[1] = e + 127;
 #pragma unroll
       for (int w = 0; w < 4; w++) pk[w] = pack8(s[2 * w], s[2 * w + 1], ps);
     }
-    if (a.zero_blocks) {
+    if (count_zero) {
       const int r = FMT == kFmtNV ? (n & 7) : n;
       const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (r & 1) == 0 && r < NR;
       if (rep) {
-        if (FMT == kFmtNV) {
+        if constexpr (FMT == kFmtNV) {
 #pragma unroll
           for (int pb = 0; pb < 2; pb++)
             if (tok0 + 32 * q4 + 16 * pb < L && ((pk[2 * pb] | pk[2 * pb + 1]) & 0x77777777u) == 0u) nzero++;
-        } else if (tok0 + 32 * q4 < L && ((pk[0] | pk[1] | pk[2] | pk[3]) & 0x77777777u) == 0u) {
-          nzero++;
+        } else {
+          if (tok0 + 32 * q4 < L && ((pk[0] | pk[1] | pk[2] | pk[3]) & 0x77777777u) == 0u) nzero++;
         }
       }
     }
@@ -421,46 +482,45 @@ __global__ __launch_bounds__(64) void gqa_partials(DecodeArgs a) {
     const float m_new = fmaxf(m_run, mt);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     const float beta = __builtin_amdgcn_exp2f(mt - m_new);
-    l_run = l_run * alpha + lt * beta;
+    l_run = fmaf(l_run, alpha, lt * beta);
     m_run = m_new;
     // ---- P.V
     v4f acc[8];
-#pragma unroll
-    for (int cg = 0; cg < 8; cg++) acc[cg] = zero;
     if constexpr (FMT == kFmtNV) {
-      uint32_t vl[8][2];
-#pragma unroll
-      for (int cg = 0; cg < 8; cg++) {
-        vl[cg][0] = lut[vsc[cg] & 0xFF];
-        vl[cg][1] = lut[(vsc[cg] >> 8) & 0xFF];
-      }
       const v8i p0 = {(int)pk[0], (int)pk[1], 0, 0, 0, 0, 0, 0};
       const v8i p1 = {0, 0, (int)pk[2], (int)pk[3], 0, 0, 0, 0};
 #pragma unroll
       for (int cg = 0; cg < 8; cg++) {
-        const v8i av = {(int)vc[cg].x, (int)vc[cg].y, (int)vc[cg].z, (int)vc[cg].w, 0, 0, 0, 0};
-        acc[cg] = mfma4<0, 0>(av, p0, acc[cg], (int)vl[cg][0], pbyte[0]);
-        acc[cg] = mfma4<1, 0>(av, p0, acc[cg], (int)vl[cg][0], pbyte[0]);
-        acc[cg] = mfma4<2, 0>(av, p0, acc[cg], (int)vl[cg][0], pbyte[0]);
-        acc[cg] = mfma4<3, 0>(av, p0, acc[cg], (int)vl[cg][0], pbyte[0]);
-        acc[cg] = mfma4<0, 0>(av, p1, acc[cg], (int)vl[cg][1], pbyte[1]);
-        acc[cg] = mfma4<1, 0>(av, p1, acc[cg], (int)vl[cg][1], pbyte[1]);
-        acc[cg] = mfma4<2, 0>(av, p1, acc[cg], (int)vl[cg][1], pbyte[1]);
-        acc[cg] = mfma4<3, 0>(av, p1, acc[cg], (int)vl[cg][1], pbyte[1]);
+        const v8i av = {(int)vt.vc[cg].x, (int)vt.vc[cg].y, (int)vt.vc[cg].z, (int)vt.vc[cg].w, 0, 0, 0, 0};
+        const int l0 = (int)lut[vt.vsc[cg] & 0xFF], l1 = (int)lut[(vt.vsc[cg] >> 8) & 0xFF];
+        v4f c = mfma4<0, 0>(av, p0, zero, l0, pbyte[0]);
+        c = mfma4<1, 0>(av, p0, c, l0, pbyte[0]);
+        c = mfma4<2, 0>(av, p0, c, l0, pbyte[0]);
+        c = mfma4<3, 0>(av, p0, c, l0, pbyte[0]);
+        c = mfma4<0, 0>(av, p1, c, l1, pbyte[1]);
+        c = mfma4<1, 0>(av, p1, c, l1, pbyte[1]);
+        c = mfma4<2, 0>(av, p1, c, l1, pbyte[1]);
+        acc[cg] = mfma4<3, 0>(av, p1, c, l1, pbyte[1]);
       }
     } else {
       const v8i pv = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
 #pragma unroll
       for (int cg = 0; cg < 8; cg++) {
-        const v8i av = {(int)vc[cg].x, (int)vc[cg].y, (int)vc[cg].z, (int)vc[cg].w, 0, 0, 0, 0};
-        acc[cg] = mfma4<0, 0>(av, pv, acc[cg], (int)vsc[cg], pbyte[0]);
+        const v8i av = {(int)vt.vc[cg].x, (int)vt.vc[cg].y, (int)vt.vc[cg].z, (int)vt.vc[cg].w, 0, 0, 0, 0};
+        acc[cg] = mfma4<0, 0>(av, pv, zero, (int)vt.vsc[cg], pbyte[0]);
       }
     }
 #pragma unroll
     for (int cg = 0; cg < 8; cg++)
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = fmaf(o_run[cg][rr], alpha, acc[cg][rr] * beta);
-    if (FMT == kFmtNV) __syncthreads();   // key-scale stage is rewritten by the next tile
+    if constexpr (FMT == kFmtNV) __syncthreads();   // key-scale stage is rewritten by the next tile
+  };
+
+  KTile kt2;
+  for (int tile = tb; tile < te; tile += 2) {
+    body(kt, kt2, tile);
+    if (tile + 1 < te) body(kt2, kt, tile + 1);
   }
 
   // ---------------- epilogue: split partials ----------------
@@ -487,6 +547,8 @@ __global__ __launch_bounds__(64) void gqa_partials(DecodeArgs a) {
 }
 
 // One wave per (sequence, query head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Lanes first take one split each for (m, l); the weights then go through LDS to the
+// channel loop (lane = 2 channels), whose loads are independent.
 __global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
   const int row = blockIdx.x, lane = threadIdx.x;
   const int b = row / a.hq;
@@ -495,17 +557,46 @@ __global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
   const int nv = min((ntiles + a.tiles_per_split - 1) / a.tiles_per_split, a.n_split);
   float2 *dst = (float2 *)(a.out + (long)row * 128) + lane;
   if (nv == 0) { *dst = float2{0.f, 0.f}; return; }
+  __shared__ float wsh[256];
   const float *ml = a.ws_ml + (long)row * a.n_split * 2;
   const float *o = a.ws_o + (long)row * a.n_split * 128;
   float M = -INFINITY;
-  for (int s = 0; s < nv; s++) M = fmaxf(M, ml[2 * s]);
-  float den = 0.f, n0 = 0.f, n1 = 0.f;
-  for (int s = 0; s < nv; s++) {
-    const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-    const float2 v = *((const float2 *)(o + (long)s * 128) + lane);
-    den = fmaf(w, ml[2 * s + 1], den);
-    n0 = fmaf(w, v.x, n0);
-    n1 = fmaf(w, v.y, n1);
+  for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
+  float den = 0.f;
+  for (int s0 = 0; s0 < nv; s0 += 256) {
+    const int cnt = min(256, nv - s0);
+    for (int s = lane; s < cnt; s += 64) {
+      const float w = __builtin_amdgcn_exp2f(ml[2 * (s0 + s)] - M);
+      wsh[s] = w;
+      den = fmaf(w, ml[2 * (s0 + s) + 1], den);
+    }
+  }
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k);
+  float n0 = 0.f, n1 = 0.f;
+  for (int s0 = 0; s0 < nv; s0 += 256) {
+    const int cnt = min(256, nv - s0);
+    __syncthreads();
+    for (int s = lane; s < cnt; s += 64) wsh[s] = __builtin_amdgcn_exp2f(ml[2 * (s0 + s)] - M);
+    __syncthreads();
+    int s = 0;
+    for (; s + 4 <= cnt; s += 4) {
+      const float2 v0 = *((const float2 *)(o + (long)(s0 + s) * 128) + lane);
+      const float2 v1 = *((const float2 *)(o + (long)(s0 + s + 1) * 128) + lane);
+      const float2 v2 = *((const float2 *)(o + (long)(s0 + s + 2) * 128) + lane);
+      const float2 v3 = *((const float2 *)(o + (long)(s0 + s + 3) * 128) + lane);
+      n0 = fmaf(wsh[s], v0.x, n0); n1 = fmaf(wsh[s], v0.y, n1);
+      n0 = fmaf(wsh[s + 1], v1.x, n0); n1 = fmaf(wsh[s + 1], v1.y, n1);
+      n0 = fmaf(wsh[s + 2], v2.x, n0); n1 = fmaf(wsh[s + 2], v2.y, n1);
+      n0 = fmaf(wsh[s + 3], v3.x, n0); n1 = fmaf(wsh[s + 3], v3.y, n1);
+    }
+    for (; s < cnt; s++) {
+      const float2 v = *((const float2 *)(o + (long)(s0 + s) * 128) + lane);
+      n0 = fmaf(wsh[s], v.x, n0);
+      n1 = fmaf(wsh[s], v.y, n1);
+    }
   }
   *dst = float2{n0 / den, n1 / den};
 }

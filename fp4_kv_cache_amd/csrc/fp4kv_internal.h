@@ -8,6 +8,10 @@
 
 namespace fp4kv {
 
+// Page-id entries one decode workgroup stages in LDS: a split covers at most
+// kMaxSplitPages / max(1, 128 / page_size) tiles of 128 tokens.
+constexpr int kMaxSplitPages = 512;
+
 struct AppendArgs {
   int fmt, attn, page_size, hkv, d, rope_dim, num_pages, max_seqs, num_tokens, bf16;
   uint8_t *k_codes, *k_scales, *v_codes, *v_scales;
@@ -39,5 +43,6 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
 
 }  // namespace fp4kv

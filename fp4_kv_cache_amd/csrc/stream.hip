@@ -25,6 +25,20 @@ __global__ __launch_bounds__(256) void stream_read(const uint4 *src, size_t n16,
   }
 }
 
+// Plain copy of n16 16-byte words (the known-size reference for the HBM traffic counters).
+__global__ __launch_bounds__(256) void stream_copy(const uint4 *src, uint4 *dst, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t s) {
+  size_t n16 = bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  stream_copy<<<(unsigned)blocks, 256, 0, s>>>((const uint4 *)src, (uint4 *)dst, n16);
+  return hipGetLastError();
+}
+
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s) {
   size_t n16 = bytes / 16;
   size_t blocks = (n16 + 1023) / 1024;

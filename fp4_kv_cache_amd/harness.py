@@ -42,11 +42,12 @@ def slots_for(bt_row, positions, P):
     return (bt_row[positions // P].astype(np.int64) * P + positions % P).astype(np.int32)
 
 
-def build(w, lens=None, copy=0, device="cuda", seqs_per_call=None, stop=None, workers=8):
+def build(w, lens=None, copy=0, device="cuda", stop=None, workers=8):
     """Allocate the cache for workload ``w`` and append every sequence's context.
 
     ``stop`` (optional int array) appends only the first stop[b] tokens of each
-    sequence; the rest can be appended later with ``append_range``.
+    sequence; the rest can be appended later with ``append_range``.  The keys
+    and values of the tokens left out are kept in ``built.tail[b]`` (GQA).
     """
     import torch
     lens = W.seq_lens(w) if lens is None else np.asarray(lens, np.int32)
@@ -59,29 +60,43 @@ def build(w, lens=None, copy=0, device="cuda", seqs_per_call=None, stop=None, wo
                           rope_dim=w["rope"], device=device)
     built = Built(w, cache, bt, lens, (ksi, qs, gk, gv), device)
     stop = lens if stop is None else np.asarray(stop)
+    built.tail = {}
     for b in range(w["batch"]):
-        append_range(built, b, 0, int(stop[b]), workers=workers)
+        built.tail[b] = append_range(built, b, 0, int(stop[b]), workers=workers, gen_end=int(lens[b]))
     return built
 
 
-def append_range(built, b, start, end, workers=8):
-    """Append positions [start, end) of sequence b in one kv_quant_append call."""
+def append_range(built, b, start, end, workers=8, gen_end=None):
+    """Append positions [start, end) of sequence b in one kv_quant_append call.
+
+    With ``gen_end`` > end the inputs are drawn up to gen_end and the rows
+    [end, gen_end) are returned as (keys, values) [n, Hkv, d] float32 (GQA).
+    """
     import torch
     w, cache, dev = built.w, built.cache, built.device
     n = end - start
-    if n <= 0:
-        return
+    gen_end = end if gen_end is None else max(gen_end, end)
+    if n <= 0 and gen_end == end:
+        return None
     pos = np.arange(start, end, dtype=np.int32)
     slots = slots_for(built.bt_np[b], pos, w["page"])
+    tail = None
     if w["attn"] == GQA:
-        ks = W.parallel_map(lambda h: W.keys(w, b, h, end)[start:end], range(w["hkv"]), workers)
-        vs = W.parallel_map(lambda h: W.values(w, b, h, end)[start:end], range(w["hkv"]), workers)
-        k = _dev(np.stack(ks, axis=1), w, torch, dev)
-        v = _dev(np.stack(vs, axis=1), w, torch, dev)
+        ks = W.parallel_map(lambda h: W.keys(w, b, h, gen_end)[start:], range(w["hkv"]), workers)
+        vs = W.parallel_map(lambda h: W.values(w, b, h, gen_end)[start:], range(w["hkv"]), workers)
+        kall, vall = np.stack(ks, axis=1), np.stack(vs, axis=1)
+        tail = (kall[n:], vall[n:])
+        if n <= 0:
+            return tail
+        k = _dev(kall[:n], w, torch, dev)
+        v = _dev(vall[:n], w, torch, dev)
         kr = None
     else:
+        if n <= 0:
+            return None
         k = _dev(W.keys(w, b, 0, end)[start:end][:, None, :], w, torch, dev)
         v = None
         kr = torch.from_numpy(W.bf16_bits(W.rope_keys(w, b, end)[start:end]).view(np.int16)).to(dev)
     cache.append(k, v, torch.from_numpy(slots).to(dev), torch.full((n,), b, dtype=torch.int32, device=dev),
                  torch.from_numpy(pos).to(dev), kr)
+    return tail

@@ -48,6 +48,7 @@ _SIGS = {
     "fp4_decode_merge": (_c_int, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int, _vp, _vp, _vp,
                                   _c_size, _vp]),
     "fp4kv_stream_read": (_c_int, [_vp, _c_size, _vp, _vp]),
+    "fp4kv_stream_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
     "fp4kv_status_string": (ctypes.c_char_p, [_c_int]),
 }
 
@@ -113,6 +114,10 @@ def fp4_decode_merge(cache, batch, num_q_heads, max_pages_per_seq, seq_lens, out
 
 def fp4kv_stream_read(src, nbytes, sink, stream):
     return load().fp4kv_stream_read(src, nbytes, sink, stream)
+
+
+def fp4kv_stream_copy(src, dst, nbytes, stream):
+    return load().fp4kv_stream_copy(src, dst, nbytes, stream)
 
 
 def fp4kv_status_string(status):

@@ -189,6 +189,10 @@ int fp4_decode_merge(const fp4kv_cache *c, int batch, int num_q_heads, int max_p
  * HBM read bandwidth next to the decode kernel. */
 int fp4kv_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
+/* Measurement helper: copies `bytes` (a multiple of 4096) from `src` to `dst`, the
+ * known-size reference against which hardware traffic counters are scaled. */
+int fp4kv_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *fp4kv_status_string(int status);
 

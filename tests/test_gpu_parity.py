@@ -57,6 +57,16 @@ def test_append_incremental_tail_requant(torch_dev):
         check_gqa_cache(built)
 
 
+def test_append_prefill_large_batch_path(torch_dev):
+    """One append call of > 65536 (token, head) rows takes the throughput kernel; it must
+    give the same bytes as the latency kernel and the oracle."""
+    w = W.workload("qwen3_4b", batch=1)
+    lens = np.array([9000], np.int32)
+    say("append large batch", lens.tolist())
+    built = harness.build(w, lens=lens)
+    check_gqa_cache(built)
+
+
 def test_append_mla_latent_tiles(torch_dev):
     w = W.workload("mla", batch=2)
     lens = np.array([100, 48], np.int32)
