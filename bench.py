@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=16)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="profiling mode: after setup, launch the decode kernel --steps times and one "
+                         "1 GiB stream copy (the known-size reference for traffic counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -177,6 +180,20 @@ def main():
         L.check(L.fp4_decode_attention(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
                                        built.seq_lens.data_ptr(), scale, out.data_ptr(), ws.data_ptr(),
                                        ws_bytes, None, stream), "fp4_decode_attention")
+
+    if args.kernel_only:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        L.check(L.fp4kv_stream_copy(src.data_ptr(), dst.data_ptr(), 1 << 30, stream), "stream_copy")
+        for i in range(args.steps):
+            c = copies[i % len(copies)]
+            L.check(L.fp4_decode_partials(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
+                                          built.seq_lens.data_ptr(), scale, ws.data_ptr(), ws_bytes, None,
+                                          stream), "fp4_decode_partials")
+        torch.cuda.synchronize()
+        log("kernel-only run done: %d decode launches, kv bytes per launch %d" % (args.steps,
+            int(np.sum(lens.astype(np.float64)) * hkv * kv_bytes_per_token_head(w))))
+        return
 
     for i in range(args.warmup):
         step(i)
