@@ -210,7 +210,9 @@ __global__ __launch_bounds__(128) void k_append_gqa(AppendArgs a) {
     v.y = sc[4 % NB] | (sc[5 % NB] << 8) | (sc[6 % NB] << 16) | ((uint32_t)sc[7 % NB] << 24);
     *(uint2 *)(a.k_scales + row * NB) = v;
   } else {
-    *(uint32_t *)(a.k_scales + row * NB) = sc[0] | (sc[1] << 8) | (sc[2 % NB] << 16) | ((uint32_t)sc[3 % NB] << 24);
+    uint8_t *sd = a.k_scales + ((long)page * a.hkv + h) * a.page_size * NB;
+#pragma unroll
+    for (int q = 0; q < NB; q++) sd[mx_kscale_off(off, q)] = sc[q];
   }
 }
 
@@ -302,7 +304,8 @@ __global__ __launch_bounds__(64) void k_append_wave(AppendArgs a) {
 #pragma unroll
     for (int j = 0; j < B / 2; j += 4)
       *(uint32_t *)(dst + j) = codes[j] | (codes[j + 1] << 8) | (codes[j + 2] << 16) | ((uint32_t)codes[j + 3] << 24);
-    a.k_scales[row * NB + blk] = sbyte;
+    if constexpr (FMT == kFmtNV) a.k_scales[row * NB + blk] = sbyte;
+    else a.k_scales[((long)page * a.hkv + h) * a.page_size * NB + mx_kscale_off(off, blk)] = sbyte;
   }
 }
 
@@ -378,7 +381,8 @@ __global__ __launch_bounds__(128) void v_append_gqa(AppendArgs a) {
 #pragma unroll
   for (int k = 0; k < B / 2; k += 4)
     *(uint32_t *)(cdst + k) = codes[k] | (codes[k + 1] << 8) | (codes[k + 2] << 16) | ((uint32_t)codes[k + 3] << 24);
-  a.v_scales[row * (a.page_size / B) + sp.off0 / B] = (uint8_t)sbyte;
+  const int J = (a.page_size < 32 ? a.page_size : 32) / B;
+  a.v_scales[((long)sp.page * a.hkv + h) * d * (a.page_size / B) + vscale_off(c, sp.off0 / B, J)] = (uint8_t)sbyte;
   if (sp.first + sp.n_new < B) {
 #pragma unroll
     for (int k = 0; k < B; k++)

@@ -105,85 +105,111 @@ __device__ __forceinline__ uint4 ld16(const uint8_t *p) {
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
-// Register tiles of one 128-token tile, loaded ahead of use.
-struct KTile {
-  uint4 kc[8];      // key codes: lane row n -> token 32*(n/4) + 4i + n%4, channels 32*q4..+31
-  uint4 ksraw;      // NVFP4: scale bytes of tokens 2*lane, 2*lane+1 (staged through LDS)
-  int ksc[8];       // MXFP4: E8M0 scale of (token of group i, channel block q4)
-};
-struct VTile {
-  uint4 vc[8];      // value codes: lane row n -> channel 16*cg + n, tokens 32*q4..+31
-  uint32_t vsc[8];  // value scale bytes of the lane's (channel, token block(s))
+// One 128-token tile of keys or values in registers: 9 x 16 bytes per lane.
+//   keys:   x[0..7] codes, lane row n -> token 32*(n/4) + 4i + n%4 (i = 0..7), channels
+//           32*q4..+31; x[8] scales: NVFP4 the 8 block scales of tokens 2*lane, 2*lane+1
+//           (staged through LDS), MXFP4 (x[8].x, x[8].y) the lane's 8 E8M0 scales, one per i.
+//   values: x[0..7] codes, lane row n -> channel 16*cg + n (cg = 0..7), tokens 32*q4..+31;
+//           x[8] the lane's value scales (see the layout notes at load_v).
+// When `live` is false the load is a placeholder issued only to keep the wait counts
+// static: every lane reads the same 16 bytes of the tile's first row.
+struct Tile {
+  uint4 x[9];
 };
 
-// Key tile: lane row n takes tokens tok0 + 32*(n/4) + 4i + n%4 (i = 0..7), i.e. 8 rows of one
-// 32-token group; for P >= 32 they sit in one page 4 rows apart, so the 8 loads share a
-// base address and differ by constant offsets.
 template <int FMT, int P>
-__device__ __forceinline__ void load_k(const DecodeArgs &a, KTile &k, const int *pgt, int kvh, int tok0,
-                                       int lane) {
-  constexpr int NPT = P >= 128 ? 1 : 128 / P;   // pages touched by a 128-token tile
+__device__ __forceinline__ void load_k(const DecodeArgs &a, Tile &k, const int *pgt, int kvh, int tok0,
+                                       int lane, bool live) {
   const int n = lane & 15, q4 = lane >> 4;
   const int tin = 32 * (n >> 2) + (n & 3);      // tile-relative token of row n, group 0
-  const int t = tok0 + tin;
   if constexpr (P >= 32) {
+    constexpr int NPT = P >= 128 ? 1 : 128 / P;
     const int pg = pgt[NPT == 1 ? 0 : tin / P];
-    const long row = ((long)pg * a.hkv + kvh) * P + (t % P);
-    const uint8_t *kb = a.k_codes + row * 64 + 16 * q4;
+    const long ph = (long)pg * a.hkv + kvh;
+    const int t = (tok0 + tin) % P;
+    const int lm = -(int)live;                  // all ones for a real load, zero for a placeholder
+    const uint8_t *kb = a.k_codes + ph * (P * 64) + ((t * 64 + 16 * q4) & lm);
 #pragma unroll
-    for (int i = 0; i < 8; i++) k.kc[i] = ld16(kb + 256 * i);
+    for (int i = 0; i < 8; i++) k.x[i] = ld16(kb + 256 * i);
     if constexpr (FMT == kFmtMX) {
-      const uint8_t *sb = a.k_scales + row * 4 + q4;
-#pragma unroll
-      for (int i = 0; i < 8; i++) k.ksc[i] = sb[16 * i];
+      // scale byte (token t, block q) at (((t/32)*4 + t%4)*4 + q)*8 + (t%32)/4
+      const int off = (((t >> 5) * 4 + (n & 3)) * 4 + q4) * 8;
+      const uint2 s = *(const uint2 *)(a.k_scales + ph * (P * 4) + (off & lm));
+      k.x[8] = uint4{s.x, s.y, 0u, 0u};
     }
   } else {  // P == 16 (NVFP4 only): rows i < 4 in one page, i >= 4 in the next
     const int pg0 = pgt[tin / P], pg1 = pgt[tin / P + 1];
-    const uint8_t *k0 = a.k_codes + (((long)pg0 * a.hkv + kvh) * P + (t % P)) * 64 + 16 * q4;
-    const uint8_t *k1 = a.k_codes + (((long)pg1 * a.hkv + kvh) * P + (t % P)) * 64 + 16 * q4;
+    const int t = tin % P;
+    const int lo = (t * 64 + 16 * q4) & -(int)live;
+    const uint8_t *k0 = a.k_codes + ((long)pg0 * a.hkv + kvh) * (P * 64) + lo;
+    const uint8_t *k1 = a.k_codes + ((long)pg1 * a.hkv + kvh) * (P * 64) + lo;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      k.kc[i] = ld16(k0 + 256 * i);
-      k.kc[i + 4] = ld16(k1 + 256 * i);
+      k.x[i] = ld16(k0 + 256 * i);
+      k.x[i + 4] = ld16(k1 + 256 * i);
     }
   }
   if constexpr (FMT == kFmtNV) {
-    const int ts = tok0 + 2 * lane;
+    constexpr int NPT = P >= 128 ? 1 : 128 / P;
     const int pg = pgt[NPT == 1 ? 0 : (2 * lane) / P];
-    k.ksraw = ld16(a.k_scales + (((long)pg * a.hkv + kvh) * P + (ts % P)) * 8);
+    const uint8_t *sb = a.k_scales + ((long)pg * a.hkv + kvh) * (P * 8);
+    k.x[8] = ld16(sb + ((((tok0 + 2 * lane) % P) * 8) & -(int)live));
   }
 }
 
-// Value tile: lane row n takes channels 16*cg + n (cg = 0..7) and tokens tok0 + 32*q4 .. +31.
+// Value scales of a page and KV head: the byte of (channel c, token block j) sits at
+// ((j/J)*16 + c%16)*8*J + (c/16)*J + j%J with J = min(P, 32)/B blocks per 32-token span,
+// so that lane (n, q4) finds the scales of channels n, 16+n, ..., 112+n over its 32
+// tokens in one contiguous run (NVFP4 P >= 32: 16 bytes, MXFP4: 8 bytes, NVFP4 P == 16:
+// 8 bytes in each of its two pages).
 template <int FMT, int P>
-__device__ __forceinline__ void load_v(const DecodeArgs &a, VTile &v, const int *pgt, int kvh, int tok0,
-                                       int lane) {
+__device__ __forceinline__ void load_v(const DecodeArgs &a, Tile &v, const int *pgt, int kvh, int tok0,
+                                       int lane, bool live) {
   constexpr int D = 128;
-  constexpr int NPT = P >= 128 ? 1 : 128 / P;
+  constexpr int B = FMT == kFmtNV ? 16 : 32;
   const int n = lane & 15, q4 = lane >> 4;
-  const int t = tok0 + 32 * q4;
   if constexpr (P >= 32) {
+    constexpr int NPT = P >= 128 ? 1 : 128 / P;
+    constexpr int J = 32 / B;
     const int pg = pgt[NPT == 1 ? 0 : (32 * q4) / P];
-    const long row = ((long)pg * a.hkv + kvh) * D + n;
-    const uint8_t *cb = a.v_codes + row * (P / 2) + (t % P) / 2;
-    const uint8_t *sb = a.v_scales + row * (P / (FMT == kFmtNV ? 16 : 32)) + (t % P) / (FMT == kFmtNV ? 16 : 32);
+    const long ph = (long)pg * a.hkv + kvh;
+    const int t = (tok0 + 32 * q4) % P;
+    const int lm = -(int)live;
+    const uint8_t *cb = a.v_codes + ph * (D * P / 2) + ((n * (P / 2) + t / 2) & lm);
 #pragma unroll
-    for (int cg = 0; cg < 8; cg++) {
-      v.vc[cg] = ld16(cb + cg * 16 * (P / 2));
-      if constexpr (FMT == kFmtNV) v.vsc[cg] = *(const uint16_t *)(sb + cg * 16 * (P / 16));
-      else v.vsc[cg] = sb[cg * 16 * (P / 32)];
+    for (int cg = 0; cg < 8; cg++) v.x[cg] = ld16(cb + cg * 16 * (P / 2));
+    const uint8_t *sb = a.v_scales + ph * (D * P / B) + ((((t >> 5) * 16 + n) * 8 * J) & lm);
+    if constexpr (FMT == kFmtNV) {
+      v.x[8] = ld16(sb);
+    } else {
+      const uint2 s = *(const uint2 *)sb;
+      v.x[8] = uint4{s.x, s.y, 0u, 0u};
     }
   } else {  // P == 16: the lane's 32 tokens span two pages
     const int pg0 = pgt[2 * q4], pg1 = pgt[2 * q4 + 1];
-    const long r0 = ((long)pg0 * a.hkv + kvh) * D + n, r1 = ((long)pg1 * a.hkv + kvh) * D + n;
+    const long p0 = (long)pg0 * a.hkv + kvh, p1 = (long)pg1 * a.hkv + kvh;
+    const int lo = (n * 8) & -(int)live;
+    const uint8_t *c0 = a.v_codes + p0 * (D * 8) + lo, *c1 = a.v_codes + p1 * (D * 8) + lo;
 #pragma unroll
     for (int cg = 0; cg < 8; cg++) {
-      uint2 c0 = *(const uint2 *)(a.v_codes + (r0 + 16 * cg) * 8), c1 = *(const uint2 *)(a.v_codes + (r1 + 16 * cg) * 8);
-      v.vc[cg] = uint4{c0.x, c0.y, c1.x, c1.y};
-      v.vsc[cg] = (uint32_t)a.v_scales[r0 + 16 * cg] | ((uint32_t)a.v_scales[r1 + 16 * cg] << 8);
+      const uint2 u0 = *(const uint2 *)(c0 + cg * 128), u1 = *(const uint2 *)(c1 + cg * 128);
+      v.x[cg] = uint4{u0.x, u0.y, u1.x, u1.y};
     }
+    const uint2 s0 = *(const uint2 *)(a.v_scales + p0 * D + lo);
+    const uint2 s1 = *(const uint2 *)(a.v_scales + p1 * D + lo);
+    v.x[8] = uint4{s0.x, s0.y, s1.x, s1.y};
   }
 }
+
+// byte k (compile-time after unrolling) of a 16-byte register group
+__device__ __forceinline__ uint32_t byte_of(const uint4 &u, int k) {
+  const uint32_t w = k < 4 ? u.x : (k < 8 ? u.y : (k < 12 ? u.z : u.w));
+  return (w >> (8 * (k & 3))) & 0xFFu;
+}
+
+// NVFP4 key scales of a tile, staged as fp32 float4 [token][parity] (blocks 2j + parity,
+// j = 0..3) with two float4 of padding after every 32 tokens (LDS bank spread).
+__device__ __forceinline__ int sk_index(int tok, int par) { return tok * 2 + par + 2 * (tok >> 5); }
 
 template <int FMT, int G, int P>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_partials(DecodeArgs a) {
@@ -191,6 +217,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   constexpr int NR = 2 * G;                    // stacked rows: (head, Q1/Q2)
   constexpr int B = FMT == kFmtNV ? 16 : 32;   // scale block
   constexpr int NBLK = D / B;
+  constexpr int NPT = P >= 128 ? 1 : 128 / P;  // pages touched by a 128-token tile
   static_assert(FMT == kFmtNV ? G <= 4 : G <= 8, "group too large for one 16-column MFMA");
   static_assert(P >= 16 && (P % B) == 0, "page size");
 
@@ -209,25 +236,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   __shared__ float qg[2][G];
   __shared__ uint32_t lut[256];                // E4M3 value scale -> four E8M0 pass bytes
   __shared__ float lutf[256];                  // E4M3 key scale -> fp32
-  __shared__ float4 sk[128 * 2];               // NVFP4 key scales of the tile: [token][parity] x 4 blocks
-
+  __shared__ float4 sk[128 * 2 + 8];           // NVFP4 key scales of the tile (sk_index)
   // physical page ids of the split's tiles: entry (tile - tb) * NPT + j is logical page
   // tile * 128 / P + j (clamped to the sequence), so per-tile lookups are LDS reads
-  constexpr int NPT = P >= 128 ? 1 : 128 / P;
   __shared__ int pgl[kMaxSplitPages];
+
+  // the query rows of this KV head go out first: lane takes elements lane + 64 k
+  constexpr int QPL = G * D / 64;
+  float qv[QPL];
+  {
+    const long q0 = ((long)b * a.hq + kvh * G) * D;
+    if (a.q_bf16) {
+#pragma unroll
+      for (int k = 0; k < QPL; k++) qv[k] = bf16_to_f32(((const uint16_t *)a.q)[q0 + lane + 64 * k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < QPL; k++) qv[k] = ((const float *)a.q)[q0 + lane + 64 * k];
+    }
+#pragma unroll
+    for (int k = 0; k < QPL; k++) qv[k] = qv[k] * a.qs[kvh * D + (lane + 64 * k) % D];
+  }
   for (int e = lane; e < (te - tb) * NPT; e += 64)
     pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
   __syncthreads();
 
-  // the first tile's keys are in flight while the query is prepared
-  KTile kt;
-  load_k<FMT, P>(a, kt, pgl, kvh, tb * 128, lane);
+  // the first tile's keys and values are in flight while the query is prepared
+  Tile ta, tv;
+  load_k<FMT, P>(a, ta, pgl, kvh, tb * 128, lane, true);
+  load_v<FMT, P>(a, tv, pgl, kvh, tb * 128, lane, true);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---------------- prologue: smoothing, rotation, dual-residual FP4 query ----------------
-  for (int e = lane; e < G * D; e += 64) {
-    int r = e / D, c = e % D;
-    long qi = ((long)b * a.hq + kvh * G + r) * D + c;
-    qy[r][c] = load_elem(a.q, qi, a.q_bf16) * a.qs[kvh * D + c];
+#pragma unroll
+  for (int k = 0; k < QPL; k++) {
+    const int e = lane + 64 * k;
+    qy[e / D][e % D] = qv[k];
   }
   __syncthreads();
   for (int h = 1; h < D; h <<= 1) {
@@ -344,7 +387,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 
   // ---------------- main loop over 128-token tiles ----------------
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f, f_run = 1.0f;
   v4f o_run[8];
 #pragma unroll
   for (int cg = 0; cg < 8; cg++) o_run[cg] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -353,31 +396,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   const bool count_zero = a.zero_blocks != nullptr;
 
-  // One tile with its keys in `kt`; the next tile's keys are loaded into `kn` meanwhile.
-  auto body = [&](KTile &kt, KTile &kn, int tile) {
+  // Tile `tile`: keys in kt, values in vt; the keys of tile + 1 are loaded into kn at the
+  // start, the values of tile + 1 into vt once P.V has read it.
+  auto body = [&](Tile &kt, Tile &vt, Tile &kn, int tile) {
     const int tok0 = tile * 128;
-    // issue order matters: loads complete in order, so this tile's values must be
-    // ahead of the next tile's keys for the P.V wait not to drain the key prefetch
-    VTile vt;
-    load_v<FMT, P>(a, vt, pgl + (tile - tb) * NPT, kvh, tok0, lane);
-    __builtin_amdgcn_sched_barrier(0);
     {
-      // unconditional, so the wait counts stay static (the last tile re-reads itself)
-      const int tn = tile + 1 < te ? tile + 1 : tile;
-      load_k<FMT, P>(a, kn, pgl + (tn - tb) * NPT, kvh, tn * 128, lane);
+      const bool live = tile + 1 < te;
+      const int tn = live ? tile + 1 : tile;
+      load_k<FMT, P>(a, kn, pgl + (tn - tb) * NPT, kvh, tn * 128, lane, live);
     }
     __builtin_amdgcn_sched_barrier(0);
-
     if constexpr (FMT == kFmtNV) {
       // stage the tile's key scales as fp32 [token][parity][j] = S(block 2j + parity)
-      const uint32_t wv[4] = {kt.ksraw.x, kt.ksraw.y, kt.ksraw.z, kt.ksraw.w};
+      const uint32_t wv[4] = {kt.x[8].x, kt.x[8].y, kt.x[8].z, kt.x[8].w};
 #pragma unroll
       for (int u = 0; u < 2; u++) {
         const uint32_t lo = wv[2 * u], hi = wv[2 * u + 1];
-        sk[(2 * lane + u) * 2 + 0] = float4{lutf[lo & 0xFF], lutf[(lo >> 16) & 0xFF], lutf[hi & 0xFF],
-                                            lutf[(hi >> 16) & 0xFF]};
-        sk[(2 * lane + u) * 2 + 1] = float4{lutf[(lo >> 8) & 0xFF], lutf[lo >> 24], lutf[(hi >> 8) & 0xFF],
-                                            lutf[hi >> 24]};
+        const int tok = 2 * lane + u;
+        sk[sk_index(tok, 0)] = float4{lutf[lo & 0xFF], lutf[(lo >> 16) & 0xFF], lutf[hi & 0xFF],
+                                      lutf[(hi >> 16) & 0xFF]};
+        sk[sk_index(tok, 1)] = float4{lutf[(lo >> 8) & 0xFF], lutf[lo >> 24], lutf[(hi >> 8) & 0xFF],
+                                      lutf[hi >> 24]};
       }
       __syncthreads();
     }
@@ -386,7 +425,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     float s[8][4];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const v8i av = {(int)kt.kc[i].x, (int)kt.kc[i].y, (int)kt.kc[i].z, (int)kt.kc[i].w, 0, 0, 0, 0};
+      const v8i av = {(int)kt.x[i].x, (int)kt.x[i].y, (int)kt.x[i].z, (int)kt.x[i].w, 0, 0, 0, 0};
       if constexpr (FMT == kFmtNV) {
         const v4f o0 = mfma4<0, 0>(av, bq, zero, 127, qsj[0]);
         const v4f o1 = mfma4<0, 0>(av, bq, zero, 127, qsj[1]);
@@ -396,7 +435,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) {
           // each block term o_j * S_j is exact in fp32, so fma(o, S, acc) == acc + o*S
-          const float4 S = sk[(32 * q4 + 4 * i + rr) * 2 + par];
+          const float4 S = sk[sk_index(32 * q4 + 4 * i + rr, par)];
           float acc = o0[rr] * S.x;
           acc = fmaf(o1[rr], S.y, acc);
           acc = fmaf(o2[rr], S.z, acc);
@@ -404,7 +443,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           s[i][rr] = acc + xlane8(acc);                  // even-block sum + odd-block sum
         }
       } else {
-        const v4f o = mfma4<0, 0>(av, bq, zero, kt.ksc[i], qsb);
+        const v4f o = mfma4<0, 0>(av, bq, zero, (int)byte_of(kt.x[8], i), qsb);
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) s[i][rr] = o[rr];
       }
@@ -478,49 +517,64 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
       }
     }
-    // ---- online rescale
+    // ---- online rescale.  The running output is kept as o_run * F (F per column): the
+    // tile's P.V is accumulated by the MFMAs on top of o_run * gamma with the tile's own
+    // weight as the new F, so no separate accumulator is needed.  A tile whose weight is
+    // below 2^-60 is weighted 2^-60 (its contribution is below fp32 resolution either way).
     const float m_new = fmaxf(m_run, mt);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     const float beta = __builtin_amdgcn_exp2f(mt - m_new);
     l_run = fmaf(l_run, alpha, lt * beta);
     m_run = m_new;
+    const float f_new = fmaxf(beta, 8.67361737988403547e-19f);   // 2^-60
+    const float gamma = (alpha * f_run) * __builtin_amdgcn_rcpf(f_new);
+    f_run = f_new;
+#pragma unroll
+    for (int cg = 0; cg < 8; cg++)
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = o_run[cg][rr] * gamma;
     // ---- P.V
-    v4f acc[8];
     if constexpr (FMT == kFmtNV) {
       const v8i p0 = {(int)pk[0], (int)pk[1], 0, 0, 0, 0, 0, 0};
       const v8i p1 = {0, 0, (int)pk[2], (int)pk[3], 0, 0, 0, 0};
 #pragma unroll
       for (int cg = 0; cg < 8; cg++) {
-        const v8i av = {(int)vt.vc[cg].x, (int)vt.vc[cg].y, (int)vt.vc[cg].z, (int)vt.vc[cg].w, 0, 0, 0, 0};
-        const int l0 = (int)lut[vt.vsc[cg] & 0xFF], l1 = (int)lut[(vt.vsc[cg] >> 8) & 0xFF];
-        v4f c = mfma4<0, 0>(av, p0, zero, l0, pbyte[0]);
+        const v8i av = {(int)vt.x[cg].x, (int)vt.x[cg].y, (int)vt.x[cg].z, (int)vt.x[cg].w, 0, 0, 0, 0};
+        // scale bytes of (channel 16*cg + n) for the lane's first and second 16 tokens
+        const uint32_t b0 = P >= 32 ? byte_of(vt.x[8], 2 * cg) : byte_of(vt.x[8], cg);
+        const uint32_t b1 = P >= 32 ? byte_of(vt.x[8], 2 * cg + 1) : byte_of(vt.x[8], 8 + cg);
+        const int l0 = (int)lut[b0], l1 = (int)lut[b1];
+        v4f c = mfma4<0, 0>(av, p0, o_run[cg], l0, pbyte[0]);
         c = mfma4<1, 0>(av, p0, c, l0, pbyte[0]);
         c = mfma4<2, 0>(av, p0, c, l0, pbyte[0]);
         c = mfma4<3, 0>(av, p0, c, l0, pbyte[0]);
         c = mfma4<0, 0>(av, p1, c, l1, pbyte[1]);
         c = mfma4<1, 0>(av, p1, c, l1, pbyte[1]);
         c = mfma4<2, 0>(av, p1, c, l1, pbyte[1]);
-        acc[cg] = mfma4<3, 0>(av, p1, c, l1, pbyte[1]);
+        o_run[cg] = mfma4<3, 0>(av, p1, c, l1, pbyte[1]);
       }
     } else {
       const v8i pv = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
 #pragma unroll
       for (int cg = 0; cg < 8; cg++) {
-        const v8i av = {(int)vt.vc[cg].x, (int)vt.vc[cg].y, (int)vt.vc[cg].z, (int)vt.vc[cg].w, 0, 0, 0, 0};
-        acc[cg] = mfma4<0, 0>(av, pv, zero, (int)vt.vsc[cg], pbyte[0]);
+        const v8i av = {(int)vt.x[cg].x, (int)vt.x[cg].y, (int)vt.x[cg].z, (int)vt.x[cg].w, 0, 0, 0, 0};
+        o_run[cg] = mfma4<0, 0>(av, pv, o_run[cg], (int)byte_of(vt.x[8], cg), pbyte[0]);
       }
     }
-#pragma unroll
-    for (int cg = 0; cg < 8; cg++)
-#pragma unroll
-      for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = fmaf(o_run[cg][rr], alpha, acc[cg][rr] * beta);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const bool live = tile + 1 < te;
+      const int tn = live ? tile + 1 : tile;
+      load_v<FMT, P>(a, vt, pgl + (tn - tb) * NPT, kvh, tn * 128, lane, live);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (FMT == kFmtNV) __syncthreads();   // key-scale stage is rewritten by the next tile
   };
 
-  KTile kt2;
+  Tile tb2;
   for (int tile = tb; tile < te; tile += 2) {
-    body(kt, kt2, tile);
-    if (tile + 1 < te) body(kt2, kt, tile + 1);
+    body(ta, tv, tb2, tile);
+    if (tile + 1 < te) body(tb2, tv, ta, tile + 1);
   }
 
   // ---------------- epilogue: split partials ----------------
@@ -530,7 +584,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   if (rep) {
     const int head = kvh * G + (r >> 1);
     const long rowi = ((long)b * a.hq + head) * a.n_split + split;
-    const float gv = FMT == kFmtNV ? a.gv[kvh] : 1.0f;
+    const float gv = (FMT == kFmtNV ? a.gv[kvh] : 1.0f) * f_run;
 #pragma unroll
     for (int cg = 0; cg < 8; cg++) {
       float4 v = {o_run[cg][0] * gv, o_run[cg][1] * gv, o_run[cg][2] * gv, o_run[cg][3] * gv};

@@ -85,6 +85,20 @@ __device__ __forceinline__ int mx_exp(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// Cache layout: byte offset of the MXFP4 key scale of (token t of the page, channel
+// block q) inside its page and KV head.  The eight scales one decode lane needs (rows
+// t, t+4, ..., t+28 of a 32-token span) are contiguous.
+__device__ __forceinline__ int mx_kscale_off(int t, int q) {
+  return (((t >> 5) * 4 + (t & 3)) * 4 + q) * 8 + ((t & 31) >> 2);
+}
+
+// Cache layout: byte offset of the value scale of (channel c, token block j) inside its
+// page and KV head (head_dim 128), with J = min(P, 32) / B blocks per 32-token span.
+// A decode lane's scales (channels c % 16 + 16 k, k = 0..7, over one span) are contiguous.
+__device__ __forceinline__ int vscale_off(int c, int j, int J) {
+  return ((j / J) * 16 + (c & 15)) * 8 * J + (c >> 4) * J + j % J;
+}
+
 // 2^e as fp32 for e in [-126, 127].
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 

@@ -215,9 +215,9 @@ class PagedFP4Cache:
         np_ = self.desc.num_pages
         v = {"k_codes": self.k_codes.view(np_, h, P, d // 2)}
         if self.attn == GQA:
-            v["k_scales"] = self.k_scales.view(np_, h, P, d // B)
+            v["k_scales"] = self.k_scales.view(np_, h, P * d // B)
             v["v_codes"] = self.v_codes.view(np_, h, d, P // 2)
-            v["v_scales"] = self.v_scales.view(np_, h, d, P // B)
+            v["v_scales"] = self.v_scales.view(np_, h, d * P // B)
         else:
             v["k_scales"] = self.k_scales.view(np_, 1, P // B, d // B)
             v["k_rope"] = self.k_rope.view(np_, 1, P, self.rope_dim)

@@ -38,10 +38,15 @@
  *   GQA (attn = FP4KV_GQA, head_dim d = 128):
  *     k_codes  u8 [num_pages][Hkv][P][d/2]  token-major; byte j holds channel 2j
  *                                            (low nibble) and 2j+1 (high nibble)
- *     k_scales u8 [num_pages][Hkv][P][d/B]  per (token, B-channel block)
+ *     k_scales u8 [num_pages][Hkv][P*d/B]   per (page token t, channel block q):
+ *                                            NVFP4 at t*8 + q (token-major); MXFP4 at
+ *                                            (((t/32)*4 + t%4)*4 + q)*8 + (t%32)/4
  *     v_codes  u8 [num_pages][Hkv][d][P/2]  channel-major; byte j holds tokens
  *                                            2j (low) and 2j+1 (high) of the page
- *     v_scales u8 [num_pages][Hkv][d][P/B]  per (channel, B-token block)
+ *     v_scales u8 [num_pages][Hkv][d*P/B]   per (channel c, page token block j) at
+ *                                            ((j/J)*16 + c%16)*8*J + (c/16)*J + j%J,
+ *                                            J = min(P, 32)/B
+ *   (the scale orders put the scales one decode lane needs in one contiguous run)
  *     stage    f32 [max_seqs][Hkv][B][d]    unquantized values of each sequence's
  *                                            last, partly filled value block
  *   MLA (attn = FP4KV_MLA, one latent head, head_dim = 512, rope_dim = 64):
