@@ -230,31 +230,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   if (tb >= te) return;
   const int last_lp = min((L - 1) / P, a.max_pages - 1);
 
-  __shared__ float qy[G][D];
   __shared__ uint32_t qc[2][G][D / 8];
   __shared__ int qe[2][G][NBLK];
   __shared__ float qg[2][G];
   __shared__ uint32_t lut[256];                // E4M3 value scale -> four E8M0 pass bytes
-  __shared__ float lutf[256];                  // E4M3 key scale -> fp32
   __shared__ float4 sk[128 * 2 + 8];           // NVFP4 key scales of the tile (sk_index)
   // physical page ids of the split's tiles: entry (tile - tb) * NPT + j is logical page
   // tile * 128 / P + j (clamped to the sequence), so per-tile lookups are LDS reads
   __shared__ int pgl[kMaxSplitPages];
 
-  // the query rows of this KV head go out first: lane takes elements lane + 64 k
-  constexpr int QPL = G * D / 64;
-  float qv[QPL];
+  // The query rows of this KV head go out first.  Lane l holds EPL consecutive channels
+  // (c0 = EPL * (l % LPR)) of stacked head r = l / LPR, i.e. elements EPL*l .. EPL*l + EPL-1
+  // of the head group's G x 128 block.
+  constexpr int LPR = 64 / G;                  // lanes per query head
+  constexpr int EPL = D / LPR;                 // channels per lane (2G)
+  const int qr = lane / LPR, c0 = EPL * (lane % LPR);
+  float y[EPL];
   {
-    const long q0 = ((long)b * a.hq + kvh * G) * D;
+    const long q0 = ((long)b * a.hq + kvh * G) * D + EPL * lane;
     if (a.q_bf16) {
+      const uint16_t *qp = (const uint16_t *)a.q + q0;
 #pragma unroll
-      for (int k = 0; k < QPL; k++) qv[k] = bf16_to_f32(((const uint16_t *)a.q)[q0 + lane + 64 * k]);
+      for (int j = 0; j < EPL; j++) y[j] = bf16_to_f32(qp[j]);
     } else {
+      const float *qp = (const float *)a.q + q0;
 #pragma unroll
-      for (int k = 0; k < QPL; k++) qv[k] = ((const float *)a.q)[q0 + lane + 64 * k];
+      for (int j = 0; j < EPL; j++) y[j] = qp[j];
     }
+    const float *sm = a.qs + kvh * D + c0;
 #pragma unroll
-    for (int k = 0; k < QPL; k++) qv[k] = qv[k] * a.qs[kvh * D + (lane + 64 * k) % D];
+    for (int j = 0; j < EPL; j++) y[j] = y[j] * sm[j];
   }
   for (int e = lane; e < (te - tb) * NPT; e += 64)
     pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
@@ -267,87 +272,93 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   __builtin_amdgcn_sched_barrier(0);
 
   // ---------------- prologue: smoothing, rotation, dual-residual FP4 query ----------------
+  // Walsh-Hadamard butterflies in the order of the stages h = 1, 2, ..., 64 (each output
+  // a single rounded sum or difference): h < EPL inside the lane, h >= EPL with lane
+  // l ^ (h / EPL), the lower lane taking x + x', the upper x' - x.
 #pragma unroll
-  for (int k = 0; k < QPL; k++) {
-    const int e = lane + 64 * k;
-    qy[e / D][e % D] = qv[k];
-  }
-  __syncthreads();
-  for (int h = 1; h < D; h <<= 1) {
-    for (int e = lane; e < G * D / 2; e += 64) {
-      int r = e / (D / 2), w = e % (D / 2);
-      int i = (w / h) * 2 * h + (w % h);
-      float x0 = qy[r][i], x1 = qy[r][i + h];
-      qy[r][i] = x0 + x1;
-      qy[r][i + h] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  {
-    const bool act = lane < G * NBLK;
-    const int ur = act ? lane / NBLK : 0, ub = lane % NBLK;
-    float y[B];
+  for (int h = 1; h < EPL; h <<= 1)
 #pragma unroll
-    for (int i = 0; i < B; i++) y[i] = act ? qy[ur][ub * B + i] : 0.0f;
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      float bmax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < B; i++) bmax = fmaxf(bmax, fabsf(y[i]));
-      uint32_t w[B / 8];
-#pragma unroll
-      for (int i = 0; i < B / 8; i++) w[i] = 0u;
-      int e;
-      float gq = 1.0f;
-      if constexpr (FMT == kFmtNV) {
-        float rmax = bmax;
-#pragma unroll
-        for (int o = 1; o < NBLK; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
-        gq = rmax / 1536.0f;
-        const bool valid = bmax > 0.0f && gq > 0.0f;
-        const float sixg = 6.0f * gq;
-        const float inv6g = sixg != 0.0f ? 1.0f / sixg : 0.0f;
-        e = ceil_log2_clamp(bmax * inv6g, -9, 8);
-        const float S = pow2f(e);
-        const float sg = S * gq;
-        const float r = (valid && sg != 0.0f) ? 1.0f / sg : 0.0f;
-#pragma unroll
-        for (int i = 0; i < B; i++) {
-          uint32_t c = e2m1_enc(y[i] * r);
-          w[i / 8] |= c << (4 * (i % 8));
-          y[i] = y[i] - (e2m1_dec(c) * S) * gq;
-        }
-        if (!valid) e = -128;
-      } else {
-        e = mx_exp(bmax);
-#pragma unroll
-        for (int i = 0; i < B; i++) {
-          uint32_t c = e2m1_enc(ldexpf(y[i], -e));
-          w[i / 8] |= c << (4 * (i % 8));
-          y[i] = y[i] - ldexpf(e2m1_dec(c), e);
-        }
+    for (int j = 0; j < EPL; j++)
+      if ((j & h) == 0) {
+        const float x0 = y[j], x1 = y[j + h];
+        y[j] = x0 + x1;
+        y[j + h] = x0 - x1;
       }
-      if (act) {
 #pragma unroll
-        for (int i = 0; i < B / 8; i++) qc[k][ur][ub * (B / 8) + i] = w[i];
-        qe[k][ur][ub] = e;
-        if (ub == 0) qg[k][ur] = gq;
+  for (int h = EPL; h < D; h <<= 1) {
+    const int m = h / EPL;
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int j = 0; j < EPL; j++) {
+      const float o = __shfl_xor(y[j], m);
+      y[j] = upper ? o - y[j] : y[j] + o;
+    }
+  }
+  // Dual-residual FP4 query: pass k quantizes the residual left by pass k - 1.  A block of
+  // B channels spans B / EPL lanes; NVFP4 also needs the row maximum (all LPR lanes).
+  constexpr int BL = B / EPL;                  // lanes per scale block
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    float bmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EPL; j++) bmax = fmaxf(bmax, fabsf(y[j]));
+#pragma unroll
+    for (int o = 1; o < BL; o <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o));
+    uint32_t w[(EPL + 7) / 8];
+#pragma unroll
+    for (int i = 0; i < (EPL + 7) / 8; i++) w[i] = 0u;
+    int e;
+    float gq = 1.0f;
+    if constexpr (FMT == kFmtNV) {
+      float rmax = bmax;
+#pragma unroll
+      for (int o = BL; o < LPR; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
+      gq = rmax / 1536.0f;
+      const bool valid = bmax > 0.0f && gq > 0.0f;
+      const float sixg = 6.0f * gq;
+      const float inv6g = sixg != 0.0f ? 1.0f / sixg : 0.0f;
+      e = ceil_log2_clamp(bmax * inv6g, -9, 8);
+      const float S = pow2f(e);
+      const float sg = S * gq;
+      const float r = (valid && sg != 0.0f) ? 1.0f / sg : 0.0f;
+#pragma unroll
+      for (int j = 0; j < EPL; j++) {
+        const uint32_t c = e2m1_enc(y[j] * r);
+        w[j / 8] |= c << (4 * (j % 8));
+        y[j] = y[j] - (e2m1_dec(c) * S) * gq;
+      }
+      if (!valid) e = -128;
+    } else {
+      e = mx_exp(bmax);
+#pragma unroll
+      for (int j = 0; j < EPL; j++) {
+        const uint32_t c = e2m1_enc(ldexpf(y[j], -e));
+        w[j / 8] |= c << (4 * (j % 8));
+        y[j] = y[j] - ldexpf(e2m1_dec(c), e);
       }
     }
-  }
-  // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale), for NVFP4 values
-  for (int c = lane; c < 256; c += 64) {
-    uint32_t w = 0u;
-    if (c < 0x7F) {
-      int ef = (c >> 3) & 15, m = c & 7;
-      int E = (ef ? ef : 1) - 7;
-      int bits[4] = {ef ? 1 : 0, (m >> 2) & 1, (m >> 1) & 1, m & 1};
+    // packed codes of channels c0 .. c0 + EPL - 1 (EPL / 2 bytes)
+    if constexpr (EPL >= 8) {
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        if (bits[j]) w |= (uint32_t)(E - j + 127) << (8 * j);
+      for (int i = 0; i < EPL / 8; i++) qc[k][qr][c0 / 8 + i] = w[i];
+    } else if constexpr (EPL == 4) {
+      ((uint16_t *)&qc[k][qr][0])[c0 / 4] = (uint16_t)w[0];
+    } else {
+      ((uint8_t *)&qc[k][qr][0])[c0 / 2] = (uint8_t)w[0];
     }
-    lut[c] = w;
-    lutf[c] = e4m3_dec((uint32_t)c);
+    if ((lane % BL) == 0) qe[k][qr][c0 / B] = e;
+    if ((lane % LPR) == 0) qg[k][qr] = gq;
+  }
+  // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale), for NVFP4 values:
+  // byte j is E - j + 127 when bit j of (implicit bit, m2, m1, m0) is set, else 0
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int c = lane + 64 * i;
+    const int ef = (c >> 3) & 15, m = c & 7;
+    const int E = (ef ? ef : 1) - 7 + 127;
+    uint32_t w = (ef ? (uint32_t)E : 0u) | ((m & 4) ? (uint32_t)(E - 1) << 8 : 0u) |
+                 ((m & 2) ? (uint32_t)(E - 2) << 16 : 0u) | ((m & 1) ? (uint32_t)(E - 3) << 24 : 0u);
+    lut[c] = c < 0x7F ? w : 0u;
   }
   __syncthreads();
 
@@ -407,16 +418,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FMT == kFmtNV) {
-      // stage the tile's key scales as fp32 [token][parity][j] = S(block 2j + parity)
+      // stage the tile's key scales as fp32 [token][parity][j] = S(block 2j + parity); the
+      // E4M3 -> fp32 conversions are exact
       const uint32_t wv[4] = {kt.x[8].x, kt.x[8].y, kt.x[8].z, kt.x[8].w};
 #pragma unroll
       for (int u = 0; u < 2; u++) {
-        const uint32_t lo = wv[2 * u], hi = wv[2 * u + 1];
+        const auto s01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[2 * u], false);
+        const auto s23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[2 * u], true);
+        const auto s45 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[2 * u + 1], false);
+        const auto s67 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[2 * u + 1], true);
         const int tok = 2 * lane + u;
-        sk[sk_index(tok, 0)] = float4{lutf[lo & 0xFF], lutf[(lo >> 16) & 0xFF], lutf[hi & 0xFF],
-                                      lutf[(hi >> 16) & 0xFF]};
-        sk[sk_index(tok, 1)] = float4{lutf[(lo >> 8) & 0xFF], lutf[lo >> 24], lutf[(hi >> 8) & 0xFF],
-                                      lutf[hi >> 24]};
+        sk[sk_index(tok, 0)] = float4{s01[0], s23[0], s45[0], s67[0]};
+        sk[sk_index(tok, 1)] = float4{s01[1], s23[1], s45[1], s67[1]};
       }
       __syncthreads();
     }
