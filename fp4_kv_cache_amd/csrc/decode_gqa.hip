@@ -99,9 +99,9 @@ __device__ __forceinline__ int phys_page(const DecodeArgs &a, int b, int lp, int
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte load of streamed cache data (read once per step).
+// 16-byte load of streamed cache data: read once per step, so marked non-temporal.
 __device__ __forceinline__ uint4 ld16(const uint8_t *p) {
-  u32x4 v = *(const u32x4 *)p;
+  const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
