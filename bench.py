@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_4b")
-    ap.add_argument("--copies", type=int, default=2, help="cache copies rotated between steps")
+    ap.add_argument("--copies", type=int, default=3, help="cache copies rotated between steps")
     ap.add_argument("--cpu-units", type=int, default=8)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
