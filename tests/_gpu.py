@@ -19,25 +19,27 @@ def cache_np(built):
     return {k: v.cpu().numpy() for k, v in built.cache.views().items()}
 
 
-def check_gqa_cache(built, seqs=None):
-    """Cache bytes of the given sequences == the oracle's one-shot quantization (bit exact)."""
+def check_gqa_cache(built, seqs=None, pairs=None):
+    """Cache bytes of the given sequences (or (sequence, KV head) pairs) == the oracle's
+    one-shot quantization (bit exact)."""
     w = built.w
     ksi, qs, gk, gv = built.calib
     views = cache_np(built)
-    seqs = range(w["batch"]) if seqs is None else seqs
-    for b in seqs:
+    if pairs is None:
+        seqs = range(w["batch"]) if seqs is None else seqs
+        pairs = [(b, h) for b in seqs for h in range(w["hkv"])]
+    for b, h in pairs:
         L = int(built.lens[b])
-        for h in range(w["hkv"]):
-            kc, ks, vc, vs = LY.gather_gqa(views, h, built.bt_np[b], L, w["fmt"])
-            okc, oks = KQ.quantize_keys(W.keys(w, b, h, L), ksi[h], gk[h], w["fmt"])
-            ovc, ovs = KQ.quantize_values(W.values(w, b, h, L), gv[h], w["fmt"])
-            for name, got, exp in (("k_codes", kc, okc), ("k_scales", ks, oks),
-                                   ("v_codes", vc, ovc), ("v_scales", vs, ovs)):
-                if not np.array_equal(got, exp):
-                    bad = np.argwhere(got != exp)
-                    raise AssertionError("seq %d head %d %s: %d mismatches, first at %s (got %s want %s)"
-                                         % (b, h, name, len(bad), bad[0].tolist(), got[tuple(bad[0])],
-                                            exp[tuple(bad[0])]))
+        kc, ks, vc, vs = LY.gather_gqa(views, h, built.bt_np[b], L, w["fmt"])
+        okc, oks = KQ.quantize_keys(W.keys(w, b, h, L), ksi[h], gk[h], w["fmt"])
+        ovc, ovs = KQ.quantize_values(W.values(w, b, h, L), gv[h], w["fmt"])
+        for name, got, exp in (("k_codes", kc, okc), ("k_scales", ks, oks),
+                               ("v_codes", vc, ovc), ("v_scales", vs, ovs)):
+            if not np.array_equal(got, exp):
+                bad = np.argwhere(got != exp)
+                raise AssertionError("seq %d head %d %s: %d mismatches, first at %s (got %s want %s)"
+                                     % (b, h, name, len(bad), bad[0].tolist(), got[tuple(bad[0])],
+                                        exp[tuple(bad[0])]))
 
 
 def check_mla_cache(built, seqs=None):
