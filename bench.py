@@ -48,7 +48,7 @@ def kv_bytes_per_token_head(w):
 
 def decode_kernel_hash():
     h = hashlib.sha256()
-    for f in ("decode_gqa.hip", "fp4kv_device.h", "fp4kv_internal.h"):
+    for f in ("decode_gqa.hip", "decode_common.h", "fp4kv_device.h", "fp4kv_internal.h"):
         h.update(open(os.path.join(ROOT, "fp4_kv_cache_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

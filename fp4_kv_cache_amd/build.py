@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4kv.so")
-SOURCES = ["api.hip", "append.hip", "decode_gqa.hip", "stream.hip"]
+SOURCES = ["api.hip", "append.hip", "decode_gqa.hip", "decode_mla.hip", "stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -11,6 +11,7 @@ using namespace fp4kv;
 namespace {
 
 constexpr int kTarget = 2048;   // workgroups to aim for: 8 single-wave groups per CU on 256 CUs
+constexpr int kTargetMla = 1024;  // MLA: one wave per SIMD
 constexpr int kMinTilesPerSplit = 4;
 constexpr int kTile = 128;
 
@@ -45,7 +46,7 @@ int check_pointers(const fp4kv_cache *c) {
   if (c->attn == FP4KV_GQA) {
     if (!c->v_codes || !c->v_scales) return FP4KV_ERR_INVALID_ARG;
     if (c->format == FP4KV_NVFP4 && !c->v_tensor_scale) return FP4KV_ERR_INVALID_ARG;
-  } else if (!c->k_rope) {
+  } else if (!c->k_rope || !c->v_codes) {
     return FP4KV_ERR_INVALID_ARG;
   }
   return FP4KV_OK;
@@ -55,11 +56,13 @@ struct SplitPlan {
   int n_split, tiles_per_split;
 };
 
-SplitPlan plan_splits(int batch, int hkv, int max_len, int page_size) {
+// units: waves per split (GQA: batch * Hkv; MLA: batch * query-head groups of 16);
+// target: waves to aim for (GQA: 8 single-wave groups per CU; MLA: one wave per SIMD)
+SplitPlan plan_splits(long units, int max_len, int page_size, long target) {
   int max_tiles = (max_len + kTile - 1) / kTile;
   if (max_tiles < 1) max_tiles = 1;
-  long units = (long)(batch > 0 ? batch : 1) * hkv;
-  long ns = (kTarget + units - 1) / units;
+  if (units < 1) units = 1;
+  long ns = (target + units - 1) / units;
   if (ns > max_tiles) ns = max_tiles;
   if (ns < 1) ns = 1;
   int tps = (int)((max_tiles + ns - 1) / ns);
@@ -73,8 +76,14 @@ SplitPlan plan_splits(int batch, int hkv, int max_len, int page_size) {
   return p;
 }
 
+SplitPlan plan_for(const fp4kv_cache *c, int batch, int hq, int max_len) {
+  const long b = batch > 0 ? batch : 1;
+  if (c->attn == FP4KV_MLA) return plan_splits(b * (hq / 16 > 0 ? hq / 16 : 1), max_len, c->page_size, kTargetMla);
+  return plan_splits(b * c->num_kv_heads, max_len, c->page_size, kTarget);
+}
+
 size_t workspace_for(const fp4kv_cache *c, int batch, int hq, int max_len, SplitPlan *out) {
-  SplitPlan p = plan_splits(batch, c->num_kv_heads, max_len, c->page_size);
+  SplitPlan p = plan_for(c, batch, hq, max_len);
   if (out) *out = p;
   size_t rows = (size_t)batch * hq * p.n_split;
   return rows * ((size_t)c->head_dim + 2) * sizeof(float);
@@ -100,7 +109,8 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
     if (!ok) return FP4KV_ERR_UNSUPPORTED;
     if (c->format == FP4KV_MXFP4 && c->page_size < 32) return FP4KV_ERR_UNSUPPORTED;
   } else {
-    return FP4KV_ERR_UNSUPPORTED;   // MLA decode: see the MLA kernel
+    // MLA: NVFP4 latent, query heads in groups of 16, pages of at least 32 tokens
+    if (c->format != FP4KV_NVFP4 || hq % 16 != 0 || c->page_size < 32) return FP4KV_ERR_UNSUPPORTED;
   }
   if ((long)max_pages * c->page_size > 0x7FFFFFFFL) return FP4KV_ERR_INVALID_ARG;
   if (batch > 0) {
@@ -178,7 +188,7 @@ int fp4kv_cache_layout(const fp4kv_cache *c, size_t bytes_out[6]) {
     bytes_out[5] = 0;
   } else {
     bytes_out[1] = np * (P / B) * (d / B);
-    bytes_out[2] = 0;
+    bytes_out[2] = np * d * (P / 2);
     bytes_out[3] = 0;
     bytes_out[5] = np * P * (size_t)c->rope_dim * 2;
   }
@@ -242,6 +252,7 @@ int fp4_decode_partials(const fp4kv_cache *c, const void *q, int q_dtype, int ba
                        softmax_scale, nullptr, workspace, workspace_bytes, zero_block_count, true,
                        false, &a);
   if (st) return st;
+  if (c->attn == FP4KV_MLA) return to_status(launch_mla_partials(a, (hipStream_t)stream));
   return to_status(launch_decode_partials(a, (hipStream_t)stream));
 }
 
@@ -253,6 +264,7 @@ int fp4_decode_merge(const fp4kv_cache *c, int batch, int num_q_heads, int max_p
   int st = fill_decode(c, nullptr, FP4KV_F32, batch, num_q_heads, &dummy_bt, max_pages_per_seq,
                        seq_lens, 1.0f, out, workspace, workspace_bytes, nullptr, false, true, &a);
   if (st) return st;
+  if (c->attn == FP4KV_MLA) return to_status(launch_mla_merge(a, (hipStream_t)stream));
   return to_status(launch_decode_merge(a, (hipStream_t)stream));
 }
 
@@ -264,9 +276,10 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
   int st = fill_decode(c, q, q_dtype, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                        softmax_scale, out, workspace, workspace_bytes, zero_block_count, true, true, &a);
   if (st) return st;
-  hipError_t e = launch_decode_partials(a, (hipStream_t)stream);
+  const bool mla = c->attn == FP4KV_MLA;
+  hipError_t e = mla ? launch_mla_partials(a, (hipStream_t)stream) : launch_decode_partials(a, (hipStream_t)stream);
   if (e != hipSuccess) return FP4KV_ERR_HIP;
-  return to_status(launch_decode_merge(a, (hipStream_t)stream));
+  return to_status(mla ? launch_mla_merge(a, (hipStream_t)stream) : launch_decode_merge(a, (hipStream_t)stream));
 }
 
 int fp4kv_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {

@@ -495,6 +495,7 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
     eb = best;
   }
   const long pbase = (long)sp.page * a.page_size;
+  // token-major codes (the key operand) ...
   for (int k = 0; k < B; k++) {
     uint8_t *dst = a.k_codes + (pbase + sp.off0 + k) * (D / 2) + ct * (B / 2);
 #pragma unroll
@@ -503,6 +504,21 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
 #pragma unroll
       for (int u = 0; u < 8; u++) {
         float x = xs[k][ct * B + 2 * j + u];
+        uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
+        w |= q << (4 * u);
+      }
+      *(uint32_t *)(dst + j) = w;
+    }
+  }
+  // ... and the same codes channel-major (the value operand): row c holds the page's tokens
+  for (int cc = 0; cc < B; cc++) {
+    uint8_t *dst = a.v_codes + ((long)sp.page * D + ct * B + cc) * (a.page_size / 2) + sp.off0 / 2;
+#pragma unroll
+    for (int j = 0; j < B / 2; j += 4) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        float x = xs[2 * j + u][ct * B + cc];
         uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
         w |= q << (4 * u);
       }

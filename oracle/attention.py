@@ -293,8 +293,8 @@ def mla_seq(q_lat, q_rope, K_lat, k_rope, k_smooth_inv, q_smooth, G_K, fmt, soft
     cs = logit_coeff(softmax_scale, D if o["rotate"] else 1)
     cr = logit_coeff(softmax_scale, 1)
     gk = G_K if fmt == NVFP4 else 1.0
-    lat = latent_dequant_exact(lc, ls, fmt, 1.0)
-    s = logits(qq, lat, G_K, cs, fmt, rope=(q_rope, np.asarray(k_rope, F32)[:L], cr))
+    lat = latent_dequant_exact(lc, ls, fmt, 1.0)          # [Lpad, D]; rows >= L are padding
+    s = logits(qq, lat[:L], G_K, cs, fmt, rope=(q_rope, np.asarray(k_rope, F32)[:L], cr))
     res = attend(s, lat * gk, L, fmt, p_mode=o["p_mode"], partials=partials)
     out = res["out"]
     if o["rotate"]:

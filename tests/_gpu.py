@@ -100,3 +100,30 @@ def compare_gqa(built, pairs=None, tol=1e-3):
         assert np.all(np.isfinite(got)), (b, h)
         assert e <= tol, "seq %d kv head %d: max row error %.3g > %.1g" % (b, h, e, tol)
     return worst, worst_ref, zgpu, zor
+
+
+def compare_mla(built, seqs=None, tol=1e-3):
+    """GPU MLA decode vs oracle on the given sequences; returns (max err, max err vs fp64 attention)."""
+    w = built.w
+    ksi, qs, gk, gv = built.calib
+    qn, out, zgpu = run_decode(built)
+    seqs = range(w["batch"]) if seqs is None else seqs
+    worst, worst_ref = 0.0, 0.0
+    sc = W.softmax_scale(w)
+    D = w["d"]
+    for b in seqs:
+        L = int(built.lens[b])
+        got = out[b]
+        assert np.all(np.isfinite(got)), b
+        if L == 0:
+            worst = max(worst, float(np.abs(got).max()))
+            continue
+        K = W.keys(w, b, 0, L)
+        kr = W.rope_keys(w, b, L)
+        res = A.mla_seq(qn[b, :, :D], qn[b, :, D:], K, kr, ksi[0], qs[0], gk[0], w["fmt"], sc, L=L)
+        ref = A.reference_attention(qn[b, :, :D], K, K, sc, q_rope=qn[b, :, D:], k_rope=kr)
+        e = float(np.max(A.row_rel_err(got, res["out"])))
+        er = float(np.max(A.row_rel_err(got, ref)))
+        worst, worst_ref = max(worst, e), max(worst_ref, er)
+        assert e <= tol, "seq %d: max row error %.3g > %.1g" % (b, e, tol)
+    return worst, worst_ref, zgpu

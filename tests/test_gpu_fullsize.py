@@ -10,7 +10,7 @@ import pytest
 
 from fp4_kv_cache_amd import workloads as W
 from fp4_kv_cache_amd import harness
-from _gpu import say, check_gqa_cache, check_mla_cache, compare_gqa
+from _gpu import say, check_gqa_cache, check_mla_cache, compare_gqa, compare_mla
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -55,9 +55,12 @@ def test_fullsize_long_underflow_no_zero_blocks(torch_dev):
     assert zg == 0 and zo == 0
 
 
-def test_fullsize_mla_append(torch_dev):
+def test_fullsize_mla(torch_dev):
     w = W.workload("mla")
     say("full size mla: batch %d, latent 512 + rope 64; building cache" % w["batch"])
     built = harness.build(w, workers=16)
     say("  checking latent codes, tile scales and rope of sequences 0 and 31")
     check_mla_cache(built, seqs=[0, 31])
+    say("  decoding the whole batch; checking sequences 0 and 31")
+    worst, worst_ref, zg = compare_mla(built, seqs=[0, 31], tol=TOL)
+    say("  max err vs oracle %.3g, vs fp64 attention %.3g, zero P blocks (whole batch) %d" % (worst, worst_ref, zg))

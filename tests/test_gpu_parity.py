@@ -8,7 +8,7 @@ import pytest
 
 from fp4_kv_cache_amd import workloads as W
 from fp4_kv_cache_amd import harness
-from _gpu import say, check_gqa_cache, check_mla_cache, compare_gqa
+from _gpu import say, check_gqa_cache, check_mla_cache, compare_gqa, compare_mla
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -114,3 +114,13 @@ def test_decode_underflow_no_zero_blocks(torch_dev):
     worst, worst_ref, zg, zo = compare_gqa(built, pairs=[(0, 0), (0, 5)], tol=TOL)
     say("underflow: err %.3g, zero blocks gpu %d oracle %d" % (worst, zg, zo))
     assert zg == 0 and zo == 0
+
+
+def test_decode_mla_ragged(torch_dev):
+    """MLA: 128 query heads on one latent head (key and value) plus the bf16 rope part."""
+    w = W.workload("mla", batch=4)
+    lens = np.array([1, 200, 777, 0], np.int32)
+    say("decode mla ragged", lens.tolist())
+    built = harness.build(w, lens=lens)
+    worst, worst_ref, zg = compare_mla(built, tol=TOL)
+    say("mla: max err vs oracle %.3g, vs fp64 attention %.3g, zero blocks %d" % (worst, worst_ref, zg))

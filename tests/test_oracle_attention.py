@@ -159,3 +159,49 @@ def test_logit_formula_closed_form():
     k_full = A.key_dequant_exact(kc, ks, KQ.NVFP4) * float(G_K)
     ref = (q_full @ k_full.T) * 0.125 * math.log2(math.e) / d
     assert np.allclose(s, ref, rtol=3e-6, atol=1e-6 * np.abs(ref).max())
+
+
+def test_mla_exact_codecs_is_textbook_attention():
+    """MLA emulation with every codec exact (grid-valued latent with power-of-two tile
+    scales, grid-valued query blocks, unquantized P; rotation and smoothing off) equals
+    textbook softmax attention with the latent as key and value plus the rope term, for a
+    context that is not a multiple of the 16-token tile."""
+    rng = np.random.default_rng(7)
+    D, r, L, R = 512, 64, 37, 3
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+    def grid_blocks(shape, exps):
+        v = rng.choice(grid, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        v[..., 0] = 6.0                                     # every block holds its maximum
+        return v * exps
+
+    # latent: 16 x 16 tiles, tile (token block, channel block) scaled by 2^e
+    tile_e = rng.integers(-3, 3, size=(-(-L // 16), D // 16)).astype(np.float64)
+    K = np.zeros((L, D))
+    for tb in range(tile_e.shape[0]):
+        for cb in range(D // 16):
+            rows = slice(16 * tb, min(L, 16 * tb + 16))
+            n = rows.stop - rows.start
+            blk = grid_blocks((n, 16), 2.0 ** tile_e[tb, cb])
+            blk[1:, 0] = blk[1:, 0] * rng.choice([-1.0, 1.0], size=n - 1)
+            K[rows, 16 * cb:16 * cb + 16] = blk
+    # query rows: 16-channel blocks scaled by 2^-j, j in 0..3; each row holds +-6 in block 0
+    q = np.zeros((R, D))
+    for i in range(R):
+        for cb in range(D // 16):
+            q[i, 16 * cb:16 * cb + 16] = grid_blocks(16, 2.0 ** (-int(rng.integers(0, 4)) if cb else 0))
+    qr = W_bf16(rng.standard_normal((R, r)))
+    kr = W_bf16(rng.standard_normal((L, r)))
+    sc = 1.0 / np.sqrt(D + r)
+    ones = np.ones(D, np.float32)
+    res = A.mla_seq(q.astype(np.float32), qr, K.astype(np.float32), kr, ones, ones, 1.0, KQ.NVFP4, sc, L=L,
+                    opts=dict(rotate=False, smooth=False, p_mode="exact"))
+    ref = A.reference_attention(q, K, K, sc, q_rope=qr, k_rope=kr)
+    assert np.max(A.row_rel_err(res["out"], ref)) < 1e-5
+    # the latent codes reproduce K exactly (no search improvement possible over zero error)
+    assert np.array_equal(A.latent_dequant_exact(res["l_codes"], res["l_scales"], KQ.NVFP4, 1.0)[:L], K)
+
+
+def W_bf16(x):
+    from fp4_kv_cache_amd.workloads import bf16_round
+    return bf16_round(np.asarray(x, np.float32))
