@@ -86,6 +86,8 @@ def cpu_baseline(w, n_units, budget_s):
     lens = W.seq_lens(w)
     units = [(b, h) for b in range(w["batch"]) for h in range(w["hkv"])][:n_units]
     done_bytes, t_total, steps = 0.0, 0.0, 0
+    if w["attn"] == 1:
+        return _cpu_baseline_mla(w, n_units, budget_s, cores)
     with threadpool_limits(limits=cores):
         prepared = []
         for b, h in units:
@@ -109,6 +111,43 @@ def cpu_baseline(w, n_units, budget_s):
             "sample": "%d (sequence, KV head) decode steps over %d of the workload's %d units, at full "
                       "context (%d tokens each); cache quantized once beforehand, untimed; %.1f s of "
                       "timed CPU work" % (steps, len(prepared), w["batch"] * w["hkv"], int(lens[0]), t_total)}
+
+
+def _cpu_baseline_mla(w, n_units, budget_s, cores):
+    """MLA: the oracle's decode step (query prep, latent + rope logits, FP4 softmax, P.V with
+    the latent, merge, un-rotation) per sequence; latent quantization done beforehand, untimed."""
+    from threadpoolctl import threadpool_limits
+    from fp4_kv_cache_amd import workloads as W
+    from oracle import attention as A
+    from oracle import kvquant as KQ
+    from oracle.query import quantize_query
+    ksi, qs, gk, gv = W.calibration(w)
+    lens = W.seq_lens(w)
+    D = w["d"]
+    sc = W.softmax_scale(w)
+    done_bytes, t_total, steps = 0.0, 0.0, 0
+    with threadpool_limits(limits=cores):
+        prepared = []
+        for b in range(min(n_units, w["batch"], 2)):
+            L = int(lens[b])
+            lc, ls, _ = KQ.quantize_latent(W.keys(w, b, 0, L), ksi[0], gk[0], w["fmt"])
+            lat = A.latent_dequant_exact(lc, ls, w["fmt"], 1.0)
+            prepared.append((L, lat, W.rope_keys(w, b, L), W.queries(w, b), W.rope_queries(w, b)))
+        while t_total < budget_s:
+            for L, lat, kr, q, qr in prepared:
+                t0 = time.perf_counter()
+                qq = quantize_query(q, qs[0], w["fmt"])
+                s = A.logits(qq, lat[:L], gk[0], A.logit_coeff(sc, D), w["fmt"],
+                             rope=(qr, kr, A.logit_coeff(sc, 1)))
+                out = A.attend(s, lat * gk[0], L, w["fmt"])["out"]
+                _ = A.fwht_f64(out) / D * qs[0].astype(np.float64)[None, :]
+                t_total += time.perf_counter() - t0
+                done_bytes += L * kv_bytes_per_token_head(w)
+                steps += 1
+    return {"value": round(done_bytes / t_total / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "%d sequence decode steps (all %d query heads) over %d of the workload's %d sequences, "
+                      "full context (%d tokens each); latent quantized once beforehand, untimed; %.1f s of "
+                      "timed CPU work" % (steps, w["hq"], len(prepared), w["batch"], int(lens[0]), t_total)}
 
 
 def main():
@@ -139,7 +178,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = W.workload(args.workload)
-    assert w["attn"] == 0, "bench covers the GQA workloads"
+    mla = w["attn"] == 1
     lens = W.seq_lens(w)
     B, hq, hkv, d, P = w["batch"], w["hq"], w["hkv"], w["d"], w["page"]
     log("workload", args.workload, "batch", B, "ctx", int(lens.max()), "fmt", "NVFP4" if w["fmt"] == 0 else "MXFP4")
@@ -149,21 +188,30 @@ def main():
     built = harness.build(w, lens=lens, stop=lens - 1, device=dev, workers=16)
     copies = [built.cache]
     for _ in range(1, args.copies):
-        c2 = L.PagedFP4Cache(w["fmt"], 0, built.cache.desc.num_pages, P, hkv, d, B, *built.calib[:2],
+        c2 = L.PagedFP4Cache(w["fmt"], w["attn"], built.cache.desc.num_pages, P, hkv, d, B, *built.calib[:2],
                              built.calib[2] if w["fmt"] == 0 else None,
-                             built.calib[3] if w["fmt"] == 0 else None, device=dev)
-        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "stage"):
-            getattr(c2, name).copy_(getattr(built.cache, name))
+                             built.calib[3] if (w["fmt"] == 0 and not mla) else None, rope_dim=w["rope"],
+                             device=dev)
+        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "stage", "k_rope"):
+            if getattr(built.cache, name, None) is not None:
+                getattr(c2, name).copy_(getattr(built.cache, name))
         copies.append(c2)
     torch.cuda.synchronize()
     log("prefill + %d cache copies: %.1f s" % (len(copies), time.time() - t0))
 
     # the step's inputs: the last token of every sequence and the decode query
     last = (lens - 1).astype(np.int32)
-    k_new = torch.from_numpy(np.stack([built.tail[b][0][0] for b in range(B)]))
-    v_new = torch.from_numpy(np.stack([built.tail[b][1][0] for b in range(B)]))
     tdt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
-    k_new, v_new = k_new.to(tdt).to(dev).contiguous(), v_new.to(tdt).to(dev).contiguous()
+    kr_new = None
+    if mla:   # the latent (as the key) and the bf16 rope key of each sequence's last token
+        k_new = torch.from_numpy(np.stack([W.keys(w, b, 0, int(lens[b]))[-1:] for b in range(B)]))
+        kr_new = torch.from_numpy(np.stack([W.bf16_bits(W.rope_keys(w, b, int(lens[b]))[-1])
+                                            for b in range(B)]).view(np.int16)).to(dev)
+        k_new, v_new = k_new.to(tdt).to(dev).contiguous(), None
+    else:
+        k_new = torch.from_numpy(np.stack([built.tail[b][0][0] for b in range(B)]))
+        v_new = torch.from_numpy(np.stack([built.tail[b][1][0] for b in range(B)]))
+        k_new, v_new = k_new.to(tdt).to(dev).contiguous(), v_new.to(tdt).to(dev).contiguous()
     slots = torch.from_numpy(np.array([harness.slots_for(built.bt_np[b], [last[b]], P)[0] for b in range(B)],
                                       np.int32)).to(dev)
     seq_ids = torch.arange(B, dtype=torch.int32, device=dev)
@@ -179,7 +227,7 @@ def main():
 
     def step(i):
         c = copies[i % len(copies)]
-        c.append(k_new, v_new, slots, seq_ids, pos)
+        c.append(k_new, v_new, slots, seq_ids, pos, kr_new)
         L.check(L.fp4_decode_attention(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
                                        built.seq_lens.data_ptr(), scale, out.data_ptr(), ws.data_ptr(),
                                        ws_bytes, None, stream), "fp4_decode_attention")
@@ -244,7 +292,7 @@ def main():
     aev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     aev[0].record()
     for i in range(args.steps):
-        copies[i % len(copies)].append(k_new, v_new, slots, seq_ids, pos)
+        copies[i % len(copies)].append(k_new, v_new, slots, seq_ids, pos, kr_new)
     aev[1].record()
     torch.cuda.synchronize()
     a_us = aev[0].elapsed_time(aev[1]) / args.steps * 1e3
@@ -280,10 +328,16 @@ def main():
         "vs_baseline": None,
         "dtype": "fp4(e2m1) x fp4 -> f32",
         "data": "synthetic",
-        "config": {"workload": "%s: batch %d, %d query / %d KV heads, head_dim %d, context %d, page %d, %s K/V, "
-                               "shuffled page table, 1 new token per sequence per step"
-                               % (args.workload, B, hq, hkv, d, int(lens.max()), P,
-                                  "NVFP4" if w["fmt"] == 0 else "MXFP4"),
+        "config": {"workload": ("%s: batch %d, %d query heads on one latent head (latent %d FP4 + rope %d bf16), "
+                                "context %d, page %d, %s, shuffled page table, 1 new token per sequence per step"
+                                % (args.workload, B, hq, d, w["rope"], int(lens.max()), P,
+                                   "NVFP4" if w["fmt"] == 0 else "MXFP4")) if mla else
+                               ("%s: batch %d, %d query / %d KV heads, head_dim %d, context %s, page %d, %s K/V, "
+                                "shuffled page table, 1 new token per sequence per step"
+                                % (args.workload, B, hq, hkv, d,
+                                   int(lens.max()) if lens.min() == lens.max() else
+                                   "%d-%d (ragged)" % (lens.min(), lens.max()), P,
+                                   "NVFP4" if w["fmt"] == 0 else "MXFP4")),
                    "global_batch": B, "seq_len": int(lens.max()), "kv_bytes_per_step": int(kv_bytes),
                    "cache_copies_rotated": len(copies)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

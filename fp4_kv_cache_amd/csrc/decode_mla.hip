@@ -96,7 +96,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int last_lp = min((L - 1) / P, a.max_pages - 1);
   const int h0 = hg * HG;
 
-  __shared__ _Float16 qh[2][HG][D];            // Q1 / Q2 block-scaled values (exact fp16)
+  // Q1 / Q2 block-scaled values (exact fp16); rows padded by 16 bytes so that the 16 lanes
+  // of a lane group (16 heads, same channels) read from different LDS banks
+  __shared__ _Float16 qh[2][HG][D + 8];
   __shared__ float qg[2][HG];
   __shared__ uint32_t lut[256];
   __shared__ int pgl[kMaxSplitPages];
@@ -224,43 +226,60 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   const bool count_zero = a.zero_blocks != nullptr;
 
+  // Loads run ahead of use: the latent and rope rows of token group i + 3 (crossing into
+  // the next tile) are issued while group i computes, in a ring of four buffers, and the
+  // next tile's key scales while this tile's last groups compute.
+  const int trow = 32 * (n >> 2) + (n & 3);   // A-operand row: tile token trow + 4 i in group i
+  auto load_group = [&](int tile, int i, uint4 *w) {
+    const bool live = tile < te;
+    const int tl = live ? tile : te - 1;
+    const int *pgt = pgl + (tl - tb) * NPT;
+    const int t = trow + 4 * i;
+    const int pg = pgt[NPT == 1 ? 0 : t / P];
+    const long row = (long)pg * P + (tl * 128 + t) % P;
+    const uint8_t *kb = a.k_codes + row * (D / 2) + 64 * q4;
+    const uint8_t *kr = (const uint8_t *)(a.k_rope + row * R + 8 * q4);
+    w[0] = ld16(kb); w[1] = ld16(kb + 16); w[2] = ld16(kb + 32); w[3] = ld16(kb + 48);
+    w[4] = ld16(kr); w[5] = ld16(kr + 64);
+  };
+  // tile scales of the lane's row tokens (token blocks for groups 0-3 and 4-7), channel
+  // blocks 8 q4 .. 8 q4 + 7, as raw E4M3 bytes
+  auto load_scales = [&](int tile, uint2 *sc) {
+    const int tl = tile < te ? tile : te - 1;
+    const int *pgt = pgl + (tl - tb) * NPT;
+#pragma unroll
+    for (int hb = 0; hb < 2; hb++) {
+      const int t = trow + 16 * hb;
+      const int pg = pgt[NPT == 1 ? 0 : t / P];
+      sc[hb] = *(const uint2 *)(a.k_scales + ((long)pg * (P / 16) + ((tl * 128 + t) % P) / 16) * 32 + 8 * q4);
+    }
+  };
+  uint4 gw[4][6];
+  uint2 scn[2];
+  load_scales(tb, scn);
+  load_group(tb, 0, gw[0]);
+  load_group(tb, 1, gw[1]);
+  load_group(tb, 2, gw[2]);
+
 #pragma unroll 1
   for (int tile = tb; tile < te; tile++) {
     const int tok0 = tile * 128;
     const int *pgt = pgl + (tile - tb) * NPT;
-    // ---- Q.K^T over 8 token groups of 16
-    float s[8][4];
-    // A-operand row of this lane: tile token 32 (n / 4) + 4 i + n % 4 in group i
-    const int trow = 32 * (n >> 2) + (n & 3);
-    // tile scales of the lane's row tokens (token blocks for groups 0-3 and 4-7),
-    // channel blocks 8 q4 .. 8 q4 + 7
     h2 sq[2][8];
 #pragma unroll
-    for (int hb = 0; hb < 2; hb++) {
-      const int t = trow + 16 * hb;          // groups 4*hb .. 4*hb+3 share this token block
-      const int pg = pgt[NPT == 1 ? 0 : t / P];
-      const uint2 sc = *(const uint2 *)(a.k_scales + ((long)pg * (P / 16) + ((tok0 + t) % P) / 16) * 32 + 8 * q4);
+    for (int hb = 0; hb < 2; hb++)
 #pragma unroll
-      for (int j = 0; j < 8; j++) sq[hb][j] = e4m3_h2((j < 4 ? sc.x : sc.y) >> (8 * (j & 3)) & 0xFFu);
-    }
-    // the latent and rope rows of token group i + 1 are in flight while group i computes
-    auto load_group = [&](int i, uint4 *w) {
-      const int t = trow + 4 * i;
-      const int pg = pgt[NPT == 1 ? 0 : t / P];
-      const long row = (long)pg * P + (tok0 + t) % P;
-      const uint8_t *kb = a.k_codes + row * (D / 2) + 64 * q4;
-      const uint8_t *kr = (const uint8_t *)(a.k_rope + row * R + 8 * q4);
-      w[0] = ld16(kb); w[1] = ld16(kb + 16); w[2] = ld16(kb + 32); w[3] = ld16(kb + 48);
-      w[4] = ld16(kr); w[5] = ld16(kr + 64);
-    };
-    uint4 gw[2][6];
-    load_group(0, gw[0]);
+      for (int j = 0; j < 8; j++) sq[hb][j] = e4m3_h2((j < 4 ? scn[hb].x : scn[hb].y) >> (8 * (j & 3)) & 0xFFu);
+    // ---- Q.K^T over 8 token groups of 16
+    float s[8][4];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < 8) load_group(i + 1, gw[(i + 1) & 1]);
+      if (i + 3 < 8) load_group(tile, i + 3, gw[(i + 3) & 3]);
+      else load_group(tile + 1, i + 3 - 8, gw[(i + 3) & 3]);
+      if (i == 4) load_scales(tile + 1, scn);
       __builtin_amdgcn_sched_barrier(0);
-      const uint4 *w = gw[i & 1];
+      const uint4 *w = gw[i & 3];
       const uint32_t ws[16] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w,
                                w[2].x, w[2].y, w[2].z, w[2].w, w[3].x, w[3].y, w[3].z, w[3].w};
       v4f acc1 = zero, acc2 = zero, accr = zero;
@@ -278,6 +297,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         s[i][rr] = t12 + cr * accr[rr];
       }
     }
+    // P.V operands of this tile go out before the softmax
+    const int tv = 32 * q4;
+    const int pgv = pgt[NPT == 1 ? 0 : tv / P];
+    const int tp = (tok0 + tv) % P;
+    const uint8_t *srow = a.k_scales + ((long)pgv * (P / 16) + tp / 16) * 32;
+    const uint8_t *vb = a.v_codes + ((long)pgv * D + n) * (P / 2) + tp / 2;
+    uint4 vw[2][8];
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 sa0 = ld16(srow), sa1 = ld16(srow + 16), sb0 = ld16(srow + 32), sb1 = ld16(srow + 48);
+#pragma unroll
+    for (int j = 0; j < 8; j++) vw[0][j] = ld16(vb + (long)j * 16 * (P / 2));
+    __builtin_amdgcn_sched_barrier(0);
     if (tok0 + 128 > L) {
 #pragma unroll
       for (int i = 0; i < 8; i++)
@@ -340,17 +371,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const v8i p0 = {(int)pk[0], (int)pk[1], 0, 0, 0, 0, 0, 0};
     const v8i p1 = {0, 0, (int)pk[2], (int)pk[3], 0, 0, 0, 0};
     {
-      const int t = 32 * q4;
-      const int pg = pgt[NPT == 1 ? 0 : t / P];
-      const int tp = (tok0 + t) % P;
-      // tile scales of the lane's two token blocks, all 32 channel blocks
-      const uint8_t *srow = a.k_scales + ((long)pg * (P / 16) + tp / 16) * 32;
-      const uint4 sa0 = ld16(srow), sa1 = ld16(srow + 16), sb0 = ld16(srow + 32), sb1 = ld16(srow + 48);
-      const uint8_t *vb = a.v_codes + ((long)pg * D + n) * (P / 2) + tp / 2;
       // channel groups in batches of 8, the next batch's loads in flight during this one
-      uint4 vw[2][8];
-#pragma unroll
-      for (int j = 0; j < 8; j++) vw[0][j] = ld16(vb + (long)j * 16 * (P / 2));
 #pragma unroll
       for (int bt = 0; bt < 4; bt++) {
         __builtin_amdgcn_sched_barrier(0);
