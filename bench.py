@@ -225,85 +225,102 @@ def main():
     qdt = L.BF16 if q.dtype == torch.bfloat16 else L.F32
     stream = torch.cuda.current_stream().cuda_stream
 
+    def cur_stream():
+        return torch.cuda.current_stream().cuda_stream
+
     def step(i):
         c = copies[i % len(copies)]
         c.append(k_new, v_new, slots, seq_ids, pos, kr_new)
         L.check(L.fp4_decode_attention(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
                                        built.seq_lens.data_ptr(), scale, out.data_ptr(), ws.data_ptr(),
-                                       ws_bytes, None, stream), "fp4_decode_attention")
+                                       ws_bytes, None, cur_stream()), "fp4_decode_attention")
+
+    def partials(i):
+        c = copies[i % len(copies)]
+        L.check(L.fp4_decode_partials(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
+                                      built.seq_lens.data_ptr(), scale, ws.data_ptr(), ws_bytes, None,
+                                      cur_stream()), "fp4_decode_partials")
+
+    def merge(i):
+        c = copies[i % len(copies)]
+        L.check(L.fp4_decode_merge(c.desc, B, hq, maxp, built.seq_lens.data_ptr(), out.data_ptr(),
+                                   ws.data_ptr(), ws_bytes, cur_stream()), "fp4_decode_merge")
+
+    def append(i):
+        copies[i % len(copies)].append(k_new, v_new, slots, seq_ids, pos, kr_new)
 
     if args.kernel_only:
+        stream = cur_stream()
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         L.check(L.fp4kv_stream_copy(src.data_ptr(), dst.data_ptr(), 1 << 30, stream), "stream_copy")
         for i in range(args.steps):
-            c = copies[i % len(copies)]
-            L.check(L.fp4_decode_partials(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
-                                          built.seq_lens.data_ptr(), scale, ws.data_ptr(), ws_bytes, None,
-                                          stream), "fp4_decode_partials")
+            partials(i)
         torch.cuda.synchronize()
         log("kernel-only run done: %d decode launches, kv bytes per launch %d" % (args.steps,
             int(np.sum(lens.astype(np.float64)) * hkv * kv_bytes_per_token_head(w))))
         return
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # eager: every launch issued from Python
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
     e0.record()
     for i in range(args.steps):
         step(i)
     e1.record()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step_eager = e0.elapsed_time(e1) / args.steps
     assert torch.isfinite(out).all().item(), "non-finite decode output"
+    out_eager = out.clone()
 
-    kv_bytes = float(np.sum(lens.astype(np.float64)) * hkv * kv_bytes_per_token_head(w))
+    # The same work replayed from HIP graphs (one graph holds one launch sequence per cache
+    # copy), which removes the host's launch overhead: the step time, and each kernel alone
+    # back to back -- the kernel's average duration as a profiler's kernel trace reports it.
+    nc = len(copies)
+    reps = max(1, args.steps // nc)
 
-    # The decode-attention kernel (split-K partials) alone: `steps` launches back to back on
-    # this stream (rotating the cache copies) between two events, i.e. the kernel's average
-    # duration as a profiler's kernel trace reports it, plus the small gap between launches.
-    def timed(fn):
-        fn(0)
+    def graph_time(fn):
+        g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.graph(g):
+            for i in range(nc):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = ev(), ev()
         t0.record()
-        for i in range(args.steps):
-            fn(i)
+        for _ in range(reps):
+            g.replay()
         t1.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / args.steps * 1e3
+        return t0.elapsed_time(t1) / (reps * nc) * 1e3, g
 
-    def partials(i):
-        c = copies[i % len(copies)]
-        L.check(L.fp4_decode_partials(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
-                                      built.seq_lens.data_ptr(), scale, ws.data_ptr(), ws_bytes, None, stream),
-                "fp4_decode_partials")
-
-    def merge(i):
-        c = copies[i % len(copies)]
-        L.check(L.fp4_decode_merge(c.desc, B, hq, maxp, built.seq_lens.data_ptr(), out.data_ptr(),
-                                   ws.data_ptr(), ws_bytes, stream), "fp4_decode_merge")
-
-    k_us = timed(partials)
-    m_us = timed(merge)
-
-    # append alone (one token per sequence)
-    aev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    aev[0].record()
-    for i in range(args.steps):
-        copies[i % len(copies)].append(k_new, v_new, slots, seq_ids, pos, kr_new)
-    aev[1].record()
+    step_us, g_step = graph_time(step)
+    # every replay recomputes the same step (appending the same token is idempotent): it must
+    # reproduce the eager output bit for bit
+    out.zero_()
+    g_step.replay()
     torch.cuda.synchronize()
-    a_us = aev[0].elapsed_time(aev[1]) / args.steps * 1e3
+    assert torch.equal(out, out_eager), "graph replay differs from the eager step"
+    ms_step = step_us * 1e-3
+    kv_bytes = float(np.sum(lens.astype(np.float64)) * hkv * kv_bytes_per_token_head(w))
+    k_us, _ = graph_time(partials)
+    m_us, _ = graph_time(merge)
+    a_us, _ = graph_time(append)
 
-    # measured streaming-read ceiling of this device (2 GiB, 16-byte loads)
+    # measured streaming-read ceiling of this device (2 GiB, 16-byte non-temporal loads)
+    stream = cur_stream()
     nbytes = 2 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.empty(8192, dtype=torch.int32, device=dev)
     for _ in range(2):
         L.check(L.fp4kv_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream), "stream_read")
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0, s1 = ev(), ev()
     s0.record()
     for _ in range(10):
         L.check(L.fp4kv_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream), "stream_read")
@@ -323,6 +340,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 2),
+        "us_per_step_eager_launches": round(ms_step_eager * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
