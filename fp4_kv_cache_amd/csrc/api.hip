@@ -10,9 +10,9 @@ using namespace fp4kv;
 
 namespace {
 
-constexpr int kTarget = 2048;   // workgroups to aim for: 8 single-wave groups per CU on 256 CUs
+constexpr int kTarget = 2048;   // GQA waves: 8 single-wave groups per CU on 256 CUs
 constexpr int kTargetMla = 1024;  // MLA: one wave per SIMD
-constexpr int kMinTilesPerSplit = 4;
+constexpr int kMinTilesPerSplit = 4;   // the partial kernels' minimum share (kMinTilesPerWave)
 constexpr int kTile = 128;
 
 int block_of(int fmt) { return fmt == FP4KV_NVFP4 ? 16 : 32; }
@@ -76,17 +76,48 @@ SplitPlan plan_splits(long units, int max_len, int page_size, long target) {
   return p;
 }
 
+// GQA: waves of the balanced partition.  Each wave takes an equal share of all tiles of
+// the batch (computed on the device from seq_lens); at most kTarget waves, but enough that
+// no share exceeds the page ids a wave stages in LDS, and no more than shares of
+// kMinTilesPerSplit tiles of the largest possible batch.
+long plan_waves(long units, int max_len, int page_size) {
+  long max_tiles = (max_len + kTile - 1) / kTile;
+  if (max_tiles < 1) max_tiles = 1;
+  if (units < 1) units = 1;
+  const long pages_per_tile = page_size >= kTile ? 1 : kTile / page_size;
+  const long max_share = kMaxSplitPages / pages_per_tile;
+  const long all = units * max_tiles;
+  long w = kTarget;
+  const long lds_min = (all + max_share - 1) / max_share;
+  if (w < lds_min) w = lds_min;
+  const long useful = (all + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
+  if (w > useful) w = useful;
+  return w < 1 ? 1 : w;
+}
+
 SplitPlan plan_for(const fp4kv_cache *c, int batch, int hq, int max_len) {
   const long b = batch > 0 ? batch : 1;
   if (c->attn == FP4KV_MLA) return plan_splits(b * (hq / 16 > 0 ? hq / 16 : 1), max_len, c->page_size, kTargetMla);
-  return plan_splits(b * c->num_kv_heads, max_len, c->page_size, kTarget);
+  SplitPlan p;
+  const long w = plan_waves(b * c->num_kv_heads, max_len, c->page_size);
+  p.n_split = w > 0x3FFFFFFFL ? -1 : (int)w;   // -1: batch too large for one launch
+  p.tiles_per_split = 0;
+  return p;
 }
 
+// Workspace: MLA [batch * hq][n_split] partial rows; GQA (n_waves + batch * Hkv) slots of
+// `group` partial rows, then the per-unit slot ranges.  A partial row is d + 2 floats.
 size_t workspace_for(const fp4kv_cache *c, int batch, int hq, int max_len, SplitPlan *out) {
   SplitPlan p = plan_for(c, batch, hq, max_len);
   if (out) *out = p;
-  size_t rows = (size_t)batch * hq * p.n_split;
-  return rows * ((size_t)c->head_dim + 2) * sizeof(float);
+  if (p.n_split < 0) return 0;
+  if (c->attn == FP4KV_MLA) {
+    size_t rows = (size_t)batch * hq * p.n_split;
+    return rows * ((size_t)c->head_dim + 2) * sizeof(float);
+  }
+  const size_t units = (size_t)batch * c->num_kv_heads;
+  const size_t rows = ((size_t)p.n_split + units) * (size_t)(hq / c->num_kv_heads);
+  return rows * ((size_t)c->head_dim + 2) * sizeof(float) + units * 2 * sizeof(int32_t);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP; }
@@ -118,8 +149,11 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
     if (need_q && !q) return FP4KV_ERR_INVALID_ARG;
     if (need_out && !out) return FP4KV_ERR_INVALID_ARG;
   }
+  // partial slots are numbered in int32 (GQA: n_waves + batch * Hkv)
+  if ((long)batch * c->num_kv_heads > 0x3FFFFFFFL) return FP4KV_ERR_INVALID_ARG;
   SplitPlan p;
   size_t need = workspace_for(c, batch, hq, max_pages * c->page_size, &p);
+  if (p.n_split < 0) return FP4KV_ERR_INVALID_ARG;
   if (ws_bytes < need) return FP4KV_ERR_WORKSPACE;
   DecodeArgs &d = *a;
   d.fmt = c->format;
@@ -133,8 +167,10 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.max_pages = max_pages;
   d.num_pages = c->num_pages;
   d.q_bf16 = q_dtype == FP4KV_BF16;
-  d.n_split = p.n_split;
-  d.tiles_per_split = p.tiles_per_split;
+  const bool mla = c->attn == FP4KV_MLA;
+  d.n_split = mla ? p.n_split : 0;
+  d.tiles_per_split = mla ? p.tiles_per_split : 0;
+  d.n_waves = mla ? 0 : p.n_split;
   d.softmax_scale = softmax_scale;
   const float l2d = (float)(1.4426950408889634 / (double)c->head_dim);
   const float l2 = (float)1.4426950408889634;
@@ -151,9 +187,11 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.q = q;
   d.block_table = block_table;
   d.seq_lens = seq_lens;
-  size_t rows = (size_t)batch * hq * p.n_split;
+  const size_t rows = mla ? (size_t)batch * hq * p.n_split
+                         : ((size_t)p.n_split + (size_t)batch * c->num_kv_heads) * (size_t)group;
   d.ws_o = (float *)ws;
   d.ws_ml = (float *)ws + rows * (size_t)c->head_dim;
+  d.ws_meta = mla ? nullptr : (int32_t *)(d.ws_ml + rows * 2);
   d.out = out;
   d.zero_blocks = zero;
   return FP4KV_OK;

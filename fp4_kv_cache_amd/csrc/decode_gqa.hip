@@ -8,7 +8,7 @@
 // transposed and its probabilities are quantized to FP4 in registers, scaled so
 // that E4M3 block scales keep long-context probabilities away from zero.
 //
-// Mapping onto CDNA4 (one wave = one workgroup = one (sequence, KV head, split)):
+// Mapping onto CDNA4 (one wave = one workgroup = an equal share of all tiles of the batch):
 //  * v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 operands: A = 16 tokens x 128
 //    channels of K (lane l: token row l%16, channels 32*(l/16)..+31), B = the
 //    stacked query rows, D lane l = column l%16, token rows 4*(l/16)..+3.
@@ -140,6 +140,88 @@ __device__ __forceinline__ void load_v(const DecodeArgs &a, Tile &v, const int *
 // j = 0..3) with two float4 of padding after every 32 tokens (LDS bank spread).
 __device__ __forceinline__ int sk_index(int tok, int par) { return tok * 2 + par + 2 * (tok >> 5); }
 
+
+// ---------------- balanced partition of the work ----------------
+// The work of one launch is the list of all 128-token tiles of all (sequence, KV head)
+// units, in the order u = b * Hkv + kvh, tiles in sequence order within a unit.  Wave i of
+// the W waves that get work takes tiles [floor(i T / W), floor((i+1) T / W)) of this list
+// (T tiles in all), so every wave streams the same number of tiles however ragged the
+// sequence lengths are.  A wave whose range crosses unit boundaries writes one partial
+// per unit it touches, into slot i + u: the ranges are ordered like the units, so no two
+// (wave, unit) pairs share a slot and the slots of one unit are consecutive.
+constexpr int kMinTilesPerWave = 4;
+
+// Tiles of a sequence, with its length clamped to [0, max_pages * P] (the pages the
+// block table can name).
+__device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int b) {
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : min(L, a.max_pages * a.page_size);
+  return (L + 127) >> 7;
+}
+
+__device__ __forceinline__ long uni_l(long v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)(v & 0xffffffffL));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+  return (long)(((unsigned long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// The wave's share: the current unit (b, kvh) with its n tiles starting at flattened
+// index ustart, and the flattened range [x, x1) still to do.
+struct Share {
+  long x, x1, ustart, total;
+  int b, kvh, n, waves;
+};
+
+// Wave count W and total T as every kernel of a launch computes them.
+__device__ __forceinline__ void work_total(const DecodeArgs &a, int lane, long &total, int &waves) {
+  long t = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64)
+    if (b0 + lane < a.batch) t += seq_tiles(a, b0 + lane);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+  total = uni_l(t * a.hkv);
+  const long useful = (total + kMinTilesPerWave - 1) / kMinTilesPerWave;
+  waves = (int)(useful < (long)a.n_waves ? useful : (long)a.n_waves);
+}
+
+// Wave that holds flattened tile x.
+__device__ __forceinline__ long owner_of(long x, long total, int waves) {
+  return ((x + 1) * waves + total - 1) / total - 1;
+}
+
+// Finds the wave's share; false when it has no tiles.
+__device__ bool find_share(const DecodeArgs &a, int wave, int lane, Share &s) {
+  work_total(a, lane, s.total, s.waves);
+  if (wave >= s.waves) return false;
+  const long T = s.total, W = s.waves;
+  s.x = wave * T / W;
+  s.x1 = (wave + 1) * T / W;
+  // the sequence whose units hold tile x: scan the tile counts 64 sequences at a time
+  long carry = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int t = b0 + lane < a.batch ? seq_tiles(a, b0 + lane) : 0;
+    int incl = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    const unsigned long long m = __ballot((carry + incl) * a.hkv > s.x);
+    if (m) {
+      const int j = __builtin_ctzll(m);
+      const int n = __builtin_amdgcn_readfirstlane(__shfl(t, j));
+      const long before = uni_l(carry + __shfl(incl, j) - n);   // tiles of sequences < b
+      s.b = b0 + j;
+      s.n = n;
+      s.kvh = (int)((s.x - before * a.hkv) / n);
+      s.ustart = before * a.hkv + (long)s.kvh * n;
+      return true;
+    }
+    carry += __shfl(incl, 63);
+  }
+  return false;   // not reached: x < T
+}
+
 template <int FMT, int G, int P>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_partials(DecodeArgs a) {
   constexpr int D = 128;
@@ -151,22 +233,43 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   static_assert(P >= 16 && (P % B) == 0, "page size");
 
   const int lane = threadIdx.x;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int L = a.seq_lens[b];
-  const int ntiles = (L + 127) >> 7;
-  const int tb = split * a.tiles_per_split;
-  const int te = min(ntiles, tb + a.tiles_per_split);
-  if (tb >= te) return;
-  const int last_lp = min((L - 1) / P, a.max_pages - 1);
+  const int wave = blockIdx.x;
+  Share sh;
+  if (!find_share(a, wave, lane, sh)) return;
 
   __shared__ uint32_t qc[2][G][D / 8];
   __shared__ int qe[2][G][NBLK];
   __shared__ float qg[2][G];
   __shared__ uint32_t lut[256];                // E4M3 value scale -> four E8M0 pass bytes
   __shared__ float4 sk[128 * 2 + 8];           // NVFP4 key scales of the tile (sk_index)
-  // physical page ids of the split's tiles: entry (tile - tb) * NPT + j is logical page
+  // physical page ids of the segment's tiles: entry (tile - tb) * NPT + j is logical page
   // tile * 128 / P + j (clamped to the sequence), so per-tile lookups are LDS reads
   __shared__ int pgl[kMaxSplitPages];
+
+  // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale), for NVFP4 values:
+  // byte j is E - j + 127 when bit j of (implicit bit, m2, m1, m0) is set, else 0
+  // (read after the first segment's barrier below)
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int c = lane + 64 * i;
+    const int ef = (c >> 3) & 15, m = c & 7;
+    const int E = (ef ? ef : 1) - 7 + 127;
+    uint32_t w = (ef ? (uint32_t)E : 0u) | ((m & 4) ? (uint32_t)(E - 1) << 8 : 0u) |
+                 ((m & 2) ? (uint32_t)(E - 2) << 16 : 0u) | ((m & 1) ? (uint32_t)(E - 3) << 24 : 0u);
+    lut[c] = c < 0x7F ? w : 0u;
+  }
+  int nzero = 0;
+  const bool count_zero = a.zero_blocks != nullptr;
+
+  // one segment per (sequence, KV head) unit the wave's share touches
+  for (;;) {
+  const int b = sh.b, kvh = sh.kvh;
+  const int L = min(a.seq_lens[b], a.max_pages * P);   // > 0: the unit has tiles
+  const long uend = sh.ustart + sh.n;
+  const int tb = (int)(sh.x - sh.ustart);
+  const int te = (int)((sh.x1 < uend ? sh.x1 : uend) - sh.ustart);
+  const int last_lp = min((L - 1) / P, a.max_pages - 1);
+  __syncthreads();   // the previous segment has finished reading the staged query and page ids
 
   // The query rows of this KV head go out first.  Lane l holds EPL consecutive channels
   // (c0 = EPL * (l % LPR)) of stacked head r = l / LPR, i.e. elements EPL*l .. EPL*l + EPL-1
@@ -278,17 +381,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if ((lane % BL) == 0) qe[k][qr][c0 / B] = e;
     if ((lane % LPR) == 0) qg[k][qr] = gq;
   }
-  // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale), for NVFP4 values:
-  // byte j is E - j + 127 when bit j of (implicit bit, m2, m1, m0) is set, else 0
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int c = lane + 64 * i;
-    const int ef = (c >> 3) & 15, m = c & 7;
-    const int E = (ef ? ef : 1) - 7 + 127;
-    uint32_t w = (ef ? (uint32_t)E : 0u) | ((m & 4) ? (uint32_t)(E - 1) << 8 : 0u) |
-                 ((m & 2) ? (uint32_t)(E - 2) << 16 : 0u) | ((m & 1) ? (uint32_t)(E - 3) << 24 : 0u);
-    lut[c] = c < 0x7F ? w : 0u;
-  }
   __syncthreads();
 
   const int q4 = lane >> 4;        // lane group: channel block (A/B operands) or token group (D)
@@ -331,10 +423,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   v4f o_run[8];
 #pragma unroll
   for (int cg = 0; cg < 8; cg++) o_run[cg] = v4f{0.f, 0.f, 0.f, 0.f};
-  int nzero = 0;
   const float inv6gp = 1.0f / (6.0f * 0.0009765625f);   // fl32(1 / fl32(6 * 2^-10))
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  const bool count_zero = a.zero_blocks != nullptr;
 
   // Tile `tile`: keys in kt, values in vt; the keys of tile + 1 are loaded into kn at the
   // start, the values of tile + 1 into vt once P.V has read it.
@@ -523,9 +613,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const float l_tot = sum_x32(sum_x16(l_run));
   const int r = FMT == kFmtNV ? (n & 7) : n;
   const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (r & 1) == 0 && r < NR;
+  const long u = (long)b * a.hkv + kvh;
+  const long slot = wave + u;
   if (rep) {
-    const int head = kvh * G + (r >> 1);
-    const long rowi = ((long)b * a.hq + head) * a.n_split + split;
+    const long rowi = slot * G + (r >> 1);
     const float gv = (FMT == kFmtNV ? a.gv[kvh] : 1.0f) * f_run;
 #pragma unroll
     for (int cg = 0; cg < 8; cg++) {
@@ -534,6 +625,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
     if (q4 == 0) *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run, l_tot};
   }
+  // the wave holding the unit's first tile records where the unit's partials are
+  if (tb == 0 && lane == 0) {
+    const long last = owner_of(uend - 1, sh.total, sh.waves);
+    *(int2 *)(a.ws_meta + 2 * u) = int2{(int)slot, (int)(last - wave + 1)};
+  }
+  if (sh.x1 <= uend) break;
+  // next unit with tiles
+  sh.x = sh.ustart = uend;
+  if (++sh.kvh == a.hkv) {
+    sh.kvh = 0;
+    do {
+      if (++sh.b >= a.batch) break;
+      sh.n = seq_tiles(a, sh.b);
+    } while (sh.n == 0);
+    if (sh.b >= a.batch) break;   // not reached: the share ends inside the batch
+  }
+  }   // segments
   if (a.zero_blocks) {
     int z = nzero;
 #pragma unroll
@@ -542,54 +650,51 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
-// One wave per (sequence, query head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// Lanes first take one split each for (m, l); the weights then go through LDS to the
-// channel loop (lane = 2 channels), whose loads are independent.
+// One wave per (sequence, query head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+// over the partials of the head's (sequence, KV head) unit.  Lanes first take one partial
+// each for (m, l); the weights then go through LDS to the channel loop (lane = 2
+// channels), whose loads are independent.
 __global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
   const int row = blockIdx.x, lane = threadIdx.x;
-  const int b = row / a.hq;
-  const int L = a.seq_lens[b];
-  const int ntiles = (L + 127) >> 7;
-  const int nv = min((ntiles + a.tiles_per_split - 1) / a.tiles_per_split, a.n_split);
+  const int b = row / a.hq, h = row % a.hq;
+  const int G = a.group;
+  const long u = (long)b * a.hkv + h / G;
   float2 *dst = (float2 *)(a.out + (long)row * 128) + lane;
-  if (nv == 0) { *dst = float2{0.f, 0.f}; return; }
+  if (seq_tiles(a, b) == 0) { *dst = float2{0.f, 0.f}; return; }
+  const int2 meta = *(const int2 *)(a.ws_meta + 2 * u);
+  const int nv = meta.y;
+  const long r0 = (long)meta.x * G + h % G;    // first partial row; one slot holds G rows
+  const float *ml = a.ws_ml + r0 * 2;
+  const float *o = a.ws_o + r0 * 128;
+  const long so = (long)G * 128, sm = 2L * G;  // strides between the unit's partials
   __shared__ float wsh[256];
-  const float *ml = a.ws_ml + (long)row * a.n_split * 2;
-  const float *o = a.ws_o + (long)row * a.n_split * 128;
   float M = -INFINITY;
-  for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[2 * s]);
+  for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[sm * s]);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
   float den = 0.f;
-  for (int s0 = 0; s0 < nv; s0 += 256) {
-    const int cnt = min(256, nv - s0);
-    for (int s = lane; s < cnt; s += 64) {
-      const float w = __builtin_amdgcn_exp2f(ml[2 * (s0 + s)] - M);
-      wsh[s] = w;
-      den = fmaf(w, ml[2 * (s0 + s) + 1], den);
-    }
-  }
+  for (int s = lane; s < nv; s += 64) den = fmaf(__builtin_amdgcn_exp2f(ml[sm * s] - M), ml[sm * s + 1], den);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k);
   float n0 = 0.f, n1 = 0.f;
   for (int s0 = 0; s0 < nv; s0 += 256) {
     const int cnt = min(256, nv - s0);
     __syncthreads();
-    for (int s = lane; s < cnt; s += 64) wsh[s] = __builtin_amdgcn_exp2f(ml[2 * (s0 + s)] - M);
+    for (int s = lane; s < cnt; s += 64) wsh[s] = __builtin_amdgcn_exp2f(ml[sm * (s0 + s)] - M);
     __syncthreads();
     int s = 0;
     for (; s + 4 <= cnt; s += 4) {
-      const float2 v0 = *((const float2 *)(o + (long)(s0 + s) * 128) + lane);
-      const float2 v1 = *((const float2 *)(o + (long)(s0 + s + 1) * 128) + lane);
-      const float2 v2 = *((const float2 *)(o + (long)(s0 + s + 2) * 128) + lane);
-      const float2 v3 = *((const float2 *)(o + (long)(s0 + s + 3) * 128) + lane);
+      const float2 v0 = *((const float2 *)(o + so * (s0 + s)) + lane);
+      const float2 v1 = *((const float2 *)(o + so * (s0 + s + 1)) + lane);
+      const float2 v2 = *((const float2 *)(o + so * (s0 + s + 2)) + lane);
+      const float2 v3 = *((const float2 *)(o + so * (s0 + s + 3)) + lane);
       n0 = fmaf(wsh[s], v0.x, n0); n1 = fmaf(wsh[s], v0.y, n1);
       n0 = fmaf(wsh[s + 1], v1.x, n0); n1 = fmaf(wsh[s + 1], v1.y, n1);
       n0 = fmaf(wsh[s + 2], v2.x, n0); n1 = fmaf(wsh[s + 2], v2.y, n1);
       n0 = fmaf(wsh[s + 3], v3.x, n0); n1 = fmaf(wsh[s + 3], v3.y, n1);
     }
     for (; s < cnt; s++) {
-      const float2 v = *((const float2 *)(o + (long)(s0 + s) * 128) + lane);
+      const float2 v = *((const float2 *)(o + so * (s0 + s)) + lane);
       n0 = fmaf(wsh[s], v.x, n0);
       n1 = fmaf(wsh[s], v.y, n1);
     }
@@ -614,7 +719,7 @@ static hipError_t launch_g(const DecodeArgs &a, dim3 grid, hipStream_t s) {
 
 hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  dim3 grid((unsigned)a.n_split, (unsigned)a.hkv, (unsigned)a.batch);
+  const dim3 grid((unsigned)a.n_waves);
   if (a.fmt == kFmtNV) {
     switch (a.group) {
       case 1: return launch_g<kFmtNV, 1>(a, grid, s);

@@ -99,5 +99,9 @@ def test_workspace_and_group_checks(lib):
 
 def test_split_plan_sizes(lib):
     c = _desc(num_kv_heads=8)
-    # Qwen3-4B shape: 16 x 8 units, 256 tiles -> 16 splits of 16 tiles
-    assert L.fp4_decode_workspace_bytes(c, 16, 32, 32768) == 16 * 32 * 16 * 130 * 4
+    # Qwen3-4B shape: 16 x 8 (sequence, KV head) units; 2048 waves share the tiles, so the
+    # workspace holds 2048 + 128 slots of 4 partial rows (128 + 2 floats) and 128 slot ranges
+    assert L.fp4_decode_workspace_bytes(c, 16, 32, 32768) == (2048 + 128) * 4 * 130 * 4 + 128 * 8
+    # tiny batches: no more waves than shares of 4 tiles (2 units x 32 tiles -> 16 waves)
+    c2 = _desc(num_kv_heads=2)
+    assert L.fp4_decode_workspace_bytes(c2, 1, 8, 4096) == (16 + 2) * 4 * 130 * 4 + 2 * 8

@@ -106,6 +106,19 @@ def test_decode_mxfp4_ragged(torch_dev, hq):
     say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
 
 
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b"])
+def test_decode_shares_span_units(torch_dev, name):
+    """Every wave takes an equal share of all tiles of the batch: with a few tiles per
+    (sequence, KV head) unit, one share runs from inside one unit across whole units (and
+    empty sequences) into the next, and long units are split over several waves."""
+    lens = np.array([1, 0, 130, 600, 0, 0, 257, 64, 1000, 5, 0, 385], np.int32)
+    w = W.workload(name, batch=len(lens))
+    say("decode shares across units", name, lens.tolist())
+    built = harness.build(w, lens=lens)
+    worst, worst_ref, zg, zo = compare_gqa(built, tol=TOL)
+    say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
+
+
 def test_decode_underflow_no_zero_blocks(torch_dev):
     w = W.workload("long_underflow", batch=1)
     lens = np.array([16384], np.int32)
