@@ -179,12 +179,22 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
 
 /* The two halves of fp4_decode_attention, for callers that merge split-K
  * partials themselves (e.g. across devices holding different pages of one
- * sequence) or time the stages separately.  fp4_decode_partials writes, for
- * every (sequence, query head, split), the unnormalized output o, the running
- * base-2 maximum m and the denominator l into the workspace; fp4_decode_merge
- * combines them: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  Both
+ * sequence) or time the stages separately.  fp4_decode_partials writes
+ * partial results (o unnormalized, m the base-2 running maximum, l the
+ * denominator) into the workspace; fp4_decode_merge combines the partials of
+ * each query head: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  Both
  * take the same arguments as fp4_decode_attention and must see the same batch
- * shape and seq_lens. */
+ * shape and seq_lens.
+ *
+ * Workspace layout (floats unless stated; W = the wave count the library plans
+ * for the batch shape, U = batch * Hkv, g = num_q_heads / Hkv):
+ *   GQA  o [W + U][g][head_dim], then (m, l) [W + U][g][2], then i32 (first
+ *        slot, count) [U].  The tiles of all (sequence, KV head) units, in the
+ *        order u = b * Hkv + kvh, are shared out equally among the waves; the
+ *        partials of unit u are the `count` consecutive slots from `first`,
+ *        row h % g of each slot belonging to query head h.  Units of empty
+ *        sequences have no partials (their range is not written).
+ *   MLA  o [batch * num_q_heads][n_split][512], then (m, l) in the same order. */
 int fp4_decode_partials(const fp4kv_cache *c, const void *q, int q_dtype, int batch,
                         int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
                         const int32_t *seq_lens, float softmax_scale, void *workspace,
