@@ -393,26 +393,37 @@ __global__ __launch_bounds__(128) void v_append_gqa(AppendArgs a) {
 // ---------------------------------------------------------------------------------------------
 // MLA latent: one workgroup (256 threads) per (leading token) = one B-token tile row of
 // the sequence.  The new tokens are smoothed and rotated over 512 channels in LDS, the
-// earlier tokens of the tile come from the stage, then one thread per B x B tile runs
-// the scale search with the objective in (token, channel) order.
+// earlier tokens of the tile come from the stage.  The scale search runs one thread per
+// (B x B tile, candidate), each summing its objective in (token, channel) order; the
+// first candidate with a strictly smaller objective wins, as in a sequential search.
+
+constexpr int kNoCand = -(1 << 30);   // marks a scale candidate outside the code range
 
 template <int FMT>
 __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
   constexpr int B = FMT == kFmtNV ? 16 : 32;
   constexpr int D = 512;
-  constexpr int NT = D / B;
-  __shared__ float xs[B][D];
+  constexpr int NT = D / B;                  // tiles of the row
+  constexpr int NC = FMT == kFmtNV ? 5 : 3;  // scale candidates
+  constexpr int DP = D + D / 16;             // row length with one pad word per 16 channels
+  // channel ch of token k at xs[k][ch + ch / 16]: tile-strided reads fall in distinct banks
+  __shared__ float xs[B][DP];
+  __shared__ float errs[NC][NT];
+  __shared__ int cand[NC][NT];
+  __shared__ float rsc[NT];
+  __shared__ int ebest[NT];
   const int i = blockIdx.x, tid = threadIdx.x;
   BlockSpan sp = block_span<B>(a, i);
   if (!sp.ok) return;
   float *stage = a.stage + (long)sp.seq * B * D;
   const float *ksi = a.ksi;
+  auto X = [&](int k, int ch) -> float & { return xs[k][ch + (ch >> 4)]; };
   for (int e = tid; e < B * D; e += 256) {
     int k = e / D, ch = e % D;
     float x = 0.0f;
     if (k < sp.first) x = stage[k * D + ch];
     else if (k < sp.first + sp.n_new) x = load_elem(a.k_new, (long)(i + k - sp.first) * D + ch, a.bf16) * ksi[ch];
-    xs[k][ch] = x;
+    X(k, ch) = x;
   }
   __syncthreads();
   // FWHT over the rows of the new tokens (stages h = 1, 2, ..., 256)
@@ -421,9 +432,9 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
       int k = e / (D / 2), w = e % (D / 2);
       if (k < sp.first || k >= sp.first + sp.n_new) continue;
       int idx = (w / h) * 2 * h + (w % h);
-      float p = xs[k][idx], q = xs[k][idx + h];
-      xs[k][idx] = p + q;
-      xs[k][idx + h] = p - q;
+      float p = X(k, idx), q = X(k, idx + h);
+      X(k, idx) = p + q;
+      X(k, idx + h) = p - q;
     }
     __syncthreads();
   }
@@ -431,7 +442,7 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
   if (sp.first + sp.n_new < B) {
     for (int e = tid; e < B * D; e += 256) {
       int k = e / D, ch = e % D;
-      if (k >= sp.first && k < sp.first + sp.n_new) stage[k * D + ch] = xs[k][ch];
+      if (k >= sp.first && k < sp.first + sp.n_new) stage[k * D + ch] = X(k, ch);
     }
   }
   // rope keys of the new tokens, copied unquantized
@@ -440,92 +451,107 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
     a.k_rope[((long)sp.page * a.page_size + sp.off0 + sp.first + k) * a.rope_dim + r] =
         ((const uint16_t *)a.k_rope_new)[(long)(i + k) * a.rope_dim + r];
   }
-  if (tid >= NT) return;
-  const int ct = tid;
-  // amax over the tile, then the search with the objective in (token, channel) order
-  float amax = 0.0f;
-  for (int k = 0; k < B; k++)
+  // ---- scale search: thread = (candidate kk, tile ct)
+  const float G = FMT == kFmtNV ? a.gk[0] : 1.0f;
+  if (tid < NC * NT) {
+    const int ct = tid % NT, kk = tid / NT;
+    float amax = 0.0f;
+    for (int k = 0; k < B; k++)
 #pragma unroll
-    for (int cc = 0; cc < B; cc++) amax = fmaxf(amax, fabsf(xs[k][ct * B + cc]));
-  uint32_t sbyte;
-  float G = 1.0f, r = 1.0f;
-  int eb = 0;
-  if (FMT == kFmtNV) {
-    G = a.gk[0];
-    uint32_t c0 = nv_default_scale(amax, G), best = c0;
-    float best_err = 0.0f;
-    const int deltas[5] = {0, 1, -1, -2, -3};
-    for (int kk = 0; kk < 5; kk++) {
-      int c = (int)c0 + deltas[kk];
-      if (c < 0 || c > 0x7E) continue;
-      float S = e4m3_dec((uint32_t)c), sg = S * G, rr = (sg != 0.0f) ? 1.0f / sg : 0.0f;
-      float err = 0.0f;
-      for (int k = 0; k < B; k++)
+      for (int cc = 0; cc < B; cc++) amax = fmaxf(amax, fabsf(X(k, ct * B + cc)));
+    float err = 0.0f;
+    int c = 0;
+    bool valid;
+    if constexpr (FMT == kFmtNV) {
+      const int deltas[5] = {0, 1, -1, -2, -3};
+      c = (int)nv_default_scale(amax, G) + deltas[kk];
+      valid = c >= 0 && c <= 0x7E;
+      if (valid) {
+        const float S = e4m3_dec((uint32_t)c), sg = S * G, rr = (sg != 0.0f) ? 1.0f / sg : 0.0f;
+        for (int k = 0; k < B; k++)
 #pragma unroll
-        for (int cc = 0; cc < B; cc++) {
-          float x = xs[k][ct * B + cc];
-          float xh = (e2m1_dec(e2m1_enc(x * rr)) * S) * G;
-          float dd = x - xh;
-          err = err + dd * dd;
-        }
-      if (kk == 0 || err < best_err) { best_err = err; best = (uint32_t)c; }
+          for (int cc = 0; cc < B; cc++) {
+            const float x = X(k, ct * B + cc);
+            const float xh = (e2m1_dec(e2m1_enc(x * rr)) * S) * G;
+            const float dd = x - xh;
+            err = err + dd * dd;
+          }
+      }
+    } else {
+      const int deltas[3] = {0, 1, -1};
+      c = mx_exp(amax) + deltas[kk];
+      valid = c >= -127 && c <= 127;
+      if (valid) {
+        for (int k = 0; k < B; k++)
+#pragma unroll
+          for (int cc = 0; cc < B; cc++) {
+            const float x = X(k, ct * B + cc);
+            const float xh = ldexpf(e2m1_dec(e2m1_enc(ldexpf(x, -c))), c);
+            const float dd = x - xh;
+            err = err + dd * dd;
+          }
+      }
     }
-    sbyte = best;
-    float S = e4m3_dec(best), sg = S * G;
-    r = (sg != 0.0f) ? 1.0f / sg : 0.0f;
-  } else {
-    int e0 = mx_exp(amax), best = e0;
-    float best_err = 0.0f;
-    const int deltas[3] = {0, 1, -1};
-    for (int kk = 0; kk < 3; kk++) {
-      int e = e0 + deltas[kk];
-      if (e < -127 || e > 127) continue;
-      float err = 0.0f;
-      for (int k = 0; k < B; k++)
-#pragma unroll
-        for (int cc = 0; cc < B; cc++) {
-          float x = xs[k][ct * B + cc];
-          float xh = ldexpf(e2m1_dec(e2m1_enc(ldexpf(x, -e))), e);
-          float dd = x - xh;
-          err = err + dd * dd;
-        }
-      if (kk == 0 || err < best_err) { best_err = err; best = e; }
-    }
-    sbyte = (uint32_t)(best + 127);
-    eb = best;
+    errs[kk][ct] = err;
+    cand[kk][ct] = valid ? c : kNoCand;
   }
+  __syncthreads();
+  uint32_t sbyte_t = 0;
+  if (tid < NT) {
+    const int ct = tid;
+    int best = cand[0][ct];               // the default candidate is always in range
+    float best_err = errs[0][ct];
+    for (int kk = 1; kk < NC; kk++)
+      if (cand[kk][ct] != kNoCand && errs[kk][ct] < best_err) { best_err = errs[kk][ct]; best = cand[kk][ct]; }
+    if constexpr (FMT == kFmtNV) {
+      const float S = e4m3_dec((uint32_t)best), sg = S * G;
+      rsc[ct] = (sg != 0.0f) ? 1.0f / sg : 0.0f;
+      sbyte_t = (uint32_t)best;
+    } else {
+      ebest[ct] = best;
+      sbyte_t = (uint32_t)(best + 127);
+    }
+    a.k_scales[((long)sp.page * (a.page_size / B) + sp.off0 / B) * NT + ct] = (uint8_t)sbyte_t;
+  }
+  __syncthreads();
   const long pbase = (long)sp.page * a.page_size;
-  // token-major codes (the key operand) ...
-  for (int k = 0; k < B; k++) {
+  // token-major codes (the key operand): task = (token k, tile ct), B / 2 bytes
+  for (int e = tid; e < B * NT; e += 256) {
+    const int k = e / NT, ct = e % NT;
+    const float r = FMT == kFmtNV ? rsc[ct] : 0.0f;
+    const int eb = FMT == kFmtNV ? 0 : ebest[ct];
     uint8_t *dst = a.k_codes + (pbase + sp.off0 + k) * (D / 2) + ct * (B / 2);
 #pragma unroll
     for (int j = 0; j < B / 2; j += 4) {
       uint32_t w = 0;
 #pragma unroll
       for (int u = 0; u < 8; u++) {
-        float x = xs[k][ct * B + 2 * j + u];
-        uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
+        const float x = X(k, ct * B + 2 * j + u);
+        const uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
         w |= q << (4 * u);
       }
       *(uint32_t *)(dst + j) = w;
     }
   }
-  // ... and the same codes channel-major (the value operand): row c holds the page's tokens
-  for (int cc = 0; cc < B; cc++) {
-    uint8_t *dst = a.v_codes + ((long)sp.page * D + ct * B + cc) * (a.page_size / 2) + sp.off0 / 2;
+  // ... and the same codes channel-major (the value operand): task = channel ch, row ch holds
+  // the page's tokens
+  for (int ch = tid; ch < D; ch += 256) {
+    const int ct = ch / B;
+    const float r = FMT == kFmtNV ? rsc[ct] : 0.0f;
+    const int eb = FMT == kFmtNV ? 0 : ebest[ct];
+    uint8_t *dst = a.v_codes + ((long)sp.page * D + ch) * (a.page_size / 2) + sp.off0 / 2;
 #pragma unroll
     for (int j = 0; j < B / 2; j += 4) {
       uint32_t w = 0;
 #pragma unroll
       for (int u = 0; u < 8; u++) {
-        float x = xs[2 * j + u][ct * B + cc];
-        uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
+        const float x = X(2 * j + u, ch);
+        const uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
         w |= q << (4 * u);
       }
       *(uint32_t *)(dst + j) = w;
     }
   }
-  a.k_scales[((long)sp.page * (a.page_size / B) + sp.off0 / B) * NT + ct] = (uint8_t)sbyte;
 }
 
 // ---------------------------------------------------------------------------------------------

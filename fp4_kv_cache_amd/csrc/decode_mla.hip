@@ -7,7 +7,8 @@
 // stacked query rows sharing each latent tile, transposed softmax with fused
 // underflow-aware FP4 probability quantization.
 //
-// Mapping onto CDNA4 (one wave = one workgroup = one (sequence, group of 16 heads, split)):
+// Mapping onto CDNA4 (one workgroup of two waves = one (sequence, group of 16 heads, split),
+// each wave owning half of the 512 latent channels):
 //  * The latent is quantized in 16-token x 16-channel tiles with an E4M3 scale each.  For
 //    Q.K^T the latent codes are widened to fp16 with their tile scale (code * S has at
 //    most six significant bits, so the fp16 value is exact) and the dual-residual query
@@ -70,15 +71,23 @@ __device__ __forceinline__ h2 e4m3_h2(uint32_t byte) {
   return h2{h, h};
 }
 
-// MLA partials.  Grid: one-dimensional; the 16-head groups of one (sequence, split) get
-// ids with equal residue mod 8 so that they tend to share an XCD's L2 (they read the
-// same latent tiles).  Performance only: any placement gives the same result.
+// MLA partials.  A workgroup of two waves serves one (sequence, group of 16 query heads,
+// split).  Wave hc owns latent channels 256 hc .. 256 hc + 255: it keeps its half of the
+// Q1 / Q2 operands in registers, computes the Q1 and Q2 dot products over its channels,
+// and accumulates P.V for its channels only.  The half dot products meet in LDS once per
+// tile; both waves add them (addition is commutative, so both get the same sums), compute
+// the 64-channel rope dot product in full, and form the same logits, softmax state and P.
+// Grid: one-dimensional; the head groups of one (sequence, split) get ids with equal
+// residue mod 8 so that they tend to share an XCD's L2 (they read the same latent tiles).
+// Performance only: any placement gives the same result.
 template <int P>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_partials(DecodeArgs a) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partials(DecodeArgs a) {
   constexpr int D = kMlaD, R = kMlaR, HG = kMlaHeads;
+  constexpr int DH = D / 2;                     // latent channels per wave
   constexpr int NPT = P >= 128 ? 1 : 128 / P;
+  constexpr int NB = 2;                         // ring of token-group loads, NB - 1 ahead (NB divides 8)
   static_assert(P >= 16 && P % 16 == 0, "page size");
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, hc = tid >> 6;
   const int nhg = a.hq / HG;
   const int units = a.batch * a.n_split;
   int id = blockIdx.x;
@@ -96,48 +105,52 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int last_lp = min((L - 1) / P, a.max_pages - 1);
   const int h0 = hg * HG;
 
-  // Q1 / Q2 block-scaled values (exact fp16); rows padded by 16 bytes so that the 16 lanes
-  // of a lane group (16 heads, same channels) read from different LDS banks
-  __shared__ _Float16 qh[2][HG][D + 8];
+  // The query (exact fp16 Q1 / Q2 values, rows padded by 16 bytes) is staged here once;
+  // afterwards the same bytes carry the half dot products the two waves exchange,
+  // [wave][group][Q1 / Q2][lane] float4.
+  constexpr int QH_BYTES = 2 * HG * (D + 8) * 2;
+  constexpr int SX_BYTES = 2 * 8 * 2 * 64 * 16;
+  __shared__ __align__(16) uint8_t stage[QH_BYTES > SX_BYTES ? QH_BYTES : SX_BYTES];
+  _Float16 (*qh)[HG][D + 8] = reinterpret_cast<_Float16 (*)[HG][D + 8]>(stage);
   __shared__ float qg[2][HG];
   __shared__ uint32_t lut[256];
   __shared__ int pgl[kMaxSplitPages];
 
-  for (int e = lane; e < (te - tb) * NPT; e += 64)
+  for (int e = tid; e < (te - tb) * NPT; e += 128)
     pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
 
   // ---------------- prologue: smoothing, rotation, dual-residual FP4 query ----------------
-  // lane l: head r = l / 4, channels c0 = 128 * (l % 4) .. + 127
+  // thread t: head r = t / 8, channels c0 = 64 * (t % 8) .. + 63
   {
-    const int r = lane >> 2, c0 = 128 * (lane & 3);
+    const int r = tid >> 3, c0 = 64 * (tid & 7);
     const long q0 = ((long)b * a.hq + h0 + r) * (D + R) + c0;
-    float y[128];
+    float y[64];
     if (a.q_bf16) {
       const uint16_t *qp = (const uint16_t *)a.q + q0;
 #pragma unroll
-      for (int j = 0; j < 128; j++) y[j] = bf16_to_f32(qp[j]);
+      for (int j = 0; j < 64; j++) y[j] = bf16_to_f32(qp[j]);
     } else {
       const float *qp = (const float *)a.q + q0;
 #pragma unroll
-      for (int j = 0; j < 128; j++) y[j] = qp[j];
+      for (int j = 0; j < 64; j++) y[j] = qp[j];
     }
 #pragma unroll
-    for (int j = 0; j < 128; j++) y[j] = y[j] * a.qs[c0 + j];
-    // Walsh-Hadamard stages h = 1 .. 64 inside the lane, 128 and 256 with lanes l ^ 1, l ^ 2
+    for (int j = 0; j < 64; j++) y[j] = y[j] * a.qs[c0 + j];
+    // Walsh-Hadamard stages h = 1 .. 32 inside the lane, 64, 128, 256 with lanes t ^ 1, ^ 2, ^ 4
 #pragma unroll
-    for (int h = 1; h < 128; h <<= 1)
+    for (int h = 1; h < 64; h <<= 1)
 #pragma unroll
-      for (int j = 0; j < 128; j++)
+      for (int j = 0; j < 64; j++)
         if ((j & h) == 0) {
           const float x0 = y[j], x1 = y[j + h];
           y[j] = x0 + x1;
           y[j + h] = x0 - x1;
         }
 #pragma unroll
-    for (int m = 1; m <= 2; m <<= 1) {
-      const bool upper = (lane & m) != 0;
+    for (int m = 1; m <= 4; m <<= 1) {
+      const bool upper = (tid & m) != 0;
 #pragma unroll
-      for (int j = 0; j < 128; j++) {
+      for (int j = 0; j < 64; j++) {
         const float o = __shfl_xor(y[j], m);
         y[j] = upper ? o - y[j] : y[j] + o;
       }
@@ -147,14 +160,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int k = 0; k < 2; k++) {
       float rmax = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 128; j++) rmax = fmaxf(rmax, fabsf(y[j]));
+      for (int j = 0; j < 64; j++) rmax = fmaxf(rmax, fabsf(y[j]));
       rmax = fmaxf(rmax, __shfl_xor(rmax, 1));
       rmax = fmaxf(rmax, __shfl_xor(rmax, 2));
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 4));
       const float gq = rmax / 1536.0f;
       const float sixg = 6.0f * gq;
       const float inv6g = sixg != 0.0f ? 1.0f / sixg : 0.0f;
 #pragma unroll
-      for (int blk = 0; blk < 8; blk++) {
+      for (int blk = 0; blk < 4; blk++) {
         float bmax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; i++) bmax = fmaxf(bmax, fabsf(y[16 * blk + i]));
@@ -172,13 +186,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
           y[16 * blk + i] = x - (e2m1_dec(c) * S) * gq;
         }
       }
-      if ((lane & 3) == 0) qg[k][r] = gq;
+      if ((tid & 7) == 0) qg[k][r] = gq;
     }
   }
   // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale) for the P.V passes
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int c = lane + 64 * i;
+  for (int i = 0; i < 2; i++) {
+    const int c = tid + 128 * i;
     const int ef = (c >> 3) & 15, m = c & 7;
     const int E = (ef ? ef : 1) - 7 + 127;
     uint32_t w = (ef ? (uint32_t)E : 0u) | ((m & 4) ? (uint32_t)(E - 1) << 8 : 0u) |
@@ -189,46 +203,51 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
   const int q4 = lane >> 4;        // lane group
   const int n = lane & 15;         // operand row / output column = head h0 + n
-  // B operands: Q1 / Q2 rows of head n, channels 128 q4 + 8 s .. + 7 in K-step s, read
-  // from LDS at each use (qh stays resident)
-  const h8 *bq0 = (const h8 *)&qh[0][n][128 * q4];
-  const h8 *bq1 = (const h8 *)&qh[1][n][128 * q4];
-  // rope query (bf16), channels 32 s + 8 q4 .. + 7 in K-step s
+  // B operands of this wave's channels: Q.K^T K-step st, lane group q4, element j is
+  // latent channel DH hc + 64 q4 + 8 st + j (the lane's A operand holds the same channels)
+  h8 bq0[8], bq1[8];
+#pragma unroll
+  for (int st = 0; st < 8; st++) {
+    bq0[st] = *(const h8 *)&qh[0][n][DH * hc + 64 * q4 + 8 * st];
+    bq1[st] = *(const h8 *)&qh[1][n][DH * hc + 64 * q4 + 8 * st];
+  }
+  // rope query (bf16): K-step s, lane group q4, element j is rope channel 32 s + 8 q4 + j
   bh8 bqr[2];
   {
-    const long qr = ((long)b * a.hq + h0 + n) * (D + R) + D;
+    const long qr = ((long)b * a.hq + h0 + n) * (D + R) + D + 8 * q4;
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
+    for (int st = 0; st < 2; st++) {
       uint16_t hb[8];
+      if (a.q_bf16) {
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int c = 32 * s + 8 * q4 + j;
-        if (a.q_bf16) {
-          hb[j] = ((const uint16_t *)a.q)[qr + c];
-        } else {  // fp32 rope query rounded to bf16 (nearest even)
-          const uint32_t u = __float_as_uint(((const float *)a.q)[qr + c]);
+        for (int j = 0; j < 8; j++) hb[j] = ((const uint16_t *)a.q)[qr + 32 * st + j];
+      } else {  // fp32 rope query rounded to bf16 (nearest even)
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const uint32_t u = __float_as_uint(((const float *)a.q)[qr + 32 * st + j]);
           hb[j] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
         }
       }
-      __builtin_memcpy(&bqr[s], hb, 16);
+      __builtin_memcpy(&bqr[st], hb, 16);
     }
   }
   const float gk = a.gk[0];
   const float a1 = (qg[0][n] * gk) * a.coef, a2 = (qg[1][n] * gk) * a.coef, cr = a.coef_rope;
+  float4 *sx = reinterpret_cast<float4 *>(stage);   // reused for the exchange (barrier in the loop)
 
   // ---------------- main loop over 128-token tiles ----------------
   float m_run = -INFINITY, l_run = 0.0f, f_run = 1.0f;
-  v4f o_run[32];
+  v4f o_run[16];
 #pragma unroll
-  for (int cg = 0; cg < 32; cg++) o_run[cg] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int cg = 0; cg < 16; cg++) o_run[cg] = v4f{0.f, 0.f, 0.f, 0.f};
   int nzero = 0;
   const float inv6gp = 1.0f / (6.0f * 0.0009765625f);   // fl32(1 / fl32(6 * 2^-10))
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  const bool count_zero = a.zero_blocks != nullptr;
+  const bool count_zero = a.zero_blocks != nullptr && hc == 0;
 
-  // Loads run ahead of use: the latent and rope rows of token group i + 3 (crossing into
-  // the next tile) are issued while group i computes, in a ring of four buffers, and the
-  // next tile's key scales while this tile's last groups compute.
+  // Loads run ahead of use: the latent and rope rows of token group i + NB - 1 (crossing
+  // into the next tile) are issued while group i computes, and the next tile's key scales
+  // while this tile's last groups compute.
   const int trow = 32 * (n >> 2) + (n & 3);   // A-operand row: tile token trow + 4 i in group i
   auto load_group = [&](int tile, int i, uint4 *w) {
     const bool live = tile < te;
@@ -237,77 +256,93 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int t = trow + 4 * i;
     const int pg = pgt[NPT == 1 ? 0 : t / P];
     const long row = (long)pg * P + (tl * 128 + t) % P;
-    const uint8_t *kb = a.k_codes + row * (D / 2) + 64 * q4;
+    const uint8_t *kb = a.k_codes + row * (D / 2) + (DH / 2) * hc + 32 * q4;
     const uint8_t *kr = (const uint8_t *)(a.k_rope + row * R + 8 * q4);
-    w[0] = ld16(kb); w[1] = ld16(kb + 16); w[2] = ld16(kb + 32); w[3] = ld16(kb + 48);
-    w[4] = ld16(kr); w[5] = ld16(kr + 64);
+    w[0] = ld16(kb); w[1] = ld16(kb + 16); w[2] = ld16(kr); w[3] = ld16(kr + 64);
   };
-  // tile scales of the lane's row tokens (token blocks for groups 0-3 and 4-7), channel
-  // blocks 8 q4 .. 8 q4 + 7, as raw E4M3 bytes
-  auto load_scales = [&](int tile, uint2 *sc) {
+  // tile scales (raw E4M3 bytes) of the lane's row tokens, token blocks of groups 0-3 and
+  // 4-7, channel blocks 16 hc + 4 q4 .. + 3
+  auto load_scales = [&](int tile, uint32_t *sc) {
     const int tl = tile < te ? tile : te - 1;
     const int *pgt = pgl + (tl - tb) * NPT;
 #pragma unroll
     for (int hb = 0; hb < 2; hb++) {
       const int t = trow + 16 * hb;
       const int pg = pgt[NPT == 1 ? 0 : t / P];
-      sc[hb] = *(const uint2 *)(a.k_scales + ((long)pg * (P / 16) + ((tl * 128 + t) % P) / 16) * 32 + 8 * q4);
+      sc[hb] = *(const uint32_t *)(a.k_scales + ((long)pg * (P / 16) + ((tl * 128 + t) % P) / 16) * 32 +
+                                   16 * hc + 4 * q4);
     }
   };
-  uint4 gw[4][6];
-  uint2 scn[2];
+  uint4 gw[NB][4];
+  uint32_t scn[2];
   load_scales(tb, scn);
-  load_group(tb, 0, gw[0]);
-  load_group(tb, 1, gw[1]);
-  load_group(tb, 2, gw[2]);
+#pragma unroll
+  for (int i = 0; i < NB - 1; i++) load_group(tb, i, gw[i]);
 
 #pragma unroll 1
   for (int tile = tb; tile < te; tile++) {
     const int tok0 = tile * 128;
     const int *pgt = pgl + (tile - tb) * NPT;
-    h2 sq[2][8];
-#pragma unroll
-    for (int hb = 0; hb < 2; hb++)
-#pragma unroll
-      for (int j = 0; j < 8; j++) sq[hb][j] = e4m3_h2((j < 4 ? scn[hb].x : scn[hb].y) >> (8 * (j & 3)) & 0xFFu);
-    // ---- Q.K^T over 8 token groups of 16
+    const uint32_t scc[2] = {scn[0], scn[1]};   // this tile's key scales (scn is refilled ahead)
+    // ---- Q.K^T: Q1 / Q2 over this wave's channels (to LDS), rope in full, 8 token groups of 16
+    __syncthreads();   // the other wave has read the previous exchange (or the query stage)
+    float4 *mine = sx + (hc * 16) * 64 + lane;
     float s[8][4];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 3 < 8) load_group(tile, i + 3, gw[(i + 3) & 3]);
-      else load_group(tile + 1, i + 3 - 8, gw[(i + 3) & 3]);
+      if (i + NB - 1 < 8) load_group(tile, i + NB - 1, gw[(i + NB - 1) % NB]);
+      else load_group(tile + 1, i + NB - 1 - 8, gw[(i + NB - 1) % NB]);
       if (i == 4) load_scales(tile + 1, scn);
       __builtin_amdgcn_sched_barrier(0);
-      const uint4 *w = gw[i & 3];
-      const uint32_t ws[16] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w,
-                               w[2].x, w[2].y, w[2].z, w[2].w, w[3].x, w[3].y, w[3].z, w[3].w};
+      const uint4 *w = gw[i % NB];
+      const uint32_t ws[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+      h2 sq[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) sq[j] = e4m3_h2((scc[i >> 2] >> (8 * j)) & 0xFFu);
       v4f acc1 = zero, acc2 = zero, accr = zero;
 #pragma unroll
-      for (int st = 0; st < 16; st++) {
-        const h8 av = fp4x8_f16(ws[st], sq[i >> 2][st >> 1]);
+      for (int st = 0; st < 8; st++) {
+        const h8 av = fp4x8_f16(ws[st], sq[st >> 1]);
         acc1 = mfma_f16(av, bq0[st], acc1);
         acc2 = mfma_f16(av, bq1[st], acc2);
       }
-      accr = mfma_bf16(as_bh8(w[4]), bqr[0], accr);
-      accr = mfma_bf16(as_bh8(w[5]), bqr[1], accr);
+      accr = mfma_bf16(as_bh8(w[2]), bqr[0], accr);
+      accr = mfma_bf16(as_bh8(w[3]), bqr[1], accr);
+      mine[64 * (2 * i)] = float4{acc1[0], acc1[1], acc1[2], acc1[3]};
+      mine[64 * (2 * i + 1)] = float4{acc2[0], acc2[1], acc2[2], acc2[3]};
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++) {
-        const float t12 = a1 * acc1[rr] + a2 * acc2[rr];
-        s[i][rr] = t12 + cr * accr[rr];
+      for (int rr = 0; rr < 4; rr++) s[i][rr] = cr * accr[rr];
+    }
+    // ---- logits from the two halves' dot products: raw = half 0 + half 1 (the same sum in
+    // both waves), s = (a1 raw1 + a2 raw2) + cr raw_rope
+    __syncthreads();
+    {
+      const float4 *h0p = sx + lane, *h1p = sx + 16 * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float4 x1 = h0p[64 * (2 * i)], y1 = h1p[64 * (2 * i)];
+        const float4 x2 = h0p[64 * (2 * i + 1)], y2 = h1p[64 * (2 * i + 1)];
+        const float r1[4] = {x1.x + y1.x, x1.y + y1.y, x1.z + y1.z, x1.w + y1.w};
+        const float r2[4] = {x2.x + y2.x, x2.y + y2.y, x2.z + y2.z, x2.w + y2.w};
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) {
+          const float t12 = a1 * r1[rr] + a2 * r2[rr];
+          s[i][rr] = t12 + s[i][rr];
+        }
       }
     }
     // P.V operands of this tile go out before the softmax
     const int tv = 32 * q4;
     const int pgv = pgt[NPT == 1 ? 0 : tv / P];
     const int tp = (tok0 + tv) % P;
-    const uint8_t *srow = a.k_scales + ((long)pgv * (P / 16) + tp / 16) * 32;
-    const uint8_t *vb = a.v_codes + ((long)pgv * D + n) * (P / 2) + tp / 2;
-    uint4 vw[2][8];
+    const uint8_t *srow = a.k_scales + ((long)pgv * (P / 16) + tp / 16) * 32 + 16 * hc;
+    const uint8_t *vb = a.v_codes + ((long)pgv * D + DH * hc + n) * (P / 2) + tp / 2;
+    uint4 vw[2][4];
     __builtin_amdgcn_sched_barrier(0);
-    const uint4 sa0 = ld16(srow), sa1 = ld16(srow + 16), sb0 = ld16(srow + 32), sb1 = ld16(srow + 48);
+    const uint4 sa = ld16(srow), sb = ld16(srow + 32);
 #pragma unroll
-    for (int j = 0; j < 8; j++) vw[0][j] = ld16(vb + (long)j * 16 * (P / 2));
+    for (int j = 0; j < 4; j++) vw[0][j] = ld16(vb + (long)j * 16 * (P / 2));
     __builtin_amdgcn_sched_barrier(0);
     if (tok0 + 128 > L) {
 #pragma unroll
@@ -364,39 +399,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const float gamma = (alpha * f_run) * __builtin_amdgcn_rcpf(f_new);
     f_run = f_new;
 #pragma unroll
-    for (int cg = 0; cg < 32; cg++)
+    for (int cg = 0; cg < 16; cg++)
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = o_run[cg][rr] * gamma;
-    // ---- P.V: channel-major latent (A: channels 16 cg + n, tokens 32 q4 .. + 31)
+    // ---- P.V over this wave's channels: channel-major latent (A: channels DH hc + 16 cg + n,
+    // tokens 32 q4 .. + 31), batches of 4 channel groups, the next batch in flight
     const v8i p0 = {(int)pk[0], (int)pk[1], 0, 0, 0, 0, 0, 0};
     const v8i p1 = {0, 0, (int)pk[2], (int)pk[3], 0, 0, 0, 0};
-    {
-      // channel groups in batches of 8, the next batch's loads in flight during this one
 #pragma unroll
-      for (int bt = 0; bt < 4; bt++) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (bt + 1 < 4) {
+    for (int bt = 0; bt < 4; bt++) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (bt + 1 < 4) {
 #pragma unroll
-          for (int j = 0; j < 8; j++) vw[(bt + 1) & 1][j] = ld16(vb + (long)(8 * (bt + 1) + j) * 16 * (P / 2));
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; j++) vw[(bt + 1) & 1][j] = ld16(vb + (long)(4 * (bt + 1) + j) * 16 * (P / 2));
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-          const int cg = 8 * bt + j;
-          const uint4 vc = vw[bt & 1][j];
-          const v8i av = {(int)vc.x, (int)vc.y, (int)vc.z, (int)vc.w, 0, 0, 0, 0};
-          const uint32_t b0 = cg < 16 ? byte_of(sa0, cg) : byte_of(sa1, cg - 16);
-          const uint32_t b1 = cg < 16 ? byte_of(sb0, cg) : byte_of(sb1, cg - 16);
-          const int l0 = (int)lut[b0], l1 = (int)lut[b1];
-          v4f c = mfma4<0, 0>(av, p0, o_run[cg], l0, pbyte[0]);
-          c = mfma4<1, 0>(av, p0, c, l0, pbyte[0]);
-          c = mfma4<2, 0>(av, p0, c, l0, pbyte[0]);
-          c = mfma4<3, 0>(av, p0, c, l0, pbyte[0]);
-          c = mfma4<0, 0>(av, p1, c, l1, pbyte[1]);
-          c = mfma4<1, 0>(av, p1, c, l1, pbyte[1]);
-          c = mfma4<2, 0>(av, p1, c, l1, pbyte[1]);
-          o_run[cg] = mfma4<3, 0>(av, p1, c, l1, pbyte[1]);
-        }
+      for (int j = 0; j < 4; j++) {
+        const int cg = 4 * bt + j;
+        const uint4 vc = vw[bt & 1][j];
+        const v8i av = {(int)vc.x, (int)vc.y, (int)vc.z, (int)vc.w, 0, 0, 0, 0};
+        const int l0 = (int)lut[byte_of(sa, cg)], l1 = (int)lut[byte_of(sb, cg)];
+        v4f c = mfma4<0, 0>(av, p0, o_run[cg], l0, pbyte[0]);
+        c = mfma4<1, 0>(av, p0, c, l0, pbyte[0]);
+        c = mfma4<2, 0>(av, p0, c, l0, pbyte[0]);
+        c = mfma4<3, 0>(av, p0, c, l0, pbyte[0]);
+        c = mfma4<0, 0>(av, p1, c, l1, pbyte[1]);
+        c = mfma4<1, 0>(av, p1, c, l1, pbyte[1]);
+        c = mfma4<2, 0>(av, p1, c, l1, pbyte[1]);
+        o_run[cg] = mfma4<3, 0>(av, p1, c, l1, pbyte[1]);
       }
     }
   }
@@ -407,13 +438,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const long rowi = ((long)b * a.hq + h0 + n) * a.n_split + split;
     const float g = gk * f_run;
 #pragma unroll
-    for (int cg = 0; cg < 32; cg++) {
+    for (int cg = 0; cg < 16; cg++) {
       float4 v = {o_run[cg][0] * g, o_run[cg][1] * g, o_run[cg][2] * g, o_run[cg][3] * g};
-      *(float4 *)(a.ws_o + rowi * D + 16 * cg + 4 * q4) = v;
+      *(float4 *)(a.ws_o + rowi * D + DH * hc + 16 * cg + 4 * q4) = v;
     }
-    if (q4 == 0) *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run, l_tot};
+    if (hc == 0 && q4 == 0) *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run, l_tot};
   }
-  if (a.zero_blocks) {
+  if (count_zero) {
     int z = nzero;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
@@ -487,11 +518,11 @@ hipError_t launch_mla_partials(const DecodeArgs &a, hipStream_t s) {
   const long units = (long)a.batch * a.n_split;
   const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nhg);
   switch (a.page_size) {
-    case 16: mla_partials<16><<<grid, 64, 0, s>>>(a); break;
-    case 32: mla_partials<32><<<grid, 64, 0, s>>>(a); break;
-    case 64: mla_partials<64><<<grid, 64, 0, s>>>(a); break;
-    case 128: mla_partials<128><<<grid, 64, 0, s>>>(a); break;
-    case 256: mla_partials<256><<<grid, 64, 0, s>>>(a); break;
+    case 16: mla_partials<16><<<grid, 128, 0, s>>>(a); break;
+    case 32: mla_partials<32><<<grid, 128, 0, s>>>(a); break;
+    case 64: mla_partials<64><<<grid, 128, 0, s>>>(a); break;
+    case 128: mla_partials<128><<<grid, 128, 0, s>>>(a); break;
+    case 256: mla_partials<256><<<grid, 128, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -67,10 +67,13 @@ def test_append_prefill_large_batch_path(torch_dev):
     check_gqa_cache(built)
 
 
-def test_append_mla_latent_tiles(torch_dev):
-    w = W.workload("mla", batch=2)
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_append_mla_latent_tiles(torch_dev, fmt):
+    """Latent tiles (16 x 16 NVFP4 / 32 x 32 MXFP4) with their scale search, incremental
+    appends that re-quantize the open tile row, both code layouts, the bf16 rope copy."""
+    w = W.workload("mla", batch=2, fmt=fmt)
     lens = np.array([100, 48], np.int32)
-    say("append mla", lens.tolist())
+    say("append mla fmt %d" % fmt, lens.tolist())
     built = harness.build(w, lens=lens, stop=np.array([60, 48]))
     harness.append_range(built, 0, 60, 61)
     harness.append_range(built, 0, 61, 100)
