@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak
 METRIC = "FP4 paged decode attention: µs/step + KV HBM GB/s (% of 8 TB/s peak)"
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -46,16 +47,23 @@ def kv_bytes_per_token_head(w):
     return d // 2 + (d // B) / B + 2 * w["rope"]
 
 
-def decode_kernel_hash():
+def decode_kernel(w):
+    """Name of the decode-partials kernel that serves workload w."""
+    return "mla" if w["attn"] == 1 else "gqa"
+
+
+def decode_kernel_hash(kernel="gqa"):
+    """Hash of the sources that define the decode-partials kernel and its launch."""
     h = hashlib.sha256()
-    for f in ("decode_gqa.hip", "decode_common.h", "fp4kv_device.h", "fp4kv_internal.h"):
+    for f in ("decode_%s.hip" % kernel, "decode_common.h", "fp4kv_device.h", "fp4kv_internal.h", "api.hip"):
         h.update(open(os.path.join(ROOT, "fp4_kv_cache_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
+def read_traffic(w, workload):
     """HBM traffic per decode launch from the committed counter summary, if it matches this kernel."""
-    path = os.path.join(PROFILES, "decode_gqa_%s_traffic.txt" % workload)
+    kernel = decode_kernel(w)
+    path = os.path.join(PROFILES, "decode_%s_%s_traffic.txt" % (kernel, workload))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -63,12 +71,18 @@ def read_traffic(workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_hash") != decode_kernel_hash():
+    if kv.get("kernel_hash") != decode_kernel_hash(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def mla_flops_per_token(w):
+    """Algorithmic flops per cached token of an MLA decode step: Q.K^T for the Q1 and Q2 rows of
+    every query head over latent + rope channels, P.V over the latent channels."""
+    return 2 * (2 * w["hq"]) * (w["d"] + w["rope"]) + 2 * w["hq"] * w["d"]
 
 
 def cpu_baseline(w, n_units, budget_s):
@@ -329,8 +343,18 @@ def main():
     stream_gbps = nbytes * 10 / (s0.elapsed_time(s1) * 1e-3) / 1e9
     del buf
 
-    achieved = kv_bytes / (k_us * 1e-6) / 1e9
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(w, args.workload)
+    if mla:   # matrix-core bound: algorithmic flops against the dense FP4 MFMA peak
+        flops = float(np.sum(lens.astype(np.float64))) * mla_flops_per_token(w)
+        achieved = flops / (k_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP4_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                    "flops_per_launch": flops,
+                    "kv_GBps": round(kv_bytes / (k_us * 1e-6) / 1e9, 1)}
+    else:
+        achieved = kv_bytes / (k_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
     res = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -358,12 +382,11 @@ def main():
                                    "NVFP4" if w["fmt"] == 0 else "MXFP4")),
                    "global_batch": B, "seq_len": int(lens.max()), "kv_bytes_per_step": int(kv_bytes),
                    "cache_copies_rotated": len(copies)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "roofline": roofline,
         "breakdown_us": {"decode_partials_kernel": round(k_us, 2), "split_merge_kernel": round(m_us, 2),
                          "kv_append_1_token": round(a_us, 2)},
         "stream_read_ceiling_GBps": round(stream_gbps, 1),
-        "decode_kernel_hash": decode_kernel_hash(),
+        "decode_kernel_hash": decode_kernel_hash(decode_kernel(w)),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
