@@ -225,22 +225,34 @@ __global__ __launch_bounds__(128) void k_append_gqa(AppendArgs a) {
 // its latency for decode-sized batches.
 
 template <int FMT>
-__global__ __launch_bounds__(64) void k_append_wave(AppendArgs a) {
-  constexpr int B = FMT == kFmtNV ? 16 : 32;
-  constexpr int NB = 128 / B;
-  constexpr int NC = FMT == kFmtNV ? 5 : 3;
-  __shared__ float xs[128];
-  __shared__ float errs[NB][NC];
-  __shared__ int cands[NB][NC];
-  const int lane = threadIdx.x;
-  const int tok = blockIdx.x, h = blockIdx.y;
-  const int slot = a.slots[tok];
-  if (slot < 0 || slot >= a.num_pages * a.page_size) return;
-  const int page = slot / a.page_size, off = slot % a.page_size;
+struct KWaveLds {
+  static constexpr int B = FMT == kFmtNV ? 16 : 32;
+  static constexpr int NB = 128 / B;
+  static constexpr int NC = FMT == kFmtNV ? 5 : 3;
+  float xs[128];
+  float errs[NB][NC];
+  int cands[NB][NC];
+};
+
+// One wave's key append for (token tok, KV head h).  Every lane of the workgroup reaches
+// both barriers; `ok` false (no such pair, or a slot outside the cache) turns the wave's
+// loads and stores off.
+template <int FMT>
+__device__ __forceinline__ void k_append_wave_body(const AppendArgs &a, int tok, int h, int lane, bool ok,
+                                                   KWaveLds<FMT> &sh) {
+  constexpr int B = KWaveLds<FMT>::B;
+  constexpr int NB = KWaveLds<FMT>::NB;
+  constexpr int NC = KWaveLds<FMT>::NC;
+  float *xs = sh.xs;
+  auto &errs = sh.errs;
+  auto &cands = sh.cands;
+  const int slot = ok ? a.slots[tok] : -1;
+  ok = ok && slot >= 0 && slot < a.num_pages * a.page_size;
+  const int page = ok ? slot / a.page_size : 0, off = ok ? slot % a.page_size : 0;
   const long base = ((long)tok * a.hkv + h) * 128 + 2 * lane;
   const float *ksi = a.ksi + (long)h * 128 + 2 * lane;
-  float x0 = load_elem(a.k_new, base, a.bf16) * ksi[0];
-  float x1 = load_elem(a.k_new, base + 1, a.bf16) * ksi[1];
+  float x0 = ok ? load_elem(a.k_new, base, a.bf16) * ksi[0] : 0.0f;
+  float x1 = ok ? load_elem(a.k_new, base + 1, a.bf16) * ksi[1] : 0.0f;
   {
     const float p = x0 + x1, m = x0 - x1;
     x0 = p;
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(64) void k_append_wave(AppendArgs a) {
   xs[2 * lane] = x0;
   xs[2 * lane + 1] = x1;
   __syncthreads();
-  const float G = FMT == kFmtNV ? a.gk[h] : 1.0f;
+  const float G = FMT == kFmtNV && ok ? a.gk[h] : 1.0f;
   if (lane < NB * NC) {
     const int blk = lane / NC, k = lane % NC;
     float x[B];
@@ -280,7 +292,7 @@ __global__ __launch_bounds__(64) void k_append_wave(AppendArgs a) {
     cands[blk][k] = cand;
   }
   __syncthreads();
-  if (lane < NB) {
+  if (ok && lane < NB) {
     const int blk = lane;
     int best = cands[blk][0];
     float be = errs[blk][0];
@@ -346,9 +358,8 @@ __device__ __forceinline__ BlockSpan block_span(const AppendArgs &a, int i) {
 // GQA values: one workgroup per (leading token, KV head), one thread per channel.
 
 template <int FMT>
-__global__ __launch_bounds__(128) void v_append_gqa(AppendArgs a) {
+__device__ __forceinline__ void v_append_body(const AppendArgs &a, int i, int h, int c) {
   constexpr int B = FMT == kFmtNV ? 16 : 32;
-  const int i = blockIdx.x, h = blockIdx.y, c = threadIdx.x;
   BlockSpan sp = block_span<B>(a, i);
   if (!sp.ok) return;
   const int d = 128;
@@ -387,6 +398,29 @@ __global__ __launch_bounds__(128) void v_append_gqa(AppendArgs a) {
 #pragma unroll
     for (int k = 0; k < B; k++)
       if (k >= sp.first && k < sp.first + sp.n_new) stage[k * d + c] = v[k];
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(128) void v_append_gqa(AppendArgs a) {
+  v_append_body<FMT>(a, blockIdx.x, blockIdx.y, threadIdx.x);
+}
+
+// Keys and values of a decode-sized batch in one launch: blocks [0, nkb) hold two key
+// waves each ((token, head) pairs 2 blk and 2 blk + 1 in token-major order), the blocks
+// after them one value block each ((leading token, head) in token-major order).
+template <int FMT>
+__global__ __launch_bounds__(128) void kv_append_small(AppendArgs a, int nkb) {
+  const int blk = blockIdx.x;
+  if (blk < nkb) {
+    __shared__ KWaveLds<FMT> sh[2];
+    const int wv = threadIdx.x >> 6;
+    const int pair = 2 * blk + wv;
+    const bool ok = pair < a.num_tokens * a.hkv;
+    k_append_wave_body<FMT>(a, ok ? pair / a.hkv : 0, ok ? pair % a.hkv : 0, threadIdx.x & 63, ok, sh[wv]);
+  } else {
+    const int u = blk - nkb;
+    v_append_body<FMT>(a, u / a.hkv, u % a.hkv, threadIdx.x);
   }
 }
 
@@ -560,18 +594,21 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   if (a.attn == FP4KV_GQA) {
     long n = (long)a.num_tokens * a.hkv;
-    dim3 gk((unsigned)((n + 127) / 128)), gw((unsigned)a.num_tokens, (unsigned)a.hkv),
-        gv((unsigned)a.num_tokens, (unsigned)a.hkv);
-    // small batches (decode): one wave per (token, head) for latency; large ones
-    // (prefill): one thread per (token, head) for throughput.  Identical results.
+    dim3 gk((unsigned)((n + 127) / 128)), gv((unsigned)a.num_tokens, (unsigned)a.hkv);
+    // small batches (decode): one wave per (token, head) for latency, keys and values in
+    // one launch; large ones (prefill): one thread per (token, head) for throughput.
+    // Identical results.
     const bool wave = n <= 65536;
-    if (a.fmt == kFmtNV) {
-      if (wave) k_append_wave<kFmtNV><<<gw, 64, 0, s>>>(a);
-      else k_append_gqa<kFmtNV><<<gk, 128, 0, s>>>(a);
+    if (wave) {   // one launch: key waves, then value blocks
+      const int nkb = (int)((n + 1) / 2);
+      const unsigned grid = (unsigned)(nkb + n);
+      if (a.fmt == kFmtNV) kv_append_small<kFmtNV><<<grid, 128, 0, s>>>(a, nkb);
+      else kv_append_small<kFmtMX><<<grid, 128, 0, s>>>(a, nkb);
+    } else if (a.fmt == kFmtNV) {
+      k_append_gqa<kFmtNV><<<gk, 128, 0, s>>>(a);
       v_append_gqa<kFmtNV><<<gv, 128, 0, s>>>(a);
     } else {
-      if (wave) k_append_wave<kFmtMX><<<gw, 64, 0, s>>>(a);
-      else k_append_gqa<kFmtMX><<<gk, 128, 0, s>>>(a);
+      k_append_gqa<kFmtMX><<<gk, 128, 0, s>>>(a);
       v_append_gqa<kFmtMX><<<gv, 128, 0, s>>>(a);
     }
   } else {
