@@ -343,6 +343,19 @@ def main():
     stream_gbps = nbytes * 10 / (s0.elapsed_time(s1) * 1e-3) / 1e9
     del buf
 
+    # the decode kernel's own reads without its arithmetic (same partition, pages and loads)
+    pattern_gbps = None
+    if not mla:
+        nsink = L.fp4kv_cache_read_sink_words(copies[0].desc, B, hq, maxp * P)
+        csink = torch.empty(max(nsink, 1), dtype=torch.int32, device=dev)
+
+        def cache_read(i):
+            c = copies[i % len(copies)]
+            L.check(L.fp4kv_cache_read(c.desc, B, hq, built.bt.data_ptr(), maxp, built.seq_lens.data_ptr(),
+                                       csink.data_ptr(), nsink, cur_stream()), "cache_read")
+        r_us, _ = graph_time(cache_read)
+        pattern_gbps = kv_bytes / (r_us * 1e-6) / 1e9
+
     traffic = read_traffic(w, args.workload)
     if mla:   # matrix-core bound: algorithmic flops against the dense FP4 MFMA peak
         flops = float(np.sum(lens.astype(np.float64))) * mla_flops_per_token(w)
@@ -386,6 +399,7 @@ def main():
         "breakdown_us": {"decode_partials_kernel": round(k_us, 2), "split_merge_kernel": round(m_us, 2),
                          "kv_append_1_token": round(a_us, 2)},
         "stream_read_ceiling_GBps": round(stream_gbps, 1),
+        "pattern_read_ceiling_GBps": round(pattern_gbps, 1) if pattern_gbps else None,
         "decode_kernel_hash": decode_kernel_hash(decode_kernel(w)),
     }
     if not args.no_cpu_baseline:

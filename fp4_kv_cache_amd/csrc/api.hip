@@ -320,6 +320,27 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
   return to_status(mla ? launch_mla_merge(a, (hipStream_t)stream) : launch_decode_merge(a, (hipStream_t)stream));
 }
 
+int fp4kv_cache_read(const fp4kv_cache *c, int batch, int num_q_heads, const int32_t *block_table,
+                     int max_pages_per_seq, const int32_t *seq_lens, uint32_t *sink, size_t sink_words,
+                     void *stream) {
+  DecodeArgs a;
+  int32_t dummy = 0;
+  // validation as for a decode call; the workspace is not used (pass a large enough size)
+  int st = fill_decode(c, &dummy, FP4KV_F32, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                       1.0f, nullptr, &dummy, ~(size_t)0, nullptr, false, false, &a);
+  if (st) return st;
+  if (c->attn != FP4KV_GQA) return FP4KV_ERR_UNSUPPORTED;
+  if (batch > 0 && (!sink || sink_words < (size_t)a.n_waves * 64)) return FP4KV_ERR_INVALID_ARG;
+  return to_status(launch_cache_read(a, sink, (hipStream_t)stream));
+}
+
+size_t fp4kv_cache_read_sink_words(const fp4kv_cache *c, int batch, int num_q_heads, int max_seq_len) {
+  if (check_shape(c) != FP4KV_OK || c->attn != FP4KV_GQA || batch < 0 || num_q_heads <= 0 || max_seq_len < 0)
+    return 0;
+  SplitPlan p = plan_for(c, batch, num_q_heads, max_seq_len);
+  return p.n_split < 0 ? 0 : (size_t)p.n_split * 64;
+}
+
 int fp4kv_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
   if (!src || !sink || bytes == 0 || bytes % 4096 != 0) return FP4KV_ERR_INVALID_ARG;
   return to_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream));

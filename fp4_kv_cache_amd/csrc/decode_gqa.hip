@@ -650,6 +650,63 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
+// Measurement only: the partial kernel's reads without its arithmetic.  Same partition,
+// same page-id staging, same tile loads in the same order (keys of tile t + 1 at the start
+// of tile t, values of tile t + 1 after tile t's values are consumed); every word of every
+// tile is folded (xor) into one word per lane, so the loads cannot be dropped and, for
+// sequences of whole tiles, the xor of the sink is the xor of every cache byte read once.
+// sink: W x 64 words.
+template <int FMT, int P>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_read_only(DecodeArgs a,
+                                                                                              uint32_t *sink) {
+  constexpr int NPT = P >= 128 ? 1 : 128 / P;
+  const int lane = threadIdx.x;
+  const int wave = blockIdx.x;
+  Share sh;
+  if (!find_share(a, wave, lane, sh)) return;
+  __shared__ int pgl[kMaxSplitPages];
+  uint32_t acc = 0;
+  auto fold = [&](const Tile &t) {
+#pragma unroll
+    for (int i = 0; i < 9; i++) acc ^= t.x[i].x ^ t.x[i].y ^ t.x[i].z ^ t.x[i].w;
+  };
+  for (;;) {
+    const int b = sh.b, kvh = sh.kvh;
+    const int L = min(a.seq_lens[b], a.max_pages * P);
+    const long uend = sh.ustart + sh.n;
+    const int tb = (int)(sh.x - sh.ustart);
+    const int te = (int)((sh.x1 < uend ? sh.x1 : uend) - sh.ustart);
+    const int last_lp = min((L - 1) / P, a.max_pages - 1);
+    __syncthreads();
+    for (int e = lane; e < (te - tb) * NPT; e += 64)
+      pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
+    __syncthreads();
+    Tile kt, kn, vt;
+    load_k<FMT, P>(a, kt, pgl, kvh, tb * 128, lane, true);
+    load_v<FMT, P>(a, vt, pgl, kvh, tb * 128, lane, true);
+    for (int tile = tb; tile < te; tile++) {
+      const bool live = tile + 1 < te;
+      const int tn = live ? tile + 1 : tile;
+      load_k<FMT, P>(a, kn, pgl + (tn - tb) * NPT, kvh, tn * 128, lane, live);
+      fold(kt);
+      fold(vt);
+      load_v<FMT, P>(a, vt, pgl + (tn - tb) * NPT, kvh, tn * 128, lane, live);
+      kt = kn;
+    }
+    if (sh.x1 <= uend) break;
+    sh.x = sh.ustart = uend;
+    if (++sh.kvh == a.hkv) {
+      sh.kvh = 0;
+      do {
+        if (++sh.b >= a.batch) break;
+        sh.n = seq_tiles(a, sh.b);
+      } while (sh.n == 0);
+      if (sh.b >= a.batch) break;
+    }
+  }
+  sink[(long)wave * 64 + lane] = acc;
+}
+
 // One wave per (sequence, query head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
 // over the partials of the head's (sequence, KV head) unit.  Lanes first take one partial
 // each for (m, l); the weights then go through LDS to the channel loop (lane = 2
@@ -735,6 +792,23 @@ hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s) {
     case 8: return launch_g<kFmtMX, 8>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_cache_read(const DecodeArgs &a, uint32_t *sink, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.n_waves);
+  const bool nv = a.fmt == kFmtNV;
+  switch (a.page_size) {
+    case 16:
+      if (nv) { gqa_read_only<kFmtNV, 16><<<grid, 64, 0, s>>>(a, sink); break; }
+      return hipErrorInvalidValue;
+    case 32: if (nv) gqa_read_only<kFmtNV, 32><<<grid, 64, 0, s>>>(a, sink); else gqa_read_only<kFmtMX, 32><<<grid, 64, 0, s>>>(a, sink); break;
+    case 64: if (nv) gqa_read_only<kFmtNV, 64><<<grid, 64, 0, s>>>(a, sink); else gqa_read_only<kFmtMX, 64><<<grid, 64, 0, s>>>(a, sink); break;
+    case 128: if (nv) gqa_read_only<kFmtNV, 128><<<grid, 64, 0, s>>>(a, sink); else gqa_read_only<kFmtMX, 128><<<grid, 64, 0, s>>>(a, sink); break;
+    case 256: if (nv) gqa_read_only<kFmtNV, 256><<<grid, 64, 0, s>>>(a, sink); else gqa_read_only<kFmtMX, 256><<<grid, 64, 0, s>>>(a, sink); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s) {

@@ -290,11 +290,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float s[8][4];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      __builtin_amdgcn_sched_barrier(0);
+      
       if (i + NB - 1 < 8) load_group(tile, i + NB - 1, gw[(i + NB - 1) % NB]);
       else load_group(tile + 1, i + NB - 1 - 8, gw[(i + NB - 1) % NB]);
       if (i == 4) load_scales(tile + 1, scn);
-      __builtin_amdgcn_sched_barrier(0);
+      
       const uint4 *w = gw[i % NB];
       const uint32_t ws[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
       h2 sq[4];
@@ -339,11 +339,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint8_t *srow = a.k_scales + ((long)pgv * (P / 16) + tp / 16) * 32 + 16 * hc;
     const uint8_t *vb = a.v_codes + ((long)pgv * D + DH * hc + n) * (P / 2) + tp / 2;
     uint4 vw[2][4];
-    __builtin_amdgcn_sched_barrier(0);
+    
     const uint4 sa = ld16(srow), sb = ld16(srow + 32);
 #pragma unroll
     for (int j = 0; j < 4; j++) vw[0][j] = ld16(vb + (long)j * 16 * (P / 2));
-    __builtin_amdgcn_sched_barrier(0);
+    
     if (tok0 + 128 > L) {
 #pragma unroll
       for (int i = 0; i < 8; i++)
@@ -408,12 +408,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const v8i p1 = {0, 0, (int)pk[2], (int)pk[3], 0, 0, 0, 0};
 #pragma unroll
     for (int bt = 0; bt < 4; bt++) {
-      __builtin_amdgcn_sched_barrier(0);
+      
       if (bt + 1 < 4) {
 #pragma unroll
         for (int j = 0; j < 4; j++) vw[(bt + 1) & 1][j] = ld16(vb + (long)(4 * (bt + 1) + j) * 16 * (P / 2));
       }
-      __builtin_amdgcn_sched_barrier(0);
+      
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const int cg = 4 * bt + j;

@@ -47,6 +47,9 @@ _SIGS = {
                                      _c_int, _vp, ctypes.c_float, _vp, _c_size, _vp, _vp]),
     "fp4_decode_merge": (_c_int, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int, _vp, _vp, _vp,
                                   _c_size, _vp]),
+    "fp4kv_cache_read": (_c_int, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _vp, _c_int, _vp, _vp, _c_size,
+                                  _vp]),
+    "fp4kv_cache_read_sink_words": (_c_size, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int]),
     "fp4kv_stream_read": (_c_int, [_vp, _c_size, _vp, _vp]),
     "fp4kv_stream_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
     "fp4kv_status_string": (ctypes.c_char_p, [_c_int]),
@@ -110,6 +113,16 @@ def fp4_decode_merge(cache, batch, num_q_heads, max_pages_per_seq, seq_lens, out
                      workspace_bytes, stream):
     return load().fp4_decode_merge(_ref(cache), batch, num_q_heads, max_pages_per_seq, seq_lens, out,
                                    workspace, workspace_bytes, stream)
+
+
+def fp4kv_cache_read(cache, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, sink, sink_words,
+                     stream):
+    return load().fp4kv_cache_read(_ref(cache), batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                                   sink, sink_words, stream)
+
+
+def fp4kv_cache_read_sink_words(cache, batch, num_q_heads, max_seq_len):
+    return load().fp4kv_cache_read_sink_words(_ref(cache), batch, num_q_heads, max_seq_len)
 
 
 def fp4kv_stream_read(src, nbytes, sink, stream):

@@ -212,6 +212,20 @@ int fp4kv_stream_read(const void *src, size_t bytes, uint32_t *sink, void *strea
  * known-size reference against which hardware traffic counters are scaled. */
 int fp4kv_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/* Measurement helper (GQA caches): performs exactly the cache reads of
+ * fp4_decode_partials for the same arguments -- same division of the batch's
+ * tiles among waves, same page lookups, same loads in the same order -- without
+ * any arithmetic, and folds the loaded words into `sink` (one word per lane, at
+ * least fp4kv_cache_read_sink_words() words), to measure the read rate of the
+ * decode kernel's own access pattern over a shuffled page table.  Arguments are
+ * validated like a decode call; MLA caches return FP4KV_ERR_UNSUPPORTED. */
+int fp4kv_cache_read(const fp4kv_cache *c, int batch, int num_q_heads, const int32_t *block_table,
+                     int max_pages_per_seq, const int32_t *seq_lens, uint32_t *sink,
+                     size_t sink_words, void *stream);
+/* Sink words fp4kv_cache_read needs for this batch shape (0 on invalid arguments). */
+size_t fp4kv_cache_read_sink_words(const fp4kv_cache *c, int batch, int num_q_heads,
+                                   int max_seq_len);
+
 /* Static description of a status code (never NULL). */
 const char *fp4kv_status_string(int status);
 

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("kv_quant_append", "fp4_decode_attention", "fp4_decode_partials", "fp4_decode_merge",
               "fp4_decode_workspace_bytes", "fp4kv_cache_layout", "fp4kv_status_string",
-              "fp4kv_stream_read"):
+              "fp4kv_stream_read", "fp4kv_cache_read", "fp4kv_cache_read_sink_words"):
         assert n in names, n
 
 
@@ -94,6 +94,11 @@ def test_workspace_and_group_checks(lib):
     assert L.kv_quant_append(c, 1, None, 0, 4, 1, 1, 1, None, None) == L.ERR_INVALID_ARG
     assert L.kv_quant_append(c, 1, 1, 0, 0, 1, 1, 1, None, None) == L.OK        # empty batch: no-op
     assert L.fp4kv_stream_read(1, 1000, 1, None) == L.ERR_INVALID_ARG
+    # same-pattern read helper: sink size from the plan, validation like a decode call
+    words = L.fp4kv_cache_read_sink_words(c, 3, 8, 1000)
+    assert words > 0 and words % 64 == 0
+    assert L.fp4kv_cache_read(c, 3, 8, 1, 16, 1, 1, words - 1, None) == L.ERR_INVALID_ARG
+    assert L.fp4kv_cache_read(c, 3, 7, 1, 16, 1, 1, words, None) == L.ERR_INVALID_ARG
     assert L.fp4kv_status_string(3) == "workspace too small"
 
 

@@ -122,6 +122,31 @@ def test_decode_shares_span_units(torch_dev, name):
     say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
 
 
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b"])
+def test_partition_reads_every_tile_once(torch_dev, name):
+    """The decode kernel's partition and tile loads (run without arithmetic by
+    fp4kv_cache_read) read every byte of the cache exactly once: with whole-tile sequences
+    the xor of everything read equals the xor of the four cache arrays."""
+    import torch
+    from fp4_kv_cache_amd import lib as L
+    lens = np.array([256, 0, 1280, 128, 640, 0, 2048, 384], np.int32)
+    w = W.workload(name, batch=len(lens))
+    say("partition coverage", name, lens.tolist())
+    built = harness.build(w, lens=lens)
+    maxp = built.bt.shape[1]
+    n = L.fp4kv_cache_read_sink_words(built.cache.desc, w["batch"], w["hq"], maxp * w["page"])
+    sink = torch.zeros(n, dtype=torch.int32, device=built.device)
+    L.check(L.fp4kv_cache_read(built.cache.desc, w["batch"], w["hq"], built.bt.data_ptr(), maxp,
+                               built.seq_lens.data_ptr(), sink.data_ptr(), n,
+                               torch.cuda.current_stream().cuda_stream), "cache_read")
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    want = np.uint32(0)
+    for name_ in ("k_codes", "k_scales", "v_codes", "v_scales"):
+        want ^= np.bitwise_xor.reduce(getattr(built.cache, name_).cpu().numpy().view(np.uint32).ravel())
+    assert got == want, (hex(int(got)), hex(int(want)))
+
+
 def test_decode_underflow_no_zero_blocks(torch_dev):
     w = W.workload("long_underflow", batch=1)
     lens = np.array([16384], np.int32)
