@@ -140,8 +140,8 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
     if (!ok) return FP4KV_ERR_UNSUPPORTED;
     if (c->format == FP4KV_MXFP4 && c->page_size < 32) return FP4KV_ERR_UNSUPPORTED;
   } else {
-    // MLA: NVFP4 latent, query heads in groups of 16, pages of at least 32 tokens
-    if (c->format != FP4KV_NVFP4 || hq % 16 != 0 || c->page_size < 32) return FP4KV_ERR_UNSUPPORTED;
+    // MLA: query heads in groups of 16, pages of at least 32 tokens
+    if (hq % 16 != 0 || c->page_size < 32) return FP4KV_ERR_UNSUPPORTED;
   }
   if ((long)max_pages * c->page_size > 0x7FFFFFFFL) return FP4KV_ERR_INVALID_ARG;
   if (batch > 0) {

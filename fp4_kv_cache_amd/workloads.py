@@ -52,6 +52,11 @@ WORKLOADS = {
     "mla": dict(id=5, attn=MLA, batch=32, hq=128, hkv=1, d=512, rope=64, ctx=16384, page=64,
                 fmt=NVFP4, dtype="bf16", shuffle=True, outlier_channels=None, outlier_scale=8.0,
                 n_outliers=10, k_std=1.0, lognormal=0.0),
+    # the MLA shape with an MXFP4 latent (32 x 32 E8M0 tiles); not one of the five headline
+    # configurations -- it exercises the natively block-scaled MLA path
+    "mla_mxfp4": dict(id=6, attn=MLA, batch=32, hq=128, hkv=1, d=512, rope=64, ctx=16384, page=64,
+                      fmt=MXFP4, dtype="bf16", shuffle=True, outlier_channels=None, outlier_scale=8.0,
+                      n_outliers=10, k_std=1.0, lognormal=0.0),
 }
 
 T_Q, T_K, T_V, T_KROPE, T_QROPE, T_LEN, T_PAGES, T_OUTL, T_KMAG, T_VMAG = range(1, 11)

@@ -55,9 +55,10 @@ def test_fullsize_long_underflow_no_zero_blocks(torch_dev):
     assert zg == 0 and zo == 0
 
 
-def test_fullsize_mla(torch_dev):
-    w = W.workload("mla")
-    say("full size mla: batch %d, latent 512 + rope 64; building cache" % w["batch"])
+@pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
+def test_fullsize_mla(torch_dev, name):
+    w = W.workload(name)
+    say("full size %s: batch %d, latent 512 + rope 64; building cache" % (name, w["batch"]))
     built = harness.build(w, workers=16)
     say("  checking latent codes, tile scales and rope of sequences 0 and 31")
     check_mla_cache(built, seqs=[0, 31])

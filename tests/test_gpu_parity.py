@@ -157,11 +157,14 @@ def test_decode_underflow_no_zero_blocks(torch_dev):
     assert zg == 0 and zo == 0
 
 
-def test_decode_mla_ragged(torch_dev):
-    """MLA: 128 query heads on one latent head (key and value) plus the bf16 rope part."""
-    w = W.workload("mla", batch=4)
+@pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
+def test_decode_mla_ragged(torch_dev, name):
+    """MLA: 128 query heads on one latent head (key and value) plus the bf16 rope part;
+    NVFP4 (16 x 16 E4M3 tiles, fp16 matrix cores for Q.K^T) and MXFP4 (32 x 32 E8M0 tiles,
+    FP4 matrix cores throughout)."""
+    w = W.workload(name, batch=4)
     lens = np.array([1, 200, 777, 0], np.int32)
-    say("decode mla ragged", lens.tolist())
+    say("decode %s ragged" % name, lens.tolist())
     built = harness.build(w, lens=lens)
     worst, worst_ref, zg = compare_mla(built, tol=TOL)
     say("mla: max err vs oracle %.3g, vs fp64 attention %.3g, zero blocks %d" % (worst, worst_ref, zg))
