@@ -147,6 +147,31 @@ def test_partition_reads_every_tile_once(torch_dev, name):
     assert got == want, (hex(int(got)), hex(int(want)))
 
 
+@pytest.mark.parametrize("name,page", [("qwen3_4b", 32), ("qwen3_4b", 128), ("qwen3_4b", 256),
+                                       ("qwen3_30b_a3b", 32), ("qwen3_30b_a3b", 128), ("qwen3_30b_a3b", 256)])
+def test_page_sizes(torch_dev, name, page):
+    """Every compiled page size: cache bytes bit-exact, decode within tolerance (a tile spans
+    four pages at 32 tokens, one page at 128, half a page at 256)."""
+    lens = np.array([1, 300, 0, 1100], np.int32)
+    w = W.workload(name, batch=len(lens), page=page)
+    say("page size %d %s" % (page, name), lens.tolist())
+    built = harness.build(w, lens=lens)
+    check_gqa_cache(built)
+    worst, worst_ref, zg, zo = compare_gqa(built, tol=TOL)
+    say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
+
+
+@pytest.mark.parametrize("name,page", [("mla", 32), ("mla", 128), ("mla_mxfp4", 32), ("mla_mxfp4", 256)])
+def test_mla_page_sizes(torch_dev, name, page):
+    lens = np.array([40, 520], np.int32)
+    w = W.workload(name, batch=len(lens), page=page)
+    say("mla page size %d %s" % (page, name), lens.tolist())
+    built = harness.build(w, lens=lens)
+    check_mla_cache(built)
+    worst, worst_ref, zg = compare_mla(built, tol=TOL)
+    say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
+
+
 def test_decode_underflow_no_zero_blocks(torch_dev):
     w = W.workload("long_underflow", batch=1)
     lens = np.array([16384], np.int32)
