@@ -164,10 +164,12 @@ def quantize_probs(pt, fmt, mode="tile"):
     return ph.reshape(R, Lt), codes
 
 
-def attend(s, vhat, L, fmt, tile=P_TILE, p_mode="tile", partials=False):
+def attend(s, vhat, L, fmt, tile=P_TILE, p_mode="tile", partials=False, row_len=None):
     """Tile-wise FP4 softmax.V emulation for rows s [R, L] (fp32 base-2 logits).
 
-    vhat: float64 [>=L, d] dequantized values (with G_V).  Returns a dict with
+    vhat: float64 [>=L, d] dequantized values (with G_V).  ``row_len`` (optional, [R],
+    each in 1..L) limits row r to tokens < row_len[r] (causal multi-token decode); a
+    tile with no valid token for a row contributes nothing to it.  Returns a dict with
     'out' [R, d] (float64), 'zero_blocks' (count of P blocks that hold at least
     one valid token and quantize to all zeros) and, if ``partials``, the
     per-tile (o, m, l).
@@ -182,24 +184,30 @@ def attend(s, vhat, L, fmt, tile=P_TILE, p_mode="tile", partials=False):
     Lt = T * tile
     sp = np.full((R, Lt), -np.inf, dtype=F32)
     sp[:, :L] = s[:, :L]
+    rl = np.full(R, L, dtype=np.int64) if row_len is None else np.asarray(row_len, np.int64)
+    for r in range(R):
+        sp[r, rl[r]:] = -np.inf
     vp = np.zeros((Lt, d))
     vp[:L] = vhat[:L]
-    nvalid_blk = -(-L // B)
+    nvalid_blk = -(-rl // B)                  # [R]: blocks holding a valid token of the row
+    blk_valid = np.arange(Lt // B)[None, :] < nvalid_blk[:, None]
     if p_mode == "vanilla":
         M = np.max(sp, axis=-1).astype(np.float64)
         p = np.exp2(sp.astype(np.float64) - M[:, None])
         p = (p / p.sum(-1, keepdims=True)).astype(F32)
         ph, codes = quantize_probs(p, fmt, "vanilla")
-        zero = int(np.sum(np.all((codes[:, :nvalid_blk] & 7) == 0, axis=-1)))
+        zero = int(np.sum(np.all((codes & 7) == 0, axis=-1) & blk_valid))
         return {"out": ph @ vp, "zero_blocks": zero}
     m = np.max(sp.reshape(R, T, tile), axis=-1)                          # fp32 [R, T]
-    diff = (sp.reshape(R, T, tile) - m[..., None]).astype(F32)
+    live = np.isfinite(m)                     # the tile holds a valid token of the row
+    diff = np.where(live[..., None], sp.reshape(R, T, tile) - np.where(live, m, 0)[..., None],
+                    -np.inf).astype(F32)
     pt = np.exp2(diff.astype(np.float64)).astype(F32).reshape(R, Lt)
     if p_mode == "exact":                     # identity codec on P (ablation / skeleton check)
         ph, codes, zero = pt.astype(np.float64), None, 0
     else:
         ph, codes = quantize_probs(pt, fmt, "tile")
-        zero = int(np.sum(np.all((codes[:, :nvalid_blk] & 7) == 0, axis=-1)))
+        zero = int(np.sum(np.all((codes & 7) == 0, axis=-1) & blk_valid))
     o_t = np.einsum("rtk,tkd->rtd", ph.reshape(R, T, tile), vp.reshape(T, tile, d))
     l_t = pt.reshape(R, T, tile).astype(np.float64).sum(-1)
     out = merge_partials(o_t, m.astype(np.float64), l_t)
@@ -249,10 +257,11 @@ DEFAULT_OPTS = dict(dual=True, smooth=True, rotate=True, search=True, p_mode="ti
 
 
 def gqa_head(q_rows, K, V, k_smooth_inv, q_smooth, G_K, G_V, fmt, softmax_scale,
-             L=None, opts=None, partials=False):
+             L=None, opts=None, partials=False, row_len=None):
     """One (sequence, KV head): the g query rows against L tokens, whole pipeline.
 
-    q_rows [g, d], K/V [>=L, d] as float32 (bf16 inputs converted exactly).
+    q_rows [g, d], K/V [>=L, d] as float32 (bf16 inputs converted exactly); ``row_len``
+    (optional) limits each row to its own prefix (see ``attend``).
     Returns the ``attend`` dict plus the cache contents and the QuantQuery.
     """
     o = dict(DEFAULT_OPTS, **(opts or {}))
@@ -269,8 +278,27 @@ def gqa_head(q_rows, K, V, k_smooth_inv, q_smooth, G_K, G_V, fmt, softmax_scale,
     s = logits(qq, key_dequant_exact(kc, ks, fmt), G_K, cs, fmt)
     gv = G_V if fmt == NVFP4 else 1.0
     res = attend(s, value_dequant_exact(vc, vs, fmt, gv), L, fmt, p_mode=o["p_mode"],
-                 partials=partials)
+                 partials=partials, row_len=row_len)
     res.update(k_codes=kc, k_scales=ks, v_codes=vc, v_scales=vs, qq=qq, s=s)
+    return res
+
+
+def gqa_head_multi(q, K, V, k_smooth_inv, q_smooth, G_K, G_V, fmt, softmax_scale, L=None, opts=None):
+    """Multi-token decode of one (sequence, KV head): q [n, g, d] holds n consecutive query
+    tokens (positions L - n .. L - 1, all already in the cache) of the g query heads; query j
+    attends to tokens 0 .. L - n + j.  The n*g rows (row j*g + h) go through ``gqa_head``
+    together -- one quantization of the cache, each row masked to its own prefix -- which
+    is the stacked-query reading of several query tokens per sequence.
+    Returns the ``gqa_head`` dict with 'out' reshaped to [n, g, d].
+    """
+    q = np.asarray(q, F32)
+    n, g, d = q.shape
+    K = np.asarray(K, F32)
+    L = K.shape[0] if L is None else L
+    row_len = np.repeat(L - n + 1 + np.arange(n), g)
+    res = gqa_head(q.reshape(n * g, d), K, V, k_smooth_inv, q_smooth, G_K, G_V, fmt, softmax_scale,
+                   L=L, opts=opts, row_len=row_len)
+    res["out"] = res["out"].reshape(n, g, d)
     return res
 
 

@@ -205,3 +205,49 @@ def test_mla_exact_codecs_is_textbook_attention():
 def W_bf16(x):
     from fp4_kv_cache_amd.workloads import bf16_round
     return bf16_round(np.asarray(x, np.float32))
+
+
+def test_multi_token_exact_codecs_is_causal_attention():
+    """Multi-token decode with every codec exact (MXFP4 grid-valued keys, values and query
+    blocks, unquantized P; rotation and smoothing off) equals textbook causal attention:
+    query j of n sees tokens 0 .. L - n + j.  L = 130 with n = 4 leaves the second 128-token
+    tile empty for the first two queries (such a tile must contribute nothing)."""
+    rng = np.random.default_rng(11)
+    d, L, n, g = 128, 130, 4, 2
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+    def grid_vals(shape):
+        return rng.choice(grid, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+
+    # keys: each token's 32-channel blocks hold a +-6 and are scaled by 2^e
+    K = grid_vals((L, d))
+    K[:, ::32] = 6.0 * rng.choice([-1.0, 1.0], size=(L, d // 32))
+    K = K * np.repeat(2.0 ** rng.integers(-2, 3, size=(L, d // 32)), 32, axis=1)
+    # values: each channel's 32-token blocks hold a +-6 (tail block: within the tokens present)
+    V = grid_vals((L, d))
+    for t0 in range(0, L, 32):
+        V[t0, :] = 6.0 * rng.choice([-1.0, 1.0], size=d)
+        V[t0:t0 + 32] *= 2.0 ** rng.integers(-2, 3, size=(1, d))
+    q = grid_vals((n, g, d))
+    q[..., ::32] = 6.0
+    q = q * np.repeat(2.0 ** rng.integers(-2, 1, size=(n, g, d // 32)), 32, axis=-1)
+    sc = 1.0 / np.sqrt(d)
+    ones = np.ones(d, np.float32)
+    res = A.gqa_head_multi(q.astype(np.float32), K.astype(np.float32), V.astype(np.float32), ones, ones,
+                           1.0, 1.0, KQ.MXFP4, sc, L=L, opts=dict(rotate=False, smooth=False, p_mode="exact"))
+    for j in range(n):
+        Lj = L - n + 1 + j
+        ref = A.reference_attention(q[j], K[:Lj], V[:Lj], sc)
+        assert np.max(A.row_rel_err(res["out"][j], ref)) < 1e-6, j
+
+
+def test_multi_token_single_query_is_gqa_head():
+    """n = 1 is the ordinary decode: same rows, same output bit for bit."""
+    rng = np.random.default_rng(12)
+    L, d, g = 300, 128, 4
+    Q, K, V = _rand_case(rng, L)
+    q = rng.standard_normal((1, g, d)).astype(np.float32)
+    ones = np.ones(d, np.float32)
+    a = A.gqa_head(q[0], K, V, ones, ones, np.float32(0.01), np.float32(0.01), KQ.NVFP4, 0.08, L=L)
+    b = A.gqa_head_multi(q, K, V, ones, ones, np.float32(0.01), np.float32(0.01), KQ.NVFP4, 0.08, L=L)
+    assert np.array_equal(a["out"], b["out"][0])
