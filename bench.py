@@ -171,6 +171,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_4b")
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated between steps")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence per step (GQA; >1: causal multi-token decode, e.g. "
+                         "speculative verification; the step appends that many tokens)")
     ap.add_argument("--cpu-units", type=int, default=8)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -193,13 +196,17 @@ def main():
     torch.cuda.set_device(dev)
     w = W.workload(args.workload)
     mla = w["attn"] == 1
+    QN = args.q_len
+    if QN > 1 and mla:
+        print("--q-len > 1 is a GQA mode", file=sys.stderr)
+        sys.exit(2)
     lens = W.seq_lens(w)
     B, hq, hkv, d, P = w["batch"], w["hq"], w["hkv"], w["d"], w["page"]
     log("workload", args.workload, "batch", B, "ctx", int(lens.max()), "fmt", "NVFP4" if w["fmt"] == 0 else "MXFP4")
 
-    # prefill all but the last token of every sequence; each step appends the last one
+    # prefill all but the last QN tokens of every sequence; each step appends them
     t0 = time.time()
-    built = harness.build(w, lens=lens, stop=lens - 1, device=dev, workers=16)
+    built = harness.build(w, lens=lens, stop=lens - QN, device=dev, workers=16)
     copies = [built.cache]
     for _ in range(1, args.copies):
         c2 = L.PagedFP4Cache(w["fmt"], w["attn"], built.cache.desc.num_pages, P, hkv, d, B, *built.calib[:2],
@@ -223,41 +230,55 @@ def main():
                                             for b in range(B)]).view(np.int16)).to(dev)
         k_new, v_new = k_new.to(tdt).to(dev).contiguous(), None
     else:
-        k_new = torch.from_numpy(np.stack([built.tail[b][0][0] for b in range(B)]))
-        v_new = torch.from_numpy(np.stack([built.tail[b][1][0] for b in range(B)]))
+        k_new = torch.from_numpy(np.concatenate([built.tail[b][0][:QN] for b in range(B)]))
+        v_new = torch.from_numpy(np.concatenate([built.tail[b][1][:QN] for b in range(B)]))
         k_new, v_new = k_new.to(tdt).to(dev).contiguous(), v_new.to(tdt).to(dev).contiguous()
-    slots = torch.from_numpy(np.array([harness.slots_for(built.bt_np[b], [last[b]], P)[0] for b in range(B)],
-                                      np.int32)).to(dev)
-    seq_ids = torch.arange(B, dtype=torch.int32, device=dev)
-    pos = torch.from_numpy(last).to(dev)
-    q = built.queries()
+    newpos = np.concatenate([np.arange(int(lens[b]) - QN, int(lens[b])) for b in range(B)]).astype(np.int32)
+    slots = torch.from_numpy(np.concatenate([harness.slots_for(built.bt_np[b], np.arange(int(lens[b]) - QN,
+                                                                                         int(lens[b])), P)
+                                             for b in range(B)]).astype(np.int32)).to(dev)
+    seq_ids = torch.from_numpy(np.repeat(np.arange(B, dtype=np.int32), QN)).to(dev)
+    pos = torch.from_numpy(newpos).to(dev)
+    q1 = built.queries()
+    q = built.queries_multi(QN) if QN > 1 else q1
     scale = W.softmax_scale(w)
     maxp = built.bt.shape[1]
-    ws_bytes = copies[0].workspace_bytes(B, hq, maxp * P)
+    ws_bytes = L.fp4_decode_multi_workspace_bytes(copies[0].desc, B, QN, hq, maxp * P)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    out = torch.empty((B, QN, hq, d) if QN > 1 else (B, hq, d), dtype=torch.float32, device=dev)
     qdt = L.BF16 if q.dtype == torch.bfloat16 else L.F32
     stream = torch.cuda.current_stream().cuda_stream
 
     def cur_stream():
         return torch.cuda.current_stream().cuda_stream
 
+    def decode_multi(i):
+        c = copies[i % len(copies)]
+        L.check(L.fp4_decode_attention_multi(c.desc, q.data_ptr(), qdt, B, QN, hq, built.bt.data_ptr(), maxp,
+                                             built.seq_lens.data_ptr(), scale, out.data_ptr(), ws.data_ptr(),
+                                             ws_bytes, None, cur_stream()), "fp4_decode_attention_multi")
+
     def step(i):
         c = copies[i % len(copies)]
         c.append(k_new, v_new, slots, seq_ids, pos, kr_new)
+        if QN > 1:
+            decode_multi(i)
+            return
         L.check(L.fp4_decode_attention(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
                                        built.seq_lens.data_ptr(), scale, out.data_ptr(), ws.data_ptr(),
                                        ws_bytes, None, cur_stream()), "fp4_decode_attention")
 
-    def partials(i):
+    def partials(i):   # one query token (the newest): the single-token decode kernel
         c = copies[i % len(copies)]
-        L.check(L.fp4_decode_partials(c.desc, q.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
+        L.check(L.fp4_decode_partials(c.desc, q1.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
                                       built.seq_lens.data_ptr(), scale, ws.data_ptr(), ws_bytes, None,
                                       cur_stream()), "fp4_decode_partials")
 
+    out1 = out if QN == 1 else torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+
     def merge(i):
         c = copies[i % len(copies)]
-        L.check(L.fp4_decode_merge(c.desc, B, hq, maxp, built.seq_lens.data_ptr(), out.data_ptr(),
+        L.check(L.fp4_decode_merge(c.desc, B, hq, maxp, built.seq_lens.data_ptr(), out1.data_ptr(),
                                    ws.data_ptr(), ws_bytes, cur_stream()), "fp4_decode_merge")
 
     def append(i):
@@ -326,6 +347,7 @@ def main():
     k_us, _ = graph_time(partials)
     m_us, _ = graph_time(merge)
     a_us, _ = graph_time(append)
+    mq_us = graph_time(decode_multi)[0] if QN > 1 else None
 
     # measured streaming-read ceiling of this device (2 GiB, 16-byte non-temporal loads)
     stream = cur_stream()
@@ -365,9 +387,11 @@ def main():
                     "flops_per_launch": flops,
                     "kv_GBps": round(kv_bytes / (k_us * 1e-6) / 1e9, 1)}
     else:
-        achieved = kv_bytes / (k_us * 1e-6) / 1e9
+        # one query token: the partial kernel; several: the whole multi-token decode (partials and
+        # merge, no separate entry point for its partials)
+        achieved = kv_bytes / ((k_us if QN == 1 else mq_us) * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic if QN == 1 else None}
     res = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -388,17 +412,24 @@ def main():
                                 % (args.workload, B, hq, d, w["rope"], int(lens.max()), P,
                                    "NVFP4" if w["fmt"] == 0 else "MXFP4")) if mla else
                                ("%s: batch %d, %d query / %d KV heads, head_dim %d, context %s, page %d, %s K/V, "
-                                "shuffled page table, 1 new token per sequence per step"
+                                "shuffled page table, %s"
                                 % (args.workload, B, hq, hkv, d,
                                    int(lens.max()) if lens.min() == lens.max() else
                                    "%d-%d (ragged)" % (lens.min(), lens.max()), P,
-                                   "NVFP4" if w["fmt"] == 0 else "MXFP4")),
+                                   "NVFP4" if w["fmt"] == 0 else "MXFP4",
+                                   "1 new token per sequence per step" if QN == 1 else
+                                   "%d new tokens per sequence per step, all %d decoded (causal)" % (QN, QN))),
                    "global_batch": B, "seq_len": int(lens.max()), "kv_bytes_per_step": int(kv_bytes),
                    "cache_copies_rotated": len(copies)},
         "roofline": roofline,
         "breakdown_us": {"decode_partials_kernel": round(k_us, 2), "split_merge_kernel": round(m_us, 2),
                          "kv_append_1_token": round(a_us, 2)},
         "stream_read_ceiling_GBps": round(stream_gbps, 1),
+        **({"multi_token": {"q_len": QN, "decode_us": round(mq_us, 2),
+                            "single_token_decode_us": round(k_us + m_us, 2),
+                            "query_tokens_per_s": round(B * QN / (mq_us * 1e-6), 1),
+                            "vs_separate_single_token_decodes": round(QN * (k_us + m_us) / mq_us, 3)}}
+           if QN > 1 else {}),
         "pattern_read_ceiling_GBps": round(pattern_gbps, 1) if pattern_gbps else None,
         "decode_kernel_hash": decode_kernel_hash(decode_kernel(w)),
     }

@@ -107,7 +107,7 @@ SplitPlan plan_for(const fp4kv_cache *c, int batch, int hq, int max_len) {
 
 // Workspace: MLA [batch * hq][n_split] partial rows; GQA (n_waves + batch * Hkv) slots of
 // `group` partial rows, then the per-unit slot ranges.  A partial row is d + 2 floats.
-size_t workspace_for(const fp4kv_cache *c, int batch, int hq, int max_len, SplitPlan *out) {
+size_t workspace_for(const fp4kv_cache *c, int batch, int hq, int max_len, SplitPlan *out, int q_len = 1) {
   SplitPlan p = plan_for(c, batch, hq, max_len);
   if (out) *out = p;
   if (p.n_split < 0) return 0;
@@ -116,7 +116,7 @@ size_t workspace_for(const fp4kv_cache *c, int batch, int hq, int max_len, Split
     return rows * ((size_t)c->head_dim + 2) * sizeof(float);
   }
   const size_t units = (size_t)batch * c->num_kv_heads;
-  const size_t rows = ((size_t)p.n_split + units) * (size_t)(hq / c->num_kv_heads);
+  const size_t rows = ((size_t)p.n_split + units) * (size_t)(hq / c->num_kv_heads) * (size_t)q_len;
   return rows * ((size_t)c->head_dim + 2) * sizeof(float) + units * 2 * sizeof(int32_t);
 }
 
@@ -125,7 +125,7 @@ int to_status(hipError_t e) { return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP;
 int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int hq,
                 const int32_t *block_table, int max_pages, const int32_t *seq_lens,
                 float softmax_scale, float *out, void *ws, size_t ws_bytes, int32_t *zero,
-                bool need_q, bool need_out, DecodeArgs *a) {
+                bool need_q, bool need_out, DecodeArgs *a, int q_len = 1) {
   int st = check_shape(c);
   if (st) return st;
   st = check_pointers(c);
@@ -135,13 +135,16 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   if (hq % c->num_kv_heads != 0) return FP4KV_ERR_INVALID_ARG;
   if (!(softmax_scale == softmax_scale)) return FP4KV_ERR_INVALID_ARG;
   int group = hq / c->num_kv_heads;
+  if (q_len < 1) return FP4KV_ERR_INVALID_ARG;
   if (c->attn == FP4KV_GQA) {
     bool ok = group == 1 || group == 2 || group == 4 || (c->format == FP4KV_MXFP4 && group == 8);
     if (!ok) return FP4KV_ERR_UNSUPPORTED;
+    // query tokens x query heads per KV head: up to two row sets of one MFMA's columns
+    if (q_len > 8 || group * q_len > (c->format == FP4KV_NVFP4 ? 8 : 16)) return FP4KV_ERR_UNSUPPORTED;
     if (c->format == FP4KV_MXFP4 && c->page_size < 32) return FP4KV_ERR_UNSUPPORTED;
   } else {
     // MLA: query heads in groups of 16, pages of at least 32 tokens
-    if (hq % 16 != 0 || c->page_size < 32) return FP4KV_ERR_UNSUPPORTED;
+    if (hq % 16 != 0 || c->page_size < 32 || q_len != 1) return FP4KV_ERR_UNSUPPORTED;
   }
   if ((long)max_pages * c->page_size > 0x7FFFFFFFL) return FP4KV_ERR_INVALID_ARG;
   if (batch > 0) {
@@ -152,7 +155,7 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   // partial slots are numbered in int32 (GQA: n_waves + batch * Hkv)
   if ((long)batch * c->num_kv_heads > 0x3FFFFFFFL) return FP4KV_ERR_INVALID_ARG;
   SplitPlan p;
-  size_t need = workspace_for(c, batch, hq, max_pages * c->page_size, &p);
+  size_t need = workspace_for(c, batch, hq, max_pages * c->page_size, &p, q_len);
   if (p.n_split < 0) return FP4KV_ERR_INVALID_ARG;
   if (ws_bytes < need) return FP4KV_ERR_WORKSPACE;
   DecodeArgs &d = *a;
@@ -167,6 +170,7 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.max_pages = max_pages;
   d.num_pages = c->num_pages;
   d.q_bf16 = q_dtype == FP4KV_BF16;
+  d.q_len = q_len;
   const bool mla = c->attn == FP4KV_MLA;
   d.n_split = mla ? p.n_split : 0;
   d.tiles_per_split = mla ? p.tiles_per_split : 0;
@@ -188,7 +192,7 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.block_table = block_table;
   d.seq_lens = seq_lens;
   const size_t rows = mla ? (size_t)batch * hq * p.n_split
-                         : ((size_t)p.n_split + (size_t)batch * c->num_kv_heads) * (size_t)group;
+                         : ((size_t)p.n_split + (size_t)batch * c->num_kv_heads) * (size_t)group * q_len;
   d.ws_o = (float *)ws;
   d.ws_ml = (float *)ws + rows * (size_t)c->head_dim;
   d.ws_meta = mla ? nullptr : (int32_t *)(d.ws_ml + rows * 2);
@@ -313,6 +317,27 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
   DecodeArgs a;
   int st = fill_decode(c, q, q_dtype, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                        softmax_scale, out, workspace, workspace_bytes, zero_block_count, true, true, &a);
+  if (st) return st;
+  const bool mla = c->attn == FP4KV_MLA;
+  hipError_t e = mla ? launch_mla_partials(a, (hipStream_t)stream) : launch_decode_partials(a, (hipStream_t)stream);
+  if (e != hipSuccess) return FP4KV_ERR_HIP;
+  return to_status(mla ? launch_mla_merge(a, (hipStream_t)stream) : launch_decode_merge(a, (hipStream_t)stream));
+}
+
+size_t fp4_decode_multi_workspace_bytes(const fp4kv_cache *c, int batch, int q_len, int num_q_heads,
+                                        int max_seq_len) {
+  if (check_shape(c) != FP4KV_OK || batch < 0 || q_len < 1 || num_q_heads <= 0 || max_seq_len < 0) return 0;
+  return workspace_for(c, batch, num_q_heads, max_seq_len, nullptr, q_len);
+}
+
+int fp4_decode_attention_multi(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int q_len,
+                               int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
+                               const int32_t *seq_lens, float softmax_scale, float *out, void *workspace,
+                               size_t workspace_bytes, int32_t *zero_block_count, void *stream) {
+  if (c && c->attn == FP4KV_MLA && q_len != 1) return FP4KV_ERR_UNSUPPORTED;
+  DecodeArgs a;
+  int st = fill_decode(c, q, q_dtype, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                       softmax_scale, out, workspace, workspace_bytes, zero_block_count, true, true, &a, q_len);
   if (st) return st;
   const bool mla = c->attn == FP4KV_MLA;
   hipError_t e = mla ? launch_mla_partials(a, (hipStream_t)stream) : launch_decode_partials(a, (hipStream_t)stream);

@@ -222,14 +222,26 @@ __device__ bool find_share(const DecodeArgs &a, int wave, int lane, Share &s) {
   return false;   // not reached: x < T
 }
 
-template <int FMT, int G, int P>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_partials(DecodeArgs a) {
+// Query rows of one KV head: GV "virtual heads" = (query token j, query head g) pairs,
+// v = j * group + g (one query token per sequence: v = g).  One 16-column MFMA holds VS of
+// them (Q1 and Q2 rows; NVFP4 also both block parities), so GV > VS runs RS row sets on
+// the same key/value tile registers.
+template <int FMT, int GV>
+constexpr int row_sets() { return (GV + (FMT == kFmtNV ? 4 : 8) - 1) / (FMT == kFmtNV ? 4 : 8); }
+
+// MQ: several query tokens per sequence (causal rows); false compiles the one-token decode
+// with every row seeing the whole sequence.
+template <int FMT, int GV, int P, bool MQ>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(row_sets<FMT, GV>() == 1 ? 2 : 1, 2)))
+void gqa_partials(DecodeArgs a) {
   constexpr int D = 128;
-  constexpr int NR = 2 * G;                    // stacked rows: (head, Q1/Q2)
+  constexpr int VS = FMT == kFmtNV ? 4 : 8;    // virtual heads per row set
+  constexpr int RS = row_sets<FMT, GV>();      // row sets
+  constexpr int NR = 2 * (GV < VS ? GV : VS);  // stacked rows per set: (virtual head, Q1/Q2)
   constexpr int B = FMT == kFmtNV ? 16 : 32;   // scale block
   constexpr int NBLK = D / B;
   constexpr int NPT = P >= 128 ? 1 : 128 / P;  // pages touched by a 128-token tile
-  static_assert(FMT == kFmtNV ? G <= 4 : G <= 8, "group too large for one 16-column MFMA");
+  static_assert(RS <= 2, "at most two row sets");
   static_assert(P >= 16 && (P % B) == 0, "page size");
 
   const int lane = threadIdx.x;
@@ -237,9 +249,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   Share sh;
   if (!find_share(a, wave, lane, sh)) return;
 
-  __shared__ uint32_t qc[2][G][D / 8];
-  __shared__ int qe[2][G][NBLK];
-  __shared__ float qg[2][G];
+  __shared__ uint32_t qc[2][GV][D / 8];
+  __shared__ int qe[2][GV][NBLK];
+  __shared__ float qg[2][GV];
   __shared__ uint32_t lut[256];                // E4M3 value scale -> four E8M0 pass bytes
   __shared__ float4 sk[128 * 2 + 8];           // NVFP4 key scales of the tile (sk_index)
   // physical page ids of the segment's tiles: entry (tile - tb) * NPT + j is logical page
@@ -260,6 +272,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
   int nzero = 0;
   const bool count_zero = a.zero_blocks != nullptr;
+  const int GQ = MQ ? a.group : GV, QL = MQ ? a.q_len : 1;   // query heads per KV head, tokens
+  const int GVr = MQ ? GQ * QL : GV;           // virtual heads in use (<= GV)
 
   // one segment per (sequence, KV head) unit the wave's share touches
   for (;;) {
@@ -271,28 +285,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int last_lp = min((L - 1) / P, a.max_pages - 1);
   __syncthreads();   // the previous segment has finished reading the staged query and page ids
 
-  // The query rows of this KV head go out first.  Lane l holds EPL consecutive channels
-  // (c0 = EPL * (l % LPR)) of stacked head r = l / LPR, i.e. elements EPL*l .. EPL*l + EPL-1
-  // of the head group's G x 128 block.
-  constexpr int LPR = 64 / G;                  // lanes per query head
-  constexpr int EPL = D / LPR;                 // channels per lane (2G)
+  // The query rows of this KV head go out first, PG virtual heads per pass.  Lane l holds
+  // EPL consecutive channels (c0 = EPL * (l % LPR)) of virtual head ps * PG + l / LPR.
+  constexpr int PG = GV < (FMT == kFmtNV ? 8 : 16) ? GV : (FMT == kFmtNV ? 8 : 16);
+  constexpr int NPASS = GV / PG;
+  constexpr int LPR = 64 / PG;                 // lanes per virtual head
+  constexpr int EPL = D / LPR;                 // channels per lane (2 PG)
   const int qr = lane / LPR, c0 = EPL * (lane % LPR);
   float y[EPL];
-  {
-    const long q0 = ((long)b * a.hq + kvh * G) * D + EPL * lane;
+  auto load_q = [&](int ps) {
+    const int v = ps * PG + qr;
+    const bool in = !MQ || v < GVr;
+    const int j = in ? v / GQ : 0, g = in ? v % GQ : 0;
+    const long q0 = (((long)b * QL + j) * a.hq + kvh * GQ + g) * D + c0;
     if (a.q_bf16) {
       const uint16_t *qp = (const uint16_t *)a.q + q0;
 #pragma unroll
-      for (int j = 0; j < EPL; j++) y[j] = bf16_to_f32(qp[j]);
+      for (int i = 0; i < EPL; i++) y[i] = in ? bf16_to_f32(qp[i]) : 0.0f;
     } else {
       const float *qp = (const float *)a.q + q0;
 #pragma unroll
-      for (int j = 0; j < EPL; j++) y[j] = qp[j];
+      for (int i = 0; i < EPL; i++) y[i] = in ? qp[i] : 0.0f;
     }
     const float *sm = a.qs + kvh * D + c0;
 #pragma unroll
-    for (int j = 0; j < EPL; j++) y[j] = y[j] * sm[j];
-  }
+    for (int i = 0; i < EPL; i++) y[i] = y[i] * sm[i];
+  };
+  load_q(0);
   for (int e = lane; e < (te - tb) * NPT; e += 64)
     pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
   __syncthreads();
@@ -304,6 +323,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   __builtin_amdgcn_sched_barrier(0);
 
   // ---------------- prologue: smoothing, rotation, dual-residual FP4 query ----------------
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ps++) {
+  if (ps > 0) load_q(ps);
+  const int vq = ps * PG + qr;                 // this lane's virtual head
   // Walsh-Hadamard butterflies in the order of the stages h = 1, 2, ..., 64 (each output
   // a single rounded sum or difference): h < EPL inside the lane, h >= EPL with lane
   // l ^ (h / EPL), the lower lane taking x + x', the upper x' - x.
@@ -372,15 +395,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // packed codes of channels c0 .. c0 + EPL - 1 (EPL / 2 bytes)
     if constexpr (EPL >= 8) {
 #pragma unroll
-      for (int i = 0; i < EPL / 8; i++) qc[k][qr][c0 / 8 + i] = w[i];
+      for (int i = 0; i < EPL / 8; i++) qc[k][vq][c0 / 8 + i] = w[i];
     } else if constexpr (EPL == 4) {
-      ((uint16_t *)&qc[k][qr][0])[c0 / 4] = (uint16_t)w[0];
+      ((uint16_t *)&qc[k][vq][0])[c0 / 4] = (uint16_t)w[0];
     } else {
-      ((uint8_t *)&qc[k][qr][0])[c0 / 2] = (uint8_t)w[0];
+      ((uint8_t *)&qc[k][vq][0])[c0 / 2] = (uint8_t)w[0];
     }
-    if ((lane % BL) == 0) qe[k][qr][c0 / B] = e;
-    if ((lane % LPR) == 0) qg[k][qr] = gq;
+    if ((lane % BL) == 0) qe[k][vq][c0 / B] = e;
+    if ((lane % LPR) == 0) qg[k][vq] = gq;
   }
+  }   // passes
   __syncthreads();
 
   const int q4 = lane >> 4;        // lane group: channel block (A/B operands) or token group (D)
@@ -389,40 +413,60 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // holds its (row, block 2*q4 + parity) half of the 32 channels; MFMA j keeps only lane
   // group j by giving every other lane group the E8M0 scale byte 0 (2^-127), whose
   // products vanish below fp32 resolution.
-  v8i bq = {0, 0, 0, 0, 0, 0, 0, 0};
-  int qsb = 127;
-  int qsj[4] = {0, 0, 0, 0};
-  float a_own = 0.0f;
-  {
+  // Per row set: column n holds stacked row r (NVFP4: r = n & 7, parity n >> 3), virtual
+  // head rs * VS + r / 2, query pass r & 1; its query token sees Lrow tokens.
+  v8i bq[RS];
+  int qsb[RS];
+  int qsj[RS][4];
+  float a_own[RS];
+  int Lrow[RS];
+  bool lrow[RS];                               // the column holds a row in use
+  const int ncol = FMT == kFmtNV ? (n & 7) : n;
+#pragma unroll
+  for (int rs = 0; rs < RS; rs++) {
+    bq[rs] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    qsb[rs] = 127;
+    a_own[rs] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) qsj[rs][j] = 0;
     const float gk = FMT == kFmtNV ? a.gk[kvh] : 1.0f;
-    const int r = FMT == kFmtNV ? (n & 7) : n;       // stacked row of this column
-    const int h = r >> 1, k = r & 1;
-    const bool live = r < NR;
+    const int r = ncol;
+    const int h = rs * VS + (r >> 1), k = r & 1;
+    const bool live = r < NR && (!MQ || h < GVr);
+    lrow[rs] = live;
+    Lrow[rs] = MQ && live ? L - QL + 1 + h / GQ : L;
     if constexpr (FMT == kFmtNV) {
       const int par = n >> 3;
       const int blk = 2 * q4 + par;
       uint32_t c0 = live ? qc[k][h][2 * blk] : 0u, c1 = live ? qc[k][h][2 * blk + 1] : 0u;
       int e = live ? qe[k][h][blk] : -128;
-      qsb = e == -128 ? 127 : e + 127;
-      if (par == 0) { bq[0] = (int)c0; bq[1] = (int)c1; }
-      else { bq[2] = (int)c0; bq[3] = (int)c1; }
+      qsb[rs] = e == -128 ? 127 : e + 127;
+      if (par == 0) { bq[rs][0] = (int)c0; bq[rs][1] = (int)c1; }
+      else { bq[rs][2] = (int)c0; bq[rs][3] = (int)c1; }
 #pragma unroll
-      for (int j = 0; j < 4; j++) qsj[j] = (j == q4) ? qsb : 0;
+      for (int j = 0; j < 4; j++) qsj[rs][j] = (j == q4) ? qsb[rs] : 0;
     } else {
       if (live) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) bq[i] = (int)qc[k][h][4 * q4 + i];
-        qsb = qe[k][h][q4] + 127;
+        for (int i = 0; i < 4; i++) bq[rs][i] = (int)qc[k][h][4 * q4 + i];
+        qsb[rs] = qe[k][h][q4] + 127;
       }
     }
-    if (live) a_own = (qg[k][h] * gk) * a.coef;
+    if (live) a_own[rs] = (qg[k][h] * gk) * a.coef;
   }
+  const int Lmin = MQ ? L - QL + 1 : L;       // the shortest row's length
 
   // ---------------- main loop over 128-token tiles ----------------
-  float m_run = -INFINITY, l_run = 0.0f, f_run = 1.0f;
-  v4f o_run[8];
+  float m_run[RS], l_run[RS], f_run[RS];
+  v4f o_run[RS][8];
 #pragma unroll
-  for (int cg = 0; cg < 8; cg++) o_run[cg] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int rs = 0; rs < RS; rs++) {
+    m_run[rs] = -INFINITY;
+    l_run[rs] = 0.0f;
+    f_run[rs] = 1.0f;
+#pragma unroll
+    for (int cg = 0; cg < 8; cg++) o_run[rs][cg] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
   const float inv6gp = 1.0f / (6.0f * 0.0009765625f);   // fl32(1 / fl32(6 * 2^-10))
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
@@ -453,16 +497,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       __syncthreads();
     }
 
+    // ---- per row set: Q.K^T, softmax, P quantization, P.V on the same key / value tile
+#pragma unroll
+    for (int rs = 0; rs < RS; rs++) {
     // ---- Q.K^T: logits for (column n, tokens 32*q4 + 4i + rr)
     float s[8][4];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const v8i av = {(int)kt.x[i].x, (int)kt.x[i].y, (int)kt.x[i].z, (int)kt.x[i].w, 0, 0, 0, 0};
       if constexpr (FMT == kFmtNV) {
-        const v4f o0 = mfma4<0, 0>(av, bq, zero, 127, qsj[0]);
-        const v4f o1 = mfma4<0, 0>(av, bq, zero, 127, qsj[1]);
-        const v4f o2 = mfma4<0, 0>(av, bq, zero, 127, qsj[2]);
-        const v4f o3 = mfma4<0, 0>(av, bq, zero, 127, qsj[3]);
+        const v4f o0 = mfma4<0, 0>(av, bq[rs], zero, 127, qsj[rs][0]);
+        const v4f o1 = mfma4<0, 0>(av, bq[rs], zero, 127, qsj[rs][1]);
+        const v4f o2 = mfma4<0, 0>(av, bq[rs], zero, 127, qsj[rs][2]);
+        const v4f o3 = mfma4<0, 0>(av, bq[rs], zero, 127, qsj[rs][3]);
         const int par = n >> 3;
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) {
@@ -475,7 +522,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           s[i][rr] = acc + xlane8(acc);                  // even-block sum + odd-block sum
         }
       } else {
-        const v4f o = mfma4<0, 0>(av, bq, zero, (int)byte_of(kt.x[8], i), qsb);
+        const v4f o = mfma4<0, 0>(av, bq[rs], zero, (int)byte_of(kt.x[8], i), qsb[rs]);
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) s[i][rr] = o[rr];
       }
@@ -485,15 +532,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int i = 0; i < 8; i++)
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
-        const float t1 = a_own * s[i][rr];
+        const float t1 = a_own[rs] * s[i][rr];
         s[i][rr] = t1 + xlane1(t1);
       }
-    if (tok0 + 128 > L) {
+    if (tok0 + 128 > Lmin) {   // past a row's own prefix (causal for several query tokens)
+      const int Lr = Lrow[rs];
 #pragma unroll
       for (int i = 0; i < 8; i++)
 #pragma unroll
         for (int rr = 0; rr < 4; rr++)
-          if (tok0 + 32 * q4 + 4 * i + rr >= L) s[i][rr] = -INFINITY;
+          if (tok0 + 32 * q4 + 4 * i + rr >= Lr) s[i][rr] = -INFINITY;
     }
     // ---- transposed softmax over the tile; block maxima of the logits give the
     // probability block maxima (exp2 is monotone)
@@ -506,12 +554,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         bm1 = fmaxf(bm1, s[i + 4][rr]);
       }
     const float mt = max_x32(max_x16(fmaxf(bm0, bm1)));
+    // a tile holding none of the row's tokens (a shorter query row) contributes nothing
+    const bool empty = MQ && mt == -INFINITY;
+    const float mts = empty ? 0.0f : mt;
     float lt = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++)
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
-        const float p = __builtin_amdgcn_exp2f(s[i][rr] - mt);
+        const float p = __builtin_amdgcn_exp2f(s[i][rr] - mts);
         s[i][rr] = p;
         lt = lt + p;
       }
@@ -519,7 +570,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     uint32_t pk[4];
     int pbyte[2];
     if constexpr (FMT == kFmtNV) {
-      const float am[2] = {__builtin_amdgcn_exp2f(bm0 - mt), __builtin_amdgcn_exp2f(bm1 - mt)};
+      const float am[2] = {__builtin_amdgcn_exp2f(bm0 - mts), __builtin_amdgcn_exp2f(bm1 - mts)};
 #pragma unroll
       for (int pb = 0; pb < 2; pb++) {
         const int e = ceil_log2_clamp(am[pb] * inv6gp, -9, 8);
@@ -529,7 +580,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         pk[2 * pb + 1] = pack8(s[4 * pb + 2], s[4 * pb + 3], ps);
       }
     } else {
-      const float am = __builtin_amdgcn_exp2f(fmaxf(bm0, bm1) - mt);
+      const float am = __builtin_amdgcn_exp2f(fmaxf(bm0, bm1) - mts);
       const int e = mx_exp(am);
       const float ps = ldexpf(1.0f, e);
       pbyte[0] = pbyte[1] = e + 127;
@@ -537,8 +588,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       for (int w = 0; w < 4; w++) pk[w] = pack8(s[2 * w], s[2 * w + 1], ps);
     }
     if (count_zero) {
-      const int r = FMT == kFmtNV ? (n & 7) : n;
-      const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (r & 1) == 0 && r < NR;
+      const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (ncol & 1) == 0 && lrow[rs];
+      const int L = Lrow[rs];
       if (rep) {
         if constexpr (FMT == kFmtNV) {
 #pragma unroll
@@ -553,18 +604,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // tile's P.V is accumulated by the MFMAs on top of o_run * gamma with the tile's own
     // weight as the new F, so no separate accumulator is needed.  A tile whose weight is
     // below 2^-60 is weighted 2^-60 (its contribution is below fp32 resolution either way).
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_new = fmaxf(m_run[rs], mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run[rs] - m_new);
     const float beta = __builtin_amdgcn_exp2f(mt - m_new);
-    l_run = fmaf(l_run, alpha, lt * beta);
-    m_run = m_new;
-    const float f_new = fmaxf(beta, 8.67361737988403547e-19f);   // 2^-60
-    const float gamma = (alpha * f_run) * __builtin_amdgcn_rcpf(f_new);
-    f_run = f_new;
+    l_run[rs] = fmaf(l_run[rs], alpha, lt * beta);
+    m_run[rs] = m_new;
+    const float f_new = empty ? f_run[rs] : fmaxf(beta, 8.67361737988403547e-19f);   // 2^-60
+    const float gamma = (alpha * f_run[rs]) * __builtin_amdgcn_rcpf(f_new);
+    f_run[rs] = f_new;
 #pragma unroll
     for (int cg = 0; cg < 8; cg++)
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = o_run[cg][rr] * gamma;
+      for (int rr = 0; rr < 4; rr++) o_run[rs][cg][rr] = o_run[rs][cg][rr] * gamma;
     // ---- P.V
     if constexpr (FMT == kFmtNV) {
       const v8i p0 = {(int)pk[0], (int)pk[1], 0, 0, 0, 0, 0, 0};
@@ -576,23 +627,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const uint32_t b0 = P >= 32 ? byte_of(vt.x[8], 2 * cg) : byte_of(vt.x[8], cg);
         const uint32_t b1 = P >= 32 ? byte_of(vt.x[8], 2 * cg + 1) : byte_of(vt.x[8], 8 + cg);
         const int l0 = (int)lut[b0], l1 = (int)lut[b1];
-        v4f c = mfma4<0, 0>(av, p0, o_run[cg], l0, pbyte[0]);
+        v4f c = mfma4<0, 0>(av, p0, o_run[rs][cg], l0, pbyte[0]);
         c = mfma4<1, 0>(av, p0, c, l0, pbyte[0]);
         c = mfma4<2, 0>(av, p0, c, l0, pbyte[0]);
         c = mfma4<3, 0>(av, p0, c, l0, pbyte[0]);
         c = mfma4<0, 0>(av, p1, c, l1, pbyte[1]);
         c = mfma4<1, 0>(av, p1, c, l1, pbyte[1]);
         c = mfma4<2, 0>(av, p1, c, l1, pbyte[1]);
-        o_run[cg] = mfma4<3, 0>(av, p1, c, l1, pbyte[1]);
+        o_run[rs][cg] = mfma4<3, 0>(av, p1, c, l1, pbyte[1]);
       }
     } else {
       const v8i pv = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
 #pragma unroll
       for (int cg = 0; cg < 8; cg++) {
         const v8i av = {(int)vt.x[cg].x, (int)vt.x[cg].y, (int)vt.x[cg].z, (int)vt.x[cg].w, 0, 0, 0, 0};
-        o_run[cg] = mfma4<0, 0>(av, pv, o_run[cg], (int)byte_of(vt.x[8], cg), pbyte[0]);
+        o_run[rs][cg] = mfma4<0, 0>(av, pv, o_run[rs][cg], (int)byte_of(vt.x[8], cg), pbyte[0]);
       }
     }
+    }   // row sets
     __builtin_amdgcn_sched_barrier(0);
     {
       const bool live = tile + 1 < te;
@@ -610,20 +662,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 
   // ---------------- epilogue: split partials ----------------
-  const float l_tot = sum_x32(sum_x16(l_run));
-  const int r = FMT == kFmtNV ? (n & 7) : n;
-  const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (r & 1) == 0 && r < NR;
   const long u = (long)b * a.hkv + kvh;
   const long slot = wave + u;
-  if (rep) {
-    const long rowi = slot * G + (r >> 1);
-    const float gv = (FMT == kFmtNV ? a.gv[kvh] : 1.0f) * f_run;
 #pragma unroll
-    for (int cg = 0; cg < 8; cg++) {
-      float4 v = {o_run[cg][0] * gv, o_run[cg][1] * gv, o_run[cg][2] * gv, o_run[cg][3] * gv};
-      *(float4 *)(a.ws_o + rowi * D + 16 * cg + 4 * q4) = v;
+  for (int rs = 0; rs < RS; rs++) {
+    const float l_tot = sum_x32(sum_x16(l_run[rs]));
+    const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (ncol & 1) == 0 && lrow[rs];
+    if (rep) {
+      const long rowi = slot * GVr + rs * VS + (ncol >> 1);   // one slot holds GVr partial rows
+      const float gv = (FMT == kFmtNV ? a.gv[kvh] : 1.0f) * f_run[rs];
+#pragma unroll
+      for (int cg = 0; cg < 8; cg++) {
+        float4 v = {o_run[rs][cg][0] * gv, o_run[rs][cg][1] * gv, o_run[rs][cg][2] * gv, o_run[rs][cg][3] * gv};
+        *(float4 *)(a.ws_o + rowi * D + 16 * cg + 4 * q4) = v;
+      }
+      if (q4 == 0) *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run[rs], l_tot};
     }
-    if (q4 == 0) *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run, l_tot};
   }
   // the wave holding the unit's first tile records where the unit's partials are
   if (tb == 0 && lane == 0) {
@@ -712,23 +766,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // each for (m, l); the weights then go through LDS to the channel loop (lane = 2
 // channels), whose loads are independent.
 __global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
-  const int row = blockIdx.x, lane = threadIdx.x;
-  const int b = row / a.hq, h = row % a.hq;
-  const int G = a.group;
+  const int row = blockIdx.x, lane = threadIdx.x;   // row = (b * q_len + j) * hq + h
+  const int G = a.group, GVr = a.group * a.q_len;
+  const int b = row / (a.q_len * a.hq), rem = row % (a.q_len * a.hq);
+  const int j = rem / a.hq, h = rem % a.hq;
   const long u = (long)b * a.hkv + h / G;
   float2 *dst = (float2 *)(a.out + (long)row * 128) + lane;
   if (seq_tiles(a, b) == 0) { *dst = float2{0.f, 0.f}; return; }
   const int2 meta = *(const int2 *)(a.ws_meta + 2 * u);
   const int nv = meta.y;
-  const long r0 = (long)meta.x * G + h % G;    // first partial row; one slot holds G rows
+  // first partial row; one slot holds GVr rows, virtual head j * G + h % G
+  const long r0 = (long)meta.x * GVr + j * G + h % G;
   const float *ml = a.ws_ml + r0 * 2;
   const float *o = a.ws_o + r0 * 128;
-  const long so = (long)G * 128, sm = 2L * G;  // strides between the unit's partials
+  const long so = (long)GVr * 128, sm = 2L * GVr;  // strides between the unit's partials
   __shared__ float wsh[256];
   float M = -INFINITY;
   for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[sm * s]);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
+  if (!(M > -INFINITY)) { *dst = float2{0.f, 0.f}; return; }   // a query row with no tokens
   float den = 0.f;
   for (int s = lane; s < nv; s += 64) den = fmaf(__builtin_amdgcn_exp2f(ml[sm * s] - M), ml[sm * s + 1], den);
 #pragma unroll
@@ -759,39 +816,56 @@ __global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
   *dst = float2{n0 / den, n1 / den};
 }
 
-template <int FMT, int G>
+template <int FMT, int GV, bool MQ>
 static hipError_t launch_g(const DecodeArgs &a, dim3 grid, hipStream_t s) {
   switch (a.page_size) {
     case 16:
-      if constexpr (FMT == kFmtNV) { gqa_partials<FMT, G, 16><<<grid, 64, 0, s>>>(a); break; }
+      if constexpr (FMT == kFmtNV) { gqa_partials<FMT, GV, 16, MQ><<<grid, 64, 0, s>>>(a); break; }
       return hipErrorInvalidValue;
-    case 32: gqa_partials<FMT, G, 32><<<grid, 64, 0, s>>>(a); break;
-    case 64: gqa_partials<FMT, G, 64><<<grid, 64, 0, s>>>(a); break;
-    case 128: gqa_partials<FMT, G, 128><<<grid, 64, 0, s>>>(a); break;
-    case 256: gqa_partials<FMT, G, 256><<<grid, 64, 0, s>>>(a); break;
+    case 32: gqa_partials<FMT, GV, 32, MQ><<<grid, 64, 0, s>>>(a); break;
+    case 64: gqa_partials<FMT, GV, 64, MQ><<<grid, 64, 0, s>>>(a); break;
+    case 128: gqa_partials<FMT, GV, 128, MQ><<<grid, 64, 0, s>>>(a); break;
+    case 256: gqa_partials<FMT, GV, 256, MQ><<<grid, 64, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// Virtual heads (query tokens x query heads per KV head) rounded up to a compiled size:
+// NVFP4 up to 8 (two row sets of 4), MXFP4 up to 16 (two row sets of 8); more row sets
+// would not fit the register file next to the resident key / value tiles.
 hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   const dim3 grid((unsigned)a.n_waves);
-  if (a.fmt == kFmtNV) {
+  if (a.q_len == 1) {   // one query token per sequence: virtual heads = query heads
+    if (a.fmt == kFmtNV) {
+      switch (a.group) {
+        case 1: return launch_g<kFmtNV, 1, false>(a, grid, s);
+        case 2: return launch_g<kFmtNV, 2, false>(a, grid, s);
+        case 4: return launch_g<kFmtNV, 4, false>(a, grid, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
     switch (a.group) {
-      case 1: return launch_g<kFmtNV, 1>(a, grid, s);
-      case 2: return launch_g<kFmtNV, 2>(a, grid, s);
-      case 4: return launch_g<kFmtNV, 4>(a, grid, s);
+      case 1: return launch_g<kFmtMX, 1, false>(a, grid, s);
+      case 2: return launch_g<kFmtMX, 2, false>(a, grid, s);
+      case 4: return launch_g<kFmtMX, 4, false>(a, grid, s);
+      case 8: return launch_g<kFmtMX, 8, false>(a, grid, s);
       default: return hipErrorInvalidValue;
     }
   }
-  switch (a.group) {
-    case 1: return launch_g<kFmtMX, 1>(a, grid, s);
-    case 2: return launch_g<kFmtMX, 2>(a, grid, s);
-    case 4: return launch_g<kFmtMX, 4>(a, grid, s);
-    case 8: return launch_g<kFmtMX, 8>(a, grid, s);
-    default: return hipErrorInvalidValue;
+  const int gv = a.group * a.q_len;
+  if (a.fmt == kFmtNV) {
+    if (gv <= 2) return launch_g<kFmtNV, 2, true>(a, grid, s);
+    if (gv <= 4) return launch_g<kFmtNV, 4, true>(a, grid, s);
+    if (gv <= 8) return launch_g<kFmtNV, 8, true>(a, grid, s);
+    return hipErrorInvalidValue;
   }
+  if (gv <= 2) return launch_g<kFmtMX, 2, true>(a, grid, s);
+  if (gv <= 4) return launch_g<kFmtMX, 4, true>(a, grid, s);
+  if (gv <= 8) return launch_g<kFmtMX, 8, true>(a, grid, s);
+  if (gv <= 16) return launch_g<kFmtMX, 16, true>(a, grid, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_cache_read(const DecodeArgs &a, uint32_t *sink, hipStream_t s) {
@@ -813,7 +887,7 @@ hipError_t launch_cache_read(const DecodeArgs &a, uint32_t *sink, hipStream_t s)
 
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  gqa_merge<<<(unsigned)(a.batch * a.hq), 64, 0, s>>>(a);
+  gqa_merge<<<(unsigned)(a.batch * a.q_len * a.hq), 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ struct AppendArgs {
 
 struct DecodeArgs {
   int fmt, page_size, hkv, group, hq, d, rope_dim, batch, max_pages, num_pages, q_bf16;
+  int q_len;             // GQA: query tokens per sequence (causal), 1 for ordinary decode
   int n_split, tiles_per_split;   // MLA: splits per (sequence, head group) and their tiles
   int n_waves;                    // GQA: waves of the balanced partition (an upper bound)
   float softmax_scale;

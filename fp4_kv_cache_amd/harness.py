@@ -36,6 +36,12 @@ class Built:
             q = np.concatenate([q, qr], axis=-1)
         return _dev(q, self.w, torch, self.device)
 
+    def queries_multi(self, n):
+        """[batch, n, Hq, d] queries of every sequence's n newest tokens (GQA)."""
+        import torch
+        q = np.stack([W.queries_multi(self.w, b, n) for b in range(self.w["batch"])])
+        return _dev(q, self.w, torch, self.device)
+
 
 def slots_for(bt_row, positions, P):
     positions = np.asarray(positions, np.int64)

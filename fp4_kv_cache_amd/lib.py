@@ -50,6 +50,9 @@ _SIGS = {
     "fp4kv_cache_read": (_c_int, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _vp, _c_int, _vp, _vp, _c_size,
                                   _vp]),
     "fp4kv_cache_read_sink_words": (_c_size, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int]),
+    "fp4_decode_multi_workspace_bytes": (_c_size, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int, _c_int]),
+    "fp4_decode_attention_multi": (_c_int, [ctypes.POINTER(FP4KVCache), _vp, _c_int, _c_int, _c_int, _c_int, _vp,
+                                            _c_int, _vp, ctypes.c_float, _vp, _vp, _c_size, _vp, _vp]),
     "fp4kv_stream_read": (_c_int, [_vp, _c_size, _vp, _vp]),
     "fp4kv_stream_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
     "fp4kv_status_string": (ctypes.c_char_p, [_c_int]),
@@ -113,6 +116,17 @@ def fp4_decode_merge(cache, batch, num_q_heads, max_pages_per_seq, seq_lens, out
                      workspace_bytes, stream):
     return load().fp4_decode_merge(_ref(cache), batch, num_q_heads, max_pages_per_seq, seq_lens, out,
                                    workspace, workspace_bytes, stream)
+
+
+def fp4_decode_multi_workspace_bytes(cache, batch, q_len, num_q_heads, max_seq_len):
+    return load().fp4_decode_multi_workspace_bytes(_ref(cache), batch, q_len, num_q_heads, max_seq_len)
+
+
+def fp4_decode_attention_multi(cache, q, q_dtype, batch, q_len, num_q_heads, block_table, max_pages_per_seq,
+                               seq_lens, softmax_scale, out, workspace, workspace_bytes, zero_block_count, stream):
+    return load().fp4_decode_attention_multi(_ref(cache), q, q_dtype, batch, q_len, num_q_heads, block_table,
+                                             max_pages_per_seq, seq_lens, softmax_scale, out, workspace,
+                                             workspace_bytes, zero_block_count, stream)
 
 
 def fp4kv_cache_read(cache, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, sink, sink_words,
@@ -219,6 +233,27 @@ class PagedFP4Cache:
                                   zero_block_count.data_ptr() if zero_block_count is not None else None,
                                   self._stream())
         check(st, "fp4_decode_attention")
+        return out
+
+    def decode_multi(self, q, block_table, seq_lens, softmax_scale, out=None, workspace=None,
+                     zero_block_count=None):
+        """q [batch, q_len, hq, d]: the q_len newest tokens of every sequence (already in the
+        cache), causal; returns [batch, q_len, hq, d] float32."""
+        torch = self.torch
+        batch, q_len, hq = q.shape[0], q.shape[1], q.shape[2]
+        maxp = block_table.shape[1]
+        if out is None:
+            out = torch.empty((batch, q_len, hq, self.head_dim), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            nb = fp4_decode_multi_workspace_bytes(self.desc, batch, q_len, hq, maxp * self.page_size)
+            workspace = torch.empty(max(nb, 4), dtype=torch.uint8, device=q.device)
+        dt = BF16 if q.dtype == torch.bfloat16 else F32
+        st = fp4_decode_attention_multi(self.desc, q.data_ptr(), dt, batch, q_len, hq, block_table.data_ptr(),
+                                        maxp, seq_lens.data_ptr(), float(softmax_scale), out.data_ptr(),
+                                        workspace.data_ptr(), workspace.numel(),
+                                        zero_block_count.data_ptr() if zero_block_count is not None else None,
+                                        self._stream())
+        check(st, "fp4_decode_attention_multi")
         return out
 
     def views(self):

@@ -151,6 +151,14 @@ def queries(w, b):
     return _cast(w, _rng(w, T_Q, b).standard_normal((w["hq"], w["d"]), dtype=np.float32))
 
 
+def queries_multi(w, b, n):
+    """Queries of the n newest tokens of sequence b, float32 [n, Hq, d] (token n - 1 is the
+    one ``queries`` draws)."""
+    rows = [_cast(w, _rng(w, T_Q, b, 1 + j).standard_normal((w["hq"], w["d"]), dtype=np.float32))
+            for j in range(n - 1)]
+    return np.stack(rows + [queries(w, b)])
+
+
 def rope_keys(w, b, L):
     return bf16_round(_rng(w, T_KROPE, b).standard_normal((L, w["rope"]), dtype=np.float32))
 

@@ -177,6 +177,26 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
                          void *workspace, size_t workspace_bytes, int32_t *zero_block_count,
                          void *stream);
 
+/* Multi-token decode (speculative or multi-token-prediction verification): q_len
+ * query tokens per sequence, the q_len newest tokens of each sequence (positions
+ * seq_lens[b] - q_len .. seq_lens[b] - 1, already appended to the cache); query j
+ * attends to tokens 0 .. seq_lens[b] - q_len + j (causal).  The rows of all q_len
+ * tokens are stacked on the same key / value tiles ("BitDecoding-FP4 : décodage
+ * natif du KV cache FP4", Analyse approfondie: query rows stacked into one matrix
+ * operation), so the cache is read once for all of them.
+ *   q    [batch][q_len][num_q_heads][head_dim], dtype q_dtype
+ *   out  f32 [batch][q_len][num_q_heads][head_dim]
+ * Other arguments as fp4_decode_attention; seq_lens[b] must be 0 or >= q_len.
+ * GQA only (MLA: q_len 1); q_len <= 8 and group * q_len <= 8 (NVFP4) or <= 16
+ * (MXFP4), else FP4KV_ERR_UNSUPPORTED.  q_len == 1 is fp4_decode_attention. */
+size_t fp4_decode_multi_workspace_bytes(const fp4kv_cache *c, int batch, int q_len, int num_q_heads,
+                                        int max_seq_len);
+int fp4_decode_attention_multi(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int q_len,
+                               int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
+                               const int32_t *seq_lens, float softmax_scale, float *out,
+                               void *workspace, size_t workspace_bytes, int32_t *zero_block_count,
+                               void *stream);
+
 /* The two halves of fp4_decode_attention, for callers that merge split-K
  * partials themselves (e.g. across devices holding different pages of one
  * sequence) or time the stages separately.  fp4_decode_partials writes

@@ -127,3 +127,40 @@ def compare_mla(built, seqs=None, tol=1e-3):
         worst, worst_ref = max(worst, e), max(worst_ref, er)
         assert e <= tol, "seq %d: max row error %.3g > %.1g" % (b, e, tol)
     return worst, worst_ref, zgpu
+
+
+def compare_gqa_multi(built, n, pairs=None, tol=1e-3):
+    """Multi-token decode (n newest tokens per sequence, causal) vs the oracle's stacked-row
+    pipeline on (sequence, KV head) pairs; returns (max err, max err vs fp64 attention)."""
+    import torch
+    w = built.w
+    g = w["hq"] // w["hkv"]
+    ksi, qs, gk, gv = built.calib
+    q = built.queries_multi(n)
+    zc = torch.zeros(1, dtype=torch.int32, device=built.device)
+    out = built.cache.decode_multi(q, built.bt, built.seq_lens, W.softmax_scale(w), zero_block_count=zc)
+    torch.cuda.synchronize()
+    qn, out = q.float().cpu().numpy(), out.cpu().numpy()
+    pairs = [(b, h) for b in range(w["batch"]) for h in range(w["hkv"])] if pairs is None else pairs
+    worst, worst_ref, zor = 0.0, 0.0, 0
+    sc = W.softmax_scale(w)
+    for b, h in pairs:
+        L = int(built.lens[b])
+        got = out[b, :, h * g:(h + 1) * g]
+        assert np.all(np.isfinite(got)), (b, h)
+        if L == 0:
+            worst = max(worst, float(np.abs(got).max()))
+            continue
+        K = W.keys(w, b, h, L)
+        V = W.values(w, b, h, L)
+        rows = qn[b, :, h * g:(h + 1) * g]
+        res = A.gqa_head_multi(rows, K, V, ksi[h], qs[h], gk[h], gv[h], w["fmt"], sc, L=L)
+        zor += res["zero_blocks"]
+        for j in range(n):
+            e = float(np.max(A.row_rel_err(got[j], res["out"][j])))
+            ref = A.reference_attention(rows[j], K[:L - n + 1 + j], V[:L - n + 1 + j], sc)
+            worst = max(worst, e)
+            worst_ref = max(worst_ref, float(np.max(A.row_rel_err(got[j], ref))))
+            assert e <= tol, "seq %d kv head %d token %d: max row error %.3g > %.1g" % (b, h, j, e, tol)
+    return worst, worst_ref, int(zc.item()), zor
+

@@ -99,6 +99,15 @@ def test_workspace_and_group_checks(lib):
     assert words > 0 and words % 64 == 0
     assert L.fp4kv_cache_read(c, 3, 8, 1, 16, 1, 1, words - 1, None) == L.ERR_INVALID_ARG
     assert L.fp4kv_cache_read(c, 3, 7, 1, 16, 1, 1, words, None) == L.ERR_INVALID_ARG
+    # multi-token decode: q_len 1 is the ordinary workspace; limits on q_len and group * q_len
+    assert L.fp4_decode_multi_workspace_bytes(c, 3, 1, 8, 1000) == need
+    assert L.fp4_decode_multi_workspace_bytes(c, 3, 2, 8, 1000) > need
+    big = 1 << 30
+    assert L.fp4_decode_attention_multi(c, 1, 0, 3, 0, 8, 1, 16, 1, 0.1, 1, 1, big, None, None) == L.ERR_INVALID_ARG
+    assert L.fp4_decode_attention_multi(c, 1, 0, 3, 9, 2, 1, 16, 1, 0.1, 1, 1, big, None, None) == L.ERR_UNSUPPORTED
+    assert L.fp4_decode_attention_multi(c, 1, 0, 3, 4, 8, 1, 16, 1, 0.1, 1, 1, big, None, None) == L.ERR_UNSUPPORTED
+    need2 = L.fp4_decode_multi_workspace_bytes(c, 3, 2, 8, 1000)
+    assert L.fp4_decode_attention_multi(c, 1, 0, 3, 2, 8, 1, 16, 1, 0.1, 1, 1, need2 - 1, None, None) == L.ERR_WORKSPACE
     assert L.fp4kv_status_string(3) == "workspace too small"
 
 

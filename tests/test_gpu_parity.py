@@ -8,7 +8,7 @@ import pytest
 
 from fp4_kv_cache_amd import workloads as W
 from fp4_kv_cache_amd import harness
-from _gpu import say, check_gqa_cache, check_mla_cache, compare_gqa, compare_mla
+from _gpu import say, check_gqa_cache, check_mla_cache, compare_gqa, compare_gqa_multi, compare_mla
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -170,6 +170,22 @@ def test_mla_page_sizes(torch_dev, name, page):
     check_mla_cache(built)
     worst, worst_ref, zg = compare_mla(built, tol=TOL)
     say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
+
+
+@pytest.mark.parametrize("name,hq,n", [("qwen3_4b", 32, 2), ("qwen3_4b", 16, 4), ("qwen3_4b", 8, 8),
+                                       ("qwen3_4b", 8, 3), ("qwen3_30b_a3b", 32, 2), ("qwen3_30b_a3b", 16, 4),
+                                       ("qwen3_30b_a3b", 8, 7)])
+def test_decode_multi_token(torch_dev, name, hq, n):
+    """Several query tokens per sequence (causal), stacked on the same key / value tiles in
+    one or two row sets; lengths put the shorter rows' last tile empty (129 = 128 + 1) and
+    across a page boundary."""
+    lens = np.array([n, 129, 0, 700, 1000 + n], np.int32)
+    w = W.workload(name, batch=len(lens), hq=hq)
+    say("decode multi-token %s hq=%d n=%d" % (name, hq, n), lens.tolist())
+    built = harness.build(w, lens=lens)
+    worst, worst_ref, zg, zo = compare_gqa_multi(built, n, tol=TOL)
+    say("max err vs oracle %.3g, vs fp64 %.3g, zero blocks gpu %d oracle %d" % (worst, worst_ref, zg, zo))
+    assert zg == zo
 
 
 def test_decode_underflow_no_zero_blocks(torch_dev):
