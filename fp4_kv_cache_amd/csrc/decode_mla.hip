@@ -7,8 +7,8 @@
 // stacked query rows sharing each latent tile, transposed softmax with fused
 // underflow-aware FP4 probability quantization.
 //
-// Mapping onto CDNA4 (one workgroup of two waves = one (sequence, group of 16 heads, split),
-// each wave owning half of the 512 latent channels):
+// Mapping onto CDNA4, NVFP4 latent (one workgroup of eight waves = one (sequence, split) for
+// four groups of 16 query heads; per group one wave for Q.K^T and softmax, one for P.V):
 //  * The latent is quantized in 16-token x 16-channel tiles with an E4M3 scale each.  For
 //    Q.K^T the latent codes are widened to fp16 with their tile scale (code * S has at
 //    most six significant bits, so the fp16 value is exact) and the dual-residual query
@@ -24,9 +24,9 @@
 //    its token's latent row per token group.
 //  * Token rows of the Q.K^T A operand are ordered like the GQA kernel (row 4q + r of
 //    token group i = tile token 32q + 4i + r), so the D layout is the P.V B operand.
-//  * P.V: the latent's channel-major copy is the A operand (16 channels x 128 tokens) and
-//    the tile scale goes through the same binary expansion into E8M0 passes as the GQA
-//    value scale (four mantissa-bit passes x two token parities).
+//  * P.V: the value operand (16 channels x 128 tokens) is read transposed from the same
+//    token-major tile in LDS, and the tile scale goes through the same binary expansion
+//    into E8M0 passes as the GQA value scale (four mantissa-bit passes x two token parities).
 //  * The merge kernel un-rotates and un-smooths the merged latent output:
 //    out = (o H / 512) * q_smooth.
 #include "decode_common.h"
@@ -71,29 +71,73 @@ __device__ __forceinline__ h2 e4m3_h2(uint32_t byte) {
   return h2{h, h};
 }
 
-// MLA partials.  A workgroup of two waves serves one (sequence, group of 16 query heads,
-// split).  Wave hc owns latent channels 256 hc .. 256 hc + 255: it keeps its half of the
-// Q1 / Q2 operands in registers, computes the Q1 and Q2 dot products over its channels,
-// and accumulates P.V for its channels only.  The half dot products meet in LDS once per
-// tile; both waves add them (addition is commutative, so both get the same sums), compute
-// the 64-channel rope dot product in full, and form the same logits, softmax state and P.
-// Grid: one-dimensional; the head groups of one (sequence, split) get ids with equal
-// residue mod 8 so that they tend to share an XCD's L2 (they read the same latent tiles).
-// Performance only: any placement gives the same result.
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at lds + 16 l (lds is
+// wave-uniform; inactive lanes write nothing).  Written as inline assembly because the compiler
+// would make every LDS read it cannot prove disjoint from a pending LDS load wait for it, which
+// defeats loading the next tile while the current one is read; the kernel waits for its own
+// loads (vmcnt) before the barrier that hands a tile to the other waves.  M0 holds the LDS base
+// (one wait state between writing M0 and the load).
+__device__ __forceinline__ void lds_load16(const void *g, const void *lds) {
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(base)), "v"(g) : "memory");
+}
+__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposed 4-bit LDS read: within each group of 16 lanes, lane 16 g + j receives nibble j of
+// the 8-byte rows addressed by lanes 16 g .. 16 g + 15, in lane order.
+typedef int v2i __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2i lds_read_tr4(const uint8_t *p) {
+  return __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(p));
+}
+
+// Value of an E2M1 code (exact), computed without branches
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const bool sub = m < 2u;
+  const int mant = sub ? (int)m : 2 + (int)(m & 1u);
+  const int ex = sub ? -1 : (int)(m >> 1) - 2;
+  return __uint_as_float(__float_as_uint(ldexpf((float)mant, ex)) | ((c & 8u) << 28));
+}
+
+// Slot of 16-byte chunk c of a staged latent row r is c ^ swz_lat(r), of a rope row c ^ swz_rope(r):
+// the 16 rows one Q.K^T operand read touches (tile tokens 32 a + b + 4 i, a, b < 4) and the 16
+// consecutive rows one transposed P.V read touches then fall on distinct banks.
+__device__ __forceinline__ int swz_lat(int r) { return (r & 15) ^ (((r >> 5) & 3) << 2); }
+__device__ __forceinline__ int swz_rope(int r) { return ((r >> 1) & 1) | (((r >> 5) & 3) << 1); }
+
+// MLA partials, NVFP4 latent.  A workgroup of eight waves serves one (sequence, split) for four
+// groups of 16 query heads.  Waves 0-3 ("score" waves, one per head group) keep that group's
+// Q1 / Q2 rows and compute Q.K^T over all 512 latent channels, the transposed softmax and the
+// FP4 probabilities; waves 4-7 ("value" waves, one per head group) keep the group's running
+// output and compute P.V one tile behind, taking the probabilities, their scales and the
+// online-softmax rescale factor from LDS.  Each SIMD holds one wave of each kind, so the
+// widening VALU work of one overlaps the matrix work of the other.  The workgroup stages
+// each 128-token tile once in LDS -- latent codes (token-major), rope keys and tile scales --
+// with direct LDS loads issued a whole tile ahead, and every wave reads its operands there:
+//  * Q.K^T: the lane's 64 bytes of its token row, widened to fp16 with the tile scale (exact)
+//    against the fp16 Q1 / Q2 rows on v_mfma_f32_16x16x32_f16; rope on the bf16 MFMA.
+//  * P.V: the value operand (16 channels x 32 tokens per lane) is read from the same
+//    token-major tile with the 4-bit transposed LDS read, so no channel-major copy is read;
+//    the tile scale's binary expansion gives the E8M0 passes as in the GQA kernel.
+// Iteration j: score waves on tile j, value waves on tile j - 1, direct loads of tile j + 1;
+// latent tiles and scales are triple-buffered, rope double-buffered, the handoff double-buffered.
+// Grid: one-dimensional, ids with equal residue mod 8 (one XCD) take the head-group quads of
+// consecutive units.  Performance only: any placement gives the same result.
 template <int P>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partials(DecodeArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partials(DecodeArgs a) {
   constexpr int D = kMlaD, R = kMlaR, HG = kMlaHeads;
-  constexpr int DH = D / 2;                     // latent channels per wave
   constexpr int NPT = P >= 128 ? 1 : 128 / P;
-  constexpr int NB = 2;                         // ring of token-group loads, NB - 1 ahead (NB divides 8)
+  constexpr int LAT = 128 * 256, ROPE = 128 * 128, SCL = 8 * 32;
   static_assert(P >= 16 && P % 16 == 0, "page size");
-  const int tid = threadIdx.x, lane = tid & 63, hc = tid >> 6;
-  const int nhg = a.hq / HG;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool scorer = wv < 4;                 // wave-uniform role
+  const int nhg = a.hq / HG, ngrp = (nhg + 3) / 4;
   const int units = a.batch * a.n_split;
   int id = blockIdx.x;
   const int slot = id & 7;
   id >>= 3;
-  const int hg = id % nhg, ublk = id / nhg;
+  const int grp = id % ngrp, ublk = id / ngrp;
   const int unit = ublk * 8 + slot;
   if (unit >= units) return;
   const int b = unit / a.n_split, split = unit % a.n_split;
@@ -102,353 +146,380 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tb = split * a.tiles_per_split;
   const int te = min(ntiles, tb + a.tiles_per_split);
   if (tb >= te) return;
+  const int nt = te - tb;
   const int last_lp = min((L - 1) / P, a.max_pages - 1);
-  const int h0 = hg * HG;
+  const int hgl = wv & 3, hg = 4 * grp + hgl;
+  const bool active = hg < nhg;               // wave-uniform: idle waves still load and sync
+  const int h0 = (active ? hg : 0) * HG;
 
-  // The query (exact fp16 Q1 / Q2 values, rows padded by 16 bytes) is staged here once;
-  // afterwards the same bytes carry the half dot products the two waves exchange,
-  // [wave][group][Q1 / Q2][lane] float4.
-  constexpr int QH_BYTES = 2 * HG * (D + 8) * 2;
-  constexpr int SX_BYTES = 2 * 8 * 2 * 64 * 16;
-  __shared__ __align__(16) uint8_t stage[QH_BYTES > SX_BYTES ? QH_BYTES : SX_BYTES];
-  _Float16 (*qh)[HG][D + 8] = reinterpret_cast<_Float16 (*)[HG][D + 8]>(stage);
-  __shared__ float qg[2][HG];
+  __shared__ __align__(16) uint8_t lat[3 * LAT];
+  __shared__ __align__(16) uint8_t rope[2 * ROPE];
+  __shared__ __align__(16) uint8_t scl[3 * SCL];
+  __shared__ __align__(16) uint4 hand[2][4][2][64];   // [tile & 1][group][part][lane]
   __shared__ uint32_t lut[256];
   __shared__ int pgl[kMaxSplitPages];
 
-  for (int e = tid; e < (te - tb) * NPT; e += 128)
+  for (int e = tid; e < nt * NPT; e += 512)
     pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
-
-  // ---------------- prologue: smoothing, rotation, dual-residual FP4 query ----------------
-  // thread t: head r = t / 8, channels c0 = 64 * (t % 8) .. + 63
-  {
-    const int r = tid >> 3, c0 = 64 * (tid & 7);
-    const long q0 = ((long)b * a.hq + h0 + r) * (D + R) + c0;
-    float y[64];
-    if (a.q_bf16) {
-      const uint16_t *qp = (const uint16_t *)a.q + q0;
-#pragma unroll
-      for (int j = 0; j < 64; j++) y[j] = bf16_to_f32(qp[j]);
-    } else {
-      const float *qp = (const float *)a.q + q0;
-#pragma unroll
-      for (int j = 0; j < 64; j++) y[j] = qp[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 64; j++) y[j] = y[j] * a.qs[c0 + j];
-    // Walsh-Hadamard stages h = 1 .. 32 inside the lane, 64, 128, 256 with lanes t ^ 1, ^ 2, ^ 4
-#pragma unroll
-    for (int h = 1; h < 64; h <<= 1)
-#pragma unroll
-      for (int j = 0; j < 64; j++)
-        if ((j & h) == 0) {
-          const float x0 = y[j], x1 = y[j + h];
-          y[j] = x0 + x1;
-          y[j + h] = x0 - x1;
-        }
-#pragma unroll
-    for (int m = 1; m <= 4; m <<= 1) {
-      const bool upper = (tid & m) != 0;
-#pragma unroll
-      for (int j = 0; j < 64; j++) {
-        const float o = __shfl_xor(y[j], m);
-        y[j] = upper ? o - y[j] : y[j] + o;
-      }
-    }
-    // dual-residual NVFP4: power-of-two block scales over 16 channels, G = row max / 1536
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      float rmax = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 64; j++) rmax = fmaxf(rmax, fabsf(y[j]));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 1));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 2));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 4));
-      const float gq = rmax / 1536.0f;
-      const float sixg = 6.0f * gq;
-      const float inv6g = sixg != 0.0f ? 1.0f / sixg : 0.0f;
-#pragma unroll
-      for (int blk = 0; blk < 4; blk++) {
-        float bmax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) bmax = fmaxf(bmax, fabsf(y[16 * blk + i]));
-        const bool valid = bmax > 0.0f && gq > 0.0f;
-        const int e = ceil_log2_clamp(bmax * inv6g, -9, 8);
-        const float S = pow2f(e);
-        const float sg = S * gq;
-        const float rr = (valid && sg != 0.0f) ? 1.0f / sg : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const float x = y[16 * blk + i];
-          const uint32_t c = e2m1_enc(x * rr);
-          const float qv = valid ? e2m1_dec(c) * S : 0.0f;
-          qh[k][r][c0 + 16 * blk + i] = (_Float16)qv;
-          y[16 * blk + i] = x - (e2m1_dec(c) * S) * gq;
-        }
-      }
-      if ((tid & 7) == 0) qg[k][r] = gq;
-    }
-  }
   // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale) for the P.V passes
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int c = tid + 128 * i;
+  if (tid < 256) {
+    const int c = tid;
     const int ef = (c >> 3) & 15, m = c & 7;
     const int E = (ef ? ef : 1) - 7 + 127;
-    uint32_t w = (ef ? (uint32_t)E : 0u) | ((m & 4) ? (uint32_t)(E - 1) << 8 : 0u) |
-                 ((m & 2) ? (uint32_t)(E - 2) << 16 : 0u) | ((m & 1) ? (uint32_t)(E - 3) << 24 : 0u);
+    const uint32_t w = (ef ? (uint32_t)E : 0u) | ((m & 4) ? (uint32_t)(E - 1) << 8 : 0u) |
+                       ((m & 2) ? (uint32_t)(E - 2) << 16 : 0u) | ((m & 1) ? (uint32_t)(E - 3) << 24 : 0u);
     lut[c] = c < 0x7F ? w : 0u;
   }
   __syncthreads();
 
+  // Physical row (page * P + offset) of token r of relative tile j
+  auto row_of = [&](int j, int r) -> long {
+    const int pg = pgl[j * NPT + (NPT == 1 ? 0 : r / P)];
+    return (long)pg * P + ((tb + j) * 128 + r) % P;
+  };
+  // Stage relative tile j: 32 latent, 16 rope and 1 scale instruction, spread over the waves
+  auto stage_tile = [&](int j) {
+    uint8_t *Lt = lat + (j % 3) * LAT;
+    uint8_t *Rt = rope + (j & 1) * ROPE;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const int g = 4 * wv + m;
+      const int r = 4 * g + (lane >> 4);
+      const int c = (lane & 15) ^ swz_lat(r);
+      lds_load16(a.k_codes + row_of(j, r) * (D / 2) + 16 * c, Lt + 1024 * g);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+      const int g = 2 * wv + m;
+      const int r = 8 * g + (lane >> 3);
+      const int c = (lane & 7) ^ swz_rope(r);
+      lds_load16((const uint8_t *)a.k_rope + row_of(j, r) * (2 * R) + 16 * c, Rt + 1024 * g);
+    }
+    if (wv == 0 && lane < 16) {
+      const int tr = lane >> 1;   // tile row (16 tokens): 32 scale bytes
+      const int pg = pgl[j * NPT + (NPT == 1 ? 0 : 16 * tr / P)];
+      const int off = (((tb + j) * 128 + 16 * tr) % P) / 16;
+      lds_load16(a.k_scales + ((long)pg * (P / 16) + off) * 32 + 16 * (lane & 1), scl + (j % 3) * SCL);
+    }
+  };
+  stage_tile(0);
+
   const int q4 = lane >> 4;        // lane group
   const int n = lane & 15;         // operand row / output column = head h0 + n
-  // B operands of this wave's channels: Q.K^T K-step st, lane group q4, element j is
-  // latent channel DH hc + 64 q4 + 8 st + j (the lane's A operand holds the same channels)
-  h8 bq0[8], bq1[8];
-#pragma unroll
-  for (int st = 0; st < 8; st++) {
-    bq0[st] = *(const h8 *)&qh[0][n][DH * hc + 64 * q4 + 8 * st];
-    bq1[st] = *(const h8 *)&qh[1][n][DH * hc + 64 * q4 + 8 * st];
-  }
-  // rope query (bf16): K-step s, lane group q4, element j is rope channel 32 s + 8 q4 + j
-  bh8 bqr[2];
-  {
-    const long qr = ((long)b * a.hq + h0 + n) * (D + R) + D + 8 * q4;
-#pragma unroll
-    for (int st = 0; st < 2; st++) {
-      uint16_t hb[8];
-      if (a.q_bf16) {
-#pragma unroll
-        for (int j = 0; j < 8; j++) hb[j] = ((const uint16_t *)a.q)[qr + 32 * st + j];
-      } else {  // fp32 rope query rounded to bf16 (nearest even)
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-          const uint32_t u = __float_as_uint(((const float *)a.q)[qr + 32 * st + j]);
-          hb[j] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-        }
-      }
-      __builtin_memcpy(&bqr[st], hb, 16);
-    }
-  }
   const float gk = a.gk[0];
-  const float a1 = (qg[0][n] * gk) * a.coef, a2 = (qg[1][n] * gk) * a.coef, cr = a.coef_rope;
-  float4 *sx = reinterpret_cast<float4 *>(stage);   // reused for the exchange (barrier in the loop)
-
-  // ---------------- main loop over 128-token tiles ----------------
-  float m_run = -INFINITY, l_run = 0.0f, f_run = 1.0f;
-  v4f o_run[16];
-#pragma unroll
-  for (int cg = 0; cg < 16; cg++) o_run[cg] = v4f{0.f, 0.f, 0.f, 0.f};
-  int nzero = 0;
-  const float inv6gp = 1.0f / (6.0f * 0.0009765625f);   // fl32(1 / fl32(6 * 2^-10))
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  const bool count_zero = a.zero_blocks != nullptr && hc == 0;
-
-  // Loads run ahead of use: the latent and rope rows of token group i + NB - 1 (crossing
-  // into the next tile) are issued while group i computes, and the next tile's key scales
-  // while this tile's last groups compute.
-  const int trow = 32 * (n >> 2) + (n & 3);   // A-operand row: tile token trow + 4 i in group i
-  auto load_group = [&](int tile, int i, uint4 *w) {
-    const bool live = tile < te;
-    const int tl = live ? tile : te - 1;
-    const int *pgt = pgl + (tl - tb) * NPT;
-    const int t = trow + 4 * i;
-    const int pg = pgt[NPT == 1 ? 0 : t / P];
-    const long row = (long)pg * P + (tl * 128 + t) % P;
-    const uint8_t *kb = a.k_codes + row * (D / 2) + (DH / 2) * hc + 32 * q4;
-    const uint8_t *kr = (const uint8_t *)(a.k_rope + row * R + 8 * q4);
-    w[0] = ld16(kb); w[1] = ld16(kb + 16); w[2] = ld16(kr); w[3] = ld16(kr + 64);
-  };
-  // tile scales (raw E4M3 bytes) of the lane's row tokens, token blocks of groups 0-3 and
-  // 4-7, channel blocks 16 hc + 4 q4 .. + 3
-  auto load_scales = [&](int tile, uint32_t *sc) {
-    const int tl = tile < te ? tile : te - 1;
-    const int *pgt = pgl + (tl - tb) * NPT;
+  if (scorer) {
+    // ---------------- score waves ----------------
+    // Prologue: smoothing, rotation, dual-residual FP4 query.  Lane (n, q4) holds channels
+    // 128 q4 .. + 127 of head h0 + n, the B-operand layout: K-step s, element j is channel
+    // 128 q4 + 8 s + j.  Walsh-Hadamard stages 1 .. 64 in the lane, 128 and 256 with lanes
+    // l ^ 16, l ^ 32 (the stage order of the oracle).
+    h8 bq0[16], bq1[16];
+    float qg0 = 0.0f, qg1 = 0.0f;
+    if (active) {
+      const long q0 = ((long)b * a.hq + h0 + n) * (D + R) + 128 * q4;
+      float y[128];
+      if (a.q_bf16) {
+        const uint16_t *qp = (const uint16_t *)a.q + q0;
 #pragma unroll
-    for (int hb = 0; hb < 2; hb++) {
-      const int t = trow + 16 * hb;
-      const int pg = pgt[NPT == 1 ? 0 : t / P];
-      sc[hb] = *(const uint32_t *)(a.k_scales + ((long)pg * (P / 16) + ((tl * 128 + t) % P) / 16) * 32 +
-                                   16 * hc + 4 * q4);
-    }
-  };
-  uint4 gw[NB][4];
-  uint32_t scn[2];
-  load_scales(tb, scn);
+        for (int j = 0; j < 128; j++) y[j] = bf16_to_f32(qp[j]);
+      } else {
+        const float *qp = (const float *)a.q + q0;
 #pragma unroll
-  for (int i = 0; i < NB - 1; i++) load_group(tb, i, gw[i]);
-
-#pragma unroll 1
-  for (int tile = tb; tile < te; tile++) {
-    const int tok0 = tile * 128;
-    const int *pgt = pgl + (tile - tb) * NPT;
-    const uint32_t scc[2] = {scn[0], scn[1]};   // this tile's key scales (scn is refilled ahead)
-    // ---- Q.K^T: Q1 / Q2 over this wave's channels (to LDS), rope in full, 8 token groups of 16
-    __syncthreads();   // the other wave has read the previous exchange (or the query stage)
-    float4 *mine = sx + (hc * 16) * 64 + lane;
-    float s[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      
-      if (i + NB - 1 < 8) load_group(tile, i + NB - 1, gw[(i + NB - 1) % NB]);
-      else load_group(tile + 1, i + NB - 1 - 8, gw[(i + NB - 1) % NB]);
-      if (i == 4) load_scales(tile + 1, scn);
-      
-      const uint4 *w = gw[i % NB];
-      const uint32_t ws[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
-      h2 sq[4];
-#pragma unroll
-      for (int j = 0; j < 4; j++) sq[j] = e4m3_h2((scc[i >> 2] >> (8 * j)) & 0xFFu);
-      v4f acc1 = zero, acc2 = zero, accr = zero;
-#pragma unroll
-      for (int st = 0; st < 8; st++) {
-        const h8 av = fp4x8_f16(ws[st], sq[st >> 1]);
-        acc1 = mfma_f16(av, bq0[st], acc1);
-        acc2 = mfma_f16(av, bq1[st], acc2);
+        for (int j = 0; j < 128; j++) y[j] = qp[j];
       }
-      accr = mfma_bf16(as_bh8(w[2]), bqr[0], accr);
-      accr = mfma_bf16(as_bh8(w[3]), bqr[1], accr);
-      mine[64 * (2 * i)] = float4{acc1[0], acc1[1], acc1[2], acc1[3]};
-      mine[64 * (2 * i + 1)] = float4{acc2[0], acc2[1], acc2[2], acc2[3]};
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++) s[i][rr] = cr * accr[rr];
-    }
-    // ---- logits from the two halves' dot products: raw = half 0 + half 1 (the same sum in
-    // both waves), s = (a1 raw1 + a2 raw2) + cr raw_rope
-    __syncthreads();
-    {
-      const float4 *h0p = sx + lane, *h1p = sx + 16 * 64 + lane;
+      for (int j = 0; j < 128; j++) y[j] = y[j] * a.qs[128 * q4 + j];
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const float4 x1 = h0p[64 * (2 * i)], y1 = h1p[64 * (2 * i)];
-        const float4 x2 = h0p[64 * (2 * i + 1)], y2 = h1p[64 * (2 * i + 1)];
-        const float r1[4] = {x1.x + y1.x, x1.y + y1.y, x1.z + y1.z, x1.w + y1.w};
-        const float r2[4] = {x2.x + y2.x, x2.y + y2.y, x2.z + y2.z, x2.w + y2.w};
+      for (int h = 1; h < 128; h <<= 1)
 #pragma unroll
-        for (int rr = 0; rr < 4; rr++) {
-          const float t12 = a1 * r1[rr] + a2 * r2[rr];
-          s[i][rr] = t12 + s[i][rr];
+        for (int j = 0; j < 128; j++)
+          if ((j & h) == 0) {
+            const float x0 = y[j], x1 = y[j + h];
+            y[j] = x0 + x1;
+            y[j + h] = x0 - x1;
+          }
+#pragma unroll
+      for (int m = 16; m <= 32; m <<= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int j = 0; j < 128; j++) {
+          const float o = __shfl_xor(y[j], m);
+          y[j] = upper ? o - y[j] : y[j] + o;
         }
       }
-    }
-    // P.V operands of this tile go out before the softmax
-    const int tv = 32 * q4;
-    const int pgv = pgt[NPT == 1 ? 0 : tv / P];
-    const int tp = (tok0 + tv) % P;
-    const uint8_t *srow = a.k_scales + ((long)pgv * (P / 16) + tp / 16) * 32 + 16 * hc;
-    const uint8_t *vb = a.v_codes + ((long)pgv * D + DH * hc + n) * (P / 2) + tp / 2;
-    uint4 vw[2][4];
-    
-    const uint4 sa = ld16(srow), sb = ld16(srow + 32);
+      // dual-residual NVFP4: power-of-two block scales over 16 channels, G = row max / 1536.
+      // The codes are kept packed (word s = channels 8 s .. 8 s + 7) with their block
+      // exponents and widened to fp16 once the rotation registers are free.
+      uint32_t qc[2][16];
+      int qe[2][8];
 #pragma unroll
-    for (int j = 0; j < 4; j++) vw[0][j] = ld16(vb + (long)j * 16 * (P / 2));
-    
-    if (tok0 + 128 > L) {
+      for (int k = 0; k < 2; k++) {
+        float rmax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; i++)
+        for (int j = 0; j < 128; j++) rmax = fmaxf(rmax, fabsf(y[j]));
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+        const float gq = rmax / 1536.0f;
+        const float sixg = 6.0f * gq;
+        const float inv6g = sixg != 0.0f ? 1.0f / sixg : 0.0f;
 #pragma unroll
-        for (int rr = 0; rr < 4; rr++)
-          if (tok0 + 32 * q4 + 4 * i + rr >= L) s[i][rr] = -INFINITY;
-    }
-    // ---- transposed softmax over the tile (lane (n, q4) holds tokens 32 q4 .. + 31 of head n)
-    float bm0 = -INFINITY, bm1 = -INFINITY;
+        for (int blk = 0; blk < 8; blk++) {
+          float bmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+          for (int i = 0; i < 16; i++) bmax = fmaxf(bmax, fabsf(y[16 * blk + i]));
+          const bool valid = bmax > 0.0f && gq > 0.0f;
+          const int e = ceil_log2_clamp(bmax * inv6g, -9, 8);
+          const float S = pow2f(e);
+          const float sg = S * gq;
+          const float rr = (valid && sg != 0.0f) ? 1.0f / sg : 0.0f;   // invalid: every code is 0
+          qe[k][blk] = e;
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++) {
-        bm0 = fmaxf(bm0, s[i][rr]);
-        bm1 = fmaxf(bm1, s[i + 4][rr]);
+          for (int h = 0; h < 2; h++) {
+            uint32_t w = 0u;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              const int ch = 16 * blk + 8 * h + i;
+              const float x = y[ch];
+              const uint32_t c = e2m1_enc(x * rr);
+              w |= c << (4 * i);
+              y[ch] = x - (e2m1_value(c) * S) * gq;
+            }
+            qc[k][2 * blk + h] = w;
+          }
+        }
+        if (k == 0) qg0 = gq;
+        else qg1 = gq;
       }
-    const float mt = max_x32(max_x16(fmaxf(bm0, bm1)));
-    float lt = 0.0f;
+      // fp16 operands: code * 2^e, exact (the convert applies a power-of-two scale exactly)
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-#pragma unroll
-      for (int rr = 0; rr < 4; rr++) {
-        const float p = __builtin_amdgcn_exp2f(s[i][rr] - mt);
-        s[i][rr] = p;
-        lt = lt + p;
+      for (int st = 0; st < 16; st++) {
+        const float s0 = pow2f(qe[0][st >> 1]), s1 = pow2f(qe[1][st >> 1]);
+        const h2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qc[0][st], s0, 0);
+        const h2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qc[0][st], s0, 1);
+        const h2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qc[0][st], s0, 2);
+        const h2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qc[0][st], s0, 3);
+        bq0[st] = h8{a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+        const h2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qc[1][st], s1, 0);
+        const h2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qc[1][st], s1, 1);
+        const h2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qc[1][st], s1, 2);
+        const h2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qc[1][st], s1, 3);
+        bq1[st] = h8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
       }
-    // ---- fused probability quantization (NVFP4, power-of-two block scales, G_P = 2^-10)
-    uint32_t pk[4];
-    int pbyte[2];
+    } else {
+#pragma unroll
+      for (int st = 0; st < 16; st++) {
+        bq0[st] = h8{};
+        bq1[st] = h8{};
+      }
+    }
+    // rope query (bf16): K-step s, lane group q4, element j is rope channel 32 s + 8 q4 + j
+    bh8 bqr[2];
     {
-      const float am[2] = {__builtin_amdgcn_exp2f(bm0 - mt), __builtin_amdgcn_exp2f(bm1 - mt)};
+      const long qr = ((long)b * a.hq + h0 + n) * (D + R) + D + 8 * q4;
 #pragma unroll
-      for (int pb = 0; pb < 2; pb++) {
-        const int e = ceil_log2_clamp(am[pb] * inv6gp, -9, 8);
-        const float ps = pow2f(e - 10);
-        pbyte[pb] = e - 10 + 127;
-        pk[2 * pb] = pack8(s[4 * pb], s[4 * pb + 1], ps);
-        pk[2 * pb + 1] = pack8(s[4 * pb + 2], s[4 * pb + 3], ps);
+      for (int st = 0; st < 2; st++) {
+        uint16_t hb[8];
+        if (a.q_bf16) {
+#pragma unroll
+          for (int j = 0; j < 8; j++) hb[j] = ((const uint16_t *)a.q)[qr + 32 * st + j];
+        } else {  // fp32 rope query rounded to bf16 (nearest even)
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const uint32_t u = __float_as_uint(((const float *)a.q)[qr + 32 * st + j]);
+            hb[j] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+          }
+        }
+        __builtin_memcpy(&bqr[st], hb, 16);
       }
+    }
+    const float a1 = (qg0 * gk) * a.coef, a2 = (qg1 * gk) * a.coef, cr = a.coef_rope;
+    float m_run = -INFINITY, l_run = 0.0f, f_run = 1.0f;
+    int nzero = 0;
+    const float inv6gp = 1.0f / (6.0f * 0.0009765625f);   // fl32(1 / fl32(6 * 2^-10))
+    const bool count_zero = a.zero_blocks != nullptr && active;
+    const int trow = 32 * (n >> 2) + (n & 3);   // A-operand row: tile token trow + 4 i in group i
+
+    wait_lds_loads();
+    __syncthreads();
+#pragma unroll 1
+    for (int j = 0; j <= nt; j++) {
+      if (j + 1 < nt) stage_tile(j + 1);
+      if (active && j < nt) {
+        const uint8_t *Lt = lat + (j % 3) * LAT;
+        const uint8_t *Rt = rope + (j & 1) * ROPE;
+        const uint8_t *St = scl + (j % 3) * SCL;
+        // ---- Q.K^T: 8 token groups of 16
+        float s[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const int r = trow + 4 * i;
+          const uint8_t *row = Lt + r * 256;
+          const int sw = swz_lat(r);
+          uint4 w4[4];
+#pragma unroll
+          for (int kk = 0; kk < 4; kk++) w4[kk] = *(const uint4 *)(row + (((4 * q4 + kk) ^ sw) << 4));
+          const uint2 sc8 = *(const uint2 *)(St + (2 * (n >> 2) + (i >> 2)) * 32 + 8 * q4);
+          const uint32_t ws[16] = {w4[0].x, w4[0].y, w4[0].z, w4[0].w, w4[1].x, w4[1].y, w4[1].z, w4[1].w,
+                                   w4[2].x, w4[2].y, w4[2].z, w4[2].w, w4[3].x, w4[3].y, w4[3].z, w4[3].w};
+          h2 sq[8];
+#pragma unroll
+          for (int k = 0; k < 8; k++) sq[k] = e4m3_h2(((k < 4 ? sc8.x : sc8.y) >> (8 * (k & 3))) & 0xFFu);
+          v4f acc1 = zero, acc2 = zero, accr = zero;
+#pragma unroll
+          for (int st = 0; st < 16; st++) {
+            const h8 av = fp4x8_f16(ws[st], sq[st >> 1]);
+            acc1 = mfma_f16(av, bq0[st], acc1);
+            acc2 = mfma_f16(av, bq1[st], acc2);
+          }
+          const uint8_t *rrow = Rt + r * 128;
+          const int swr = swz_rope(r);
+          accr = mfma_bf16(as_bh8(*(const uint4 *)(rrow + ((q4 ^ swr) << 4))), bqr[0], accr);
+          accr = mfma_bf16(as_bh8(*(const uint4 *)(rrow + (((4 + q4) ^ swr) << 4))), bqr[1], accr);
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) {
+            const float t12 = a1 * acc1[rr] + a2 * acc2[rr];
+            s[i][rr] = t12 + cr * accr[rr];
+          }
+        }
+        // ---- transposed softmax (lane (n, q4) holds tokens 32 q4 .. + 31 of head n)
+        const int tok0 = (tb + j) * 128;
+        if (tok0 + 128 > L) {
+#pragma unroll
+          for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++)
+              if (tok0 + 32 * q4 + 4 * i + rr >= L) s[i][rr] = -INFINITY;
+        }
+        float bm0 = -INFINITY, bm1 = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) {
+            bm0 = fmaxf(bm0, s[i][rr]);
+            bm1 = fmaxf(bm1, s[i + 4][rr]);
+          }
+        const float mt = max_x32(max_x16(fmaxf(bm0, bm1)));
+        float lt = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) {
+            const float p = __builtin_amdgcn_exp2f(s[i][rr] - mt);
+            s[i][rr] = p;
+            lt = lt + p;
+          }
+        // ---- fused probability quantization (NVFP4, power-of-two block scales, G_P = 2^-10)
+        uint32_t pk[4];
+        int pbyte[2];
+        const float am[2] = {__builtin_amdgcn_exp2f(bm0 - mt), __builtin_amdgcn_exp2f(bm1 - mt)};
+#pragma unroll
+        for (int pb = 0; pb < 2; pb++) {
+          const int e = ceil_log2_clamp(am[pb] * inv6gp, -9, 8);
+          const float ps = pow2f(e - 10);
+          pbyte[pb] = e - 10 + 127;
+          pk[2 * pb] = pack8(s[4 * pb], s[4 * pb + 1], ps);
+          pk[2 * pb + 1] = pack8(s[4 * pb + 2], s[4 * pb + 3], ps);
+        }
+        if (count_zero) {
+#pragma unroll
+          for (int pb = 0; pb < 2; pb++)
+            if (tok0 + 32 * q4 + 16 * pb < L && ((pk[2 * pb] | pk[2 * pb + 1]) & 0x77777777u) == 0u) nzero++;
+        }
+        // ---- online softmax: the value waves keep the output as o_run * f_run and rescale
+        // it by gamma before adding this tile
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float beta = __builtin_amdgcn_exp2f(mt - m_new);
+        l_run = fmaf(l_run, alpha, lt * beta);
+        m_run = m_new;
+        const float f_new = fmaxf(beta, 8.67361737988403547e-19f);   // 2^-60
+        const float gamma = (alpha * f_run) * __builtin_amdgcn_rcpf(f_new);
+        f_run = f_new;
+        hand[j & 1][hgl][0][lane] = uint4{pk[0], pk[1], pk[2], pk[3]};
+        hand[j & 1][hgl][1][lane] = uint4{(uint32_t)pbyte[0] | ((uint32_t)pbyte[1] << 8), __float_as_uint(gamma),
+                                          __float_as_uint(f_run), 0u};
+      }
+      wait_lds_loads();
+      __syncthreads();
+    }
+    if (!active) return;
+    const float l_tot = sum_x32(sum_x16(l_run));
+    if (q4 == 0) {
+      const long rowi = ((long)b * a.hq + h0 + n) * a.n_split + split;
+      *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run, l_tot};
     }
     if (count_zero) {
+      int z = nzero;
 #pragma unroll
-      for (int pb = 0; pb < 2; pb++)
-        if (tok0 + 32 * q4 + 16 * pb < L && ((pk[2 * pb] | pk[2 * pb + 1]) & 0x77777777u) == 0u) nzero++;
+      for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
+      if (lane == 0 && z) atomicAdd(a.zero_blocks, z);
     }
-    // ---- online rescale (running output kept as o_run * f_run, as in the GQA kernel)
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float beta = __builtin_amdgcn_exp2f(mt - m_new);
-    l_run = fmaf(l_run, alpha, lt * beta);
-    m_run = m_new;
-    const float f_new = fmaxf(beta, 8.67361737988403547e-19f);   // 2^-60
-    const float gamma = (alpha * f_run) * __builtin_amdgcn_rcpf(f_new);
-    f_run = f_new;
+  } else {
+    // ---------------- value waves ----------------
+    v4f o_run[32];
 #pragma unroll
-    for (int cg = 0; cg < 16; cg++)
+    for (int cg = 0; cg < 32; cg++) o_run[cg] = zero;
+    float f_run = 1.0f;
+    const int ra = 32 * q4 + n, rb = ra + 16;   // rows of the lane's two transposed reads
+    const int swa = swz_lat(ra), swb = swz_lat(rb);
+    wait_lds_loads();
+    __syncthreads();
+#pragma unroll 1
+    for (int j = 0; j <= nt; j++) {
+      if (j + 1 < nt) stage_tile(j + 1);
+      if (active && j >= 1) {
+        const int jp = j - 1;
+        const uint8_t *Lt = lat + (jp % 3) * LAT;
+        const uint8_t *St = scl + (jp % 3) * SCL;
+        const uint4 hp = hand[jp & 1][hgl][0][lane];
+        const uint4 hs = hand[jp & 1][hgl][1][lane];
+        const int pb0 = (int)(hs.x & 0xFFu), pb1 = (int)((hs.x >> 8) & 0xFFu);
+        const float gamma = __uint_as_float(hs.y);
+        f_run = __uint_as_float(hs.z);
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = o_run[cg][rr] * gamma;
-    // ---- P.V over this wave's channels: channel-major latent (A: channels DH hc + 16 cg + n,
-    // tokens 32 q4 .. + 31), batches of 4 channel groups, the next batch in flight
-    const v8i p0 = {(int)pk[0], (int)pk[1], 0, 0, 0, 0, 0, 0};
-    const v8i p1 = {0, 0, (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+        for (int cg = 0; cg < 32; cg++)
 #pragma unroll
-    for (int bt = 0; bt < 4; bt++) {
-      
-      if (bt + 1 < 4) {
+          for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = o_run[cg][rr] * gamma;
+        const v8i p0 = {(int)hp.x, (int)hp.y, 0, 0, 0, 0, 0, 0};
+        const v8i p1 = {0, 0, (int)hp.z, (int)hp.w, 0, 0, 0, 0};
+        const uint8_t *rowa = Lt + ra * 256, *rowb = Lt + rb * 256;
+        // P.V: channels 16 cg + n, tokens 32 q4 .. + 31, in chunks of four channel groups
 #pragma unroll
-        for (int j = 0; j < 4; j++) vw[(bt + 1) & 1][j] = ld16(vb + (long)(4 * (bt + 1) + j) * 16 * (P / 2));
+        for (int i = 0; i < 8; i++) {
+          const uint32_t s0 = *(const uint32_t *)(St + (2 * q4) * 32 + 4 * i);
+          const uint32_t s1 = *(const uint32_t *)(St + (2 * q4 + 1) * 32 + 4 * i);
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const int cg = 4 * i + k;
+            const int off = 8 * (cg & 1);
+            const v2i lo = lds_read_tr4(rowa + (((cg >> 1) ^ swa) << 4) + off);
+            const v2i hi = lds_read_tr4(rowb + (((cg >> 1) ^ swb) << 4) + off);
+            const v8i av = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
+            const int l0 = (int)lut[(s0 >> (8 * k)) & 0xFFu], l1 = (int)lut[(s1 >> (8 * k)) & 0xFFu];
+            v4f c = mfma4<0, 0>(av, p0, o_run[cg], l0, pb0);
+            c = mfma4<1, 0>(av, p0, c, l0, pb0);
+            c = mfma4<2, 0>(av, p0, c, l0, pb0);
+            c = mfma4<3, 0>(av, p0, c, l0, pb0);
+            c = mfma4<0, 0>(av, p1, c, l1, pb1);
+            c = mfma4<1, 0>(av, p1, c, l1, pb1);
+            c = mfma4<2, 0>(av, p1, c, l1, pb1);
+            o_run[cg] = mfma4<3, 0>(av, p1, c, l1, pb1);
+          }
+        }
       }
-      
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int cg = 4 * bt + j;
-        const uint4 vc = vw[bt & 1][j];
-        const v8i av = {(int)vc.x, (int)vc.y, (int)vc.z, (int)vc.w, 0, 0, 0, 0};
-        const int l0 = (int)lut[byte_of(sa, cg)], l1 = (int)lut[byte_of(sb, cg)];
-        v4f c = mfma4<0, 0>(av, p0, o_run[cg], l0, pbyte[0]);
-        c = mfma4<1, 0>(av, p0, c, l0, pbyte[0]);
-        c = mfma4<2, 0>(av, p0, c, l0, pbyte[0]);
-        c = mfma4<3, 0>(av, p0, c, l0, pbyte[0]);
-        c = mfma4<0, 0>(av, p1, c, l1, pbyte[1]);
-        c = mfma4<1, 0>(av, p1, c, l1, pbyte[1]);
-        c = mfma4<2, 0>(av, p1, c, l1, pbyte[1]);
-        o_run[cg] = mfma4<3, 0>(av, p1, c, l1, pbyte[1]);
-      }
+      wait_lds_loads();
+      __syncthreads();
     }
-  }
-
-  // ---------------- epilogue: split partials (latent output, still rotated) ----------------
-  const float l_tot = sum_x32(sum_x16(l_run));
-  {
+    if (!active) return;
+    // split partials (latent output, still rotated)
     const long rowi = ((long)b * a.hq + h0 + n) * a.n_split + split;
     const float g = gk * f_run;
 #pragma unroll
-    for (int cg = 0; cg < 16; cg++) {
+    for (int cg = 0; cg < 32; cg++) {
       float4 v = {o_run[cg][0] * g, o_run[cg][1] * g, o_run[cg][2] * g, o_run[cg][3] * g};
-      *(float4 *)(a.ws_o + rowi * D + DH * hc + 16 * cg + 4 * q4) = v;
+      *(float4 *)(a.ws_o + rowi * D + 16 * cg + 4 * q4) = v;
     }
-    if (hc == 0 && q4 == 0) *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run, l_tot};
-  }
-  if (count_zero) {
-    int z = nzero;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
-    if (lane == 0 && z) atomicAdd(a.zero_blocks, z);
   }
 }
 
@@ -611,8 +682,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const long row = (long)pg * P + (tl * 128 + t) % P;
     const uint8_t *kb = a.k_codes + row * (D / 2) + 16 * q4;
     const uint8_t *kr = (const uint8_t *)(a.k_rope + row * R + 8 * q4);
-    w[0] = ld16(kb); w[1] = ld16(kb + 64); w[2] = ld16(kb + 128); w[3] = ld16(kb + 192);
-    w[4] = ld16(kr); w[5] = ld16(kr + 64);
+    w[0] = ldc16(kb); w[1] = ldc16(kb + 64); w[2] = ldc16(kb + 128); w[3] = ldc16(kb + 192);
+    w[4] = ldc16(kr); w[5] = ldc16(kr + 64);
   };
   // E8M0 tile scales of the lane's row tokens (token block n / 4 of the tile): the 16
   // channel blocks of that token block
@@ -665,7 +736,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const uint8_t *vb = a.v_codes + ((long)pgv * D + n) * (P / 2) + tp / 2;
     uint4 vw[2][8];
 #pragma unroll
-    for (int j = 0; j < 8; j++) vw[0][j] = ld16(vb + (long)j * 16 * (P / 2));
+    for (int j = 0; j < 8; j++) vw[0][j] = ldc16(vb + (long)j * 16 * (P / 2));
     if (tok0 + 128 > L) {
 #pragma unroll
       for (int i = 0; i < 8; i++)
@@ -719,7 +790,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int bt = 0; bt < 4; bt++) {
       if (bt + 1 < 4) {
 #pragma unroll
-        for (int j = 0; j < 8; j++) vw[(bt + 1) & 1][j] = ld16(vb + (long)(8 * (bt + 1) + j) * 16 * (P / 2));
+        for (int j = 0; j < 8; j++) vw[(bt + 1) & 1][j] = ldc16(vb + (long)(8 * (bt + 1) + j) * 16 * (P / 2));
       }
 #pragma unroll
       for (int j = 0; j < 8; j++) {
@@ -826,13 +897,12 @@ hipError_t launch_mla_partials(const DecodeArgs &a, hipStream_t s) {
     return hipGetLastError();
   }
   const long units = (long)a.batch * a.n_split;
-  const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nhg);
+  const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * ((nhg + 3) / 4));
   switch (a.page_size) {
-    case 16: mla_partials<16><<<grid, 128, 0, s>>>(a); break;
-    case 32: mla_partials<32><<<grid, 128, 0, s>>>(a); break;
-    case 64: mla_partials<64><<<grid, 128, 0, s>>>(a); break;
-    case 128: mla_partials<128><<<grid, 128, 0, s>>>(a); break;
-    case 256: mla_partials<256><<<grid, 128, 0, s>>>(a); break;
+    case 32: mla_partials<32><<<grid, 512, 0, s>>>(a); break;
+    case 64: mla_partials<64><<<grid, 512, 0, s>>>(a); break;
+    case 128: mla_partials<128><<<grid, 512, 0, s>>>(a); break;
+    case 256: mla_partials<256><<<grid, 512, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
