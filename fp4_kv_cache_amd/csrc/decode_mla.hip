@@ -100,6 +100,20 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
   return __uint_as_float(__float_as_uint(ldexpf((float)mant, ex)) | ((c & 8u) << 28));
 }
 
+// One Walsh-Hadamard butterfly across lanes l and l ^ 16 (permlane16_swap) or l and l ^ 32
+// (permlane32_swap): both return the pair as (value of the lane with the bit clear, value of
+// the lane with it set) in both lanes; the first lane keeps the sum, the second the difference.
+__device__ __forceinline__ float bfly_x16(float x, bool upper) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);
+  return upper ? lo - hi : lo + hi;
+}
+__device__ __forceinline__ float bfly_x32(float x, bool upper) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);
+  return upper ? lo - hi : lo + hi;
+}
+
 // Slot of 16-byte chunk c of a staged latent row r is c ^ swz_lat(r), of a rope row c ^ swz_rope(r):
 // the 16 rows one Q.K^T operand read touches (tile tokens 32 a + b + 4 i, a, b < 4) and the 16
 // consecutive rows one transposed P.V read touches then fall on distinct banks.
@@ -240,14 +254,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             y[j + h] = x0 - x1;
           }
 #pragma unroll
-      for (int m = 16; m <= 32; m <<= 1) {
-        const bool upper = (lane & m) != 0;
+      for (int j = 0; j < 128; j++) y[j] = bfly_x16(y[j], (lane & 16) != 0);
 #pragma unroll
-        for (int j = 0; j < 128; j++) {
-          const float o = __shfl_xor(y[j], m);
-          y[j] = upper ? o - y[j] : y[j] + o;
-        }
-      }
+      for (int j = 0; j < 128; j++) y[j] = bfly_x32(y[j], (lane & 32) != 0);
       // dual-residual NVFP4: power-of-two block scales over 16 channels, G = row max / 1536.
       // The codes are kept packed (word s = channels 8 s .. 8 s + 7) with their block
       // exponents and widened to fp16 once the rotation registers are free.
@@ -484,19 +493,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const v8i p0 = {(int)hp.x, (int)hp.y, 0, 0, 0, 0, 0, 0};
         const v8i p1 = {0, 0, (int)hp.z, (int)hp.w, 0, 0, 0, 0};
         const uint8_t *rowa = Lt + ra * 256, *rowb = Lt + rb * 256;
-        // P.V: channels 16 cg + n, tokens 32 q4 .. + 31, in chunks of four channel groups
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-          const uint32_t s0 = *(const uint32_t *)(St + (2 * q4) * 32 + 4 * i);
-          const uint32_t s1 = *(const uint32_t *)(St + (2 * q4 + 1) * 32 + 4 * i);
+        // P.V: channels 16 cg + n, tokens 32 q4 .. + 31, in chunks of four channel groups; the
+        // value operands and pass bytes of chunk i + 1 are read while chunk i computes
+        const uint4 sa0 = *(const uint4 *)(St + (2 * q4) * 32), sa1 = *(const uint4 *)(St + (2 * q4) * 32 + 16);
+        const uint4 sb0 = *(const uint4 *)(St + (2 * q4 + 1) * 32), sb1 = *(const uint4 *)(St + (2 * q4 + 1) * 32 + 16);
+        v2i vt[2][4][2];
+        int lt[2][4][2];
+        auto read_vals = [&](int i, v2i (*o)[2], int (*l)[2]) {
 #pragma unroll
           for (int k = 0; k < 4; k++) {
             const int cg = 4 * i + k;
             const int off = 8 * (cg & 1);
-            const v2i lo = lds_read_tr4(rowa + (((cg >> 1) ^ swa) << 4) + off);
-            const v2i hi = lds_read_tr4(rowb + (((cg >> 1) ^ swb) << 4) + off);
+            o[k][0] = lds_read_tr4(rowa + (((cg >> 1) ^ swa) << 4) + off);
+            o[k][1] = lds_read_tr4(rowb + (((cg >> 1) ^ swb) << 4) + off);
+            l[k][0] = (int)lut[byte_of(cg < 16 ? sa0 : sa1, cg & 15)];
+            l[k][1] = (int)lut[byte_of(cg < 16 ? sb0 : sb1, cg & 15)];
+          }
+        };
+        read_vals(0, vt[0], lt[0]);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          if (i < 7) read_vals(i + 1, vt[(i + 1) & 1], lt[(i + 1) & 1]);
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const int cg = 4 * i + k;
+            const v2i lo = vt[i & 1][k][0], hi = vt[i & 1][k][1];
             const v8i av = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
-            const int l0 = (int)lut[(s0 >> (8 * k)) & 0xFFu], l1 = (int)lut[(s1 >> (8 * k)) & 0xFFu];
+            const int l0 = lt[i & 1][k][0], l1 = lt[i & 1][k][1];
             v4f c = mfma4<0, 0>(av, p0, o_run[cg], l0, pb0);
             c = mfma4<1, 0>(av, p0, c, l0, pb0);
             c = mfma4<2, 0>(av, p0, c, l0, pb0);
@@ -526,27 +549,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // MLA partials, MXFP4 latent.  The 32-token x 32-channel tiles carry E8M0 scales, which is
 // the block-scaled MFMA's own scale granularity (32 K-elements per lane), so Q.K^T and P.V
 // both run as native FP4 x FP4 MFMAs with both scales applied in hardware and no widening:
-// per 16 tokens, four MFMAs per query pass over the 512 channels (the four products of one
-// 128-channel step are summed by the matrix core, the steps chained on its accumulator)
-// plus two bf16 MFMAs for the rope part; per tile, one MFMA per 16 output channels.
-// One wave per (sequence, group of 16 query heads, split); lane (n, q4): head h0 + n.
+// per 16 tokens, four MFMAs per query pass over the 512 channels plus two bf16 MFMAs for the
+// rope part; per tile, one MFMA per 16 output channels.  The workgroup structure is the NVFP4
+// kernel's: eight waves for one (sequence, split) and four groups of 16 query heads, score
+// waves 0-3 (Q.K^T, softmax, FP4 probabilities) and value waves 4-7 (P.V one tile behind,
+// the value operand read transposed from the token-major tile), latent tiles, rope keys and
+// scales staged once per workgroup in LDS with direct loads a tile ahead.
 // The query is rotated and quantized directly in the B-operand layout: lane (n, q4) holds
 // channels 128 st + 32 q4 + j (st = 0..3, j = 0..31), so the Walsh-Hadamard stages on
 // channel bits 0-4 and 7-8 stay in the lane, bits 5 and 6 pair lanes l ^ 16 and l ^ 32,
 // and every 32-channel MX block is one lane's own.
 template <int P>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_partials_mx(DecodeArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_partials_mx(DecodeArgs a) {
   constexpr int D = kMlaD, R = kMlaR, HG = kMlaHeads;
   constexpr int NPT = P >= 128 ? 1 : 128 / P;
-  constexpr int NB = 2;                         // ring of token-group loads, NB - 1 ahead (NB divides 8)
+  constexpr int LAT = 128 * 256, ROPE = 128 * 128, SCL = 4 * 16;
   static_assert(P >= 32 && P % 32 == 0, "page size");
-  const int lane = threadIdx.x;
-  const int nhg = a.hq / HG;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool scorer = wv < 4;                 // wave-uniform role
+  const int nhg = a.hq / HG, ngrp = (nhg + 3) / 4;
   const int units = a.batch * a.n_split;
   int id = blockIdx.x;
   const int slot = id & 7;
   id >>= 3;
-  const int hg = id % nhg, ublk = id / nhg;
+  const int grp = id % ngrp, ublk = id / ngrp;
   const int unit = ublk * 8 + slot;
   if (unit >= units) return;
   const int b = unit / a.n_split, split = unit % a.n_split;
@@ -555,269 +581,339 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int tb = split * a.tiles_per_split;
   const int te = min(ntiles, tb + a.tiles_per_split);
   if (tb >= te) return;
+  const int nt = te - tb;
   const int last_lp = min((L - 1) / P, a.max_pages - 1);
-  const int h0 = hg * HG;
-  const int q4 = lane >> 4, n = lane & 15;
+  const int hgl = wv & 3, hg = 4 * grp + hgl;
+  const bool active = hg < nhg;               // wave-uniform: idle waves still load and sync
+  const int h0 = (active ? hg : 0) * HG;
 
+  __shared__ __align__(16) uint8_t lat[3 * LAT];
+  __shared__ __align__(16) uint8_t rope[2 * ROPE];
+  __shared__ __align__(16) uint8_t scl[3 * SCL];
+  __shared__ __align__(16) uint4 hand[2][4][2][64];   // [tile & 1][group][part][lane]
   __shared__ int pgl[kMaxSplitPages];
-  for (int e = lane; e < (te - tb) * NPT; e += 64)
-    pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
 
-  // ---------------- prologue: smoothing, rotation, dual-residual MXFP4 query ----------------
-  v8i bq[2][4];            // [pass][K-step]: FP4 codes of channels 128 st + 32 q4 .. + 31
-  int qsb[2][4];           // their E8M0 scale bytes
-  {
-    const long q0 = ((long)b * a.hq + h0 + n) * (D + R) + 32 * q4;
-    float y[4][32];
-#pragma unroll
-    for (int st = 0; st < 4; st++) {
-      if (a.q_bf16) {
-        const uint16_t *qp = (const uint16_t *)a.q + q0 + 128 * st;
-#pragma unroll
-        for (int j = 0; j < 32; j++) y[st][j] = bf16_to_f32(qp[j]);
-      } else {
-        const float *qp = (const float *)a.q + q0 + 128 * st;
-#pragma unroll
-        for (int j = 0; j < 32; j++) y[st][j] = qp[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 32; j++) y[st][j] = y[st][j] * a.qs[128 * st + 32 * q4 + j];
-    }
-    // stages h = 1 .. 16 (channel bits 0-4) in the lane
-#pragma unroll
-    for (int h = 1; h < 32; h <<= 1)
-#pragma unroll
-      for (int st = 0; st < 4; st++)
-#pragma unroll
-        for (int j = 0; j < 32; j++)
-          if ((j & h) == 0) {
-            const float x0 = y[st][j], x1 = y[st][j + h];
-            y[st][j] = x0 + x1;
-            y[st][j + h] = x0 - x1;
-          }
-    // stages h = 32, 64 (channel bits 5, 6 = lane bits 4, 5)
-#pragma unroll
-    for (int m = 16; m <= 32; m <<= 1) {
-      const bool upper = (lane & m) != 0;
-#pragma unroll
-      for (int st = 0; st < 4; st++)
-#pragma unroll
-        for (int j = 0; j < 32; j++) {
-          const float o = __shfl_xor(y[st][j], m);
-          y[st][j] = upper ? o - y[st][j] : y[st][j] + o;
-        }
-    }
-    // stages h = 128, 256 (channel bits 7, 8 = the K-step index) in the lane
-#pragma unroll
-    for (int hs = 1; hs < 4; hs <<= 1)
-#pragma unroll
-      for (int st = 0; st < 4; st++)
-        if ((st & hs) == 0) {
-#pragma unroll
-          for (int j = 0; j < 32; j++) {
-            const float x0 = y[st][j], x1 = y[st + hs][j];
-            y[st][j] = x0 + x1;
-            y[st + hs][j] = x0 - x1;
-          }
-        }
-    // pass k quantizes the residual of pass k - 1: E8M0 per 32 channels, no tensor scale
-#pragma unroll
-    for (int k = 0; k < 2; k++)
-#pragma unroll
-      for (int st = 0; st < 4; st++) {
-        float bmax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 32; j++) bmax = fmaxf(bmax, fabsf(y[st][j]));
-        const int e = mx_exp(bmax);
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 32; j++) {
-          const uint32_t c = e2m1_enc(ldexpf(y[st][j], -e));
-          w[j / 8] |= c << (4 * (j % 8));
-          y[st][j] = y[st][j] - ldexpf(e2m1_dec(c), e);
-        }
-        bq[k][st] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-        qsb[k][st] = e + 127;
-      }
-  }
-  // rope query (bf16): K-step s, lane group q4, element j is rope channel 32 s + 8 q4 + j
-  bh8 bqr[2];
-  {
-    const long qr = ((long)b * a.hq + h0 + n) * (D + R) + D + 8 * q4;
-#pragma unroll
-    for (int st = 0; st < 2; st++) {
-      uint16_t hb[8];
-      if (a.q_bf16) {
-#pragma unroll
-        for (int j = 0; j < 8; j++) hb[j] = ((const uint16_t *)a.q)[qr + 32 * st + j];
-      } else {  // fp32 rope query rounded to bf16 (nearest even)
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-          const uint32_t u = __float_as_uint(((const float *)a.q)[qr + 32 * st + j]);
-          hb[j] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-        }
-      }
-      __builtin_memcpy(&bqr[st], hb, 16);
-    }
-  }
-  const float c1 = a.coef, cr = a.coef_rope;   // MXFP4: no tensor scales, a1 = a2 = c
+  for (int e = tid; e < nt * NPT; e += 512)
+    pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
   __syncthreads();
 
-  // ---------------- main loop over 128-token tiles ----------------
-  float m_run = -INFINITY, l_run = 0.0f, f_run = 1.0f;
-  v4f o_run[32];
+  auto row_of = [&](int j, int r) -> long {
+    const int pg = pgl[j * NPT + (NPT == 1 ? 0 : r / P)];
+    return (long)pg * P + ((tb + j) * 128 + r) % P;
+  };
+  // Stage relative tile j: 32 latent, 16 rope and 1 scale instruction, spread over the waves
+  auto stage_tile = [&](int j) {
+    uint8_t *Lt = lat + (j % 3) * LAT;
+    uint8_t *Rt = rope + (j & 1) * ROPE;
 #pragma unroll
-  for (int cg = 0; cg < 32; cg++) o_run[cg] = v4f{0.f, 0.f, 0.f, 0.f};
-  int nzero = 0;
+    for (int m = 0; m < 4; m++) {
+      const int g = 4 * wv + m;
+      const int r = 4 * g + (lane >> 4);
+      const int c = (lane & 15) ^ swz_lat(r);
+      lds_load16(a.k_codes + row_of(j, r) * (D / 2) + 16 * c, Lt + 1024 * g);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+      const int g = 2 * wv + m;
+      const int r = 8 * g + (lane >> 3);
+      const int c = (lane & 7) ^ swz_rope(r);
+      lds_load16((const uint8_t *)a.k_rope + row_of(j, r) * (2 * R) + 16 * c, Rt + 1024 * g);
+    }
+    if (wv == 0 && lane < 4) {
+      const int t = 32 * lane;   // token block (32 tokens): 16 scale bytes
+      const int pg = pgl[j * NPT + (NPT == 1 ? 0 : t / P)];
+      lds_load16(a.k_scales + ((long)pg * (P / 32) + (((tb + j) * 128 + t) % P) / 32) * 16, scl + (j % 3) * SCL);
+    }
+  };
+  stage_tile(0);
+
+  const int q4 = lane >> 4;        // lane group
+  const int n = lane & 15;         // operand row / output column = head h0 + n
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  const bool count_zero = a.zero_blocks != nullptr;
-
-  const int trow = 32 * (n >> 2) + (n & 3);   // A-operand row: tile token trow + 4 i in group i
-  auto load_group = [&](int tile, int i, uint4 *w) {
-    const bool live = tile < te;
-    const int tl = live ? tile : te - 1;
-    const int *pgt = pgl + (tl - tb) * NPT;
-    const int t = trow + 4 * i;
-    const int pg = pgt[NPT == 1 ? 0 : t / P];
-    const long row = (long)pg * P + (tl * 128 + t) % P;
-    const uint8_t *kb = a.k_codes + row * (D / 2) + 16 * q4;
-    const uint8_t *kr = (const uint8_t *)(a.k_rope + row * R + 8 * q4);
-    w[0] = ldc16(kb); w[1] = ldc16(kb + 64); w[2] = ldc16(kb + 128); w[3] = ldc16(kb + 192);
-    w[4] = ldc16(kr); w[5] = ldc16(kr + 64);
-  };
-  // E8M0 tile scales of the lane's row tokens (token block n / 4 of the tile): the 16
-  // channel blocks of that token block
-  auto load_scales = [&](int tile) -> uint4 {
-    const int tl = tile < te ? tile : te - 1;
-    const int *pgt = pgl + (tl - tb) * NPT;
-    const int t = 32 * (n >> 2);
-    const int pg = pgt[NPT == 1 ? 0 : t / P];
-    return *(const uint4 *)(a.k_scales + ((long)pg * (P / 32) + ((tl * 128 + t) % P) / 32) * 16);
-  };
-  uint4 gw[NB][6];
-  uint4 scn = load_scales(tb);
-#pragma unroll
-  for (int i = 0; i < NB - 1; i++) load_group(tb, i, gw[i]);
-
-#pragma unroll 1
-  for (int tile = tb; tile < te; tile++) {
-    const int tok0 = tile * 128;
-    const int *pgt = pgl + (tile - tb) * NPT;
-    const uint4 scc = scn;
-    // ---- Q.K^T over 8 token groups of 16
-    float s[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      if (i + NB - 1 < 8) load_group(tile, i + NB - 1, gw[(i + NB - 1) % NB]);
-      else load_group(tile + 1, i + NB - 1 - 8, gw[(i + NB - 1) % NB]);
-      if (i == 4) scn = load_scales(tile + 1);
-      const uint4 *w = gw[i % NB];
-      v4f acc1 = zero, acc2 = zero, accr = zero;
-#pragma unroll
+  if (scorer) {
+    // ---------------- score waves ----------------
+    v8i bq[2][4];            // [pass][K-step]: FP4 codes of channels 128 st + 32 q4 .. + 31
+    int qsb[2][4];           // their E8M0 scale bytes
+    if (active) {
+      // prologue: smoothing, rotation, dual-residual MXFP4 query
+      const long q0 = ((long)b * a.hq + h0 + n) * (D + R) + 32 * q4;
+      float y[4][32];
+  #pragma unroll
       for (int st = 0; st < 4; st++) {
-        const v8i av = {(int)w[st].x, (int)w[st].y, (int)w[st].z, (int)w[st].w, 0, 0, 0, 0};
-        const int sa = (int)byte_of(scc, 4 * st + q4);
-        acc1 = mfma4<0, 0>(av, bq[0][st], acc1, sa, qsb[0][st]);
-        acc2 = mfma4<0, 0>(av, bq[1][st], acc2, sa, qsb[1][st]);
+        if (a.q_bf16) {
+          const uint16_t *qp = (const uint16_t *)a.q + q0 + 128 * st;
+  #pragma unroll
+          for (int j = 0; j < 32; j++) y[st][j] = bf16_to_f32(qp[j]);
+        } else {
+          const float *qp = (const float *)a.q + q0 + 128 * st;
+  #pragma unroll
+          for (int j = 0; j < 32; j++) y[st][j] = qp[j];
+        }
+  #pragma unroll
+        for (int j = 0; j < 32; j++) y[st][j] = y[st][j] * a.qs[128 * st + 32 * q4 + j];
       }
-      accr = mfma_bf16(as_bh8(w[4]), bqr[0], accr);
-      accr = mfma_bf16(as_bh8(w[5]), bqr[1], accr);
+      // stages h = 1 .. 16 (channel bits 0-4) in the lane
+  #pragma unroll
+      for (int h = 1; h < 32; h <<= 1)
+  #pragma unroll
+        for (int st = 0; st < 4; st++)
+  #pragma unroll
+          for (int j = 0; j < 32; j++)
+            if ((j & h) == 0) {
+              const float x0 = y[st][j], x1 = y[st][j + h];
+              y[st][j] = x0 + x1;
+              y[st][j + h] = x0 - x1;
+            }
+      // stages h = 32, 64 (channel bits 5, 6 = lane bits 4, 5)
+  #pragma unroll
+      for (int st = 0; st < 4; st++)
+  #pragma unroll
+        for (int j = 0; j < 32; j++) y[st][j] = bfly_x16(y[st][j], (lane & 16) != 0);
+  #pragma unroll
+      for (int st = 0; st < 4; st++)
+  #pragma unroll
+        for (int j = 0; j < 32; j++) y[st][j] = bfly_x32(y[st][j], (lane & 32) != 0);
+      // stages h = 128, 256 (channel bits 7, 8 = the K-step index) in the lane
+  #pragma unroll
+      for (int hs = 1; hs < 4; hs <<= 1)
+  #pragma unroll
+        for (int st = 0; st < 4; st++)
+          if ((st & hs) == 0) {
+  #pragma unroll
+            for (int j = 0; j < 32; j++) {
+              const float x0 = y[st][j], x1 = y[st + hs][j];
+              y[st][j] = x0 + x1;
+              y[st + hs][j] = x0 - x1;
+            }
+          }
+      // pass k quantizes the residual of pass k - 1: E8M0 per 32 channels, no tensor scale
+  #pragma unroll
+      for (int k = 0; k < 2; k++)
+  #pragma unroll
+        for (int st = 0; st < 4; st++) {
+          float bmax = 0.0f;
+  #pragma unroll
+          for (int j = 0; j < 32; j++) bmax = fmaxf(bmax, fabsf(y[st][j]));
+          const int e = mx_exp(bmax);
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+  #pragma unroll
+          for (int j = 0; j < 32; j++) {
+            const uint32_t c = e2m1_enc(ldexpf(y[st][j], -e));
+            w[j / 8] |= c << (4 * (j % 8));
+            y[st][j] = y[st][j] - ldexpf(e2m1_value(c), e);
+          }
+          bq[k][st] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+          qsb[k][st] = e + 127;
+        }
+    } else {
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++) {
-        const float t12 = c1 * acc1[rr] + c1 * acc2[rr];
-        s[i][rr] = t12 + cr * accr[rr];
-      }
+      for (int k = 0; k < 2; k++)
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+          bq[k][st] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          qsb[k][st] = 0;
+        }
     }
-    // P.V operands of this tile go out before the softmax
-    const int tv = 32 * q4;
-    const int pgv = pgt[NPT == 1 ? 0 : tv / P];
-    const int tp = (tok0 + tv) % P;
-    const uint4 sv = *(const uint4 *)(a.k_scales + ((long)pgv * (P / 32) + tp / 32) * 16);
-    const uint8_t *vb = a.v_codes + ((long)pgv * D + n) * (P / 2) + tp / 2;
-    uint4 vw[2][8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) vw[0][j] = ldc16(vb + (long)j * 16 * (P / 2));
-    if (tok0 + 128 > L) {
-#pragma unroll
-      for (int i = 0; i < 8; i++)
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++)
-          if (tok0 + 32 * q4 + 4 * i + rr >= L) s[i][rr] = -INFINITY;
-    }
-    // ---- transposed softmax over the tile (lane (n, q4) holds tokens 32 q4 .. + 31 of head n)
-    float bm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-#pragma unroll
-      for (int rr = 0; rr < 4; rr++) bm = fmaxf(bm, s[i][rr]);
-    const float mt = max_x32(max_x16(bm));
-    float lt = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-#pragma unroll
-      for (int rr = 0; rr < 4; rr++) {
-        const float p = __builtin_amdgcn_exp2f(s[i][rr] - mt);
-        s[i][rr] = p;
-        lt = lt + p;
-      }
-    // ---- fused probability quantization (MXFP4: the lane's 32 tokens are one block)
-    uint32_t pk[4];
-    const int pe = mx_exp(__builtin_amdgcn_exp2f(bm - mt));
-    const int pbyte = pe + 127;
+    // rope query (bf16): K-step s, lane group q4, element j is rope channel 32 s + 8 q4 + j
+    bh8 bqr[2];
     {
-      const float ps = ldexpf(1.0f, pe);
-#pragma unroll
-      for (int w = 0; w < 4; w++) pk[w] = pack8(s[2 * w], s[2 * w + 1], ps);
-    }
-    if (count_zero && tok0 + 32 * q4 < L && ((pk[0] | pk[1] | pk[2] | pk[3]) & 0x77777777u) == 0u) nzero++;
-    // ---- online rescale (running output kept as o_run * f_run)
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float beta = __builtin_amdgcn_exp2f(mt - m_new);
-    l_run = fmaf(l_run, alpha, lt * beta);
-    m_run = m_new;
-    const float f_new = fmaxf(beta, 8.67361737988403547e-19f);   // 2^-60
-    const float gamma = (alpha * f_run) * __builtin_amdgcn_rcpf(f_new);
-    f_run = f_new;
-#pragma unroll
-    for (int cg = 0; cg < 32; cg++)
-#pragma unroll
-      for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = o_run[cg][rr] * gamma;
-    // ---- P.V: channel-major latent (A: channels 16 cg + n, tokens 32 q4 .. + 31), one MFMA
-    // per channel group with the tile scale of (token block, channel block cg / 2)
-    const v8i pv = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};
-#pragma unroll
-    for (int bt = 0; bt < 4; bt++) {
-      if (bt + 1 < 4) {
-#pragma unroll
-        for (int j = 0; j < 8; j++) vw[(bt + 1) & 1][j] = ldc16(vb + (long)(8 * (bt + 1) + j) * 16 * (P / 2));
-      }
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int cg = 8 * bt + j;
-        const uint4 vc = vw[bt & 1][j];
-        const v8i av = {(int)vc.x, (int)vc.y, (int)vc.z, (int)vc.w, 0, 0, 0, 0};
-        o_run[cg] = mfma4<0, 0>(av, pv, o_run[cg], (int)byte_of(sv, cg >> 1), pbyte);
+      const long qr = ((long)b * a.hq + h0 + n) * (D + R) + D + 8 * q4;
+  #pragma unroll
+      for (int st = 0; st < 2; st++) {
+        uint16_t hb[8];
+        if (a.q_bf16) {
+  #pragma unroll
+          for (int j = 0; j < 8; j++) hb[j] = ((const uint16_t *)a.q)[qr + 32 * st + j];
+        } else {  // fp32 rope query rounded to bf16 (nearest even)
+  #pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const uint32_t u = __float_as_uint(((const float *)a.q)[qr + 32 * st + j]);
+            hb[j] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+          }
+        }
+        __builtin_memcpy(&bqr[st], hb, 16);
       }
     }
-  }
+    const float c1 = a.coef, cr = a.coef_rope;   // MXFP4: no tensor scales, a1 = a2 = c
+    float m_run = -INFINITY, l_run = 0.0f, f_run = 1.0f;
+    int nzero = 0;
+    const bool count_zero = a.zero_blocks != nullptr && active;
+    const int trow = 32 * (n >> 2) + (n & 3);   // A-operand row: tile token trow + 4 i in group i
 
-  // ---------------- epilogue: split partials (latent output, still rotated) ----------------
-  const float l_tot = sum_x32(sum_x16(l_run));
-  {
+    wait_lds_loads();
+    __syncthreads();
+#pragma unroll 1
+    for (int j = 0; j <= nt; j++) {
+      if (j + 1 < nt) stage_tile(j + 1);
+      if (active && j < nt) {
+        const uint8_t *Lt = lat + (j % 3) * LAT;
+        const uint8_t *Rt = rope + (j & 1) * ROPE;
+        // E8M0 scales of the lane's token block (n / 4): its 16 channel blocks
+        const uint4 scc = *(const uint4 *)(scl + (j % 3) * SCL + 16 * (n >> 2));
+        // ---- Q.K^T: 8 token groups of 16; the operands of group i + 1 (four latent chunks,
+        // two rope chunks) are read from LDS while group i computes
+        float s[8][4];
+        uint4 opd[2][6];
+        auto read_ops = [&](int i, uint4 *o) {
+          const int r = trow + 4 * i;
+          const uint8_t *row = Lt + r * 256;
+          const int sw = swz_lat(r);
+#pragma unroll
+          for (int st = 0; st < 4; st++) o[st] = *(const uint4 *)(row + (((4 * st + q4) ^ sw) << 4));
+          const uint8_t *rrow = Rt + r * 128;
+          const int swr = swz_rope(r);
+          o[4] = *(const uint4 *)(rrow + ((q4 ^ swr) << 4));
+          o[5] = *(const uint4 *)(rrow + (((4 + q4) ^ swr) << 4));
+        };
+        read_ops(0, opd[0]);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          if (i < 7) read_ops(i + 1, opd[(i + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          const uint4 *o = opd[i & 1];
+          v4f acc1 = zero, acc2 = zero, accr = zero;
+#pragma unroll
+          for (int st = 0; st < 4; st++) {
+            const v8i av = {(int)o[st].x, (int)o[st].y, (int)o[st].z, (int)o[st].w, 0, 0, 0, 0};
+            const int sa = (int)byte_of(scc, 4 * st + q4);
+            acc1 = mfma4<0, 0>(av, bq[0][st], acc1, sa, qsb[0][st]);
+            acc2 = mfma4<0, 0>(av, bq[1][st], acc2, sa, qsb[1][st]);
+          }
+          accr = mfma_bf16(as_bh8(o[4]), bqr[0], accr);
+          accr = mfma_bf16(as_bh8(o[5]), bqr[1], accr);
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) {
+            const float t12 = c1 * acc1[rr] + c1 * acc2[rr];
+            s[i][rr] = t12 + cr * accr[rr];
+          }
+        }
+        // ---- transposed softmax (lane (n, q4) holds tokens 32 q4 .. + 31 of head n)
+        const int tok0 = (tb + j) * 128;
+        if (tok0 + 128 > L) {
+#pragma unroll
+          for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++)
+              if (tok0 + 32 * q4 + 4 * i + rr >= L) s[i][rr] = -INFINITY;
+        }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) bm = fmaxf(bm, s[i][rr]);
+        const float mt = max_x32(max_x16(bm));
+        float lt = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) {
+            const float p = __builtin_amdgcn_exp2f(s[i][rr] - mt);
+            s[i][rr] = p;
+            lt = lt + p;
+          }
+        // ---- fused probability quantization (MXFP4: the lane's 32 tokens are one block)
+        uint32_t pk[4];
+        const int pe = mx_exp(__builtin_amdgcn_exp2f(bm - mt));
+        const int pbyte = pe + 127;
+        {
+          const float ps = ldexpf(1.0f, pe);
+#pragma unroll
+          for (int w = 0; w < 4; w++) pk[w] = pack8(s[2 * w], s[2 * w + 1], ps);
+        }
+        if (count_zero && tok0 + 32 * q4 < L && ((pk[0] | pk[1] | pk[2] | pk[3]) & 0x77777777u) == 0u) nzero++;
+        // ---- online softmax: the value waves keep the output as o_run * f_run
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float beta = __builtin_amdgcn_exp2f(mt - m_new);
+        l_run = fmaf(l_run, alpha, lt * beta);
+        m_run = m_new;
+        const float f_new = fmaxf(beta, 8.67361737988403547e-19f);   // 2^-60
+        const float gamma = (alpha * f_run) * __builtin_amdgcn_rcpf(f_new);
+        f_run = f_new;
+        hand[j & 1][hgl][0][lane] = uint4{pk[0], pk[1], pk[2], pk[3]};
+        hand[j & 1][hgl][1][lane] = uint4{(uint32_t)pbyte, __float_as_uint(gamma), __float_as_uint(f_run), 0u};
+      }
+      wait_lds_loads();
+      __syncthreads();
+    }
+    if (!active) return;
+    const float l_tot = sum_x32(sum_x16(l_run));
+    if (q4 == 0) {
+      const long rowi = ((long)b * a.hq + h0 + n) * a.n_split + split;
+      *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run, l_tot};
+    }
+    if (count_zero) {
+      int z = nzero;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
+      if (lane == 0 && z) atomicAdd(a.zero_blocks, z);
+    }
+  } else {
+    // ---------------- value waves ----------------
+    v4f o_run[32];
+#pragma unroll
+    for (int cg = 0; cg < 32; cg++) o_run[cg] = zero;
+    float f_run = 1.0f;
+    const int ra = 32 * q4 + n, rb = ra + 16;   // rows of the lane's two transposed reads
+    const int swa = swz_lat(ra), swb = swz_lat(rb);
+    wait_lds_loads();
+    __syncthreads();
+#pragma unroll 1
+    for (int j = 0; j <= nt; j++) {
+      if (j + 1 < nt) stage_tile(j + 1);
+      if (active && j >= 1) {
+        const int jp = j - 1;
+        const uint8_t *Lt = lat + (jp % 3) * LAT;
+        const uint4 hp = hand[jp & 1][hgl][0][lane];
+        const uint4 hs = hand[jp & 1][hgl][1][lane];
+        const int pbyte = (int)hs.x;
+        const float gamma = __uint_as_float(hs.y);
+        f_run = __uint_as_float(hs.z);
+        // E8M0 scales of the lane's token block q4: its 16 channel blocks
+        const uint4 sv = *(const uint4 *)(scl + (jp % 3) * SCL + 16 * q4);
+#pragma unroll
+        for (int cg = 0; cg < 32; cg++)
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) o_run[cg][rr] = o_run[cg][rr] * gamma;
+        const v8i pv = {(int)hp.x, (int)hp.y, (int)hp.z, (int)hp.w, 0, 0, 0, 0};
+        const uint8_t *rowa = Lt + ra * 256, *rowb = Lt + rb * 256;
+        // P.V: channels 16 cg + n, tokens 32 q4 .. + 31, one MFMA per channel group with the
+        // scale of (token block q4, channel block cg / 2)
+        // value operands of channel groups 4 c .. 4 c + 3 are read while chunk c - 1 computes
+        v2i vt[2][4][2];
+        auto read_vals = [&](int c, v2i (*o)[2]) {
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const int cg = 4 * c + k;
+            const int off = 8 * (cg & 1);
+            o[k][0] = lds_read_tr4(rowa + (((cg >> 1) ^ swa) << 4) + off);
+            o[k][1] = lds_read_tr4(rowb + (((cg >> 1) ^ swb) << 4) + off);
+          }
+        };
+        read_vals(0, vt[0]);
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+          if (c < 7) read_vals(c + 1, vt[(c + 1) & 1]);
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const int cg = 4 * c + k;
+            const v2i lo = vt[c & 1][k][0], hi = vt[c & 1][k][1];
+            const v8i av = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
+            o_run[cg] = mfma4<0, 0>(av, pv, o_run[cg], (int)byte_of(sv, cg >> 1), pbyte);
+          }
+        }
+      }
+      wait_lds_loads();
+      __syncthreads();
+    }
+    if (!active) return;
+    // split partials (latent output, still rotated)
     const long rowi = ((long)b * a.hq + h0 + n) * a.n_split + split;
 #pragma unroll
     for (int cg = 0; cg < 32; cg++) {
       float4 v = {o_run[cg][0] * f_run, o_run[cg][1] * f_run, o_run[cg][2] * f_run, o_run[cg][3] * f_run};
       *(float4 *)(a.ws_o + rowi * D + 16 * cg + 4 * q4) = v;
     }
-    if (q4 == 0) *(float2 *)(a.ws_ml + rowi * 2) = float2{m_run, l_tot};
-  }
-  if (count_zero) {
-    int z = nzero;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
-    if (lane == 0 && z) atomicAdd(a.zero_blocks, z);
   }
 }
 
@@ -886,12 +982,12 @@ hipError_t launch_mla_partials(const DecodeArgs &a, hipStream_t s) {
   const int nhg = a.hq / kMlaHeads;
   if (a.fmt == kFmtMX) {
     const long units = (long)a.batch * a.n_split;
-    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nhg);
+    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * ((nhg + 3) / 4));
     switch (a.page_size) {
-      case 32: mla_partials_mx<32><<<grid, 64, 0, s>>>(a); break;
-      case 64: mla_partials_mx<64><<<grid, 64, 0, s>>>(a); break;
-      case 128: mla_partials_mx<128><<<grid, 64, 0, s>>>(a); break;
-      case 256: mla_partials_mx<256><<<grid, 64, 0, s>>>(a); break;
+      case 32: mla_partials_mx<32><<<grid, 512, 0, s>>>(a); break;
+      case 64: mla_partials_mx<64><<<grid, 512, 0, s>>>(a); break;
+      case 128: mla_partials_mx<128><<<grid, 512, 0, s>>>(a); break;
+      case 256: mla_partials_mx<256><<<grid, 512, 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
