@@ -46,7 +46,7 @@ int check_pointers(const fp4kv_cache *c) {
   if (c->attn == FP4KV_GQA) {
     if (!c->v_codes || !c->v_scales) return FP4KV_ERR_INVALID_ARG;
     if (c->format == FP4KV_NVFP4 && !c->v_tensor_scale) return FP4KV_ERR_INVALID_ARG;
-  } else if (!c->k_rope || !c->v_codes) {
+  } else if (!c->k_rope) {
     return FP4KV_ERR_INVALID_ARG;
   }
   return FP4KV_OK;
@@ -230,7 +230,7 @@ int fp4kv_cache_layout(const fp4kv_cache *c, size_t bytes_out[6]) {
     bytes_out[5] = 0;
   } else {
     bytes_out[1] = np * (P / B) * (d / B);
-    bytes_out[2] = np * d * (P / 2);
+    bytes_out[2] = 0;
     bytes_out[3] = 0;
     bytes_out[5] = np * P * (size_t)c->rope_dim * 2;
   }

@@ -549,7 +549,8 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
   }
   __syncthreads();
   const long pbase = (long)sp.page * a.page_size;
-  // token-major codes (the key operand): task = (token k, tile ct), B / 2 bytes
+  // token-major codes (the key operand, read transposed as the value operand): task = (token k,
+  // tile ct), B / 2 bytes
   for (int e = tid; e < B * NT; e += 256) {
     const int k = e / NT, ct = e % NT;
     const float r = FMT == kFmtNV ? rsc[ct] : 0.0f;
@@ -561,25 +562,6 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
 #pragma unroll
       for (int u = 0; u < 8; u++) {
         const float x = X(k, ct * B + 2 * j + u);
-        const uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
-        w |= q << (4 * u);
-      }
-      *(uint32_t *)(dst + j) = w;
-    }
-  }
-  // ... and the same codes channel-major (the value operand): task = channel ch, row ch holds
-  // the page's tokens
-  for (int ch = tid; ch < D; ch += 256) {
-    const int ct = ch / B;
-    const float r = FMT == kFmtNV ? rsc[ct] : 0.0f;
-    const int eb = FMT == kFmtNV ? 0 : ebest[ct];
-    uint8_t *dst = a.v_codes + ((long)sp.page * D + ch) * (a.page_size / 2) + sp.off0 / 2;
-#pragma unroll
-    for (int j = 0; j < B / 2; j += 4) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const float x = X(2 * j + u, ch);
         const uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
         w |= q << (4 * u);
       }

@@ -132,7 +132,7 @@ __device__ __forceinline__ int swz_rope(int r) { return ((r >> 1) & 1) | (((r >>
 //  * Q.K^T: the lane's 64 bytes of its token row, widened to fp16 with the tile scale (exact)
 //    against the fp16 Q1 / Q2 rows on v_mfma_f32_16x16x32_f16; rope on the bf16 MFMA.
 //  * P.V: the value operand (16 channels x 32 tokens per lane) is read from the same
-//    token-major tile with the 4-bit transposed LDS read, so no channel-major copy is read;
+//    token-major tile with the 4-bit transposed LDS read, so the cache holds the latent once;
 //    the tile scale's binary expansion gives the E8M0 passes as in the GQA kernel.
 // Iteration j: score waves on tile j, value waves on tile j - 1, direct loads of tile j + 1;
 // latent tiles and scales are triple-buffered, rope double-buffered, the handoff double-buffered.

@@ -268,6 +268,5 @@ class PagedFP4Cache:
             v["v_scales"] = self.v_scales.view(np_, h, d * P // B)
         else:
             v["k_scales"] = self.k_scales.view(np_, 1, P // B, d // B)
-            v["v_codes"] = self.v_codes.view(np_, 1, d, P // 2)
             v["k_rope"] = self.k_rope.view(np_, 1, P, self.rope_dim)
         return v

@@ -52,12 +52,10 @@
  *   MLA (attn = FP4KV_MLA, one latent head, head_dim = 512, rope_dim = 64):
  *     k_codes  u8 [num_pages][1][P][256]    rotated latent, token-major
  *     k_scales u8 [num_pages][1][P/B][512/B] one scale per B-token x B-channel tile
- *     v_codes  u8 [num_pages][1][512][P/2]  the same latent codes channel-major (byte j
- *                                            of channel row c holds tokens 2j, 2j+1): the
- *                                            latent also serves as the value, and P.V
- *                                            contracts over tokens
  *     k_rope   bf16 [num_pages][1][P][64]   rope key, unquantized
  *     stage    f32 [max_seqs][1][B][512]    rotated latent of the partial tile
+ *   (v_codes and v_scales are unused for MLA and may be NULL: the latent also serves as the
+ *   value, and the decode reads its value operand from the token-major codes)
  *     v_scales unused (the tile scales serve both copies).
  *   Codes are E2M1 (bit 3 sign, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6); NVFP4
  *   scales are E4M3 (OCP "FN"), MXFP4 scales E8M0.  A partially filled value

@@ -20,9 +20,7 @@ GQA (per page, per KV head; head_dim d = 128):
                                             ((j//J)*16 + c%16)*8*J + (c//16)*J + j%J,
                                             J = min(P, 32)//B blocks per 32-token span
 MLA (one latent head, D = 512, rope r = 64):
-  k_codes  uint8 [num_pages][1][P][D/2]     token-major latent
-  v_codes  uint8 [num_pages][1][D][P/2]     the same codes channel-major (byte j of row c
-                                            = tok[2j] | tok[2j+1] << 4)
+  k_codes  uint8 [num_pages][1][P][D/2]     token-major latent (key and value)
   k_scales uint8 [num_pages][1][P/B][D/B]   one scale per (B-token, B-channel) tile
   k_rope   bf16  [num_pages][1][P][r]       unquantized rope key (stored as uint16 here)
 """
@@ -107,15 +105,12 @@ def scatter_mla(cache, bt_row, L, lc, ls, k_rope_bits, fmt):
         b0, b1 = t0 // B, -(-t1 // B)
         tv1 = b1 * B
         cache["k_codes"][pg, 0, : tv1 - t0] = lpk[t0:tv1]
-        if "v_codes" in cache:
-            cache["v_codes"][pg, 0, :, : (tv1 - t0) // 2] = pack_nibbles(lc[t0:tv1].T)
         cache["k_scales"][pg, 0, : b1 - b0] = ls[b0:b1]
         cache["k_rope"][pg, 0, : t1 - t0] = k_rope_bits[t0:t1]
 
 
 def gather_mla(cache, bt_row, L, fmt):
-    """Read back (lc [Lpad, D], ls [Lpad/B, D/B], k_rope uint16 [L, r]); with a channel-major
-    copy present, also check that it holds the same codes (AssertionError otherwise)."""
+    """Read back (lc [Lpad, D], ls [Lpad/B, D/B], k_rope uint16 [L, r])."""
     P = cache["k_codes"].shape[2]
     D = cache["k_codes"].shape[3] * 2
     r = cache["k_rope"].shape[3]
@@ -130,12 +125,6 @@ def gather_mla(cache, bt_row, L, fmt):
         b0, b1 = t0 // B, -(-t1 // B)
         tv1 = b1 * B
         lc[t0:tv1] = unpack_nibbles(cache["k_codes"][pg, 0, : tv1 - t0])
-        if "v_codes" in cache:
-            vt = unpack_nibbles(cache["v_codes"][pg, 0, :, : (tv1 - t0) // 2]).T
-            if not np.array_equal(vt, lc[t0:tv1]):
-                bad = np.argwhere(vt != lc[t0:tv1])[0]
-                raise AssertionError("channel-major latent copy differs at page-local token %d, channel %d"
-                                     % (bad[0], bad[1]))
         ls[b0:b1] = cache["k_scales"][pg, 0, : b1 - b0]
         kr[t0:t1] = cache["k_rope"][pg, 0, : t1 - t0]
     return lc, ls, kr

@@ -76,20 +76,13 @@ def test_mla_round_trip():
     ls = rng.integers(0, 127, (nblk, D // B)).astype(np.uint8)
     kr = rng.integers(0, 65535, (L, r)).astype(np.uint16)
     cache = dict(k_codes=np.zeros((4, 1, P, D // 2), np.uint8),
-                 v_codes=np.zeros((4, 1, D, P // 2), np.uint8),
                  k_scales=np.zeros((4, 1, P // B, D // B), np.uint8),
                  k_rope=np.zeros((4, 1, P, r), np.uint16))
     LY.scatter_mla(cache, bt, L, lc, ls, kr, KQ.NVFP4)
     assert cache["k_scales"][0, 0, 1, 7] == ls[5, 7]          # token block 5 = page 1, block 1
-    # token 70 = page 0 (physical), slot 6; channel 300: byte 3 of channel row 300, low nibble
-    assert cache["v_codes"][0, 0, 300, 3] & 0xF == lc[70, 300]
-    assert cache["v_codes"][0, 0, 300, 3] >> 4 == lc[71, 300]
+    # token 70 = page 0 (physical), slot 6; channel 300: byte 150 of the token row, low nibble
+    assert cache["k_codes"][0, 0, 6, 150] & 0xF == lc[70, 300]
+    assert cache["k_codes"][0, 0, 6, 150] >> 4 == lc[70, 301]
     g = LY.gather_mla(cache, bt, L, KQ.NVFP4)
     for a, b in zip(g, (lc, ls, kr)):
         assert np.array_equal(a, b)
-    cache["v_codes"][3, 0, 5, 2] ^= 0x10                      # a corrupted copy is caught
-    try:
-        LY.gather_mla(cache, bt, L, KQ.NVFP4)
-        raise AssertionError("corrupted channel-major copy not detected")
-    except AssertionError as e:
-        assert "differs" in str(e)
