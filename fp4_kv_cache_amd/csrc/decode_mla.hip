@@ -91,15 +91,6 @@ __device__ __forceinline__ v2i lds_read_tr4(const uint8_t *p) {
   return __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(p));
 }
 
-// Value of an E2M1 code (exact), computed without branches
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t m = c & 7u;
-  const bool sub = m < 2u;
-  const int mant = sub ? (int)m : 2 + (int)(m & 1u);
-  const int ex = sub ? -1 : (int)(m >> 1) - 2;
-  return __uint_as_float(__float_as_uint(ldexpf((float)mant, ex)) | ((c & 8u) << 28));
-}
-
 // One Walsh-Hadamard butterfly across lanes l and l ^ 16 (permlane16_swap) or l and l ^ 32
 // (permlane32_swap): both return the pair as (value of the lane with the bit clear, value of
 // the lane with it set) in both lanes; the first lane keeps the sum, the second the difference.
@@ -292,7 +283,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const float x = y[ch];
               const uint32_t c = e2m1_enc(x * rr);
               w |= c << (4 * i);
-              y[ch] = x - (e2m1_value(c) * S) * gq;
+              y[ch] = x - (e2m1_dec(c) * S) * gq;
             }
             qc[k][2 * blk + h] = w;
           }
@@ -700,7 +691,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int j = 0; j < 32; j++) {
             const uint32_t c = e2m1_enc(ldexpf(y[st][j], -e));
             w[j / 8] |= c << (4 * (j % 8));
-            y[st][j] = y[st][j] - ldexpf(e2m1_value(c), e);
+            y[st][j] = y[st][j] - ldexpf(e2m1_dec(c), e);
           }
           bq[k][st] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
           qsb[k][st] = e + 127;

@@ -34,12 +34,14 @@ __device__ __forceinline__ uint32_t e2m1_enc(float y) {
   return idx | ((__float_as_uint(y) >> 28) & 8u);
 }
 
-// Value of an E2M1 code (exact).
+// Value of an E2M1 code (exact), without branches: magnitude m >= 2 is (2 + (m & 1)) *
+// 2^((m >> 1) - 2), m < 2 is m / 2; the sign is bit 3.
 __device__ __forceinline__ float e2m1_dec(uint32_t c) {
-  uint32_t m = c & 7u;
-  // magnitude bits: m >= 2 -> (1 + (m&1)/2) * 2^((m>>1)-1); m == 1 -> 0.5; m == 0 -> 0
-  uint32_t bits = (m >= 2u) ? (((126u + (m >> 1)) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
-  return __uint_as_float(bits | ((c & 8u) << 28));
+  const uint32_t m = c & 7u;
+  const bool sub = m < 2u;
+  const float mant = (float)(sub ? m : 2u + (m & 1u));
+  const int ex = sub ? -1 : (int)(m >> 1) - 2;
+  return __uint_as_float(__float_as_uint(ldexpf(mant, ex)) | ((c & 8u) << 28));
 }
 
 // E4M3 byte -> fp32 (exact).  0x7F / 0xFF decode to NaN.
