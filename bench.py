@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak
+F16_MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 matrix peak
 METRIC = "FP4 paged decode attention: µs/step + KV HBM GB/s (% of 8 TB/s peak)"
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -83,6 +84,18 @@ def mla_flops_per_token(w):
     """Algorithmic flops per cached token of an MLA decode step: Q.K^T for the Q1 and Q2 rows of
     every query head over latent + rope channels, P.V over the latent channels."""
     return 2 * (2 * w["hq"]) * (w["d"] + w["rope"]) + 2 * w["hq"] * w["d"]
+
+
+def mla_matrix_peak_tflops(w):
+    """Dense matrix peak for the MLA decode's contractions, weighted by their algorithmic flops
+    (the peak at which all of them together would run): Q.K^T over the latent on fp16 MFMAs
+    for an NVFP4 latent (its E4M3 2-D tile scales are applied by an exact fp16 widening) and on
+    FP4 MFMAs for MXFP4, the rope part on bf16 MFMAs, P.V on FP4 MFMAs."""
+    hq, d, r = w["hq"], w["d"], w["rope"]
+    qk, rope, pv = 2 * (2 * hq) * d, 2 * (2 * hq) * r, 2 * hq * d
+    qk_peak = F16_MFMA_PEAK_TFLOPS if w["fmt"] == 0 else FP4_MFMA_PEAK_TFLOPS
+    t = qk / qk_peak + rope / F16_MFMA_PEAK_TFLOPS + pv / FP4_MFMA_PEAK_TFLOPS
+    return (qk + rope + pv) / t
 
 
 def cpu_baseline(w, n_units, budget_s):
@@ -379,11 +392,12 @@ def main():
         pattern_gbps = kv_bytes / (r_us * 1e-6) / 1e9
 
     traffic = read_traffic(w, args.workload)
-    if mla:   # matrix-core bound: algorithmic flops against the dense FP4 MFMA peak
+    if mla:   # matrix-core bound: algorithmic flops against the flop-weighted dense matrix peak
         flops = float(np.sum(lens.astype(np.float64))) * mla_flops_per_token(w)
         achieved = flops / (k_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP4_MFMA_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+        peak = mla_matrix_peak_tflops(w)
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                     "flops_per_launch": flops,
                     "kv_GBps": round(kv_bytes / (k_us * 1e-6) / 1e9, 1)}
     else:
