@@ -911,6 +911,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Merge of one (sequence, query head) row: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
 // then un-rotated (Walsh-Hadamard over the 512 channels, / 512) and un-smoothed (* q_smooth).
 // Lane l holds channels 8 l .. 8 l + 7.
+constexpr int kMlaMergeFast = 8;   // splits per row that the merge loads all at once
+
 __global__ __launch_bounds__(64) void mla_merge(DecodeArgs a) {
   constexpr int D = kMlaD;
   const int row = blockIdx.x, lane = threadIdx.x;
@@ -926,20 +928,50 @@ __global__ __launch_bounds__(64) void mla_merge(DecodeArgs a) {
   }
   const float *ml = a.ws_ml + (long)row * a.n_split * 2;
   const float *o = a.ws_o + (long)row * a.n_split * D + 8 * lane;
+  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (nv <= kMlaMergeFast) {
+    // every split's (m, l) and partial output in flight at once; the same operations in the
+    // same order as the general path below
+    float2 mlv = float2{-INFINITY, 0.f};
+    if (lane < nv) mlv = *(const float2 *)(ml + 2 * lane);
+    float4 u[kMlaMergeFast][2];
+#pragma unroll
+    for (int s = 0; s < kMlaMergeFast; s++) {
+      u[s][0] = s < nv ? *(const float4 *)(o + (long)s * D) : float4{0.f, 0.f, 0.f, 0.f};
+      u[s][1] = s < nv ? *(const float4 *)(o + (long)s * D + 4) : float4{0.f, 0.f, 0.f, 0.f};
+    }
+    float M = mlv.x;
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
+    const float wl = lane < nv ? __builtin_amdgcn_exp2f(mlv.x - M) : 0.f;
+    den = lane < nv ? fmaf(wl, mlv.y, 0.f) : 0.f;
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k);
+#pragma unroll
+    for (int s = 0; s < kMlaMergeFast; s++) {
+      if (s < nv) {
+        const float w = __shfl(wl, s);
+        y[0] = fmaf(w, u[s][0].x, y[0]); y[1] = fmaf(w, u[s][0].y, y[1]);
+        y[2] = fmaf(w, u[s][0].z, y[2]); y[3] = fmaf(w, u[s][0].w, y[3]);
+        y[4] = fmaf(w, u[s][1].x, y[4]); y[5] = fmaf(w, u[s][1].y, y[5]);
+        y[6] = fmaf(w, u[s][1].z, y[6]); y[7] = fmaf(w, u[s][1].w, y[7]);
+      }
+    }
+  } else {
   float M = -INFINITY;
   for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
-  float den = 0.f;
   for (int s = lane; s < nv; s += 64) den = fmaf(__builtin_amdgcn_exp2f(ml[2 * s] - M), ml[2 * s + 1], den);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k);
-  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < nv; s++) {
     const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
     const float4 u0 = *(const float4 *)(o + (long)s * D), u1 = *(const float4 *)(o + (long)s * D + 4);
     y[0] = fmaf(w, u0.x, y[0]); y[1] = fmaf(w, u0.y, y[1]); y[2] = fmaf(w, u0.z, y[2]); y[3] = fmaf(w, u0.w, y[3]);
     y[4] = fmaf(w, u1.x, y[4]); y[5] = fmaf(w, u1.y, y[5]); y[6] = fmaf(w, u1.z, y[6]); y[7] = fmaf(w, u1.w, y[7]);
+  }
   }
   const float inv = 1.0f / den;
 #pragma unroll
