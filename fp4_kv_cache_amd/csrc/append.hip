@@ -336,6 +336,10 @@ template <int B>
 __device__ __forceinline__ BlockSpan block_span(const AppendArgs &a, int i) {
   BlockSpan sp;
   sp.ok = false;
+  // the next token's id and position are read with this token's, so that one new token per
+  // sequence (a decode step) costs a single round of loads
+  const bool has_next = i + 1 < a.num_tokens;
+  const int s_next = has_next ? a.seq_ids[i + 1] : -1, pos_next = has_next ? a.positions[i + 1] : 0;
   int s = a.seq_ids[i], pos = a.positions[i];
   bool leader = (i == 0) || (a.seq_ids[i - 1] != s) || (pos % B == 0);
   int slot = a.slots[i];
@@ -345,7 +349,10 @@ __device__ __forceinline__ BlockSpan block_span(const AppendArgs &a, int i) {
   sp.bstart = pos - pos % B;
   sp.first = pos - sp.bstart;
   int n = 1;
-  while (i + n < a.num_tokens && a.seq_ids[i + n] == s && a.positions[i + n] < sp.bstart + B) n++;
+  if (has_next && s_next == s && pos_next < sp.bstart + B) {
+    n = 2;
+    while (i + n < a.num_tokens && a.seq_ids[i + n] == s && a.positions[i + n] < sp.bstart + B) n++;
+  }
   sp.n_new = n;
   sp.page = slot / a.page_size;
   sp.off0 = (slot % a.page_size) - sp.first;
@@ -360,15 +367,18 @@ __device__ __forceinline__ BlockSpan block_span(const AppendArgs &a, int i) {
 template <int FMT>
 __device__ __forceinline__ void v_append_body(const AppendArgs &a, int i, int h, int c) {
   constexpr int B = FMT == kFmtNV ? 16 : 32;
+  const int d = 128;
+  // the leading token's own value is read in the same round as the token bookkeeping
+  const float v_lead = i < a.num_tokens ? load_elem(a.v_new, ((long)i * a.hkv + h) * d + c, a.bf16) : 0.0f;
   BlockSpan sp = block_span<B>(a, i);
   if (!sp.ok) return;
-  const int d = 128;
   float *stage = a.stage + ((long)sp.seq * a.hkv + h) * B * d;
   float v[B];
 #pragma unroll
   for (int k = 0; k < B; k++) {
     float x = 0.0f;
     if (k < sp.first) x = stage[k * d + c];
+    else if (k == sp.first) x = v_lead;
     else if (k < sp.first + sp.n_new) x = load_elem(a.v_new, ((long)(i + k - sp.first) * a.hkv + h) * d + c, a.bf16);
     v[k] = x;
   }
