@@ -172,6 +172,20 @@ def test_mla_page_sizes(torch_dev, name, page):
     say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
 
 
+@pytest.mark.parametrize("name,hq", [("mla", 16), ("mla", 48), ("mla_mxfp4", 16), ("mla_mxfp4", 80)])
+def test_decode_mla_head_counts(torch_dev, name, hq):
+    """MLA workgroups serve four groups of 16 query heads; head counts that leave some of a
+    workgroup's waves without a group (16 heads: three idle per role; 48 and 80: a partly
+    filled quad) still stage tiles and join every barrier, and the active groups match the
+    oracle."""
+    lens = np.array([300, 1025], np.int32)
+    w = W.workload(name, batch=len(lens), hq=hq)
+    say("decode %s hq=%d" % (name, hq), lens.tolist())
+    built = harness.build(w, lens=lens)
+    worst, worst_ref, zg = compare_mla(built, tol=TOL)
+    say("mla hq=%d: max err vs oracle %.3g, vs fp64 attention %.3g, zero blocks %d" % (hq, worst, worst_ref, zg))
+
+
 @pytest.mark.parametrize("name,hq,n", [("qwen3_4b", 32, 2), ("qwen3_4b", 16, 4), ("qwen3_4b", 8, 8),
                                        ("qwen3_4b", 8, 3), ("qwen3_30b_a3b", 32, 2), ("qwen3_30b_a3b", 16, 4),
                                        ("qwen3_30b_a3b", 8, 7)])
