@@ -72,10 +72,6 @@ __device__ __forceinline__ uint4 ld16(const uint8_t *p) {
   return uint4{v[0], v[1], v[2], v[3]};
 }
 
-// 16-byte load of cache data that several workgroups read in turn (the MLA latent tile is read
-// by every head group of its sequence): an ordinary load, so that L2 keeps the line for them.
-__device__ __forceinline__ uint4 ldc16(const uint8_t *p) { return *(const uint4 *)p; }
-
 // byte k (compile-time after unrolling) of a 16-byte register group
 __device__ __forceinline__ uint32_t byte_of(const uint4 &u, int k) {
   const uint32_t w = k < 4 ? u.x : (k < 8 ? u.y : (k < 12 ? u.z : u.w));

@@ -64,11 +64,6 @@ __device__ __forceinline__ uint32_t e4m3_enc_sat(float t) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// E4M3 byte of 2^e for e in [-9, 8].
-__device__ __forceinline__ uint32_t e4m3_pow2_code(int e) {
-  return e >= -6 ? (uint32_t)(e + 7) << 3 : (1u << (e + 9));
-}
-
 // ceil(log2 t) for t > 0 finite or +inf, clamped to [lo, hi]; t == 0 gives lo.
 __device__ __forceinline__ int ceil_log2_clamp(float t, int lo, int hi) {
   uint32_t b = __float_as_uint(t);
