@@ -462,19 +462,20 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
   float *stage = a.stage + (long)sp.seq * B * D;
   const float *ksi = a.ksi;
   auto X = [&](int k, int ch) -> float & { return xs[k][ch + (ch >> 4)]; };
-  for (int e = tid; e < B * D; e += 256) {
-    int k = e / D, ch = e % D;
-    float x = 0.0f;
-    if (k < sp.first) x = stage[k * D + ch];
-    else if (k < sp.first + sp.n_new) x = load_elem(a.k_new, (long)(i + k - sp.first) * D + ch, a.bf16) * ksi[ch];
-    X(k, ch) = x;
+  // earlier tokens of the tile from the stage, the new tokens, zeros after them: three loops
+  // without branches inside, so that their loads are issued back to back
+#pragma unroll 8
+  for (int e = tid; e < sp.first * D; e += 256) X(e / D, e % D) = stage[e];
+  for (int e = tid; e < sp.n_new * D; e += 256) {
+    const int k = e / D, ch = e % D;
+    X(sp.first + k, ch) = load_elem(a.k_new, (long)(i + k) * D + ch, a.bf16) * ksi[ch];
   }
+  for (int e = (sp.first + sp.n_new) * D + tid; e < B * D; e += 256) X(e / D, e % D) = 0.0f;
   __syncthreads();
   // FWHT over the rows of the new tokens (stages h = 1, 2, ..., 256)
   for (int h = 1; h < D; h <<= 1) {
-    for (int e = tid; e < B * (D / 2); e += 256) {
-      int k = e / (D / 2), w = e % (D / 2);
-      if (k < sp.first || k >= sp.first + sp.n_new) continue;
+    for (int e = tid; e < sp.n_new * (D / 2); e += 256) {
+      const int k = sp.first + e / (D / 2), w = e % (D / 2);
       int idx = (w / h) * 2 * h + (w % h);
       float p = X(k, idx), q = X(k, idx + h);
       X(k, idx) = p + q;
@@ -484,9 +485,9 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
   }
   // stage the rotated new tokens when the tile stays incomplete
   if (sp.first + sp.n_new < B) {
-    for (int e = tid; e < B * D; e += 256) {
-      int k = e / D, ch = e % D;
-      if (k >= sp.first && k < sp.first + sp.n_new) stage[k * D + ch] = X(k, ch);
+    for (int e = tid; e < sp.n_new * D; e += 256) {
+      const int k = sp.first + e / D, ch = e % D;
+      stage[k * D + ch] = X(k, ch);
     }
   }
   // rope keys of the new tokens, copied unquantized
@@ -495,16 +496,31 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
     a.k_rope[((long)sp.page * a.page_size + sp.off0 + sp.first + k) * a.rope_dim + r] =
         ((const uint16_t *)a.k_rope_new)[(long)(i + k) * a.rope_dim + r];
   }
-  // ---- scale search: thread = (candidate kk, tile ct)
+  // ---- scale search.  Each tile's amax by TPT threads; then per candidate every element's
+  // squared error by all threads into LDS, and one thread per tile summing them in (token,
+  // channel) order -- the same fp32 operations in the same order as a sequential search.
+  constexpr int TPT = 256 / NT;              // threads per tile (NVFP4 8, MXFP4 16)
+  constexpr int EPT = B * B / TPT;           // elements per thread and tile
+  constexpr int DDP = B * B + 1;             // padded row: the summing threads hit distinct banks
+  __shared__ float dd[NT][DDP];
+  __shared__ float tmax[NT];
   const float G = FMT == kFmtNV ? a.gk[0] : 1.0f;
-  if (tid < NC * NT) {
-    const int ct = tid % NT, kk = tid / NT;
-    float amax = 0.0f;
-    for (int k = 0; k < B; k++)
+  const int st_ct = tid / TPT, st_sub = tid % TPT;   // tile and element stride of this thread
+  {
+    float m = 0.0f;
+#pragma unroll 8
+    for (int j = 0; j < EPT; j++) {
+      const int idx = st_sub + TPT * j;      // element idx = token * B + channel of the tile
+      m = fmaxf(m, fabsf(X(idx / B, st_ct * B + idx % B)));
+    }
 #pragma unroll
-      for (int cc = 0; cc < B; cc++) amax = fmaxf(amax, fabsf(X(k, ct * B + cc)));
-    float err = 0.0f;
-    int c = 0;
+    for (int o = TPT / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));   // TPT consecutive lanes
+    if (st_sub == 0) tmax[st_ct] = m;
+  }
+  __syncthreads();
+  for (int kk = 0; kk < NC; kk++) {
+    const float amax = tmax[st_ct];
+    int c;
     bool valid;
     if constexpr (FMT == kFmtNV) {
       const int deltas[5] = {0, 1, -1, -2, -3};
@@ -512,34 +528,40 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
       valid = c >= 0 && c <= 0x7E;
       if (valid) {
         const float S = e4m3_dec((uint32_t)c), sg = S * G, rr = (sg != 0.0f) ? 1.0f / sg : 0.0f;
-        for (int k = 0; k < B; k++)
-#pragma unroll
-          for (int cc = 0; cc < B; cc++) {
-            const float x = X(k, ct * B + cc);
-            const float xh = (e2m1_dec(e2m1_enc(x * rr)) * S) * G;
-            const float dd = x - xh;
-            err = err + dd * dd;
-          }
+#pragma unroll 8
+        for (int j = 0; j < EPT; j++) {
+          const int idx = st_sub + TPT * j;
+          const float x = X(idx / B, st_ct * B + idx % B);
+          const float dx = x - (e2m1_dec(e2m1_enc(x * rr)) * S) * G;
+          dd[st_ct][idx] = dx * dx;
+        }
       }
     } else {
       const int deltas[3] = {0, 1, -1};
       c = mx_exp(amax) + deltas[kk];
       valid = c >= -127 && c <= 127;
       if (valid) {
-        for (int k = 0; k < B; k++)
-#pragma unroll
-          for (int cc = 0; cc < B; cc++) {
-            const float x = X(k, ct * B + cc);
-            const float xh = ldexpf(e2m1_dec(e2m1_enc(ldexpf(x, -c))), c);
-            const float dd = x - xh;
-            err = err + dd * dd;
-          }
+#pragma unroll 8
+        for (int j = 0; j < EPT; j++) {
+          const int idx = st_sub + TPT * j;
+          const float x = X(idx / B, st_ct * B + idx % B);
+          const float dx = x - ldexpf(e2m1_dec(e2m1_enc(ldexpf(x, -c))), c);
+          dd[st_ct][idx] = dx * dx;
+        }
       }
     }
-    errs[kk][ct] = err;
-    cand[kk][ct] = valid ? c : kNoCand;
+    if (st_sub == 0) cand[kk][st_ct] = valid ? c : kNoCand;
+    __syncthreads();
+    if (tid < NT) {
+      float err = 0.0f;
+      if (cand[kk][tid] != kNoCand) {
+#pragma unroll 16
+        for (int idx = 0; idx < B * B; idx++) err = err + dd[tid][idx];
+      }
+      errs[kk][tid] = err;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   uint32_t sbyte_t = 0;
   if (tid < NT) {
     const int ct = tid;
