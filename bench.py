@@ -195,8 +195,7 @@ def main():
                          "1 GiB stream copy (the known-size reference for traffic counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the design notes describe how it would shard); got --gpus %d" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path; got --gpus %d" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
