@@ -496,13 +496,17 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
     a.k_rope[((long)sp.page * a.page_size + sp.off0 + sp.first + k) * a.rope_dim + r] =
         ((const uint16_t *)a.k_rope_new)[(long)(i + k) * a.rope_dim + r];
   }
-  // ---- scale search.  Each tile's amax by TPT threads; then per candidate every element's
-  // squared error by all threads into LDS, and one thread per tile summing them in (token,
-  // channel) order -- the same fp32 operations in the same order as a sequential search.
+  // ---- scale search.  Each tile's amax by TPT threads.  Then, chunk by chunk of each
+  // tile's elements, every (candidate, tile, element) squared error by all threads into LDS,
+  // and one thread per (candidate, tile) adding its chunk to a running sum in (token, channel)
+  // order -- for every candidate the same fp32 operations in the same order as a sequential
+  // search, with the candidates' sums running side by side.
   constexpr int TPT = 256 / NT;              // threads per tile (NVFP4 8, MXFP4 16)
   constexpr int EPT = B * B / TPT;           // elements per thread and tile
-  constexpr int DDP = B * B + 1;             // padded row: the summing threads hit distinct banks
-  __shared__ float dd[NT][DDP];
+  constexpr int CH = FMT == kFmtNV ? 128 : 256;   // elements per chunk of a tile
+  constexpr int DDP = CH + 4;                // padded rows: 16-byte aligned, on distinct banks
+  static_assert(NC * NT <= 256 && (B * B) % CH == 0, "one summing thread per (candidate, tile)");
+  __shared__ __attribute__((aligned(16))) float dd[NC][NT][DDP];
   __shared__ float tmax[NT];
   const float G = FMT == kFmtNV ? a.gk[0] : 1.0f;
   const int st_ct = tid / TPT, st_sub = tid % TPT;   // tile and element stride of this thread
@@ -518,50 +522,71 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
     if (st_sub == 0) tmax[st_ct] = m;
   }
   __syncthreads();
-  for (int kk = 0; kk < NC; kk++) {
-    const float amax = tmax[st_ct];
+  const bool summer = tid < NC * NT;
+  const int s_kk = tid / NT, s_ct = tid % NT;   // the summing thread's (candidate, tile)
+  if (summer) {
+    const float amax = tmax[s_ct];
     int c;
     bool valid;
     if constexpr (FMT == kFmtNV) {
       const int deltas[5] = {0, 1, -1, -2, -3};
-      c = (int)nv_default_scale(amax, G) + deltas[kk];
+      c = (int)nv_default_scale(amax, G) + deltas[s_kk];
       valid = c >= 0 && c <= 0x7E;
-      if (valid) {
-        const float S = e4m3_dec((uint32_t)c), sg = S * G, rr = (sg != 0.0f) ? 1.0f / sg : 0.0f;
-#pragma unroll 8
-        for (int j = 0; j < EPT; j++) {
-          const int idx = st_sub + TPT * j;
-          const float x = X(idx / B, st_ct * B + idx % B);
-          const float dx = x - (e2m1_dec(e2m1_enc(x * rr)) * S) * G;
-          dd[st_ct][idx] = dx * dx;
-        }
-      }
     } else {
       const int deltas[3] = {0, 1, -1};
-      c = mx_exp(amax) + deltas[kk];
+      c = mx_exp(amax) + deltas[s_kk];
       valid = c >= -127 && c <= 127;
-      if (valid) {
-#pragma unroll 8
-        for (int j = 0; j < EPT; j++) {
-          const int idx = st_sub + TPT * j;
-          const float x = X(idx / B, st_ct * B + idx % B);
-          const float dx = x - ldexpf(e2m1_dec(e2m1_enc(ldexpf(x, -c))), c);
-          dd[st_ct][idx] = dx * dx;
-        }
+    }
+    cand[s_kk][s_ct] = valid ? c : kNoCand;
+  }
+  __syncthreads();
+  // this thread's tile st_ct: every candidate's scale (an out-of-range candidate is evaluated
+  // with a clamped code and its sum is never used)
+  float c_s[NC], c_r[NC];
+  int c_e[NC];
+#pragma unroll
+  for (int kk = 0; kk < NC; kk++) {
+    const int c = cand[kk][st_ct];
+    if constexpr (FMT == kFmtNV) {
+      const float S = e4m3_dec((uint32_t)(c == kNoCand ? 0 : c)), sg = S * G;
+      c_s[kk] = S;
+      c_r[kk] = (sg != 0.0f) ? 1.0f / sg : 0.0f;
+      c_e[kk] = 0;
+    } else {
+      c_s[kk] = c_r[kk] = 0.0f;
+      c_e[kk] = c == kNoCand ? 0 : c;
+    }
+  }
+  float err = 0.0f;
+  for (int ch0 = 0; ch0 < B * B; ch0 += CH) {
+#pragma unroll 4
+    for (int j = 0; j < CH / TPT; j++) {
+      const int e = st_sub + TPT * j, idx = ch0 + e;   // element idx = token * B + channel
+      const float x = X(idx / B, st_ct * B + idx % B);
+#pragma unroll
+      for (int kk = 0; kk < NC; kk++) {
+        float dx;
+        if constexpr (FMT == kFmtNV) dx = x - (e2m1_dec(e2m1_enc(x * c_r[kk])) * c_s[kk]) * G;
+        else dx = x - ldexpf(e2m1_dec(e2m1_enc(ldexpf(x, -c_e[kk]))), c_e[kk]);
+        dd[kk][st_ct][e] = dx * dx;
       }
     }
-    if (st_sub == 0) cand[kk][st_ct] = valid ? c : kNoCand;
     __syncthreads();
-    if (tid < NT) {
-      float err = 0.0f;
-      if (cand[kk][tid] != kNoCand) {
-#pragma unroll 16
-        for (int idx = 0; idx < B * B; idx++) err = err + dd[tid][idx];
+    if (summer && cand[s_kk][s_ct] != kNoCand) {
+      const float *row = dd[s_kk][s_ct];
+#pragma unroll 8
+      for (int e = 0; e < CH; e += 4) {
+        const float4 v = *(const float4 *)(row + e);
+        err = err + v.x;
+        err = err + v.y;
+        err = err + v.z;
+        err = err + v.w;
       }
-      errs[kk][tid] = err;
     }
     __syncthreads();
   }
+  if (summer) errs[s_kk][s_ct] = err;
+  __syncthreads();
   uint32_t sbyte_t = 0;
   if (tid < NT) {
     const int ct = tid;
