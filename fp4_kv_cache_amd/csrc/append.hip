@@ -435,16 +435,17 @@ __global__ __launch_bounds__(128) void kv_append_small(AppendArgs a, int nkb) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// MLA latent: one workgroup (256 threads) per (leading token) = one B-token tile row of
+// MLA latent: one workgroup (512 threads) per (leading token) = one B-token tile row of
 // the sequence.  The new tokens are smoothed and rotated over 512 channels in LDS, the
 // earlier tokens of the tile come from the stage.  The scale search runs one thread per
 // (B x B tile, candidate), each summing its objective in (token, channel) order; the
 // first candidate with a strictly smaller objective wins, as in a sequential search.
 
 constexpr int kNoCand = -(1 << 30);   // marks a scale candidate outside the code range
+constexpr int kLatThreads = 512;      // threads of a latent-append workgroup
 
 template <int FMT>
-__global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
+__global__ __launch_bounds__(kLatThreads) void latent_append(AppendArgs a) {
   constexpr int B = FMT == kFmtNV ? 16 : 32;
   constexpr int D = 512;
   constexpr int NT = D / B;                  // tiles of the row
@@ -465,16 +466,16 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
   // earlier tokens of the tile from the stage, the new tokens, zeros after them: three loops
   // without branches inside, so that their loads are issued back to back
 #pragma unroll 8
-  for (int e = tid; e < sp.first * D; e += 256) X(e / D, e % D) = stage[e];
-  for (int e = tid; e < sp.n_new * D; e += 256) {
+  for (int e = tid; e < sp.first * D; e += kLatThreads) X(e / D, e % D) = stage[e];
+  for (int e = tid; e < sp.n_new * D; e += kLatThreads) {
     const int k = e / D, ch = e % D;
     X(sp.first + k, ch) = load_elem(a.k_new, (long)(i + k) * D + ch, a.bf16) * ksi[ch];
   }
-  for (int e = (sp.first + sp.n_new) * D + tid; e < B * D; e += 256) X(e / D, e % D) = 0.0f;
+  for (int e = (sp.first + sp.n_new) * D + tid; e < B * D; e += kLatThreads) X(e / D, e % D) = 0.0f;
   __syncthreads();
   // FWHT over the rows of the new tokens (stages h = 1, 2, ..., 256)
   for (int h = 1; h < D; h <<= 1) {
-    for (int e = tid; e < sp.n_new * (D / 2); e += 256) {
+    for (int e = tid; e < sp.n_new * (D / 2); e += kLatThreads) {
       const int k = sp.first + e / (D / 2), w = e % (D / 2);
       int idx = (w / h) * 2 * h + (w % h);
       float p = X(k, idx), q = X(k, idx + h);
@@ -485,13 +486,13 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
   }
   // stage the rotated new tokens when the tile stays incomplete
   if (sp.first + sp.n_new < B) {
-    for (int e = tid; e < sp.n_new * D; e += 256) {
+    for (int e = tid; e < sp.n_new * D; e += kLatThreads) {
       const int k = sp.first + e / D, ch = e % D;
       stage[k * D + ch] = X(k, ch);
     }
   }
   // rope keys of the new tokens, copied unquantized
-  for (int e = tid; e < sp.n_new * a.rope_dim; e += 256) {
+  for (int e = tid; e < sp.n_new * a.rope_dim; e += kLatThreads) {
     int k = e / a.rope_dim, r = e % a.rope_dim;
     a.k_rope[((long)sp.page * a.page_size + sp.off0 + sp.first + k) * a.rope_dim + r] =
         ((const uint16_t *)a.k_rope_new)[(long)(i + k) * a.rope_dim + r];
@@ -501,11 +502,11 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
   // and one thread per (candidate, tile) adding its chunk to a running sum in (token, channel)
   // order -- for every candidate the same fp32 operations in the same order as a sequential
   // search, with the candidates' sums running side by side.
-  constexpr int TPT = 256 / NT;              // threads per tile (NVFP4 8, MXFP4 16)
+  constexpr int TPT = kLatThreads / NT;      // threads per tile (NVFP4 16, MXFP4 32)
   constexpr int EPT = B * B / TPT;           // elements per thread and tile
   constexpr int CH = FMT == kFmtNV ? 128 : 256;   // elements per chunk of a tile
   constexpr int DDP = CH + 4;                // padded rows: 16-byte aligned, on distinct banks
-  static_assert(NC * NT <= 256 && (B * B) % CH == 0, "one summing thread per (candidate, tile)");
+  static_assert(NC * NT <= kLatThreads && (B * B) % CH == 0, "one summing thread per (candidate, tile)");
   __shared__ __attribute__((aligned(16))) float dd[NC][NT][DDP];
   __shared__ float tmax[NT];
   const float G = FMT == kFmtNV ? a.gk[0] : 1.0f;
@@ -608,7 +609,7 @@ __global__ __launch_bounds__(256) void latent_append(AppendArgs a) {
   const long pbase = (long)sp.page * a.page_size;
   // token-major codes (the key operand, read transposed as the value operand): task = (token k,
   // tile ct), B / 2 bytes
-  for (int e = tid; e < B * NT; e += 256) {
+  for (int e = tid; e < B * NT; e += kLatThreads) {
     const int k = e / NT, ct = e % NT;
     const float r = FMT == kFmtNV ? rsc[ct] : 0.0f;
     const int eb = FMT == kFmtNV ? 0 : ebest[ct];
@@ -651,8 +652,8 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
       v_append_gqa<kFmtMX><<<gv, 128, 0, s>>>(a);
     }
   } else {
-    if (a.fmt == kFmtNV) latent_append<kFmtNV><<<a.num_tokens, 256, 0, s>>>(a);
-    else latent_append<kFmtMX><<<a.num_tokens, 256, 0, s>>>(a);
+    if (a.fmt == kFmtNV) latent_append<kFmtNV><<<a.num_tokens, kLatThreads, 0, s>>>(a);
+    else latent_append<kFmtMX><<<a.num_tokens, kLatThreads, 0, s>>>(a);
   }
   return hipGetLastError();
 }
