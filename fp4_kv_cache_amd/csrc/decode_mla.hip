@@ -917,30 +917,36 @@ __global__ __launch_bounds__(64) void mla_merge(DecodeArgs a) {
   constexpr int D = kMlaD;
   const int row = blockIdx.x, lane = threadIdx.x;
   const int b = row / a.hq;
+  float4 *dst = (float4 *)(a.out + (long)row * D + 8 * lane);
+  const float *ml = a.ws_ml + (long)row * a.n_split * 2;
+  const float *o = a.ws_o + (long)row * a.n_split * D + 8 * lane;
+  // up to kMlaMergeFast splits: every split row of the workspace is loaded together with the
+  // sequence length, before the count of splits in use is known (rows past that count hold
+  // stale values and are not used)
+  const bool fast = a.n_split <= kMlaMergeFast;
+  float2 mlf = float2{-INFINITY, 0.f};
+  float4 u[kMlaMergeFast][2];
+  if (fast) {
+    if (lane < a.n_split) mlf = *(const float2 *)(ml + 2 * lane);
+#pragma unroll
+    for (int s = 0; s < kMlaMergeFast; s++) {
+      u[s][0] = s < a.n_split ? *(const float4 *)(o + (long)s * D) : float4{0.f, 0.f, 0.f, 0.f};
+      u[s][1] = s < a.n_split ? *(const float4 *)(o + (long)s * D + 4) : float4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   const int L = a.seq_lens[b];
   const int ntiles = (L + 127) >> 7;
   const int nv = min((ntiles + a.tiles_per_split - 1) / a.tiles_per_split, a.n_split);
-  float *dst = a.out + (long)row * D + 8 * lane;
   if (nv == 0) {
-#pragma unroll
-    for (int j = 0; j < 8; j++) dst[j] = 0.0f;
+    dst[0] = float4{0.f, 0.f, 0.f, 0.f};
+    dst[1] = float4{0.f, 0.f, 0.f, 0.f};
     return;
   }
-  const float *ml = a.ws_ml + (long)row * a.n_split * 2;
-  const float *o = a.ws_o + (long)row * a.n_split * D + 8 * lane;
   float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  if (nv <= kMlaMergeFast) {
-    // every split's (m, l) and partial output in flight at once; the same operations in the
-    // same order as the general path below
-    float2 mlv = float2{-INFINITY, 0.f};
-    if (lane < nv) mlv = *(const float2 *)(ml + 2 * lane);
-    float4 u[kMlaMergeFast][2];
-#pragma unroll
-    for (int s = 0; s < kMlaMergeFast; s++) {
-      u[s][0] = s < nv ? *(const float4 *)(o + (long)s * D) : float4{0.f, 0.f, 0.f, 0.f};
-      u[s][1] = s < nv ? *(const float4 *)(o + (long)s * D + 4) : float4{0.f, 0.f, 0.f, 0.f};
-    }
+  if (fast) {
+    // the same operations in the same order as the general path below
+    const float2 mlv = lane < nv ? mlf : float2{-INFINITY, 0.f};
     float M = mlv.x;
 #pragma unroll
     for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
@@ -997,7 +1003,9 @@ __global__ __launch_bounds__(64) void mla_merge(DecodeArgs a) {
   }
   const float *qs = a.qs + 8 * lane;
 #pragma unroll
-  for (int j = 0; j < 8; j++) dst[j] = y[j] * (1.0f / 512.0f) * qs[j];
+  for (int j = 0; j < 8; j++) y[j] = y[j] * (1.0f / 512.0f) * qs[j];
+  dst[0] = float4{y[0], y[1], y[2], y[3]};
+  dst[1] = float4{y[4], y[5], y[6], y[7]};
 }
 
 hipError_t launch_mla_partials(const DecodeArgs &a, hipStream_t s) {
