@@ -504,7 +504,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_append(AppendArgs a) {
   // search, with the candidates' sums running side by side.
   constexpr int TPT = kLatThreads / NT;      // threads per tile (NVFP4 16, MXFP4 32)
   constexpr int EPT = B * B / TPT;           // elements per thread and tile
-  constexpr int CH = FMT == kFmtNV ? 128 : 256;   // elements per chunk of a tile
+  constexpr int CH = FMT == kFmtNV ? 64 : 256;    // elements per chunk of a tile
   constexpr int DDP = CH + 4;                // padded rows: 16-byte aligned, on distinct banks
   static_assert(NC * NT <= kLatThreads && (B * B) % CH == 0, "one summing thread per (candidate, tile)");
   __shared__ __attribute__((aligned(16))) float dd[NC][NT][DDP];
