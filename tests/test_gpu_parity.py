@@ -172,6 +172,19 @@ def test_mla_page_sizes(torch_dev, name, page):
     say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
 
 
+@pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
+def test_decode_mla_many_splits(torch_dev, name):
+    """One sequence with few head groups is split into more parts than the MLA merge loads
+    at once (12 splits of 4 tiles for 6000 tokens and 16 heads), so the merge takes its
+    general path; the output still matches the oracle."""
+    lens = np.array([6000], np.int32)
+    w = W.workload(name, batch=1, hq=16)
+    say("decode %s many splits" % name, lens.tolist())
+    built = harness.build(w, lens=lens)
+    worst, worst_ref, zg = compare_mla(built, tol=TOL)
+    say("mla many splits: max err vs oracle %.3g, vs fp64 attention %.3g" % (worst, worst_ref))
+
+
 @pytest.mark.parametrize("name,hq", [("mla", 16), ("mla", 48), ("mla_mxfp4", 16), ("mla_mxfp4", 80)])
 def test_decode_mla_head_counts(torch_dev, name, hq):
     """MLA workgroups serve four groups of 16 query heads; head counts that leave some of a
