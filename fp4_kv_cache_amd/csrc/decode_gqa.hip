@@ -151,13 +151,13 @@ __device__ __forceinline__ int sk_index(int tok, int par) { return tok * 2 + par
 // (wave, unit) pairs share a slot and the slots of one unit are consecutive.
 constexpr int kMinTilesPerWave = 4;
 
-// Tiles of a sequence, with its length clamped to [0, max_pages * P] (the pages the
-// block table can name).
-__device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int b) {
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : min(L, a.max_pages * a.page_size);
-  return (L + 127) >> 7;
+// A sequence's length clamped to [0, max_pages * P] (the pages the block table can name),
+// and its tiles.
+__device__ __forceinline__ int seq_len_clamped(const DecodeArgs &a, int b) {
+  const int L = a.seq_lens[b];
+  return L < 0 ? 0 : min(L, a.max_pages * a.page_size);
 }
+__device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int b) { return (seq_len_clamped(a, b) + 127) >> 7; }
 
 __device__ __forceinline__ long uni_l(long v) {
   const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)(v & 0xffffffffL));
@@ -166,10 +166,10 @@ __device__ __forceinline__ long uni_l(long v) {
 }
 
 // The wave's share: the current unit (b, kvh) with its n tiles starting at flattened
-// index ustart, and the flattened range [x, x1) still to do.
+// index ustart, and the flattened range [x, x1) still to do; L is sequence b's length.
 struct Share {
   long x, x1, ustart, total;
-  int b, kvh, n, waves;
+  int b, kvh, n, waves, L;
 };
 
 // Wave count W and total T as every kernel of a launch computes them.
@@ -191,6 +191,34 @@ __device__ __forceinline__ long owner_of(long x, long total, int waves) {
 
 // Finds the wave's share; false when it has no tiles.
 __device__ bool find_share(const DecodeArgs &a, int wave, int lane, Share &s) {
+  if (a.batch <= 64) {
+    // one pass: lane b holds sequence b's length; the total is the scan's last entry
+    const int len = lane < a.batch ? seq_len_clamped(a, lane) : 0;
+    const int t = (len + 127) >> 7;
+    int incl = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    s.total = uni_l((long)__shfl(incl, 63) * a.hkv);
+    const long useful = (s.total + kMinTilesPerWave - 1) / kMinTilesPerWave;
+    s.waves = (int)(useful < (long)a.n_waves ? useful : (long)a.n_waves);
+    if (wave >= s.waves) return false;
+    const long T = s.total, W = s.waves;
+    s.x = wave * T / W;
+    s.x1 = (wave + 1) * T / W;
+    const unsigned long long m = __ballot((long)incl * a.hkv > s.x);
+    const int j = __builtin_ctzll(m);   // m != 0: x < T
+    const int n = __builtin_amdgcn_readfirstlane(__shfl(t, j));
+    const long before = uni_l((long)__shfl(incl, j) - n);   // tiles of sequences < b
+    s.b = j;
+    s.n = n;
+    s.L = __builtin_amdgcn_readfirstlane(__shfl(len, j));
+    s.kvh = (int)((s.x - before * a.hkv) / n);
+    s.ustart = before * a.hkv + (long)s.kvh * n;
+    return true;
+  }
   work_total(a, lane, s.total, s.waves);
   if (wave >= s.waves) return false;
   const long T = s.total, W = s.waves;
@@ -199,7 +227,8 @@ __device__ bool find_share(const DecodeArgs &a, int wave, int lane, Share &s) {
   // the sequence whose units hold tile x: scan the tile counts 64 sequences at a time
   long carry = 0;
   for (int b0 = 0; b0 < a.batch; b0 += 64) {
-    const int t = b0 + lane < a.batch ? seq_tiles(a, b0 + lane) : 0;
+    const int len = b0 + lane < a.batch ? seq_len_clamped(a, b0 + lane) : 0;
+    const int t = (len + 127) >> 7;
     int incl = t;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -213,6 +242,7 @@ __device__ bool find_share(const DecodeArgs &a, int wave, int lane, Share &s) {
       const long before = uni_l(carry + __shfl(incl, j) - n);   // tiles of sequences < b
       s.b = b0 + j;
       s.n = n;
+      s.L = __builtin_amdgcn_readfirstlane(__shfl(len, j));
       s.kvh = (int)((s.x - before * a.hkv) / n);
       s.ustart = before * a.hkv + (long)s.kvh * n;
       return true;
@@ -278,7 +308,7 @@ void gqa_partials(DecodeArgs a) {
   // one segment per (sequence, KV head) unit the wave's share touches
   for (;;) {
   const int b = sh.b, kvh = sh.kvh;
-  const int L = min(a.seq_lens[b], a.max_pages * P);   // > 0: the unit has tiles
+  const int L = sh.L;   // > 0: the unit has tiles
   const long uend = sh.ustart + sh.n;
   const int tb = (int)(sh.x - sh.ustart);
   const int te = (int)((sh.x1 < uend ? sh.x1 : uend) - sh.ustart);
@@ -691,7 +721,8 @@ void gqa_partials(DecodeArgs a) {
     sh.kvh = 0;
     do {
       if (++sh.b >= a.batch) break;
-      sh.n = seq_tiles(a, sh.b);
+      sh.L = seq_len_clamped(a, sh.b);
+      sh.n = (sh.L + 127) >> 7;
     } while (sh.n == 0);
     if (sh.b >= a.batch) break;   // not reached: the share ends inside the batch
   }
@@ -726,7 +757,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
   for (;;) {
     const int b = sh.b, kvh = sh.kvh;
-    const int L = min(a.seq_lens[b], a.max_pages * P);
+    const int L = sh.L;
     const long uend = sh.ustart + sh.n;
     const int tb = (int)(sh.x - sh.ustart);
     const int te = (int)((sh.x1 < uend ? sh.x1 : uend) - sh.ustart);
@@ -753,7 +784,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       sh.kvh = 0;
       do {
         if (++sh.b >= a.batch) break;
-        sh.n = seq_tiles(a, sh.b);
+        sh.L = seq_len_clamped(a, sh.b);
+        sh.n = (sh.L + 127) >> 7;
       } while (sh.n == 0);
       if (sh.b >= a.batch) break;
     }
