@@ -106,3 +106,26 @@ def append_range(built, b, start, end, workers=8, gen_end=None):
     cache.append(k, v, torch.from_numpy(slots).to(dev), torch.full((n,), b, dtype=torch.int32, device=dev),
                  torch.from_numpy(pos).to(dev), kr)
     return tail
+
+
+def append_step(built, pos):
+    """One kv_quant_append call holding token pos[b] of every sequence b with pos[b] >= 0
+    (a decode step: one new token per sequence, in sequence order)."""
+    import torch
+    w, cache, dev = built.w, built.cache, built.device
+    seqs = [b for b in range(w["batch"]) if pos[b] >= 0]
+    if not seqs:
+        return
+    p = np.array([pos[b] for b in seqs], dtype=np.int32)
+    slots = np.concatenate([slots_for(built.bt_np[b], [int(pos[b])], w["page"]) for b in seqs])
+    if w["attn"] == GQA:
+        k = np.stack([np.stack([W.keys(w, b, h, int(pos[b]) + 1)[-1] for h in range(w["hkv"])]) for b in seqs])
+        v = np.stack([np.stack([W.values(w, b, h, int(pos[b]) + 1)[-1] for h in range(w["hkv"])]) for b in seqs])
+        k, v, kr = _dev(k, w, torch, dev), _dev(v, w, torch, dev), None
+    else:
+        k = _dev(np.stack([W.keys(w, b, 0, int(pos[b]) + 1)[-1:] for b in seqs]), w, torch, dev)
+        v = None
+        kr = torch.from_numpy(np.stack([W.bf16_bits(W.rope_keys(w, b, int(pos[b]) + 1)[-1]) for b in seqs])
+                              .view(np.int16)).to(dev)
+    cache.append(k, v, torch.from_numpy(slots.astype(np.int32)).to(dev),
+                 torch.tensor(seqs, dtype=torch.int32, device=dev), torch.from_numpy(p).to(dev), kr)

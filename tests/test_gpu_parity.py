@@ -57,6 +57,24 @@ def test_append_incremental_tail_requant(torch_dev):
         check_gqa_cache(built)
 
 
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b", "mla", "mla_mxfp4"])
+def test_append_decode_steps(torch_dev, name):
+    """Decode-step appends: after a prefill, every call adds one token to each sequence
+    (three sequences at different offsets inside their blocks), across block and page
+    boundaries; the cache must equal the one-shot quantization of the final sequences."""
+    stop = np.array([40, 63, 95], np.int32)
+    lens = stop + 40
+    w = W.workload(name, batch=len(lens))
+    say("append decode steps", name, stop.tolist(), lens.tolist())
+    built = harness.build(w, lens=lens, stop=stop)
+    for k in range(40):
+        harness.append_step(built, stop + k)
+    if w["attn"] == 0:
+        check_gqa_cache(built)
+    else:
+        check_mla_cache(built)
+
+
 def test_append_prefill_large_batch_path(torch_dev):
     """One append call of > 65536 (token, head) rows takes the throughput kernel; it must
     give the same bytes as the latency kernel and the oracle."""
