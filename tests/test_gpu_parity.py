@@ -190,6 +190,23 @@ def test_mla_page_sizes(torch_dev, name, page):
     say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
 
 
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b", "mla", "mla_mxfp4"])
+def test_decode_all_sequences_empty(torch_dev, name):
+    """A batch whose sequence lengths are all zero: no wave or workgroup has tiles, and
+    every output row is exactly zero (GQA: the merge writes the zeros; MLA: likewise)."""
+    import torch
+    lens = np.array([64, 200, 1], np.int32)
+    w = W.workload(name, batch=len(lens))
+    say("decode all empty", name)
+    built = harness.build(w, lens=lens)
+    built.seq_lens.zero_()
+    q = built.queries()
+    out = built.cache.decode(q, built.bt, built.seq_lens, W.softmax_scale(w))
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert o.shape[0] == len(lens) and not np.any(o), "non-zero output for empty sequences"
+
+
 @pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
 def test_decode_mla_many_splits(torch_dev, name):
     """One sequence with few head groups is split into more parts than the MLA merge loads
