@@ -59,6 +59,12 @@ __device__ __forceinline__ uint32_t pack8(const float *x0, const float *x1, floa
 // (tokens past the end are masked, but their loads must stay inside the pool); a page
 // id outside the pool is clamped into it, so a bad table reads wrong data, not memory
 // outside the cache.
+// A sequence's length clamped to [0, max_pages * P] (the tokens the block table can name).
+__device__ __forceinline__ int seq_len_clamped(const DecodeArgs &a, int b) {
+  const int L = a.seq_lens[b];
+  return L < 0 ? 0 : min(L, a.max_pages * a.page_size);
+}
+
 __device__ __forceinline__ int phys_page(const DecodeArgs &a, int b, int lp, int last_lp) {
   int pg = a.block_table[(long)b * a.max_pages + (lp < last_lp ? lp : last_lp)];
   return pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);

@@ -151,12 +151,7 @@ __device__ __forceinline__ int sk_index(int tok, int par) { return tok * 2 + par
 // (wave, unit) pairs share a slot and the slots of one unit are consecutive.
 constexpr int kMinTilesPerWave = 4;
 
-// A sequence's length clamped to [0, max_pages * P] (the pages the block table can name),
-// and its tiles.
-__device__ __forceinline__ int seq_len_clamped(const DecodeArgs &a, int b) {
-  const int L = a.seq_lens[b];
-  return L < 0 ? 0 : min(L, a.max_pages * a.page_size);
-}
+// A sequence's tiles of 128 tokens.
 __device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int b) { return (seq_len_clamped(a, b) + 127) >> 7; }
 
 __device__ __forceinline__ long uni_l(long v) {

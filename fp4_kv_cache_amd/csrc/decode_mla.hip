@@ -146,7 +146,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int unit = ublk * 8 + slot;
   if (unit >= units) return;
   const int b = unit / a.n_split, split = unit % a.n_split;
-  const int L = a.seq_lens[b];
+  const int L = seq_len_clamped(a, b);
   const int ntiles = (L + 127) >> 7;
   const int tb = split * a.tiles_per_split;
   const int te = min(ntiles, tb + a.tiles_per_split);
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int unit = ublk * 8 + slot;
   if (unit >= units) return;
   const int b = unit / a.n_split, split = unit % a.n_split;
-  const int L = a.seq_lens[b];
+  const int L = seq_len_clamped(a, b);
   const int ntiles = (L + 127) >> 7;
   const int tb = split * a.tiles_per_split;
   const int te = min(ntiles, tb + a.tiles_per_split);
@@ -934,7 +934,7 @@ __global__ __launch_bounds__(64) void mla_merge(DecodeArgs a) {
       u[s][1] = s < a.n_split ? *(const float4 *)(o + (long)s * D + 4) : float4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  const int L = a.seq_lens[b];
+  const int L = seq_len_clamped(a, b);
   const int ntiles = (L + 127) >> 7;
   const int nv = min((ntiles + a.tiles_per_split - 1) / a.tiles_per_split, a.n_split);
   if (nv == 0) {

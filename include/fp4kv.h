@@ -156,8 +156,9 @@ size_t fp4_decode_workspace_bytes(const fp4kv_cache *c, int batch, int num_q_hea
 /* Decode attention: one query token per sequence against its whole cached context.
  *   q          [batch][num_q_heads][head_dim (+ rope_dim for MLA)], dtype q_dtype
  *   block_table i32 [batch][max_pages_per_seq]; seq_lens i32 [batch] (0 allowed,
- *              giving a zero output row); entries past a sequence's pages are
- *              never read
+ *              giving a zero output row; a length is read as clamped to
+ *              [0, max_pages_per_seq * page_size]); entries past a sequence's
+ *              pages are never read
  *   softmax_scale  multiplies q.k (the 1/head_dim of the unnormalized Hadamard
  *              rotation is applied internally)
  *   out        f32 [batch][num_q_heads][head_dim] (MLA: the 512-d latent
