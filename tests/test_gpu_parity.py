@@ -190,6 +190,23 @@ def test_mla_page_sizes(torch_dev, name, page):
     say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
 
 
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b", "mla", "mla_mxfp4"])
+def test_fp32_inputs(torch_dev, name):
+    """fp32 keys, values and queries (the other configurations feed bf16; the tiny one
+    covers GQA NVFP4 in fp32): the append's and the decode's fp32 input paths."""
+    lens = np.array([300, 129], np.int32)
+    w = W.workload(name, batch=len(lens), dtype="fp32")
+    say("fp32 inputs", name, lens.tolist())
+    built = harness.build(w, lens=lens)
+    if w["attn"] == 0:
+        check_gqa_cache(built)
+        worst, worst_ref, zg, zo = compare_gqa(built, tol=TOL)
+    else:
+        check_mla_cache(built)
+        worst, worst_ref, zg = compare_mla(built, tol=TOL)
+    say("fp32 inputs: max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
+
+
 @pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b", "mla", "mla_mxfp4"])
 def test_decode_all_sequences_empty(torch_dev, name):
     """A batch whose sequence lengths are all zero: no wave or workgroup has tiles, and
