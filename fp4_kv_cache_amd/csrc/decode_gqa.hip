@@ -629,9 +629,11 @@ void gqa_partials(DecodeArgs a) {
     // tile's P.V is accumulated by the MFMAs on top of o_run * gamma with the tile's own
     // weight as the new F, so no separate accumulator is needed.  A tile whose weight is
     // below 2^-60 is weighted 2^-60 (its contribution is below fp32 resolution either way).
-    const float m_new = fmaxf(m_run[rs], mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run[rs] - m_new);
-    const float beta = __builtin_amdgcn_exp2f(mt - m_new);
+    // An empty tile leaves the running state as it is (alpha 1, beta 0): a share whose first
+    // tile is empty for a row would otherwise take exp2(-inf - -inf) = NaN.
+    const float m_new = empty ? m_run[rs] : fmaxf(m_run[rs], mt);
+    const float alpha = empty ? 1.0f : __builtin_amdgcn_exp2f(m_run[rs] - m_new);
+    const float beta = empty ? 0.0f : __builtin_amdgcn_exp2f(mt - m_new);
     l_run[rs] = fmaf(l_run[rs], alpha, lt * beta);
     m_run[rs] = m_new;
     const float f_new = empty ? f_run[rs] : fmaxf(beta, 8.67361737988403547e-19f);   // 2^-60

@@ -253,7 +253,11 @@ def test_decode_mla_head_counts(torch_dev, name, hq):
 
 @pytest.mark.parametrize("name,hq,n", [("qwen3_4b", 32, 2), ("qwen3_4b", 16, 4), ("qwen3_4b", 8, 8),
                                        ("qwen3_4b", 8, 3), ("qwen3_30b_a3b", 32, 2), ("qwen3_30b_a3b", 16, 4),
-                                       ("qwen3_30b_a3b", 8, 7)])
+                                       ("qwen3_30b_a3b", 8, 7),
+                                       # pages of 16, fp32 inputs; with 2 KV heads the partition
+                                       # starts a share at the 129-token sequence's second tile,
+                                       # which holds none of its first row's tokens
+                                       ("tiny", 8, 2), ("tiny", 4, 4)])
 def test_decode_multi_token(torch_dev, name, hq, n):
     """Several query tokens per sequence (causal), stacked on the same key / value tiles in
     one or two row sets; lengths put the shorter rows' last tile empty (129 = 128 + 1) and
