@@ -190,6 +190,31 @@ def test_mla_page_sizes(torch_dev, name, page):
     say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
 
 
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b", "mla", "mla_mxfp4"])
+def test_block_table_entries_past_the_pages_unused(torch_dev, name):
+    """Block-table entries past a sequence's pages may hold anything (here ids outside the
+    cache, negative and huge): the decode never uses them, and the output matches the
+    oracle."""
+    import torch
+    lens = np.array([130, 1, 700, 64], np.int32)
+    w = W.workload(name, batch=len(lens))
+    say("block table garbage", name, lens.tolist())
+    built = harness.build(w, lens=lens)
+    bt = built.bt_np.copy()
+    npg = -(-lens // w["page"])
+    rng = np.random.default_rng(3)
+    for b in range(len(lens)):
+        tail = bt.shape[1] - npg[b]
+        if tail > 0:
+            bt[b, npg[b]:] = rng.choice([-7, 1 << 30, -(1 << 31), 12345678], size=tail)
+    built.bt = torch.from_numpy(bt).to(built.device)
+    if w["attn"] == 0:
+        worst, worst_ref, zg, zo = compare_gqa(built, tol=TOL)
+    else:
+        worst, worst_ref, zg = compare_mla(built, tol=TOL)
+    say("block table garbage: max err vs oracle %.3g" % worst)
+
+
 @pytest.mark.parametrize("name", ["qwen3_30b_a3b", "mla", "mla_mxfp4"])
 def test_fp32_inputs(torch_dev, name):
     """fp32 keys, values and queries (the other configurations feed bf16; the tiny one
