@@ -296,6 +296,21 @@ def test_decode_multi_token(torch_dev, name, hq, n):
     assert zg == zo
 
 
+@pytest.mark.parametrize("name,hq,n,page", [("qwen3_4b", 32, 2, 32), ("qwen3_4b", 16, 3, 128),
+                                            ("qwen3_4b", 8, 5, 256), ("qwen3_30b_a3b", 32, 2, 32),
+                                            ("qwen3_30b_a3b", 16, 4, 128), ("qwen3_30b_a3b", 8, 6, 256)])
+def test_decode_multi_token_page_sizes(torch_dev, name, hq, n, page):
+    """Multi-token decode with pages of 32, 128 and 256 tokens (one, two or four 128-token
+    tiles per page boundary case)."""
+    lens = np.array([n, 129, 300, 700 + n], np.int32)
+    w = W.workload(name, batch=len(lens), hq=hq, page=page)
+    say("decode multi-token %s hq=%d n=%d page=%d" % (name, hq, n, page), lens.tolist())
+    built = harness.build(w, lens=lens)
+    worst, worst_ref, zg, zo = compare_gqa_multi(built, n, tol=TOL)
+    say("max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
+    assert zg == zo
+
+
 def test_decode_underflow_no_zero_blocks(torch_dev):
     w = W.workload("long_underflow", batch=1)
     lens = np.array([16384], np.int32)
