@@ -117,7 +117,7 @@ def test_decode_nvfp4_ragged(torch_dev, hq):
     say("max err vs oracle %.3g, vs fp64 %.3g, zero blocks %d/%d" % (worst, worst_ref, zg, zo))
 
 
-@pytest.mark.parametrize("hq", [32, 16])
+@pytest.mark.parametrize("hq", [32, 16, 8, 4])   # query heads per KV head 8, 4, 2, 1
 def test_decode_mxfp4_ragged(torch_dev, hq):
     w = W.workload("qwen3_30b_a3b", batch=4, hq=hq)
     lens = np.array([33, 128, 777, 3000], np.int32)
