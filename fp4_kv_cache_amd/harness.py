@@ -111,21 +111,30 @@ def append_range(built, b, start, end, workers=8, gen_end=None):
 def append_step(built, pos):
     """One kv_quant_append call holding token pos[b] of every sequence b with pos[b] >= 0
     (a decode step: one new token per sequence, in sequence order)."""
+    append_ranges(built, [(b, int(pos[b]), int(pos[b]) + 1) for b in range(built.w["batch"]) if pos[b] >= 0])
+
+
+def append_ranges(built, ranges):
+    """One kv_quant_append call holding positions [start, end) of each (b, start, end) in
+    `ranges` (sequences in increasing order, each at most once)."""
     import torch
     w, cache, dev = built.w, built.cache, built.device
-    seqs = [b for b in range(w["batch"]) if pos[b] >= 0]
-    if not seqs:
+    ranges = [(b, s, e) for b, s, e in ranges if e > s]
+    if not ranges:
         return
-    p = np.array([pos[b] for b in seqs], dtype=np.int32)
-    slots = np.concatenate([slots_for(built.bt_np[b], [int(pos[b])], w["page"]) for b in seqs])
+    seq_ids = np.concatenate([np.full(e - s, b, np.int32) for b, s, e in ranges])
+    p = np.concatenate([np.arange(s, e, dtype=np.int32) for _, s, e in ranges])
+    slots = np.concatenate([slots_for(built.bt_np[b], np.arange(s, e), w["page"]) for b, s, e in ranges])
     if w["attn"] == GQA:
-        k = np.stack([np.stack([W.keys(w, b, h, int(pos[b]) + 1)[-1] for h in range(w["hkv"])]) for b in seqs])
-        v = np.stack([np.stack([W.values(w, b, h, int(pos[b]) + 1)[-1] for h in range(w["hkv"])]) for b in seqs])
+        k = np.concatenate([np.stack([W.keys(w, b, h, e)[s:e] for h in range(w["hkv"])], axis=1)
+                            for b, s, e in ranges])
+        v = np.concatenate([np.stack([W.values(w, b, h, e)[s:e] for h in range(w["hkv"])], axis=1)
+                            for b, s, e in ranges])
         k, v, kr = _dev(k, w, torch, dev), _dev(v, w, torch, dev), None
     else:
-        k = _dev(np.stack([W.keys(w, b, 0, int(pos[b]) + 1)[-1:] for b in seqs]), w, torch, dev)
+        k = _dev(np.concatenate([W.keys(w, b, 0, e)[s:e][:, None, :] for b, s, e in ranges]), w, torch, dev)
         v = None
-        kr = torch.from_numpy(np.stack([W.bf16_bits(W.rope_keys(w, b, int(pos[b]) + 1)[-1]) for b in seqs])
+        kr = torch.from_numpy(np.concatenate([W.bf16_bits(W.rope_keys(w, b, e)[s:e]) for b, s, e in ranges])
                               .view(np.int16)).to(dev)
-    cache.append(k, v, torch.from_numpy(slots.astype(np.int32)).to(dev),
-                 torch.tensor(seqs, dtype=torch.int32, device=dev), torch.from_numpy(p).to(dev), kr)
+    cache.append(k, v, torch.from_numpy(slots.astype(np.int32)).to(dev), torch.from_numpy(seq_ids).to(dev),
+                 torch.from_numpy(p).to(dev), kr)

@@ -75,6 +75,28 @@ def test_append_decode_steps(torch_dev, name):
         check_mla_cache(built)
 
 
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b", "mla", "mla_mxfp4"])
+def test_append_mixed_chunks_one_call(torch_dev, name):
+    """One append call holding chunks of several sequences at once (3, 1, 0, 17 and 40
+    tokens, starting inside and at block boundaries), twice in a row; the cache must equal
+    the one-shot quantization of the final sequences."""
+    stop = np.array([10, 64, 33, 95], np.int32)
+    first = [3, 1, 0, 17]
+    second = [40, 2, 31, 1]
+    lens = stop + np.array(first) + np.array(second)
+    w = W.workload(name, batch=len(lens))
+    say("append mixed chunks", name, stop.tolist(), lens.tolist())
+    built = harness.build(w, lens=lens, stop=stop)
+    p = stop.copy()
+    for chunk in (first, second):
+        harness.append_ranges(built, [(b, int(p[b]), int(p[b]) + chunk[b]) for b in range(len(lens))])
+        p += np.array(chunk, np.int32)
+    if w["attn"] == 0:
+        check_gqa_cache(built)
+    else:
+        check_mla_cache(built)
+
+
 def test_append_prefill_large_batch_path(torch_dev):
     """One append call of > 65536 (token, head) rows takes the throughput kernel; it must
     give the same bytes as the latency kernel and the oracle."""
