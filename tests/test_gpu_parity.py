@@ -163,15 +163,31 @@ def test_decode_shares_span_units(torch_dev, name):
 
 
 @pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b"])
+def test_decode_batch_over_64(torch_dev, name):
+    """More than 64 sequences: the partition lookup scans the lengths 64 sequences at a
+    time (batches up to 64 take a single pass); sampled (sequence, KV head) pairs match the
+    oracle, among them sequences past the first 64."""
+    rng = np.random.default_rng(17)
+    lens = rng.integers(1, 700, size=100).astype(np.int32)
+    lens[rng.random(100) < 0.15] = 0
+    w = W.workload(name, batch=len(lens))
+    say("decode batch 100", name)
+    built = harness.build(w, lens=lens)
+    pairs = [(b, h) for b in (0, 5, 63, 64, 65, 80, 99) for h in (0, w["hkv"] - 1)]
+    worst, worst_ref, zg, zo = compare_gqa(built, pairs=pairs, tol=TOL)
+    say("batch 100: max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
+
+
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b"])
 def test_partition_reads_every_tile_once(torch_dev, name):
     """The decode kernel's partition and tile loads (run without arithmetic by
     fp4kv_cache_read) read every byte of the cache exactly once: with whole-tile sequences
     the xor of everything read equals the xor of the four cache arrays."""
     import torch
     from fp4_kv_cache_amd import lib as L
-    lens = np.array([256, 0, 1280, 128, 640, 0, 2048, 384], np.int32)
+    lens = np.array([256, 0, 1280, 128, 640, 0, 2048, 384] * 9, np.int32)   # 72 sequences
     w = W.workload(name, batch=len(lens))
-    say("partition coverage", name, lens.tolist())
+    say("partition coverage", name, len(lens))
     built = harness.build(w, lens=lens)
     maxp = built.bt.shape[1]
     n = L.fp4kv_cache_read_sink_words(built.cache.desc, w["batch"], w["hq"], maxp * w["page"])
