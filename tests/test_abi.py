@@ -119,3 +119,16 @@ def test_split_plan_sizes(lib):
     # tiny batches: no more waves than shares of 4 tiles (2 units x 32 tiles -> 16 waves)
     c2 = _desc(num_kv_heads=2)
     assert L.fp4_decode_workspace_bytes(c2, 1, 8, 4096) == (16 + 2) * 4 * 130 * 4 + 2 * 8
+
+
+def test_header_is_plain_c():
+    """include/fp4kv.h compiles as C99 (no C++ or torch types at the boundary)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp4kv.h")
+    r = subprocess.run([cc, "-fsyntax-only", "-x", "c", "-std=c99", "-Wall", "-Werror", hdr],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
