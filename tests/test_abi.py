@@ -132,3 +132,23 @@ def test_header_is_plain_c():
     r = subprocess.run([cc, "-fsyntax-only", "-x", "c", "-std=c99", "-Wall", "-Werror", hdr],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_host_entry_points_from_c(lib, tmp_path):
+    """A plain C program (tests/c/abi_host.c) links libfp4kv.so and calls the size queries and
+    the host-side validation: the boundary is usable without Python."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(L.LIB_PATH)
+    exe = str(tmp_path / "abi_host")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(root, "include"),
+                        os.path.join(root, "tests", "c", "abi_host.c"), "-L", libdir, "-lfp4kv",
+                        "-Wl,-rpath," + libdir, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "FAIL" not in r.stdout
