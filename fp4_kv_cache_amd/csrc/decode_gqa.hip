@@ -21,9 +21,10 @@
 //    E8M0-scaled MFMA cannot take.  Each MFMA therefore sees one 16-channel
 //    block per output column (query rows masked to one block), giving the exact
 //    block dot 2^eQ * sum(code_q * code_k); the key scale multiplies it in fp32
-//    and the 8 block terms are added in the fixed order ((T0+T2)+T4)+T6 +
-//    (((T1+T3)+T5)+T7) -- every term is exact, so the logit is reproducible bit
-//    for bit.  Columns: 8 * parity + stacked row (row = 2*head + {Q1, Q2}).
+//    and the 8 block terms are added in fp32 (even-block sum + odd-block sum);
+//    every term is exact, so the logit differs from the exact dot rounded once
+//    only by those few roundings.  Columns: 8 * parity + stacked row
+//    (row = 2*head + {Q1, Q2}).
 //  * MXFP4 keys (32-channel E8M0 blocks = one lane group) use one native MFMA
 //    per 16 tokens with both scales in hardware.
 //  * Probabilities: NVFP4 with power-of-two block scales and tensor scale 2^-10

@@ -14,11 +14,8 @@
 //    most six significant bits, so the fp16 value is exact) and the dual-residual query
 //    rows are fp16 as well (FP4 code times a power-of-two block scale, exact); the
 //    contraction runs on v_mfma_f32_16x16x32_f16 with exact products and fp32
-//    accumulation.  Per-16-channel exact block terms summed in a fixed order (the
-//    reading the GQA kernel reproduces bit for bit) would cost one fp32 FMA per
-//    (token, query row, block) -- 8192 per token at 128 heads -- so here the block terms
-//    are accumulated in the matrix core's fp32 order instead; the logits agree with
-//    that reading to fp32 rounding.  The rope part runs on the bf16 MFMA.
+//    accumulation, so the logit is the exact dot up to the matrix core's fp32
+//    summation order.  The rope part runs on the bf16 MFMA.
 //  * MFMA K index -> channel: lane group q (lanes 16q..16q+15) takes channels
 //    128q + 8s .. 128q + 8s + 7 in K-step s, so each lane reads 64 contiguous bytes of
 //    its token's latent row per token group.

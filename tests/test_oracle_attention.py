@@ -251,3 +251,92 @@ def test_multi_token_single_query_is_gqa_head():
     a = A.gqa_head(q[0], K, V, ones, ones, np.float32(0.01), np.float32(0.01), KQ.NVFP4, 0.08, L=L)
     b = A.gqa_head_multi(q, K, V, ones, ones, np.float32(0.01), np.float32(0.01), KQ.NVFP4, 0.08, L=L)
     assert np.array_equal(a["out"], b["out"][0])
+
+
+def _nearest_f32(x):
+    """The fp32 values nearest to the exact rational x (one, or two on a tie)."""
+    from fractions import Fraction
+    c = np.float32(float(x))
+    best = []
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        best.append((abs(Fraction(float(cand)) - x), cand))
+    dmin = min(d for d, _ in best)
+    return [v for d, v in best if d == dmin]
+
+
+@pytest.mark.parametrize("fmt", [KQ.NVFP4, KQ.MXFP4])
+def test_raw_dot_is_exact_dot_rounded_once(fmt):
+    """raw = fl32(<q^, k^>): the exact rational dot of the block-scaled values (brute force
+    with fractions) rounded once to the nearest fp32, for random codes and scales whose
+    products span the whole E4M3 / power-of-two range (R11)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(35)
+    d, R, L = 128, 3, 6
+    Q = (rng.standard_normal((R, d)) * np.exp2(rng.integers(-6, 6, size=(R, d)))).astype(F32)
+    K = (rng.standard_normal((L, d)) * np.exp2(rng.integers(-6, 6, size=(L, d)))).astype(F32)
+    ones = np.ones(d, F32)
+    kc, ks = KQ.quantize_keys(K, ones, F32(0.01) if fmt == KQ.NVFP4 else 1.0, fmt)
+    khat = A.key_dequant_exact(kc, ks, fmt)
+    qq = quantize_query(Q, ones, fmt)
+    for which in (1, 2):
+        qhat = qq.dequant_exact(which)
+        raw = A.raw_dot(qhat, khat)
+        for r in range(R):
+            for t in range(L):
+                exact = sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qhat[r], khat[t])),
+                            Fraction(0))
+                assert raw[r, t] in _nearest_f32(exact), (which, r, t)
+
+
+def _hadamard_preimage(x, factors):
+    """z with FWHT(fl32(z * factors)) == x exactly: z = (x H / n) / factors, for x on a
+    grid fine enough that every Walsh-Hadamard stage stays exact in fp32."""
+    import scipy.linalg
+    n = x.shape[-1]
+    return ((np.asarray(x, np.float64) @ scipy.linalg.hadamard(n) / n) / factors).astype(F32)
+
+
+def test_mla_rotated_smoothed_exact_codecs_is_textbook_attention():
+    """The MLA pipeline with smoothing and rotation ON and exact codecs equals textbook
+    attention over the original latent (as key and value) plus the rope term.
+
+    The inputs are chosen so that the transformed latent x = FWHT(K * k_smooth_inv) and the
+    transformed query y = FWHT(q * q_smooth) are grid-valued with power-of-two scales (every
+    codec exact, Q2 = 0).  Logit invariance <yH, xH>/512 = <q, k> and the output un-rotation
+    o = (o'' H / 512) * q_smooth must then give softmax(q K^T + q_r k_r^T) K.  Taking
+    k_smooth_inv for q_smooth in the un-rotation, dropping the / 512, or a wrong smoothing
+    direction each moves the output by a large factor."""
+    rng = np.random.default_rng(36)
+    D, r, L, R = 512, 64, 45, 3
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    # smoothing: powers of two, q_smooth * k_smooth_inv == 1
+    lam = np.exp2(rng.integers(-2, 3, size=D)).astype(F32)
+    ksi, qs = (1.0 / lam).astype(F32), lam
+    # transformed latent: 16 x 16 tiles of grid values, each tile holding a +-6, scaled 2^e
+    x = rng.choice(grid, size=(L, D)) * rng.choice([-1.0, 1.0], size=(L, D))
+    tile_e = rng.integers(-3, 3, size=(-(-L // 16), D // 16))
+    for tb in range(tile_e.shape[0]):
+        for cb in range(D // 16):
+            x[16 * tb, 16 * cb] = 6.0
+            x[16 * tb:16 * tb + 16, 16 * cb:16 * cb + 16] *= 2.0 ** tile_e[tb, cb]
+    # transformed query rows: 16-channel blocks scaled by 2^-j, a +-6 in block 0 (so Q1 is exact)
+    y = rng.choice(grid, size=(R, D)) * rng.choice([-1.0, 1.0], size=(R, D))
+    y[:, ::16] = 6.0
+    ex = rng.integers(0, 4, size=(R, D // 16))
+    ex[:, 0] = 0
+    y = y * np.repeat(2.0 ** -ex, 16, axis=1)
+    K = _hadamard_preimage(x, ksi)
+    q = _hadamard_preimage(y, qs)
+    qr = W_bf16(rng.standard_normal((R, r)))
+    kr = W_bf16(rng.standard_normal((L, r)))
+    sc = 1.0 / np.sqrt(D + r)
+    res = A.mla_seq(q, qr, K, kr, ksi, qs, 1.0, KQ.NVFP4, sc, L=L, opts=dict(p_mode="exact"))
+    # the transforms really were exact: codes reproduce x, the query residual is zero
+    assert np.array_equal(A.latent_dequant_exact(res["l_codes"], res["l_scales"], KQ.NVFP4, 1.0)[:L], x)
+    assert np.all(res["qq"].c2 & 7 == 0)
+    ref = A.reference_attention(q, K, K, sc, q_rope=qr, k_rope=kr)
+    assert np.max(A.row_rel_err(res["out"], ref)) < 1e-5
+    # the same pin fails for the plausible mistakes it is meant to catch
+    wrong_smooth = res["out"] / qs.astype(np.float64) * ksi.astype(np.float64)
+    assert np.max(A.row_rel_err(wrong_smooth, ref)) > 0.1                     # k_smooth_inv for q_smooth
+    assert np.max(A.row_rel_err(res["out"] * D, ref)) > 0.1                   # missing / 512
