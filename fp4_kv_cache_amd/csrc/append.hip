@@ -326,10 +326,19 @@ __device__ __forceinline__ void k_append_wave_body(const AppendArgs &a, int tok,
 // block when it is the first token of its sequence in this batch or its position
 // starts a block; the block's new tokens are i .. i + n_new - 1 and its first
 // `first` positions were appended by earlier calls (their values are in the stage).
+//
+// The stage holds one open block per sequence, so inside one call only one workgroup may
+// touch a sequence's stage rows: the workgroup of the sequence's first block in the batch
+// (`chunk_first`).  It reads the rows earlier calls left (its `first` rows) and, once it has
+// read them, writes the rows of the chunk's last block when that block stays incomplete --
+// also when that block is a later one, whose own workgroup then leaves the stage alone.
+// (Letting the later block's workgroup write would race with the first block's reads.)
 
 struct BlockSpan {
   int seq, bstart, first, n_new, page, off0;
   bool ok;
+  bool chunk_first;   // i is the first token of its sequence in the batch
+  bool continues;     // the sequence's tokens go on past this block (i + n_new is one of them)
 };
 
 template <int B>
@@ -354,11 +363,47 @@ __device__ __forceinline__ BlockSpan block_span(const AppendArgs &a, int i) {
     while (i + n < a.num_tokens && a.seq_ids[i + n] == s && a.positions[i + n] < sp.bstart + B) n++;
   }
   sp.n_new = n;
+  sp.chunk_first = (i == 0) || (a.seq_ids[i - 1] != s);
+  sp.continues = i + n < a.num_tokens && a.seq_ids[i + n] == s;
   sp.page = slot / a.page_size;
   sp.off0 = (slot % a.page_size) - sp.first;
   // the block must sit inside the slot's page (slot and position disagree otherwise)
   sp.ok = sp.off0 >= 0 && (sp.off0 % B) == 0 && sp.off0 + B <= a.page_size;
   return sp;
+}
+
+// End of the chunk of sequence s that starts at batch index i0: the first index after i0
+// whose token belongs to another sequence (or num_tokens).  The sequence's tokens are
+// contiguous in the batch (a documented precondition), so "index j holds sequence s" is true
+// up to the end and false after it; every round probes nthr evenly spaced indices of the open
+// range and keeps the interval between the last true and the first false probe, so a chunk
+// of n tokens takes about log(n) / log(nthr) rounds.  All nthr threads of the workgroup call it.
+__device__ int chunk_end(const AppendArgs &a, int i0, int s, int tid, int nthr) {
+  int lo = i0, hi = a.num_tokens;            // seq_ids[lo] == s; index hi counts as another sequence
+  while (hi - lo > 1) {
+    const int step = (hi - lo - 1 + nthr - 1) / nthr;   // >= 1; the last probe reaches hi - 1
+    const long j = (long)lo + (long)step * (tid + 1);
+    const int hit = j < hi && a.seq_ids[j] == s;
+    const int cnt = __syncthreads_count(hit);
+    lo = lo + step * cnt;
+    hi = min(hi, lo + step);
+  }
+  return hi;
+}
+
+// The chunk's last block, seen from the chunk's first block (sp.continues): the batch index
+// of its first token and its token count; false when it fills its block (nothing to stage)
+// or the batch breaks the contiguity precondition.
+struct TailSpan {
+  int i, n;
+};
+template <int B>
+__device__ bool chunk_tail(const AppendArgs &a, const BlockSpan &sp, int i0, int tid, int nthr, TailSpan &t) {
+  const int i1 = chunk_end(a, i0, sp.seq, tid, nthr);
+  const int pos_last = a.positions[i1 - 1];
+  t.n = pos_last % B + 1;
+  t.i = i1 - t.n;
+  return t.n < B && t.i > i0 && a.positions[t.i] == pos_last - (t.n - 1);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -372,6 +417,9 @@ __device__ __forceinline__ void v_append_body(const AppendArgs &a, int i, int h,
   const float v_lead = i < a.num_tokens ? load_elem(a.v_new, ((long)i * a.hkv + h) * d + c, a.bf16) : 0.0f;
   BlockSpan sp = block_span<B>(a, i);
   if (!sp.ok) return;
+  // the workgroup of the chunk's first block stages the chunk's incomplete last block
+  TailSpan tail{0, 0};
+  const bool stage_tail = sp.chunk_first && sp.continues && chunk_tail<B>(a, sp, i, c, 128, tail);
   float *stage = a.stage + ((long)sp.seq * a.hkv + h) * B * d;
   float v[B];
 #pragma unroll
@@ -404,10 +452,15 @@ __device__ __forceinline__ void v_append_body(const AppendArgs &a, int i, int h,
     *(uint32_t *)(cdst + k) = codes[k] | (codes[k + 1] << 8) | (codes[k + 2] << 16) | ((uint32_t)codes[k + 3] << 24);
   const int J = (a.page_size < 32 ? a.page_size : 32) / B;
   a.v_scales[((long)sp.page * a.hkv + h) * d * (a.page_size / B) + vscale_off(c, sp.off0 / B, J)] = (uint8_t)sbyte;
-  if (sp.first + sp.n_new < B) {
+  // this thread read its stage rows above, before it writes any (one thread per channel)
+  if (sp.chunk_first && !sp.continues && sp.first + sp.n_new < B) {
 #pragma unroll
     for (int k = 0; k < B; k++)
       if (k >= sp.first && k < sp.first + sp.n_new) stage[k * d + c] = v[k];
+  }
+  if (stage_tail) {
+    for (int k = 0; k < tail.n; k++)
+      stage[k * d + c] = load_elem(a.v_new, ((long)(tail.i + k) * a.hkv + h) * d + c, a.bf16);
   }
 }
 
@@ -484,8 +537,9 @@ __global__ __launch_bounds__(kLatThreads) void latent_append(AppendArgs a) {
     }
     __syncthreads();
   }
-  // stage the rotated new tokens when the tile stays incomplete
-  if (sp.first + sp.n_new < B) {
+  // stage the rotated new tokens when the tile stays incomplete and is the chunk's only one
+  // (every stage read of this workgroup happened before the barriers above)
+  if (sp.chunk_first && !sp.continues && sp.first + sp.n_new < B) {
     for (int e = tid; e < sp.n_new * D; e += kLatThreads) {
       const int k = sp.first + e / D, ch = e % D;
       stage[k * D + ch] = X(k, ch);
@@ -626,6 +680,28 @@ __global__ __launch_bounds__(kLatThreads) void latent_append(AppendArgs a) {
       *(uint32_t *)(dst + j) = w;
     }
   }
+  // The chunk's first tile stages the chunk's incomplete last tile (a later tile of the same
+  // call, whose own workgroup leaves the stage alone): its rows smoothed and rotated as above.
+  if (!(sp.chunk_first && sp.continues)) return;
+  TailSpan tail;
+  if (!chunk_tail<B>(a, sp, i, tid, kLatThreads, tail)) return;
+  __syncthreads();   // every thread is done reading xs
+  for (int e = tid; e < tail.n * D; e += kLatThreads) {
+    const int k = e / D, ch = e % D;
+    X(k, ch) = load_elem(a.k_new, (long)(tail.i + k) * D + ch, a.bf16) * ksi[ch];
+  }
+  __syncthreads();
+  for (int h = 1; h < D; h <<= 1) {
+    for (int e = tid; e < tail.n * (D / 2); e += kLatThreads) {
+      const int k = e / (D / 2), w = e % (D / 2);
+      const int idx = (w / h) * 2 * h + (w % h);
+      const float p = X(k, idx), q = X(k, idx + h);
+      X(k, idx) = p + q;
+      X(k, idx + h) = p - q;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < tail.n * D; e += kLatThreads) stage[e] = X(e / D, e % D);
 }
 
 // ---------------------------------------------------------------------------------------------
