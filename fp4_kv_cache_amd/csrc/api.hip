@@ -3,6 +3,7 @@
 // kernel launches on the caller's stream.  Nothing here allocates or syncs.
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "fp4kv_internal.h"
 
@@ -11,7 +12,7 @@ using namespace fp4kv;
 namespace {
 
 constexpr int kTarget = 2048;   // GQA waves: 8 single-wave groups per CU on 256 CUs
-constexpr int kTargetMla = 1024;  // MLA: one wave per SIMD
+constexpr int kMlaWorkgroups = 256;   // MLA: one eight-wave workgroup per CU
 constexpr int kMinTilesPerSplit = 4;   // the partial kernels' minimum share (kMinTilesPerWave)
 constexpr int kTile = 128;
 
@@ -52,72 +53,49 @@ int check_pointers(const fp4kv_cache *c) {
   return FP4KV_OK;
 }
 
-struct SplitPlan {
-  int n_split, tiles_per_split;
-};
-
-// units: waves per split (GQA: batch * Hkv; MLA: batch * query-head groups of 16);
-// target: waves to aim for (GQA: 8 single-wave groups per CU; MLA: one wave per SIMD)
-SplitPlan plan_splits(long units, int max_len, int page_size, long target) {
-  int max_tiles = (max_len + kTile - 1) / kTile;
-  if (max_tiles < 1) max_tiles = 1;
-  if (units < 1) units = 1;
-  long ns = (target + units - 1) / units;
-  if (ns > max_tiles) ns = max_tiles;
-  if (ns < 1) ns = 1;
-  int tps = (int)((max_tiles + ns - 1) / ns);
-  if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit < max_tiles ? kMinTilesPerSplit : max_tiles;
-  // a split's page ids are staged in LDS by the decode kernel
-  const int pages_per_tile = page_size >= kTile ? 1 : kTile / page_size;
-  if (tps * pages_per_tile > kMaxSplitPages) tps = kMaxSplitPages / pages_per_tile;
-  SplitPlan p;
-  p.tiles_per_split = tps;
-  p.n_split = (max_tiles + tps - 1) / tps;
-  return p;
+// Shares of the balanced partition (GQA: one wave each; MLA: one eight-wave workgroup per
+// group of 64 query heads each).  Each share takes an equal part of all 128-token tiles of the
+// batch (computed on the device from seq_lens).  The most a launch uses: GQA kTarget waves,
+// MLA kMlaWorkgroups workgroups.
+// The environment variable FP4KV_MAX_SHARES (a positive integer) lowers that maximum, e.g. to
+// leave compute units to work on other streams.
+long max_shares(const fp4kv_cache *c, int hq) {
+  long w = kTarget;
+  if (c->attn == FP4KV_MLA) {
+    const long nhg = hq / 16 > 0 ? hq / 16 : 1;
+    w = kMlaWorkgroups / ((nhg + 3) / 4);
+  }
+  if (const char *env = getenv("FP4KV_MAX_SHARES")) {
+    const long cap = strtol(env, nullptr, 10);
+    if (cap > 0 && cap < w) w = cap;
+  }
+  return w > 0 ? w : 1;
 }
 
-// GQA: waves of the balanced partition.  Each wave takes an equal share of all tiles of
-// the batch (computed on the device from seq_lens); at most kTarget waves, but enough that
-// no share exceeds the page ids a wave stages in LDS, and no more than shares of
-// kMinTilesPerSplit tiles of the largest possible batch.
-long plan_waves(long units, int max_len, int page_size) {
+// Shares a decode launch plans: the most a launch uses, but no more than shares of
+// kMinTilesPerSplit tiles of the largest batch the block table can name (the device count
+// follows the actual lengths and never exceeds this).  units: GQA batch * Hkv, MLA batch.
+long plan_shares(const fp4kv_cache *c, long units, int hq, long max_len) {
   long max_tiles = (max_len + kTile - 1) / kTile;
   if (max_tiles < 1) max_tiles = 1;
   if (units < 1) units = 1;
-  const long pages_per_tile = page_size >= kTile ? 1 : kTile / page_size;
-  const long max_share = kMaxSplitPages / pages_per_tile;
-  const long all = units * max_tiles;
-  long w = kTarget;
-  const long lds_min = (all + max_share - 1) / max_share;
-  if (w < lds_min) w = lds_min;
-  const long useful = (all + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
-  if (w > useful) w = useful;
-  return w < 1 ? 1 : w;
+  const long useful = (units * max_tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
+  const long w = max_shares(c, hq);
+  return w < useful ? w : (useful < 1 ? 1 : useful);
 }
 
-SplitPlan plan_for(const fp4kv_cache *c, int batch, int hq, int max_len) {
-  const long b = batch > 0 ? batch : 1;
-  if (c->attn == FP4KV_MLA) return plan_splits(b * (hq / 16 > 0 ? hq / 16 : 1), max_len, c->page_size, kTargetMla);
-  SplitPlan p;
-  const long w = plan_waves(b * c->num_kv_heads, max_len, c->page_size);
-  p.n_split = w > 0x3FFFFFFFL ? -1 : (int)w;   // -1: batch too large for one launch
-  p.tiles_per_split = 0;
-  return p;
-}
+long units_of(const fp4kv_cache *c, long batch) { return c->attn == FP4KV_MLA ? batch : batch * c->num_kv_heads; }
 
-// Workspace: MLA [batch * hq][n_split] partial rows; GQA (n_waves + batch * Hkv) slots of
-// `group` partial rows, then the per-unit slot ranges.  A partial row is d + 2 floats.
-size_t workspace_for(const fp4kv_cache *c, int batch, int hq, int max_len, SplitPlan *out, int q_len = 1) {
-  SplitPlan p = plan_for(c, batch, hq, max_len);
-  if (out) *out = p;
-  if (p.n_split < 0) return 0;
-  if (c->attn == FP4KV_MLA) {
-    size_t rows = (size_t)batch * hq * p.n_split;
-    return rows * ((size_t)c->head_dim + 2) * sizeof(float);
-  }
-  const size_t units = (size_t)batch * c->num_kv_heads;
-  const size_t rows = ((size_t)p.n_split + units) * (size_t)(hq / c->num_kv_heads) * (size_t)q_len;
-  return rows * ((size_t)c->head_dim + 2) * sizeof(float) + units * 2 * sizeof(int32_t);
+// Workspace for `shares` shares: (shares + units) partial slots -- GQA `group * q_len` rows each,
+// MLA `hq` rows each -- of d + 2 floats, then the per-unit slot ranges (two int32 per unit).
+size_t workspace_rows(const fp4kv_cache *c, long batch, int hq, long shares, int q_len) {
+  const size_t units = (size_t)units_of(c, batch);
+  const size_t per = c->attn == FP4KV_MLA ? (size_t)hq : (size_t)(hq / c->num_kv_heads) * (size_t)q_len;
+  return ((size_t)shares + units) * per;
+}
+size_t workspace_size(const fp4kv_cache *c, long batch, int hq, long shares, int q_len) {
+  const size_t rows = workspace_rows(c, batch, hq, shares, q_len);
+  return rows * ((size_t)c->head_dim + 2) * sizeof(float) + (size_t)units_of(c, batch) * 2 * sizeof(int32_t);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP; }
@@ -152,12 +130,11 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
     if (need_q && !q) return FP4KV_ERR_INVALID_ARG;
     if (need_out && !out) return FP4KV_ERR_INVALID_ARG;
   }
-  // partial slots are numbered in int32 (GQA: n_waves + batch * Hkv)
+  // partial slots are numbered in int32 (shares + units)
   if ((long)batch * c->num_kv_heads > 0x3FFFFFFFL) return FP4KV_ERR_INVALID_ARG;
-  SplitPlan p;
-  size_t need = workspace_for(c, batch, hq, max_pages * c->page_size, &p, q_len);
-  if (p.n_split < 0) return FP4KV_ERR_INVALID_ARG;
-  if (ws_bytes < need) return FP4KV_ERR_WORKSPACE;
+  // the workspace must hold what the size query reports (any launch's need is at most that)
+  if (ws_bytes < workspace_size(c, batch, hq, max_shares(c, hq), q_len)) return FP4KV_ERR_WORKSPACE;
+  const long shares = plan_shares(c, units_of(c, batch), hq, (long)max_pages * c->page_size);
   DecodeArgs &d = *a;
   d.fmt = c->format;
   d.page_size = c->page_size;
@@ -171,10 +148,7 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.num_pages = c->num_pages;
   d.q_bf16 = q_dtype == FP4KV_BF16;
   d.q_len = q_len;
-  const bool mla = c->attn == FP4KV_MLA;
-  d.n_split = mla ? p.n_split : 0;
-  d.tiles_per_split = mla ? p.tiles_per_split : 0;
-  d.n_waves = mla ? 0 : p.n_split;
+  d.n_waves = (int)shares;
   d.softmax_scale = softmax_scale;
   const float l2d = (float)(1.4426950408889634 / (double)c->head_dim);
   const float l2 = (float)1.4426950408889634;
@@ -191,11 +165,10 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.q = q;
   d.block_table = block_table;
   d.seq_lens = seq_lens;
-  const size_t rows = mla ? (size_t)batch * hq * p.n_split
-                         : ((size_t)p.n_split + (size_t)batch * c->num_kv_heads) * (size_t)group * q_len;
+  const size_t rows = workspace_rows(c, batch, hq, shares, q_len);
   d.ws_o = (float *)ws;
   d.ws_ml = (float *)ws + rows * (size_t)c->head_dim;
-  d.ws_meta = mla ? nullptr : (int32_t *)(d.ws_ml + rows * 2);
+  d.ws_meta = (int32_t *)(d.ws_ml + rows * 2);
   d.out = out;
   d.zero_blocks = zero;
   return FP4KV_OK;
@@ -282,7 +255,7 @@ int kv_quant_append(const fp4kv_cache *c, const void *k_new, const void *v_new, 
 
 size_t fp4_decode_workspace_bytes(const fp4kv_cache *c, int batch, int num_q_heads, int max_seq_len) {
   if (check_shape(c) != FP4KV_OK || batch < 0 || num_q_heads <= 0 || max_seq_len < 0) return 0;
-  return workspace_for(c, batch, num_q_heads, max_seq_len, nullptr);
+  return workspace_size(c, batch, num_q_heads, max_shares(c, num_q_heads), 1);
 }
 
 int fp4_decode_partials(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int num_q_heads,
@@ -327,7 +300,7 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
 size_t fp4_decode_multi_workspace_bytes(const fp4kv_cache *c, int batch, int q_len, int num_q_heads,
                                         int max_seq_len) {
   if (check_shape(c) != FP4KV_OK || batch < 0 || q_len < 1 || num_q_heads <= 0 || max_seq_len < 0) return 0;
-  return workspace_for(c, batch, num_q_heads, max_seq_len, nullptr, q_len);
+  return workspace_size(c, batch, num_q_heads, max_shares(c, num_q_heads), q_len);
 }
 
 int fp4_decode_attention_multi(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int q_len,
@@ -355,15 +328,14 @@ int fp4kv_cache_read(const fp4kv_cache *c, int batch, int num_q_heads, const int
                        1.0f, nullptr, &dummy, ~(size_t)0, nullptr, false, false, &a);
   if (st) return st;
   if (c->attn != FP4KV_GQA) return FP4KV_ERR_UNSUPPORTED;
-  if (batch > 0 && (!sink || sink_words < (size_t)a.n_waves * 64)) return FP4KV_ERR_INVALID_ARG;
+  if (batch > 0 && (!sink || sink_words < (size_t)max_shares(c, num_q_heads) * 64)) return FP4KV_ERR_INVALID_ARG;
   return to_status(launch_cache_read(a, sink, (hipStream_t)stream));
 }
 
 size_t fp4kv_cache_read_sink_words(const fp4kv_cache *c, int batch, int num_q_heads, int max_seq_len) {
   if (check_shape(c) != FP4KV_OK || c->attn != FP4KV_GQA || batch < 0 || num_q_heads <= 0 || max_seq_len < 0)
     return 0;
-  SplitPlan p = plan_for(c, batch, num_q_heads, max_seq_len);
-  return p.n_split < 0 ? 0 : (size_t)p.n_split * 64;
+  return (size_t)max_shares(c, num_q_heads) * 64;
 }
 
 int fp4kv_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {

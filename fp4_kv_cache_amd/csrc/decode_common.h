@@ -84,4 +84,127 @@ __device__ __forceinline__ uint32_t byte_of(const uint4 &u, int k) {
   return (w >> (8 * (k & 3))) & 0xFFu;
 }
 
+// ---------------- balanced partition of the work ----------------
+// The work of one launch is the list of all 128-token tiles of all (sequence, KV head)
+// units (MLA: one latent head, so a unit is a sequence), in the order u = b * Hkv + kvh,
+// tiles in sequence order within a unit.  Wave i of
+// the W waves that get work takes tiles [floor(i T / W), floor((i+1) T / W)) of this list
+// (T tiles in all), so every wave streams the same number of tiles however ragged the
+// sequence lengths are.  A wave whose range crosses unit boundaries writes one partial
+// per unit it touches, into slot i + u: the ranges are ordered like the units, so no two
+// (wave, unit) pairs share a slot and the slots of one unit are consecutive.
+constexpr int kMinTilesPerWave = 4;
+
+// A sequence's tiles of 128 tokens.
+__device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int b) { return (seq_len_clamped(a, b) + 127) >> 7; }
+
+__device__ __forceinline__ long uni_l(long v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)(v & 0xffffffffL));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+  return (long)(((unsigned long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// The wave's share: the current unit (b, kvh) with its n tiles starting at flattened
+// index ustart, and the flattened range [x, x1) still to do; L is sequence b's length.
+struct Share {
+  long x, x1, ustart, total;
+  int b, kvh, n, waves, L;
+};
+
+// Wave count W and total T as every kernel of a launch computes them.
+__device__ __forceinline__ void work_total(const DecodeArgs &a, int lane, long &total, int &waves) {
+  long t = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64)
+    if (b0 + lane < a.batch) t += seq_tiles(a, b0 + lane);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+  total = uni_l(t * a.hkv);
+  const long useful = (total + kMinTilesPerWave - 1) / kMinTilesPerWave;
+  waves = (int)(useful < (long)a.n_waves ? useful : (long)a.n_waves);
+}
+
+// Wave that holds flattened tile x.
+__device__ __forceinline__ long owner_of(long x, long total, int waves) {
+  return ((x + 1) * waves + total - 1) / total - 1;
+}
+
+// Finds the wave's share; false when it has no tiles.
+__device__ inline bool find_share(const DecodeArgs &a, int wave, int lane, Share &s) {
+  if (a.batch <= 64) {
+    // one pass: lane b holds sequence b's length; the total is the scan's last entry
+    const int len = lane < a.batch ? seq_len_clamped(a, lane) : 0;
+    const int t = (len + 127) >> 7;
+    int incl = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    s.total = uni_l((long)__shfl(incl, 63) * a.hkv);
+    const long useful = (s.total + kMinTilesPerWave - 1) / kMinTilesPerWave;
+    s.waves = (int)(useful < (long)a.n_waves ? useful : (long)a.n_waves);
+    if (wave >= s.waves) return false;
+    const long T = s.total, W = s.waves;
+    s.x = wave * T / W;
+    s.x1 = (wave + 1) * T / W;
+    const unsigned long long m = __ballot((long)incl * a.hkv > s.x);
+    const int j = __builtin_ctzll(m);   // m != 0: x < T
+    const int n = __builtin_amdgcn_readfirstlane(__shfl(t, j));
+    const long before = uni_l((long)__shfl(incl, j) - n);   // tiles of sequences < b
+    s.b = j;
+    s.n = n;
+    s.L = __builtin_amdgcn_readfirstlane(__shfl(len, j));
+    s.kvh = (int)((s.x - before * a.hkv) / n);
+    s.ustart = before * a.hkv + (long)s.kvh * n;
+    return true;
+  }
+  work_total(a, lane, s.total, s.waves);
+  if (wave >= s.waves) return false;
+  const long T = s.total, W = s.waves;
+  s.x = wave * T / W;
+  s.x1 = (wave + 1) * T / W;
+  // the sequence whose units hold tile x: scan the tile counts 64 sequences at a time
+  long carry = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int len = b0 + lane < a.batch ? seq_len_clamped(a, b0 + lane) : 0;
+    const int t = (len + 127) >> 7;
+    int incl = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    const unsigned long long m = __ballot((carry + incl) * a.hkv > s.x);
+    if (m) {
+      const int j = __builtin_ctzll(m);
+      const int n = __builtin_amdgcn_readfirstlane(__shfl(t, j));
+      const long before = uni_l(carry + __shfl(incl, j) - n);   // tiles of sequences < b
+      s.b = b0 + j;
+      s.n = n;
+      s.L = __builtin_amdgcn_readfirstlane(__shfl(len, j));
+      s.kvh = (int)((s.x - before * a.hkv) / n);
+      s.ustart = before * a.hkv + (long)s.kvh * n;
+      return true;
+    }
+    carry += __shfl(incl, 63);
+  }
+  return false;   // not reached: x < T
+}
+
+// Moves a share past the unit that ends at flattened tile uend to the next unit that has
+// tiles; false when the share ends there.
+__device__ inline bool next_unit(const DecodeArgs &a, Share &s, long uend) {
+  if (s.x1 <= uend) return false;
+  s.x = s.ustart = uend;
+  if (++s.kvh == a.hkv) {
+    s.kvh = 0;
+    do {
+      if (++s.b >= a.batch) return false;
+      s.L = seq_len_clamped(a, s.b);
+      s.n = (s.L + 127) >> 7;
+    } while (s.n == 0);
+  }
+  return true;
+}
+
 }  // namespace fp4kv

@@ -142,112 +142,6 @@ __device__ __forceinline__ void load_v(const DecodeArgs &a, Tile &v, const int *
 __device__ __forceinline__ int sk_index(int tok, int par) { return tok * 2 + par + 2 * (tok >> 5); }
 
 
-// ---------------- balanced partition of the work ----------------
-// The work of one launch is the list of all 128-token tiles of all (sequence, KV head)
-// units, in the order u = b * Hkv + kvh, tiles in sequence order within a unit.  Wave i of
-// the W waves that get work takes tiles [floor(i T / W), floor((i+1) T / W)) of this list
-// (T tiles in all), so every wave streams the same number of tiles however ragged the
-// sequence lengths are.  A wave whose range crosses unit boundaries writes one partial
-// per unit it touches, into slot i + u: the ranges are ordered like the units, so no two
-// (wave, unit) pairs share a slot and the slots of one unit are consecutive.
-constexpr int kMinTilesPerWave = 4;
-
-// A sequence's tiles of 128 tokens.
-__device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int b) { return (seq_len_clamped(a, b) + 127) >> 7; }
-
-__device__ __forceinline__ long uni_l(long v) {
-  const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)(v & 0xffffffffL));
-  const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
-  return (long)(((unsigned long)(unsigned)hi << 32) | (unsigned)lo);
-}
-
-// The wave's share: the current unit (b, kvh) with its n tiles starting at flattened
-// index ustart, and the flattened range [x, x1) still to do; L is sequence b's length.
-struct Share {
-  long x, x1, ustart, total;
-  int b, kvh, n, waves, L;
-};
-
-// Wave count W and total T as every kernel of a launch computes them.
-__device__ __forceinline__ void work_total(const DecodeArgs &a, int lane, long &total, int &waves) {
-  long t = 0;
-  for (int b0 = 0; b0 < a.batch; b0 += 64)
-    if (b0 + lane < a.batch) t += seq_tiles(a, b0 + lane);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
-  total = uni_l(t * a.hkv);
-  const long useful = (total + kMinTilesPerWave - 1) / kMinTilesPerWave;
-  waves = (int)(useful < (long)a.n_waves ? useful : (long)a.n_waves);
-}
-
-// Wave that holds flattened tile x.
-__device__ __forceinline__ long owner_of(long x, long total, int waves) {
-  return ((x + 1) * waves + total - 1) / total - 1;
-}
-
-// Finds the wave's share; false when it has no tiles.
-__device__ bool find_share(const DecodeArgs &a, int wave, int lane, Share &s) {
-  if (a.batch <= 64) {
-    // one pass: lane b holds sequence b's length; the total is the scan's last entry
-    const int len = lane < a.batch ? seq_len_clamped(a, lane) : 0;
-    const int t = (len + 127) >> 7;
-    int incl = t;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
-    s.total = uni_l((long)__shfl(incl, 63) * a.hkv);
-    const long useful = (s.total + kMinTilesPerWave - 1) / kMinTilesPerWave;
-    s.waves = (int)(useful < (long)a.n_waves ? useful : (long)a.n_waves);
-    if (wave >= s.waves) return false;
-    const long T = s.total, W = s.waves;
-    s.x = wave * T / W;
-    s.x1 = (wave + 1) * T / W;
-    const unsigned long long m = __ballot((long)incl * a.hkv > s.x);
-    const int j = __builtin_ctzll(m);   // m != 0: x < T
-    const int n = __builtin_amdgcn_readfirstlane(__shfl(t, j));
-    const long before = uni_l((long)__shfl(incl, j) - n);   // tiles of sequences < b
-    s.b = j;
-    s.n = n;
-    s.L = __builtin_amdgcn_readfirstlane(__shfl(len, j));
-    s.kvh = (int)((s.x - before * a.hkv) / n);
-    s.ustart = before * a.hkv + (long)s.kvh * n;
-    return true;
-  }
-  work_total(a, lane, s.total, s.waves);
-  if (wave >= s.waves) return false;
-  const long T = s.total, W = s.waves;
-  s.x = wave * T / W;
-  s.x1 = (wave + 1) * T / W;
-  // the sequence whose units hold tile x: scan the tile counts 64 sequences at a time
-  long carry = 0;
-  for (int b0 = 0; b0 < a.batch; b0 += 64) {
-    const int len = b0 + lane < a.batch ? seq_len_clamped(a, b0 + lane) : 0;
-    const int t = (len + 127) >> 7;
-    int incl = t;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
-    const unsigned long long m = __ballot((carry + incl) * a.hkv > s.x);
-    if (m) {
-      const int j = __builtin_ctzll(m);
-      const int n = __builtin_amdgcn_readfirstlane(__shfl(t, j));
-      const long before = uni_l(carry + __shfl(incl, j) - n);   // tiles of sequences < b
-      s.b = b0 + j;
-      s.n = n;
-      s.L = __builtin_amdgcn_readfirstlane(__shfl(len, j));
-      s.kvh = (int)((s.x - before * a.hkv) / n);
-      s.ustart = before * a.hkv + (long)s.kvh * n;
-      return true;
-    }
-    carry += __shfl(incl, 63);
-  }
-  return false;   // not reached: x < T
-}
-
 // Query rows of one KV head: GV "virtual heads" = (query token j, query head g) pairs,
 // v = j * group + g (one query token per sequence: v = g).  One 16-column MFMA holds VS of
 // them (Q1 and Q2 rows; NVFP4 also both block parities), so GV > VS runs RS row sets on
@@ -267,6 +161,7 @@ void gqa_partials(DecodeArgs a) {
   constexpr int B = FMT == kFmtNV ? 16 : 32;   // scale block
   constexpr int NBLK = D / B;
   constexpr int NPT = P >= 128 ? 1 : 128 / P;  // pages touched by a 128-token tile
+  constexpr int CAPG = kMaxSplitPages / NPT;   // tiles whose page ids the LDS window holds
   static_assert(RS <= 2, "at most two row sets");
   static_assert(P >= 16 && (P % B) == 0, "page size");
 
@@ -280,8 +175,9 @@ void gqa_partials(DecodeArgs a) {
   __shared__ float qg[2][GV];
   __shared__ uint32_t lut[256];                // E4M3 value scale -> four E8M0 pass bytes
   __shared__ float4 sk[128 * 2 + 8];           // NVFP4 key scales of the tile (sk_index)
-  // physical page ids of the segment's tiles: entry (tile - tb) * NPT + j is logical page
-  // tile * 128 / P + j (clamped to the sequence), so per-tile lookups are LDS reads
+  // physical page ids of the segment's tiles: entry ((tile - tb) % CAPG) * NPT + j is logical
+  // page tile * 128 / P + j (clamped to the sequence), so per-tile lookups are LDS reads; a
+  // segment longer than CAPG tiles re-stages the window every CAPG tiles
   __shared__ int pgl[kMaxSplitPages];
 
   // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale), for NVFP4 values:
@@ -338,8 +234,13 @@ void gqa_partials(DecodeArgs a) {
     for (int i = 0; i < EPL; i++) y[i] = y[i] * sm[i];
   };
   load_q(0);
-  for (int e = lane; e < (te - tb) * NPT; e += 64)
-    pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
+  // page ids of tiles t0 .. t0 + CAPG - 1 ((t0 - tb) a multiple of CAPG)
+  auto stage_ids = [&](int t0) {
+    const int cnt = min(CAPG, te - t0) * NPT;
+    for (int e = lane; e < cnt; e += 64)
+      pgl[e] = phys_page(a, b, ((t0 + e / NPT) * 128) / P + e % NPT, last_lp);
+  };
+  stage_ids(tb);
   __syncthreads();
 
   // the first tile's keys and values are in flight while the query is prepared
@@ -500,10 +401,15 @@ void gqa_partials(DecodeArgs a) {
   // start, the values of tile + 1 into vt once P.V has read it.
   auto body = [&](Tile &kt, Tile &vt, Tile &kn, int tile) {
     const int tok0 = tile * 128;
+    if (tile + 1 < te && (tile + 1 - tb) % CAPG == 0) {
+      // window edge: the ids of this tile were last read by the previous tile's loads
+      stage_ids(tile + 1);
+      __syncthreads();
+    }
     {
       const bool live = tile + 1 < te;
       const int tn = live ? tile + 1 : tile;
-      load_k<FMT, P>(a, kn, pgl + (tn - tb) * NPT, kvh, tn * 128, lane, live);
+      load_k<FMT, P>(a, kn, pgl + ((tn - tb) % CAPG) * NPT, kvh, tn * 128, lane, live);
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FMT == kFmtNV) {
@@ -677,7 +583,7 @@ void gqa_partials(DecodeArgs a) {
     {
       const bool live = tile + 1 < te;
       const int tn = live ? tile + 1 : tile;
-      load_v<FMT, P>(a, vt, pgl + (tn - tb) * NPT, kvh, tn * 128, lane, live);
+      load_v<FMT, P>(a, vt, pgl + ((tn - tb) % CAPG) * NPT, kvh, tn * 128, lane, live);
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FMT == kFmtNV) __syncthreads();   // key-scale stage is rewritten by the next tile
@@ -743,6 +649,7 @@ template <int FMT, int P>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_read_only(DecodeArgs a,
                                                                                               uint32_t *sink) {
   constexpr int NPT = P >= 128 ? 1 : 128 / P;
+  constexpr int CAPG = kMaxSplitPages / NPT;
   const int lane = threadIdx.x;
   const int wave = blockIdx.x;
   Share sh;
@@ -760,20 +667,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int tb = (int)(sh.x - sh.ustart);
     const int te = (int)((sh.x1 < uend ? sh.x1 : uend) - sh.ustart);
     const int last_lp = min((L - 1) / P, a.max_pages - 1);
+    auto stage_ids = [&](int t0) {
+      const int cnt = min(CAPG, te - t0) * NPT;
+      for (int e = lane; e < cnt; e += 64)
+        pgl[e] = phys_page(a, b, ((t0 + e / NPT) * 128) / P + e % NPT, last_lp);
+    };
     __syncthreads();
-    for (int e = lane; e < (te - tb) * NPT; e += 64)
-      pgl[e] = phys_page(a, b, ((tb + e / NPT) * 128) / P + e % NPT, last_lp);
+    stage_ids(tb);
     __syncthreads();
     Tile kt, kn, vt;
     load_k<FMT, P>(a, kt, pgl, kvh, tb * 128, lane, true);
     load_v<FMT, P>(a, vt, pgl, kvh, tb * 128, lane, true);
     for (int tile = tb; tile < te; tile++) {
+      if (tile + 1 < te && (tile + 1 - tb) % CAPG == 0) {
+        stage_ids(tile + 1);
+        __syncthreads();
+      }
       const bool live = tile + 1 < te;
       const int tn = live ? tile + 1 : tile;
-      load_k<FMT, P>(a, kn, pgl + (tn - tb) * NPT, kvh, tn * 128, lane, live);
+      load_k<FMT, P>(a, kn, pgl + ((tn - tb) % CAPG) * NPT, kvh, tn * 128, lane, live);
       fold(kt);
       fold(vt);
-      load_v<FMT, P>(a, vt, pgl + (tn - tb) * NPT, kvh, tn * 128, lane, live);
+      load_v<FMT, P>(a, vt, pgl + ((tn - tb) % CAPG) * NPT, kvh, tn * 128, lane, live);
       kt = kn;
     }
     if (sh.x1 <= uend) break;

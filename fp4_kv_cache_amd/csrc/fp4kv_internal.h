@@ -8,8 +8,8 @@
 
 namespace fp4kv {
 
-// Page-id entries one decode workgroup stages in LDS: a split (GQA: a wave's share of one
-// sequence) covers at most kMaxSplitPages / max(1, 128 / page_size) tiles of 128 tokens.
+// Page-id entries a decode workgroup holds in LDS at once: the ids of kMaxSplitPages /
+// max(1, 128 / page_size) consecutive tiles of its segment, re-staged at every window edge.
 constexpr int kMaxSplitPages = 512;
 
 struct AppendArgs {
@@ -25,8 +25,8 @@ struct AppendArgs {
 struct DecodeArgs {
   int fmt, page_size, hkv, group, hq, d, rope_dim, batch, max_pages, num_pages, q_bf16;
   int q_len;             // GQA: query tokens per sequence (causal), 1 for ordinary decode
-  int n_split, tiles_per_split;   // MLA: splits per (sequence, head group) and their tiles
-  int n_waves;                    // GQA: waves of the balanced partition (an upper bound)
+  int n_waves;           // shares of the balanced partition (an upper bound; GQA one wave each,
+                         // MLA one workgroup per group of 64 query heads each)
   float softmax_scale;
   float coef;            // fl32(softmax_scale * fl32(log2(e) / head_dim))
   float coef_rope;       // fl32(softmax_scale * fl32(log2(e)))
@@ -35,9 +35,10 @@ struct DecodeArgs {
   const float *gk, *gv, *qs;
   const void *q;
   const int32_t *block_table, *seq_lens;
-  float *ws_o;           // MLA: [batch * hq][n_split][d]; GQA: [n_waves + batch * hkv][group][d]
+  float *ws_o;           // partial slots [n_waves + units][rows][d]: GQA units = batch * hkv,
+                         // rows = group * q_len; MLA units = batch, rows = hq
   float *ws_ml;          // same rows, [2] each
-  int32_t *ws_meta;      // GQA: [batch * hkv][2] = first partial slot of the unit, partial count
+  int32_t *ws_meta;      // [units][2] = first partial slot of the unit, partial count
   float *out;            // [batch * hq][d]
   int32_t *zero_blocks;  // nullable
 };

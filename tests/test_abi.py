@@ -113,12 +113,35 @@ def test_workspace_and_group_checks(lib):
 
 def test_split_plan_sizes(lib):
     c = _desc(num_kv_heads=8)
-    # Qwen3-4B shape: 16 x 8 (sequence, KV head) units; 2048 waves share the tiles, so the
-    # workspace holds 2048 + 128 slots of 4 partial rows (128 + 2 floats) and 128 slot ranges
+    # Qwen3-4B shape: 16 x 8 (sequence, KV head) units; at most 2048 waves share the tiles, so
+    # the workspace holds 2048 + 128 slots of 4 partial rows (128 + 2 floats) and 128 slot ranges
     assert L.fp4_decode_workspace_bytes(c, 16, 32, 32768) == (2048 + 128) * 4 * 130 * 4 + 128 * 8
-    # tiny batches: no more waves than shares of 4 tiles (2 units x 32 tiles -> 16 waves)
     c2 = _desc(num_kv_heads=2)
-    assert L.fp4_decode_workspace_bytes(c2, 1, 8, 4096) == (16 + 2) * 4 * 130 * 4 + 2 * 8
+    assert L.fp4_decode_workspace_bytes(c2, 1, 8, 4096) == (2048 + 2) * 4 * 130 * 4 + 2 * 8
+    # MLA: at most 128 shares (256 workgroups of 64 query heads for 128 heads) + 32 sequences,
+    # 128 partial rows of 512 + 2 floats each, and 32 slot ranges
+    cm = _desc(attn=1, num_kv_heads=1, head_dim=512, rope_dim=64, page_size=64)
+    assert L.fp4_decode_workspace_bytes(cm, 32, 128, 16384) == (128 + 32) * 128 * 514 * 4 + 32 * 8
+
+
+@pytest.mark.parametrize("attn", [0, 1])
+def test_workspace_does_not_depend_on_max_seq_len(lib, attn):
+    """The size query covers every block table: a caller passing any bound on the sequence
+    lengths -- also one below max_pages_per_seq * page_size, which the decode call plans from
+    -- gets a workspace the decode call accepts (its need never exceeds this size)."""
+    if attn:
+        c = _desc(attn=1, num_kv_heads=1, head_dim=512, rope_dim=64, page_size=64)
+        hq = 128
+    else:
+        c = _desc(num_kv_heads=2, page_size=64)
+        hq = 8
+    sizes = {L.fp4_decode_workspace_bytes(c, 1, hq, m) for m in (0, 1, 4096, 65 * 64, 1 << 24)}
+    assert len(sizes) == 1 and sizes.pop() > 0
+    if not attn:
+        multi = {L.fp4_decode_multi_workspace_bytes(c, 1, 2, hq, m) for m in (1, 4096, 65 * 64)}
+        assert len(multi) == 1
+        words = {L.fp4kv_cache_read_sink_words(c, 1, hq, m) for m in (1, 4096, 65 * 64)}
+        assert len(words) == 1
 
 
 def test_header_is_plain_c():

@@ -289,8 +289,8 @@ def test_decode_all_sequences_empty(torch_dev, name):
 
 @pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
 def test_decode_mla_many_splits(torch_dev, name):
-    """One sequence with few head groups is split into more parts than the MLA merge loads
-    at once (12 splits of 4 tiles for 6000 tokens and 16 heads), so the merge takes its
+    """One sequence with few head groups is split into more shares than the MLA merge loads
+    at once (12 shares of 3-4 tiles for 6000 tokens and 16 heads), so the merge takes its
     general path; the output still matches the oracle."""
     lens = np.array([6000], np.int32)
     w = W.workload(name, batch=1, hq=16)
@@ -370,3 +370,54 @@ def test_decode_mla_ragged(torch_dev, name):
     built = harness.build(w, lens=lens)
     worst, worst_ref, zg = compare_mla(built, tol=TOL)
     say("mla: max err vs oracle %.3g, vs fp64 attention %.3g, zero blocks %d" % (worst, worst_ref, zg))
+
+
+@pytest.mark.parametrize("name,lens,hq,page", [
+    # GQA NVFP4, 16-token pages: the window holds 64 tiles; one share of 71 tiles per unit
+    ("tiny", [9000], 8, 16),
+    # GQA MXFP4, 64-token pages: the window holds 256 tiles; one wave streams 4 units of 259 tiles
+    ("qwen3_30b_a3b", [33100], 32, 64),
+    # MLA, 32-token pages: the window holds 128 tiles; one share of 134 tiles (and a second sequence)
+    ("mla", [17100, 300], 16, 32),
+    ("mla_mxfp4", [17100, 300], 16, 32),
+])
+def test_decode_long_shares_restage_page_ids(torch_dev, name, lens, hq, page, monkeypatch):
+    """With the decode limited to one share (FP4KV_MAX_SHARES=1) a share runs past the page-id
+    window the kernels hold in LDS and re-stages it; the output still matches the oracle."""
+    monkeypatch.setenv("FP4KV_MAX_SHARES", "1")
+    lens = np.array(lens, np.int32)
+    w = W.workload(name, batch=len(lens), hq=hq, page=page)
+    say("decode long shares %s" % name, lens.tolist())
+    built = harness.build(w, lens=lens)
+    if w["attn"] == 0:
+        pairs = [(0, h) for h in range(min(w["hkv"], 2))] + [(0, w["hkv"] - 1)]
+        worst, worst_ref, zg, zo = compare_gqa(built, pairs=pairs, tol=TOL)
+    else:
+        worst, worst_ref, zg = compare_mla(built, tol=TOL)
+    say("long shares: max err vs oracle %.3g, vs fp64 %.3g" % (worst, worst_ref))
+
+
+@pytest.mark.parametrize("name", ["qwen3_4b", "mla"])
+def test_workspace_from_a_bound_below_the_block_table(torch_dev, name):
+    """The workspace size query takes any bound on the sequence lengths: a workspace sized for
+    max(seq_lens) is accepted by a decode whose block table names far more pages."""
+    import torch
+    lens = np.array([130, 700], np.int32)
+    w = W.workload(name, batch=len(lens))
+    say("workspace bound", name, lens.tolist())
+    built = harness.build(w, lens=lens)
+    wide = np.zeros((len(lens), built.bt_np.shape[1] + 40), np.int32)
+    wide[:, :built.bt_np.shape[1]] = built.bt_np
+    built.bt_np = wide
+    built.bt = torch.from_numpy(wide).to(built.device)
+    q = built.queries()
+    nb = built.cache.workspace_bytes(len(lens), w["hq"], int(lens.max()))
+    ws = torch.empty(nb, dtype=torch.uint8, device=built.device)
+    out = built.cache.decode(q, built.bt, built.seq_lens, W.softmax_scale(w), workspace=ws)
+    ref = built.cache.decode(q, built.bt, built.seq_lens, W.softmax_scale(w))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    if w["attn"] == 0:
+        compare_gqa(built, tol=TOL)
+    else:
+        compare_mla(built, tol=TOL)
