@@ -30,7 +30,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak
-F16_MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 matrix peak
 METRIC = "FP4 paged decode attention: µs/step + KV HBM GB/s (% of 8 TB/s peak)"
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -82,20 +81,10 @@ def read_traffic(w, workload):
 
 def mla_flops_per_token(w):
     """Algorithmic flops per cached token of an MLA decode step: Q.K^T for the Q1 and Q2 rows of
-    every query head over latent + rope channels, P.V over the latent channels."""
-    return 2 * (2 * w["hq"]) * (w["d"] + w["rope"]) + 2 * w["hq"] * w["d"]
-
-
-def mla_matrix_peak_tflops(w):
-    """Dense matrix peak for the MLA decode's contractions, weighted by their algorithmic flops
-    (the peak at which all of them together would run): Q.K^T over the latent on fp16 MFMAs
-    for an NVFP4 latent (its E4M3 2-D tile scales are applied by an exact fp16 widening) and on
-    FP4 MFMAs for MXFP4, the rope part on bf16 MFMAs, P.V on FP4 MFMAs."""
+    every query head over the latent channels, the rope part once per head (it is not
+    quantized, so the dual query does not apply to it), P.V over the latent channels."""
     hq, d, r = w["hq"], w["d"], w["rope"]
-    qk, rope, pv = 2 * (2 * hq) * d, 2 * (2 * hq) * r, 2 * hq * d
-    qk_peak = F16_MFMA_PEAK_TFLOPS if w["fmt"] == 0 else FP4_MFMA_PEAK_TFLOPS
-    t = qk / qk_peak + rope / F16_MFMA_PEAK_TFLOPS + pv / FP4_MFMA_PEAK_TFLOPS
-    return (qk + rope + pv) / t
+    return 2 * (2 * hq) * d + 2 * hq * r + 2 * hq * d
 
 
 def cpu_baseline(w, n_units, budget_s):
@@ -133,11 +122,26 @@ def cpu_baseline(w, n_units, budget_s):
                 t_total += time.perf_counter() - t0
                 done_bytes += L * kv_bytes_per_token_head(w)
                 steps += 1
+    # the same steps with one BLAS thread (the oracle's elementwise work is single-threaded anyway)
+    one_bytes, t_one = 0.0, 0.0
+    with threadpool_limits(limits=1):
+        while t_one < budget_s / 3:
+            for b, h, L, kc, ks, vc, vs, q in prepared[:2]:
+                t0 = time.perf_counter()
+                qq = quantize_query(q, qs[h], w["fmt"])
+                s = A.logits(qq, A.key_dequant_exact(kc, ks, w["fmt"]), gk[h],
+                             A.logit_coeff(W.softmax_scale(w), w["d"]), w["fmt"])
+                A.attend(s, A.value_dequant_exact(vc, vs, w["fmt"], gv[h] if w["fmt"] == 0 else 1.0), L,
+                         w["fmt"])
+                t_one += time.perf_counter() - t0
+                one_bytes += L * kv_bytes_per_token_head(w)
     return {"value": round(done_bytes / t_total / 1e9, 5), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
+            "value_1_thread": round(one_bytes / t_one / 1e9, 5),
             "sample": "%d (sequence, KV head) decode steps over %d of the workload's %d units, at full "
                       "context (%d tokens each); cache quantized once beforehand, untimed; %.1f s of "
-                      "timed CPU work" % (steps, len(prepared), w["batch"] * w["hkv"], int(lens[0]), t_total)}
+                      "timed CPU work with %d BLAS threads, %.1f s with one" % (
+                          steps, len(prepared), w["batch"] * w["hkv"], int(lens[0]), t_total, cores, t_one)}
 
 
 def _cpu_baseline_mla(w, n_units, budget_s, cores):
@@ -171,10 +175,23 @@ def _cpu_baseline_mla(w, n_units, budget_s, cores):
                 t_total += time.perf_counter() - t0
                 done_bytes += L * kv_bytes_per_token_head(w)
                 steps += 1
+    one_bytes, t_one = 0.0, 0.0
+    with threadpool_limits(limits=1):
+        while t_one < budget_s / 3:
+            L, lat, kr, q, qr = prepared[0]
+            t0 = time.perf_counter()
+            qq = quantize_query(q, qs[0], w["fmt"])
+            s = A.logits(qq, lat[:L], gk[0], A.logit_coeff(sc, D), w["fmt"], rope=(qr, kr, A.logit_coeff(sc, 1)))
+            out = A.attend(s, lat * gk[0], L, w["fmt"])["out"]
+            _ = A.fwht_f64(out) / D * qs[0].astype(np.float64)[None, :]
+            t_one += time.perf_counter() - t0
+            one_bytes += L * kv_bytes_per_token_head(w)
     return {"value": round(done_bytes / t_total / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "value_1_thread": round(one_bytes / t_one / 1e9, 5),
             "sample": "%d sequence decode steps (all %d query heads) over %d of the workload's %d sequences, "
                       "full context (%d tokens each); latent quantized once beforehand, untimed; %.1f s of "
-                      "timed CPU work" % (steps, w["hq"], len(prepared), w["batch"], int(lens[0]), t_total)}
+                      "timed CPU work with %d BLAS threads, %.1f s with one" % (
+                          steps, w["hq"], len(prepared), w["batch"], int(lens[0]), t_total, cores, t_one)}
 
 
 def main():
@@ -325,48 +342,55 @@ def main():
     assert torch.isfinite(out).all().item(), "non-finite decode output"
     out_eager = out.clone()
 
-    # The same work replayed from HIP graphs (one graph holds one launch sequence per cache
-    # copy), which removes the host's launch overhead: the step time, and each kernel alone
-    # back to back -- the kernel's average duration as a profiler's kernel trace reports it.
+    # The same work replayed from a HIP graph that holds exactly `steps` launch sequences
+    # (rotating over the cache copies), which removes the host's launch overhead: the step time,
+    # and each kernel alone back to back -- the kernel's average duration as a profiler's kernel
+    # trace reports it.
     nc = len(copies)
-    reps = max(1, args.steps // nc)
 
-    def graph_time(fn):
+    def graph_time(fn, n=None):
+        n = args.steps if n is None else n
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            for i in range(nc):
+            for i in range(n):
                 fn(i)
         # untimed warm-up replays, at least ~30 ms of device time: the first milliseconds of
         # work after the host-side capture run at ramping clocks (the same graph timed first
         # measured ~10% slower than timed again later)
         t_w = time.time()
         while True:
-            for _ in range(8):
-                g.replay()
+            g.replay()
             torch.cuda.synchronize()
             if time.time() - t_w > 0.03:
                 break
         t0, t1 = ev(), ev()
         t0.record()
-        for _ in range(reps):
-            g.replay()
+        g.replay()
         t1.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / (reps * nc) * 1e3, g
+        return t0.elapsed_time(t1) / n * 1e3, g
 
     step_us, g_step = graph_time(step)
-    # every replay recomputes the same step (appending the same token is idempotent): it must
+    # every replay recomputes the same steps (appending the same token is idempotent): it must
     # reproduce the eager output bit for bit
     out.zero_()
     g_step.replay()
     torch.cuda.synchronize()
     assert torch.equal(out, out_eager), "graph replay differs from the eager step"
+    del g_step
     ms_step = step_us * 1e-3
     kv_bytes = float(np.sum(lens.astype(np.float64)) * hkv * kv_bytes_per_token_head(w))
     k_us, _ = graph_time(partials)
     m_us, _ = graph_time(merge)
     a_us, _ = graph_time(append)
+
+    def decode(i):   # fp4_decode_attention alone: partials + merge
+        c = copies[i % len(copies)]
+        L.check(L.fp4_decode_attention(c.desc, q1.data_ptr(), qdt, B, hq, built.bt.data_ptr(), maxp,
+                                       built.seq_lens.data_ptr(), scale, out1.data_ptr(), ws.data_ptr(),
+                                       ws_bytes, None, cur_stream()), "fp4_decode_attention")
+    d_us, _ = graph_time(decode)
     mq_us = graph_time(decode_multi)[0] if QN > 1 else None
 
     # measured streaming-read ceiling of this device (2 GiB, 16-byte non-temporal loads)
@@ -399,14 +423,14 @@ def main():
         pattern_gbps = kv_bytes / (r_us * 1e-6) / 1e9
 
     traffic = read_traffic(w, args.workload)
-    if mla:   # matrix-core bound: algorithmic flops against the flop-weighted dense matrix peak
+    if mla:   # matrix-core bound: algorithmic flops against the dense FP4 matrix peak
         flops = float(np.sum(lens.astype(np.float64))) * mla_flops_per_token(w)
         achieved = flops / (k_us * 1e-6) / 1e12
-        peak = mla_matrix_peak_tflops(w)
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP4_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
                     "flops_per_launch": flops,
-                    "kv_GBps": round(kv_bytes / (k_us * 1e-6) / 1e9, 1)}
+                    "kv_GBps": round(kv_bytes / (k_us * 1e-6) / 1e9, 1),
+                    "kv_frac_of_hbm_peak": round(kv_bytes / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     else:
         # one query token: the partial kernel; several: the whole multi-token decode (partials and
         # merge, no separate entry point for its partials)
@@ -445,6 +469,9 @@ def main():
         "roofline": roofline,
         "breakdown_us": {"decode_partials_kernel": round(k_us, 2), "split_merge_kernel": round(m_us, 2),
                          "kv_append_1_token": round(a_us, 2)},
+        # fp4_decode_attention alone (partials + merge, one launch after the other)
+        "decode_attention": {"us": round(d_us, 2), "kv_GBps": round(kv_bytes / (d_us * 1e-6) / 1e9, 1),
+                             "frac_of_hbm_peak": round(kv_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
         "stream_read_ceiling_GBps": round(stream_gbps, 1),
         **({"multi_token": {"q_len": QN, "decode_us": round(mq_us, 2),
                             "single_token_decode_us": round(k_us + m_us, 2),

@@ -28,18 +28,15 @@ def test_qwen3_4b_bytes_per_step():
     assert int(lens.sum()) * w["hkv"] * bench.kv_bytes_per_token_head(w) == 603979776
 
 
-def test_mla_flops_and_matrix_peak():
+def test_mla_flops_per_step():
     w = W.workload("mla")
-    # Q1 and Q2 rows of 128 heads over 512 latent + 64 rope channels, P.V over 512 channels
-    assert bench.mla_flops_per_token(w) == 2 * 256 * 576 + 2 * 128 * 512
-    # the peak at which those flops would run: latent Q.K^T (2*256*512 flops) on fp16 MFMAs for an
-    # NVFP4 latent (FP4 for MXFP4), rope (2*256*64) on bf16, P.V (2*128*512) on FP4
-    qk, rope, pv = 262144, 32768, 131072
-    nv = (qk + rope + pv) / (qk / 2500.0 + rope / 2500.0 + pv / 10100.0)
-    mx = (qk + rope + pv) / (qk / 10100.0 + rope / 2500.0 + pv / 10100.0)
-    assert bench.mla_matrix_peak_tflops(w) == pytest.approx(nv, rel=1e-12)
-    assert bench.mla_matrix_peak_tflops(W.workload("mla_mxfp4")) == pytest.approx(mx, rel=1e-12)
-    assert 3253 < nv < 3254 and 8185 < mx < 8186
+    # Q1 and Q2 rows of 128 heads over the 512 latent channels, the rope part once per head
+    # (64 channels, unquantized), P.V over the 512 latent channels
+    assert bench.mla_flops_per_token(w) == 2 * 256 * 512 + 2 * 128 * 64 + 2 * 128 * 512
+    lens = W.seq_lens(w)
+    total = float(lens.sum()) * bench.mla_flops_per_token(w)
+    assert 214.7e9 < total < 214.8e9        # 32 x 16384 tokens: 214.7 GFLOP per step
+    assert bench.FP4_MFMA_PEAK_TFLOPS == 10100.0
 
 
 def test_more_than_one_gpu_exits():
