@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "fp4kv_internal.h"
 
 using namespace fp4kv;
@@ -174,6 +176,30 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   return FP4KV_OK;
 }
 
+// Scratch of fp4_decode_attention_noalloc: a file-scope device array, so every GPU the library
+// runs on holds one copy (allocated with the code object, kept until the process ends).  In host
+// code `scratch` names a host-side stand-in, not device memory: its device address is taken once
+// per device with hipGetSymbolAddress and only that address is handed to kernels.
+__device__ __align__(256) uint8_t scratch[FP4KV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first call on that device).
+int scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4KV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FP4KV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP4KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +321,23 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
   hipError_t e = mla ? launch_mla_partials(a, (hipStream_t)stream) : launch_decode_partials(a, (hipStream_t)stream);
   if (e != hipSuccess) return FP4KV_ERR_HIP;
   return to_status(mla ? launch_mla_merge(a, (hipStream_t)stream) : launch_decode_merge(a, (hipStream_t)stream));
+}
+
+int fp4_decode_attention_noalloc(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int num_q_heads,
+                                 const int32_t *block_table, int max_pages_per_seq, const int32_t *seq_lens,
+                                 float softmax_scale, float *out, int32_t *zero_block_count, void *stream) {
+  int st = check_shape(c);
+  if (st) return st;
+  if (batch < 0 || num_q_heads <= 0) return FP4KV_ERR_INVALID_ARG;
+  // the workspace fp4_decode_attention would need must fit the scratch array
+  if (workspace_size(c, batch, num_q_heads, max_shares(c, num_q_heads), 1) > (size_t)FP4KV_NOALLOC_SCRATCH_BYTES)
+    return FP4KV_ERR_WORKSPACE;
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st) return st;
+  return fp4_decode_attention(c, q, q_dtype, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                              softmax_scale, out, ws, (size_t)FP4KV_NOALLOC_SCRATCH_BYTES, zero_block_count,
+                              stream);
 }
 
 size_t fp4_decode_multi_workspace_bytes(const fp4kv_cache *c, int batch, int q_len, int num_q_heads,

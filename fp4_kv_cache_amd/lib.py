@@ -50,6 +50,8 @@ _SIGS = {
     "fp4kv_cache_read": (_c_int, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _vp, _c_int, _vp, _vp, _c_size,
                                   _vp]),
     "fp4kv_cache_read_sink_words": (_c_size, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int]),
+    "fp4_decode_attention_noalloc": (_c_int, [ctypes.POINTER(FP4KVCache), _vp, _c_int, _c_int, _c_int, _vp, _c_int,
+                                              _vp, ctypes.c_float, _vp, _vp, _vp]),
     "fp4_decode_multi_workspace_bytes": (_c_size, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int, _c_int]),
     "fp4_decode_attention_multi": (_c_int, [ctypes.POINTER(FP4KVCache), _vp, _c_int, _c_int, _c_int, _c_int, _vp,
                                             _c_int, _vp, ctypes.c_float, _vp, _vp, _c_size, _vp, _vp]),
@@ -116,6 +118,13 @@ def fp4_decode_merge(cache, batch, num_q_heads, max_pages_per_seq, seq_lens, out
                      workspace_bytes, stream):
     return load().fp4_decode_merge(_ref(cache), batch, num_q_heads, max_pages_per_seq, seq_lens, out,
                                    workspace, workspace_bytes, stream)
+
+
+def fp4_decode_attention_noalloc(cache, q, q_dtype, batch, num_q_heads, block_table, max_pages_per_seq,
+                                 seq_lens, softmax_scale, out, zero_block_count, stream):
+    return load().fp4_decode_attention_noalloc(_ref(cache), q, q_dtype, batch, num_q_heads, block_table,
+                                               max_pages_per_seq, seq_lens, softmax_scale, out,
+                                               zero_block_count, stream)
 
 
 def fp4_decode_multi_workspace_bytes(cache, batch, q_len, num_q_heads, max_seq_len):

@@ -176,6 +176,27 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
                          void *workspace, size_t workspace_bytes, int32_t *zero_block_count,
                          void *stream);
 
+/* fp4_decode_attention without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the split-K partials go to a scratch array of FP4KV_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on, from the first call on that GPU until the process
+ * ends.  The call itself allocates and frees nothing.  It uses the scratch of the current
+ * device (`stream` must belong to that device).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
+ * different streams, or from several host threads) race and give undefined results; calls
+ * ordered on one stream are safe.  The scratch keeps the last call's contents; nothing in it
+ * needs clearing between calls.
+ * Returns FP4KV_ERR_WORKSPACE when fp4_decode_workspace_bytes() for this shape exceeds
+ * FP4KV_NOALLOC_SCRATCH_BYTES (64 MiB: GQA up to about 30,000 (sequence, KV head) units at 4
+ * query heads per KV head; MLA with 128 query heads up to 127 sequences), and
+ * FP4KV_ERR_HIP when the scratch address cannot be obtained; otherwise exactly as
+ * fp4_decode_attention, whose kernels it runs. */
+#define FP4KV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fp4_decode_attention_noalloc(const fp4kv_cache *c, const void *q, int q_dtype, int batch,
+                                 int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
+                                 const int32_t *seq_lens, float softmax_scale, float *out,
+                                 int32_t *zero_block_count, void *stream);
+
 /* Multi-token decode (speculative or multi-token-prediction verification): q_len
  * query tokens per sequence, the q_len newest tokens of each sequence (positions
  * seq_lens[b] - q_len .. seq_lens[b] - 1, already appended to the cache); query j

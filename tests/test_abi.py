@@ -175,3 +175,21 @@ def test_host_entry_points_from_c(lib, tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "FAIL" not in r.stdout
+
+
+def test_noalloc_limit_checked_on_the_host(lib):
+    """fp4_decode_attention_noalloc refuses, before touching the device, a batch whose workspace
+    would not fit its 64 MiB scratch; the stated limits (GQA ~30,000 units at group 4, MLA 127
+    sequences at 128 heads) follow from fp4_decode_workspace_bytes."""
+    limit = 64 << 20
+    c = _desc(num_kv_heads=8)
+    assert L.fp4_decode_workspace_bytes(c, 3700, 32, 4096) <= limit        # 29,600 units
+    assert L.fp4_decode_workspace_bytes(c, 3800, 32, 4096) > limit         # 30,400 units
+    cm = _desc(attn=1, num_kv_heads=1, head_dim=512, rope_dim=64, page_size=64)
+    assert L.fp4_decode_workspace_bytes(cm, 127, 128, 4096) <= limit
+    assert L.fp4_decode_workspace_bytes(cm, 128, 128, 4096) > limit
+    for f in ("k_codes", "k_scales", "v_codes", "v_scales", "stage", "k_tensor_scale", "v_tensor_scale",
+              "k_smooth_inv", "q_smooth"):
+        setattr(c, f, 0x1000)
+    assert L.fp4_decode_attention_noalloc(c, 1, 0, 3800, 32, 1, 16, 1, 0.1, 1, None, None) == L.ERR_WORKSPACE
+    assert L.fp4_decode_attention_noalloc(c, 1, 0, -1, 32, 1, 16, 1, 0.1, 1, None, None) == L.ERR_INVALID_ARG
