@@ -122,11 +122,17 @@ typedef struct fp4kv_cache {
 } fp4kv_cache;
 
 /* Byte sizes of the six cache buffers for descriptor `c` (host pointer), in the
- * order k_codes, k_scales, v_codes, v_scales, stage, k_rope (0 for unused ones).
- * Only the scalar fields of `c` are read.  bytes_out is a host array of 6. */
+ * order k_codes, k_scales, v_codes, v_scales, stage, k_rope (0 for unused ones):
+ * the paged 4-bit microscaling KV cache of "BitDecoding-FP4: Native FP4 KV Cache
+ * Decoding via Algorithm-System Co-Design" (Article Summary) in this library's
+ * layout (above).  Only the scalar fields of `c` are read.  bytes_out is a host
+ * array of 6. */
 int fp4kv_cache_layout(const fp4kv_cache *c, size_t bytes_out[6]);
 
-/* Append new tokens to the cache: the KV-append quantizer.
+/* Append new tokens to the cache: the KV-append quantizer (Outlier-Aware Key
+ * Quantization of "BitDecoding-FP4: Native FP4 KV Cache Decoding via
+ * Algorithm-System Co-Design", Article Summary, and "FP4 KV Cache Done Right",
+ * section "What is actually new in BitDecoding-FP4?").
  *   k_new   [num_tokens][Hkv][head_dim] keys (MLA: the latent), dtype F32 or BF16
  *   v_new   [num_tokens][Hkv][head_dim] values (GQA); NULL for MLA
  *   k_rope_new  bf16 [num_tokens][rope_dim] (MLA), NULL for GQA
@@ -136,8 +142,10 @@ int fp4kv_cache_layout(const fp4kv_cache *c, size_t bytes_out[6]);
  * sequence are contiguous in the batch, in increasing and consecutive
  * positions, and the first of them continues that sequence (its position is
  * the number of tokens the cache already holds for it); a token's slot lies in
- * the page that block_table assigns to its position.  Calls on one stream are
- * applied in order.  Keys: smoothing, FWHT over head_dim, per-block scale
+ * the page that block_table assigns to its position.  Tokens whose slot or
+ * sequence id is out of range are skipped; when that is the first token of a
+ * sequence's chunk, the chunk's open value block is not staged either.  Calls
+ * on one stream are applied in order.  Keys: smoothing, FWHT over head_dim, per-block scale
  * search, E2M1 packing.  Values: channel-wise scales over page-aligned blocks
  * of B tokens; the block holding the last new token of a sequence is
  * re-quantized from the stage on every call, so the bytes equal those of
@@ -147,13 +155,22 @@ int kv_quant_append(const fp4kv_cache *c, const void *k_new, const void *v_new, 
                     const int32_t *positions, const void *k_rope_new, void *stream);
 
 /* Workspace bytes fp4_decode_attention / fp4_decode_partials need for this
- * batch shape (host function; reads only scalar fields of `c`).  max_seq_len is
- * an upper bound of seq_lens (max_pages_per_seq * page_size is always valid).
+ * batch shape (host function; reads only scalar fields of `c`).  The size covers
+ * every block table and every set of lengths: max_seq_len is validated (>= 0)
+ * but does not change it.  The decode calls refuse a smaller workspace with
+ * FP4KV_ERR_WORKSPACE.  The environment variable FP4KV_MAX_SHARES (a positive
+ * integer) lowers the number of shares a decode launch divides the batch's tiles
+ * into -- and with it this size -- e.g. to leave compute units to other streams.
  * Returns 0 on invalid arguments. */
 size_t fp4_decode_workspace_bytes(const fp4kv_cache *c, int batch, int num_q_heads,
                                   int max_seq_len);
 
-/* Decode attention: one query token per sequence against its whole cached context.
+/* Decode attention: one query token per sequence against its whole cached context
+ * ("BitDecoding-FP4: Native FP4 KV Cache Decoding via Algorithm-System
+ * Co-Design", Article Summary: dual-residual FP4 query, FP4 Q.K^T and P.V on the
+ * matrix cores, transposed softmax with underflow-aware FP4 probabilities;
+ * "BitDecoding-FP4 : décodage natif du KV cache FP4", Analyse approfondie:
+ * stacked query rows sharing one cache tile), split-K over the paged blocks.
  *   q          [batch][num_q_heads][head_dim (+ rope_dim for MLA)], dtype q_dtype
  *   block_table i32 [batch][max_pages_per_seq]; seq_lens i32 [batch] (0 allowed,
  *              giving a zero output row; a length is read as clamped to
@@ -226,15 +243,15 @@ int fp4_decode_attention_multi(const fp4kv_cache *c, const void *q, int q_dtype,
  * take the same arguments as fp4_decode_attention and must see the same batch
  * shape and seq_lens.
  *
- * Workspace layout (floats unless stated; W = the wave count the library plans
- * for the batch shape, U = batch * Hkv, g = num_q_heads / Hkv):
- *   GQA  o [W + U][g][head_dim], then (m, l) [W + U][g][2], then i32 (first
- *        slot, count) [U].  The tiles of all (sequence, KV head) units, in the
- *        order u = b * Hkv + kvh, are shared out equally among the waves; the
- *        partials of unit u are the `count` consecutive slots from `first`,
- *        row h % g of each slot belonging to query head h.  Units of empty
- *        sequences have no partials (their range is not written).
- *   MLA  o [batch * num_q_heads][n_split][512], then (m, l) in the same order. */
+ * Workspace layout (floats unless stated; W = the number of shares the library
+ * plans for the batch shape, U = the units, R = rows per slot):
+ *   o [W + U][R][head_dim], then (m, l) [W + U][R][2], then i32 (first slot,
+ *   count) [U].  GQA: U = batch * Hkv units (sequence, KV head), in the order
+ *   u = b * Hkv + kvh, R = num_q_heads / Hkv (row h % R of a slot belongs to
+ *   query head h).  MLA: U = batch (a sequence is a unit), R = num_q_heads.
+ *   The tiles of all units are shared out equally among the W shares; the
+ *   partials of unit u are the `count` consecutive slots from `first`.  Units
+ *   of empty sequences have no partials (their range is not written). */
 int fp4_decode_partials(const fp4kv_cache *c, const void *q, int q_dtype, int batch,
                         int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
                         const int32_t *seq_lens, float softmax_scale, void *workspace,
