@@ -2,6 +2,9 @@
 
 Usage: ``python -m fp4_kv_cache_amd.build`` or ``fp4_kv_cache_amd.build.build()``.
 Objects go to ``fp4_kv_cache_amd/_build/``; the library to ``fp4_kv_cache_amd/libfp4kv.so``.
+The same sources compiled with -DFP4KV_ABLATION give ``libfp4kv_ablate.so``, the study
+build whose technique switches (fp4kv_ablation_set) turn parts of the method off; the product
+library has none of that code.
 """
 import os
 import subprocess
@@ -12,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4kv.so")
+LIB_ABLATION = os.path.join(HERE, "libfp4kv_ablate.so")
 SOURCES = ["api.hip", "append.hip", "decode_gqa.hip", "decode_mla.hip", "stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -33,21 +37,27 @@ def _run(cmd):
 
 
 def build(verbose=False):
-    """Compile every source for gfx950 and link libfp4kv.so (always rebuilds)."""
+    """Compile every source for gfx950 and link libfp4kv.so and the ablation-study build
+    libfp4kv_ablate.so (always rebuilds both)."""
     os.makedirs(OUT, exist_ok=True)
+    os.makedirs(os.path.join(OUT, "ablation"), exist_ok=True)
 
-    def compile_one(src):
-        obj = os.path.join(OUT, src + ".o")
-        err = _run([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+    def compile_one(job):
+        src, abl = job
+        obj = os.path.join(OUT, "ablation" if abl else "", src + ".o")
+        extra = ["-DFP4KV_ABLATION"] if abl else []
+        err = _run([HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and err.strip():
             print(err, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
+    jobs = [(s, False) for s in SOURCES] + [(s, True) for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(compile_one, jobs))
+    for lib, group in ((LIB, objs[:len(SOURCES)]), (LIB_ABLATION, objs[len(SOURCES):])):
+        tmp = lib + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + group)
+        os.replace(tmp, lib)
     return LIB
 
 

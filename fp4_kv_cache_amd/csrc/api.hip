@@ -102,6 +102,9 @@ size_t workspace_size(const fp4kv_cache *c, long batch, int hq, long shares, int
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP; }
 
+// Technique switches for the next calls (ablation-study build only; always 0 otherwise).
+int g_ablation = 0;
+
 int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int hq,
                 const int32_t *block_table, int max_pages, const int32_t *seq_lens,
                 float softmax_scale, float *out, void *ws, size_t ws_bytes, int32_t *zero,
@@ -150,9 +153,12 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.num_pages = c->num_pages;
   d.q_bf16 = q_dtype == FP4KV_BF16;
   d.q_len = q_len;
+  d.abl = kAblation ? g_ablation : 0;
+  if (d.abl && c->attn != FP4KV_GQA) return FP4KV_ERR_UNSUPPORTED;
   d.n_waves = (int)shares;
   d.softmax_scale = softmax_scale;
-  const float l2d = (float)(1.4426950408889634 / (double)c->head_dim);
+  // 1/head_dim of the unnormalized rotation (1 when the rotation is switched off)
+  const float l2d = (float)(1.4426950408889634 / (double)((d.abl & kAblNoRotation) ? 1 : c->head_dim));
   const float l2 = (float)1.4426950408889634;
   d.coef = softmax_scale * l2d;
   d.coef_rope = softmax_scale * l2;
@@ -203,6 +209,16 @@ int scratch_of_current_device(void **out) {
 }  // namespace
 
 extern "C" {
+
+#ifdef FP4KV_ABLATION
+// Ablation-study build only: technique switches (kAbl* bits) for the following GQA append
+// and decode calls of this process.
+int fp4kv_ablation_set(int flags) {
+  if (flags & ~(kAblSingleQ | kAblNoRotation | kAblNoSearch)) return FP4KV_ERR_INVALID_ARG;
+  g_ablation = flags;
+  return FP4KV_OK;
+}
+#endif
 
 const char *fp4kv_status_string(int s) {
   switch (s) {
@@ -261,6 +277,8 @@ int kv_quant_append(const fp4kv_cache *c, const void *k_new, const void *v_new, 
   a.max_seqs = c->max_seqs;
   a.num_tokens = num_tokens;
   a.bf16 = dtype == FP4KV_BF16;
+  a.abl = kAblation ? g_ablation : 0;
+  if (a.abl && c->attn != FP4KV_GQA) return FP4KV_ERR_UNSUPPORTED;
   a.k_codes = c->k_codes;
   a.k_scales = c->k_scales;
   a.v_codes = c->v_codes;

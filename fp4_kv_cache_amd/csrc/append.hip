@@ -176,7 +176,8 @@ __global__ __launch_bounds__(128) void k_append_gqa(AppendArgs a) {
   for (int c = 0; c < 128; c += 8) load8(a.k_new, base + c, a.bf16, x + c);
 #pragma unroll
   for (int c = 0; c < 128; c++) x[c] = x[c] * ksi[c];
-  fwht128(x);
+  if (!(kAblation && (a.abl & kAblNoRotation))) fwht128(x);
+  const bool search = !(kAblation && (a.abl & kAblNoSearch));
 
   const float G = FMT == kFmtNV ? a.gk[h] : 1.0f;
   uint8_t codes[64];
@@ -184,11 +185,11 @@ __global__ __launch_bounds__(128) void k_append_gqa(AppendArgs a) {
 #pragma unroll
   for (int blk = 0; blk < NB; blk++) {
     if (FMT == kFmtNV) {
-      uint32_t c = nv_search<B>(x + blk * B, G, true);
+      uint32_t c = nv_search<B>(x + blk * B, G, search);
       nv_block_codes<B>(x + blk * B, c, G, codes + blk * B / 2);
       sc[blk] = (uint8_t)c;
     } else {
-      int e = mx_search<B>(x + blk * B, true);
+      int e = mx_search<B>(x + blk * B, search);
       mx_block_codes<B>(x + blk * B, e, codes + blk * B / 2);
       sc[blk] = (uint8_t)(e + 127);
     }
@@ -253,17 +254,19 @@ __device__ __forceinline__ void k_append_wave_body(const AppendArgs &a, int tok,
   const float *ksi = a.ksi + (long)h * 128 + 2 * lane;
   float x0 = ok ? load_elem(a.k_new, base, a.bf16) * ksi[0] : 0.0f;
   float x1 = ok ? load_elem(a.k_new, base + 1, a.bf16) * ksi[1] : 0.0f;
-  {
-    const float p = x0 + x1, m = x0 - x1;
-    x0 = p;
-    x1 = m;
-  }
+  if (!(kAblation && (a.abl & kAblNoRotation))) {
+    {
+      const float p = x0 + x1, m = x0 - x1;
+      x0 = p;
+      x1 = m;
+    }
 #pragma unroll
-  for (int hh = 2; hh < 128; hh <<= 1) {
-    const int lb = hh >> 1;
-    const float y0 = __shfl_xor(x0, lb), y1 = __shfl_xor(x1, lb);
-    if (lane & lb) { x0 = y0 - x0; x1 = y1 - x1; }
-    else { x0 = x0 + y0; x1 = x1 + y1; }
+    for (int hh = 2; hh < 128; hh <<= 1) {
+      const int lb = hh >> 1;
+      const float y0 = __shfl_xor(x0, lb), y1 = __shfl_xor(x1, lb);
+      if (lane & lb) { x0 = y0 - x0; x1 = y1 - x1; }
+      else { x0 = x0 + y0; x1 = x1 + y1; }
+    }
   }
   xs[2 * lane] = x0;
   xs[2 * lane + 1] = x1;
@@ -279,14 +282,16 @@ __device__ __forceinline__ void k_append_wave_body(const AppendArgs &a, int tok,
     for (int i = 0; i < B; i++) amax = fmaxf(amax, fabsf(x[i]));
     float err = INFINITY;
     int cand;
+    // (the ablation build's no-search switch leaves only the default candidate)
+    const bool try_it = k == 0 || !(kAblation && (a.abl & kAblNoSearch));
     if constexpr (FMT == kFmtNV) {
       const int deltas[5] = {0, 1, -1, -2, -3};
       cand = (int)nv_default_scale(amax, G) + deltas[k];
-      if (cand >= 0 && cand <= 0x7E) err = nv_block_err<B>(x, (uint32_t)cand, G);
+      if (try_it && cand >= 0 && cand <= 0x7E) err = nv_block_err<B>(x, (uint32_t)cand, G);
     } else {
       const int deltas[3] = {0, 1, -1};
       cand = mx_exp(amax) + deltas[k];
-      if (cand >= -127 && cand <= 127) err = mx_block_err<B>(x, cand);
+      if (try_it && cand >= -127 && cand <= 127) err = mx_block_err<B>(x, cand);
     }
     errs[blk][k] = err;
     cands[blk][k] = cand;

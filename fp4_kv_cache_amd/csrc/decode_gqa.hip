@@ -257,6 +257,7 @@ void gqa_partials(DecodeArgs a) {
   // Walsh-Hadamard butterflies in the order of the stages h = 1, 2, ..., 64 (each output
   // a single rounded sum or difference): h < EPL inside the lane, h >= EPL with lane
   // l ^ (h / EPL), the lower lane taking x + x', the upper x' - x.
+  if (!(kAblation && (a.abl & kAblNoRotation))) {
 #pragma unroll
   for (int h = 1; h < EPL; h <<= 1)
 #pragma unroll
@@ -275,6 +276,7 @@ void gqa_partials(DecodeArgs a) {
       const float o = __shfl_xor(y[j], m);
       y[j] = upper ? o - y[j] : y[j] + o;
     }
+  }
   }
   // Dual-residual FP4 query: pass k quantizes the residual left by pass k - 1.  A block of
   // B channels spans B / EPL lanes; NVFP4 also needs the row maximum (all LPR lanes).
@@ -330,6 +332,10 @@ void gqa_partials(DecodeArgs a) {
     }
     if ((lane % BL) == 0) qe[k][vq][c0 / B] = e;
     if ((lane % LPR) == 0) qg[k][vq] = gq;
+    if (kAblation && (a.abl & kAblSingleQ)) {   // single-pass query: the second pass sees zeros
+#pragma unroll
+      for (int j = 0; j < EPL; j++) y[j] = 0.0f;
+    }
   }
   }   // passes
   __syncthreads();

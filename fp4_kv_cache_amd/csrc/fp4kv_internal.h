@@ -12,8 +12,20 @@ namespace fp4kv {
 // max(1, 128 / page_size) consecutive tiles of its segment, re-staged at every window edge.
 constexpr int kMaxSplitPages = 512;
 
+// Technique switches of the ablation-study build of the library (sources compiled with
+// -DFP4KV_ABLATION; the product build compiles every switch out).  GQA only.
+constexpr int kAblSingleQ = 1;      // no dual residual: the query's second FP4 pass is zero
+constexpr int kAblNoRotation = 2;   // no Hadamard rotation of keys and queries
+constexpr int kAblNoSearch = 4;     // every key block keeps its default scale
+#ifdef FP4KV_ABLATION
+constexpr bool kAblation = true;
+#else
+constexpr bool kAblation = false;
+#endif
+
 struct AppendArgs {
   int fmt, attn, page_size, hkv, d, rope_dim, num_pages, max_seqs, num_tokens, bf16;
+  int abl;               // ablation switches (0 in the product build)
   uint8_t *k_codes, *k_scales, *v_codes, *v_scales;
   float *stage;
   uint16_t *k_rope;
@@ -25,6 +37,7 @@ struct AppendArgs {
 struct DecodeArgs {
   int fmt, page_size, hkv, group, hq, d, rope_dim, batch, max_pages, num_pages, q_bf16;
   int q_len;             // GQA: query tokens per sequence (causal), 1 for ordinary decode
+  int abl;               // ablation switches (0 in the product build)
   int n_waves;           // shares of the balanced partition (an upper bound; GQA one wave each,
                          // MLA one workgroup per group of 64 query heads each)
   float softmax_scale;

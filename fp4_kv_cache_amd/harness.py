@@ -48,17 +48,18 @@ def slots_for(bt_row, positions, P):
     return (bt_row[positions // P].astype(np.int64) * P + positions % P).astype(np.int32)
 
 
-def build(w, lens=None, copy=0, device="cuda", stop=None, workers=8):
+def build(w, lens=None, copy=0, device="cuda", stop=None, workers=8, calib=None):
     """Allocate the cache for workload ``w`` and append every sequence's context.
 
     ``stop`` (optional int array) appends only the first stop[b] tokens of each
     sequence; the rest can be appended later with ``append_range``.  The keys
     and values of the tokens left out are kept in ``built.tail[b]`` (GQA).
+    ``calib`` replaces the workload's calibration (k_smooth_inv, q_smooth, G_K, G_V).
     """
     import torch
     lens = W.seq_lens(w) if lens is None else np.asarray(lens, np.int32)
     bt, num_pages = W.page_table(w, lens, copy)
-    ksi, qs, gk, gv = W.calibration(w)
+    ksi, qs, gk, gv = W.calibration(w) if calib is None else calib
     attn = w["attn"]
     cache = PagedFP4Cache(w["fmt"], attn, num_pages, w["page"], w["hkv"], w["d"], w["batch"],
                           ksi, qs, gk if w["fmt"] == 0 else None,

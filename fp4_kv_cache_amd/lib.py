@@ -13,6 +13,10 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfp4kv.so")
+# the ablation-study build (same sources with -DFP4KV_ABLATION): the product entry points plus
+# fp4kv_ablation_set, whose switches turn techniques of the method off (study only)
+LIB_ABLATION_PATH = os.path.join(HERE, "libfp4kv_ablate.so")
+ABL_SINGLE_Q, ABL_NO_ROTATION, ABL_NO_SEARCH = 1, 2, 4
 
 NVFP4, MXFP4 = 0, 1
 F32, BF16 = 0, 1
@@ -63,20 +67,60 @@ _SIGS = {
 _lib = None
 
 
+def _open(path):
+    if not os.path.exists(path):
+        raise RuntimeError("%s not found: build it with `python -m fp4_kv_cache_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
 def load():
     """Load libfp4kv.so from the package directory (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libfp4kv.so not found at %s: build it with "
-                               "`python -m fp4_kv_cache_amd.build`" % LIB_PATH)
-        lib = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGS.items():
-            f = getattr(lib, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = lib
+        _lib = _open(LIB_PATH)
     return _lib
+
+
+_abl = None
+
+
+def load_ablation():
+    """Load the ablation-study build libfp4kv_ablate.so (raises if it has not been built)."""
+    global _abl
+    if _abl is None:
+        lib = _open(LIB_ABLATION_PATH)
+        lib.fp4kv_ablation_set.restype = _c_int
+        lib.fp4kv_ablation_set.argtypes = [_c_int]
+        _abl = lib
+    return _abl
+
+
+class ablation:
+    """Context manager: inside the block every entry point of this module runs on the
+    ablation-study build with the given technique switches (ABL_* bits, GQA only)."""
+
+    def __init__(self, flags):
+        self.flags = flags
+
+    def __enter__(self):
+        global _lib
+        load()
+        self.saved = _lib
+        lib = load_ablation()
+        check(lib.fp4kv_ablation_set(self.flags), "fp4kv_ablation_set")
+        _lib = lib
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _abl.fp4kv_ablation_set(0)
+        _lib = self.saved
+        return False
 
 
 def _ref(cache):
