@@ -207,6 +207,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=8)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true",
+                    help="skip the BF16-KV comparison decode (GQA workloads)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="profiling mode: after setup, launch the decode kernel --steps times and one "
                          "1 GiB stream copy (the known-size reference for traffic counters), then exit")
@@ -422,6 +424,32 @@ def main():
         r_us, _ = graph_time(cache_read)
         pattern_gbps = kv_bytes / (r_us * 1e-6) / 1e9
 
+    # the same decode over a BF16 KV cache of the same workload (the pages' comparison system):
+    # one cache copy suffices, its 512 B per token-head dwarf the 256 MB Infinity Cache
+    bf16_cmp = None
+    if not mla and QN == 1 and not args.no_bf16:
+        t0 = time.time()
+        del copies[1:]
+        torch.cuda.empty_cache()
+        b16 = harness.build_bf16(w, lens=lens, device=dev, workers=16)
+        ws16_bytes = L.bf16_decode_workspace_bytes(b16.cache.desc, B, hq, maxp * P)
+        ws16 = torch.empty(ws16_bytes, dtype=torch.uint8, device=dev)
+        out16 = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+        log("bf16 cache: %.1f s" % (time.time() - t0))
+
+        def decode_bf16(i):
+            L.check(L.bf16_decode_attention(b16.cache.desc, q1.data_ptr(), qdt, B, hq, b16.bt.data_ptr(), maxp,
+                                            b16.seq_lens.data_ptr(), scale, out16.data_ptr(), ws16.data_ptr(),
+                                            ws16_bytes, cur_stream()), "bf16_decode_attention")
+        b_us, _ = graph_time(decode_bf16)
+        assert torch.isfinite(out16).all().item(), "non-finite bf16 decode output"
+        bf16_bytes = float(np.sum(lens.astype(np.float64))) * hkv * 2 * d * 2
+        bf16_cmp = {"decode_attention_us": round(b_us, 2), "kv_bytes_per_step": int(bf16_bytes),
+                    "kv_GBps": round(bf16_bytes / (b_us * 1e-6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(bf16_bytes / (b_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "fp4_decode_speedup": round(b_us / d_us, 3)}
+        del b16, ws16, out16
+
     traffic = read_traffic(w, args.workload)
     if mla:   # matrix-core bound: algorithmic flops against the dense FP4 matrix peak
         flops = float(np.sum(lens.astype(np.float64))) * mla_flops_per_token(w)
@@ -453,8 +481,10 @@ def main():
         "dtype": "fp4(e2m1) x fp4 -> f32",
         "data": "synthetic",
         "config": {"workload": ("%s: batch %d, %d query heads on one latent head (latent %d FP4 + rope %d bf16), "
-                                "context %d, page %d, %s, shuffled page table, 1 new token per sequence per step"
-                                % (args.workload, B, hq, d, w["rope"], int(lens.max()), P,
+                                "context %s, page %d, %s, shuffled page table, 1 new token per sequence per step"
+                                % (args.workload, B, hq, d, w["rope"],
+                                   int(lens.max()) if lens.min() == lens.max() else
+                                   "%d-%d (ragged)" % (lens.min(), lens.max()), P,
                                    "NVFP4" if w["fmt"] == 0 else "MXFP4")) if mla else
                                ("%s: batch %d, %d query / %d KV heads, head_dim %d, context %s, page %d, %s K/V, "
                                 "shuffled page table, %s"
@@ -473,6 +503,7 @@ def main():
         "decode_attention": {"us": round(d_us, 2), "kv_GBps": round(kv_bytes / (d_us * 1e-6) / 1e9, 1),
                              "frac_of_hbm_peak": round(kv_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
         "stream_read_ceiling_GBps": round(stream_gbps, 1),
+        **({"bf16_kv_comparison": bf16_cmp} if bf16_cmp else {}),
         **({"multi_token": {"q_len": QN, "decode_us": round(mq_us, 2),
                             "single_token_decode_us": round(k_us + m_us, 2),
                             "query_tokens_per_s": round(B * QN / (mq_us * 1e-6), 1),

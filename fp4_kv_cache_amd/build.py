@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4kv.so")
 LIB_ABLATION = os.path.join(HERE, "libfp4kv_ablate.so")
-SOURCES = ["api.hip", "append.hip", "decode_gqa.hip", "decode_mla.hip", "stream.hip"]
+SOURCES = ["api.hip", "append.hip", "decode_gqa.hip", "decode_mla.hip", "decode_bf16.hip", "stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

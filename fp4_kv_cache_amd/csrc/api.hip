@@ -206,9 +206,120 @@ int scratch_of_current_device(void **out) {
   return FP4KV_OK;
 }
 
+// BF16 comparison cache: scalar checks, and the GQA FP4 descriptor with the same shape
+// (the two share the partition, the workspace layout and the merge).
+int check_bf16(const fp4kv_bf16_cache *c) {
+  if (!c) return FP4KV_ERR_INVALID_ARG;
+  if (c->num_pages <= 0 || c->num_kv_heads <= 0 || c->page_size <= 0) return FP4KV_ERR_INVALID_ARG;
+  if (!pow2_page(c->page_size)) return FP4KV_ERR_UNSUPPORTED;
+  if ((long)c->num_pages * c->page_size > 0x7FFFFFFFL) return FP4KV_ERR_INVALID_ARG;
+  if (c->head_dim != 128) return c->head_dim > 0 ? FP4KV_ERR_UNSUPPORTED : FP4KV_ERR_INVALID_ARG;
+  return FP4KV_OK;
+}
+
+fp4kv_cache gqa_twin(const fp4kv_bf16_cache *c) {
+  fp4kv_cache t{};
+  t.format = FP4KV_MXFP4;
+  t.attn = FP4KV_GQA;
+  t.num_pages = c->num_pages;
+  t.page_size = c->page_size;
+  t.num_kv_heads = c->num_kv_heads;
+  t.head_dim = 128;
+  t.rope_dim = 0;
+  t.max_seqs = 1;
+  return t;
+}
+
 }  // namespace
 
 extern "C" {
+
+int bf16kv_cache_layout(const fp4kv_bf16_cache *c, size_t bytes_out[2]) {
+  if (!bytes_out) return FP4KV_ERR_INVALID_ARG;
+  const int st = check_bf16(c);
+  if (st) return st;
+  bytes_out[0] = bytes_out[1] = (size_t)c->num_pages * c->num_kv_heads * c->page_size * 128 * 2;
+  return FP4KV_OK;
+}
+
+int bf16kv_append(const fp4kv_bf16_cache *c, const void *k_new, const void *v_new, int dtype, int num_tokens,
+                  const int32_t *slot_mapping, void *stream) {
+  int st = check_bf16(c);
+  if (st) return st;
+  if (dtype != FP4KV_F32 && dtype != FP4KV_BF16) return FP4KV_ERR_INVALID_ARG;
+  if (num_tokens < 0) return FP4KV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return FP4KV_OK;
+  if (!c->k || !c->v || !k_new || !v_new || !slot_mapping) return FP4KV_ERR_INVALID_ARG;
+  AppendArgs a{};
+  a.page_size = c->page_size;
+  a.hkv = c->num_kv_heads;
+  a.d = 128;
+  a.num_pages = c->num_pages;
+  a.num_tokens = num_tokens;
+  a.bf16 = dtype == FP4KV_BF16;
+  a.k_codes = (uint8_t *)c->k;
+  a.v_codes = (uint8_t *)c->v;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = slot_mapping;
+  return to_status(launch_bf16_append(a, (hipStream_t)stream));
+}
+
+size_t bf16_decode_workspace_bytes(const fp4kv_bf16_cache *c, int batch, int num_q_heads, int max_seq_len) {
+  if (check_bf16(c) != FP4KV_OK || batch < 0 || num_q_heads <= 0 || max_seq_len < 0) return 0;
+  const fp4kv_cache t = gqa_twin(c);
+  return workspace_size(&t, batch, num_q_heads, max_shares(&t, num_q_heads), 1);
+}
+
+int bf16_decode_attention(const fp4kv_bf16_cache *c, const void *q, int q_dtype, int batch, int num_q_heads,
+                          const int32_t *block_table, int max_pages_per_seq, const int32_t *seq_lens,
+                          float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  int st = check_bf16(c);
+  if (st) return st;
+  if (batch < 0 || num_q_heads <= 0 || max_pages_per_seq <= 0) return FP4KV_ERR_INVALID_ARG;
+  if (q_dtype != FP4KV_F32 && q_dtype != FP4KV_BF16) return FP4KV_ERR_INVALID_ARG;
+  if (num_q_heads % c->num_kv_heads != 0) return FP4KV_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale)) return FP4KV_ERR_INVALID_ARG;
+  const int group = num_q_heads / c->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return FP4KV_ERR_UNSUPPORTED;
+  if ((long)max_pages_per_seq * c->page_size > 0x7FFFFFFFL) return FP4KV_ERR_INVALID_ARG;
+  if ((long)batch * c->num_kv_heads > 0x3FFFFFFFL) return FP4KV_ERR_INVALID_ARG;
+  if (batch > 0 && (!c->k || !c->v || !q || !block_table || !seq_lens || !out || !workspace))
+    return FP4KV_ERR_INVALID_ARG;
+  const fp4kv_cache t = gqa_twin(c);
+  if (workspace_bytes < workspace_size(&t, batch, num_q_heads, max_shares(&t, num_q_heads), 1))
+    return FP4KV_ERR_WORKSPACE;
+  const long shares = plan_shares(&t, units_of(&t, batch), num_q_heads, (long)max_pages_per_seq * c->page_size);
+  DecodeArgs d{};
+  d.page_size = c->page_size;
+  d.hkv = c->num_kv_heads;
+  d.group = group;
+  d.hq = num_q_heads;
+  d.d = 128;
+  d.batch = batch;
+  d.max_pages = max_pages_per_seq;
+  d.num_pages = c->num_pages;
+  d.q_bf16 = q_dtype == FP4KV_BF16;
+  d.q_len = 1;
+  d.n_waves = (int)shares;
+  d.softmax_scale = softmax_scale;
+  d.coef = softmax_scale * (float)1.4426950408889634;
+  d.k_codes = (const uint8_t *)c->k;
+  d.v_codes = (const uint8_t *)c->v;
+  d.q = q;
+  d.block_table = block_table;
+  d.seq_lens = seq_lens;
+  const size_t rows = workspace_rows(&t, batch, num_q_heads, shares, 1);
+  d.ws_o = (float *)workspace;
+  d.ws_ml = d.ws_o + rows * 128;
+  d.ws_meta = (int32_t *)(d.ws_ml + rows * 2);
+  d.out = out;
+  const hipError_t e = launch_bf16_partials(d, (hipStream_t)stream);
+  if (e != hipSuccess) return FP4KV_ERR_HIP;
+  return to_status(launch_decode_merge(d, (hipStream_t)stream));
+}
+
 
 #ifdef FP4KV_ABLATION
 // Ablation-study build only: technique switches (kAbl* bits) for the following GQA append

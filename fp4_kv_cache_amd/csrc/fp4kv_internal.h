@@ -61,6 +61,8 @@ hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_mla_partials(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_mla_merge(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_bf16_partials(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_bf16_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_cache_read(const DecodeArgs &a, uint32_t *sink, hipStream_t s);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t s);

@@ -7,7 +7,7 @@ all quantization happens in the HIP kernels.
 import numpy as np
 
 from . import workloads as W
-from .lib import PagedFP4Cache, GQA, MLA
+from .lib import PagedFP4Cache, PagedBF16Cache, GQA, MLA
 
 
 def _dev(x, w, torch, device):
@@ -139,3 +139,24 @@ def append_ranges(built, ranges):
                               .view(np.int16)).to(dev)
     cache.append(k, v, torch.from_numpy(slots.astype(np.int32)).to(dev), torch.from_numpy(seq_ids).to(dev),
                  torch.from_numpy(p).to(dev), kr)
+
+
+def build_bf16(w, lens=None, copy=0, device="cuda", workers=8):
+    """The same workload's keys and values in the BF16 comparison cache (GQA workloads):
+    every sequence appended with bf16kv_append, the same page table as ``build``."""
+    import torch
+    assert w["attn"] == GQA
+    lens = W.seq_lens(w) if lens is None else np.asarray(lens, np.int32)
+    bt, num_pages = W.page_table(w, lens, copy)
+    cache = PagedBF16Cache(num_pages, w["page"], w["hkv"], device=device)
+    built = Built(w, cache, bt, lens, None, device)
+    for b in range(w["batch"]):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        ks = W.parallel_map(lambda h: W.keys(w, b, h, L), range(w["hkv"]), workers)
+        vs = W.parallel_map(lambda h: W.values(w, b, h, L), range(w["hkv"]), workers)
+        slots = slots_for(bt[b], np.arange(L), w["page"])
+        cache.append(_dev(np.stack(ks, axis=1), w, torch, device), _dev(np.stack(vs, axis=1), w, torch, device),
+                     torch.from_numpy(slots).to(device))
+    return built

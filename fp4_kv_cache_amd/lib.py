@@ -28,6 +28,12 @@ _c_size = ctypes.c_size_t
 _vp = ctypes.c_void_p
 
 
+class BF16KVCache(ctypes.Structure):
+    """Mirror of ``struct fp4kv_bf16_cache`` (the BF16 comparison cache)."""
+    _fields_ = [("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("k", _vp), ("v", _vp)]
+
+
 class FP4KVCache(ctypes.Structure):
     """Mirror of ``struct fp4kv_cache``."""
     _fields_ = [
@@ -56,6 +62,11 @@ _SIGS = {
     "fp4kv_cache_read_sink_words": (_c_size, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int]),
     "fp4_decode_attention_noalloc": (_c_int, [ctypes.POINTER(FP4KVCache), _vp, _c_int, _c_int, _c_int, _vp, _c_int,
                                               _vp, ctypes.c_float, _vp, _vp, _vp]),
+    "bf16kv_cache_layout": (_c_int, [ctypes.POINTER(BF16KVCache), ctypes.POINTER(_c_size)]),
+    "bf16kv_append": (_c_int, [ctypes.POINTER(BF16KVCache), _vp, _vp, _c_int, _c_int, _vp, _vp]),
+    "bf16_decode_workspace_bytes": (_c_size, [ctypes.POINTER(BF16KVCache), _c_int, _c_int, _c_int]),
+    "bf16_decode_attention": (_c_int, [ctypes.POINTER(BF16KVCache), _vp, _c_int, _c_int, _c_int, _vp, _c_int,
+                                       _vp, ctypes.c_float, _vp, _vp, _c_size, _vp]),
     "fp4_decode_multi_workspace_bytes": (_c_size, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int, _c_int]),
     "fp4_decode_attention_multi": (_c_int, [ctypes.POINTER(FP4KVCache), _vp, _c_int, _c_int, _c_int, _c_int, _vp,
                                             _c_int, _vp, ctypes.c_float, _vp, _vp, _c_size, _vp, _vp]),
@@ -169,6 +180,27 @@ def fp4_decode_attention_noalloc(cache, q, q_dtype, batch, num_q_heads, block_ta
     return load().fp4_decode_attention_noalloc(_ref(cache), q, q_dtype, batch, num_q_heads, block_table,
                                                max_pages_per_seq, seq_lens, softmax_scale, out,
                                                zero_block_count, stream)
+
+
+def bf16kv_cache_layout(cache):
+    out = (_c_size * 2)()
+    st = load().bf16kv_cache_layout(_ref(cache), out)
+    return st, list(out)
+
+
+def bf16kv_append(cache, k_new, v_new, dtype, num_tokens, slot_mapping, stream):
+    return load().bf16kv_append(_ref(cache), k_new, v_new, dtype, num_tokens, slot_mapping, stream)
+
+
+def bf16_decode_workspace_bytes(cache, batch, num_q_heads, max_seq_len):
+    return load().bf16_decode_workspace_bytes(_ref(cache), batch, num_q_heads, max_seq_len)
+
+
+def bf16_decode_attention(cache, q, q_dtype, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                          softmax_scale, out, workspace, workspace_bytes, stream):
+    return load().bf16_decode_attention(_ref(cache), q, q_dtype, batch, num_q_heads, block_table,
+                                        max_pages_per_seq, seq_lens, softmax_scale, out, workspace,
+                                        workspace_bytes, stream)
 
 
 def fp4_decode_multi_workspace_bytes(cache, batch, q_len, num_q_heads, max_seq_len):
@@ -323,3 +355,50 @@ class PagedFP4Cache:
             v["k_scales"] = self.k_scales.view(np_, 1, P // B, d // B)
             v["k_rope"] = self.k_rope.view(np_, 1, P, self.rope_dim)
         return v
+
+
+class PagedBF16Cache:
+    """The BF16 comparison cache: k and v as torch uint16 device tensors in the library's layout."""
+
+    def __init__(self, num_pages, page_size, num_kv_heads, device="cuda"):
+        import torch
+        self.torch = torch
+        c = BF16KVCache(num_pages, page_size, num_kv_heads, 128)
+        st, sizes = bf16kv_cache_layout(c)
+        check(st, "bf16kv_cache_layout")
+        dev = torch.device(device)
+        self.k = torch.zeros(sizes[0] // 2, dtype=torch.int16, device=dev)
+        self.v = torch.zeros(sizes[1] // 2, dtype=torch.int16, device=dev)
+        c.k, c.v = self.k.data_ptr(), self.v.data_ptr()
+        self.desc = c
+        self.page_size, self.num_kv_heads, self.head_dim = page_size, num_kv_heads, 128
+
+    def append(self, k_new, v_new, slot_mapping):
+        torch = self.torch
+        dt = BF16 if k_new.dtype == torch.bfloat16 else F32
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        st = bf16kv_append(self.desc, k_new.data_ptr(), v_new.data_ptr(), dt, int(slot_mapping.numel()),
+                           slot_mapping.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        check(st, "bf16kv_append")
+
+    def decode(self, q, block_table, seq_lens, softmax_scale, out=None, workspace=None):
+        torch = self.torch
+        batch, hq = q.shape[0], q.shape[1]
+        maxp = block_table.shape[1]
+        if out is None:
+            out = torch.empty((batch, hq, 128), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            nb = bf16_decode_workspace_bytes(self.desc, batch, hq, maxp * self.page_size)
+            workspace = torch.empty(max(nb, 4), dtype=torch.uint8, device=q.device)
+        dt = BF16 if q.dtype == torch.bfloat16 else F32
+        st = bf16_decode_attention(self.desc, q.data_ptr(), dt, batch, hq, block_table.data_ptr(), maxp,
+                                   seq_lens.data_ptr(), float(softmax_scale), out.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel(), torch.cuda.current_stream().cuda_stream)
+        check(st, "bf16_decode_attention")
+        return out
+
+    def views(self):
+        """k [pages][Hkv][P][128] and v [pages][Hkv][128][P] as uint16 device tensors."""
+        P, h = self.page_size, self.num_kv_heads
+        np_ = self.desc.num_pages
+        return {"k": self.k.view(np_, h, P, 128), "v": self.v.view(np_, h, 128, P)}

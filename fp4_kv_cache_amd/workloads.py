@@ -24,6 +24,8 @@ so these synthetic batches stand in for them):
                   K ~ N(0, 0.05^2): nearly flat logits, probabilities ~1e-5
   mla             B=32, Hq=128, one latent head, D=512 + rope 64, L=16384, page 64,
                   NVFP4, bf16, 10 seeded latent channels x8
+  mla_ragged      as mla with L ~ U[1024, 32768]
+  mla_mxfp4       as mla with an MXFP4 latent
 """
 import math
 from concurrent.futures import ThreadPoolExecutor
@@ -52,6 +54,11 @@ WORKLOADS = {
     "mla": dict(id=5, attn=MLA, batch=32, hq=128, hkv=1, d=512, rope=64, ctx=16384, page=64,
                 fmt=NVFP4, dtype="bf16", shuffle=True, outlier_channels=None, outlier_scale=8.0,
                 n_outliers=10, k_std=1.0, lognormal=0.0),
+    # the MLA shape with ragged contexts (uniform in [1024, 32768], mean close to the uniform
+    # batch's 16384): the balanced partition's per-token rate against the uniform batch's
+    "mla_ragged": dict(id=7, attn=MLA, batch=32, hq=128, hkv=1, d=512, rope=64, ctx=(1024, 32768), page=64,
+                       fmt=NVFP4, dtype="bf16", shuffle=True, outlier_channels=None, outlier_scale=8.0,
+                       n_outliers=10, k_std=1.0, lognormal=0.0),
     # the MLA shape with an MXFP4 latent (32 x 32 E8M0 tiles); not one of the five headline
     # configurations -- it exercises the natively block-scaled MLA path
     "mla_mxfp4": dict(id=6, attn=MLA, batch=32, hq=128, hkv=1, d=512, rope=64, ctx=16384, page=64,

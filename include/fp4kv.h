@@ -283,6 +283,49 @@ int fp4kv_cache_read(const fp4kv_cache *c, int batch, int num_q_heads, const int
 size_t fp4kv_cache_read_sink_words(const fp4kv_cache *c, int batch, int num_q_heads,
                                    int max_seq_len);
 
+/* ---------------------------------------------------------------------------
+ * BF16 KV cache: the comparison system of the FP4 path.  The pages report the FP4
+ * cache's serving gain over a BF16 KV cache ("FP4 KV Cache Done Right", section
+ * "How good are the results, really?"); these entry points give the same paged
+ * decode with a bfloat16 cache on the same partition and merge, so that the two
+ * can be timed side by side on one GPU.  Plain softmax attention (no smoothing,
+ * rotation or quantization); query and probabilities in bf16, sums in fp32.
+ * Layout (head_dim 128, P = page_size tokens per page, Hkv heads):
+ *   k  bf16 [num_pages][Hkv][P][128]   token-major
+ *   v  bf16 [num_pages][Hkv][128][P]   channel-major
+ * page_size is 16, 32, 64, 128 or 256; a token's slot is page * P + position % P. */
+typedef struct fp4kv_bf16_cache {
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  uint16_t *k;
+  uint16_t *v;
+} fp4kv_bf16_cache;
+
+/* Byte sizes of k and v (host function; reads only the scalar fields). */
+int bf16kv_cache_layout(const fp4kv_bf16_cache *c, size_t bytes_out[2]);
+
+/* Append num_tokens tokens: k_new, v_new [num_tokens][Hkv][128] of dtype F32 or BF16,
+ * rounded to bf16 (nearest even) into the slots slot_mapping i32 [num_tokens]; slots
+ * outside the pool are skipped.  num_tokens == 0 is a no-op. */
+int bf16kv_append(const fp4kv_bf16_cache *c, const void *k_new, const void *v_new, int dtype,
+                  int num_tokens, const int32_t *slot_mapping, void *stream);
+
+/* Workspace bytes of bf16_decode_attention for this batch shape (0 on invalid
+ * arguments); like fp4_decode_workspace_bytes it covers every block table. */
+size_t bf16_decode_workspace_bytes(const fp4kv_bf16_cache *c, int batch, int num_q_heads,
+                                   int max_seq_len);
+
+/* Decode attention over the BF16 cache, arguments and outputs as fp4_decode_attention
+ * (q [batch][num_q_heads][128] of dtype q_dtype; out f32 [batch][num_q_heads][128];
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}).  Softmax over tiles of 64 tokens:
+ * p = 2^(s - tile max), rounded to bf16 for P.V, the denominator summing the fp32 p. */
+int bf16_decode_attention(const fp4kv_bf16_cache *c, const void *q, int q_dtype, int batch,
+                          int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
+                          const int32_t *seq_lens, float softmax_scale, float *out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *fp4kv_status_string(int status);
 
