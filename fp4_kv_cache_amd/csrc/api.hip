@@ -515,6 +515,11 @@ int fp4kv_stream_read(const void *src, size_t bytes, uint32_t *sink, void *strea
   return to_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream));
 }
 
+int fp4kv_pack_e2m1(const float *x, size_t n, int scale_exp, uint8_t *out, void *stream) {
+  if (!x || !out || n == 0 || n % 8 != 0 || scale_exp < -126 || scale_exp > 127) return FP4KV_ERR_INVALID_ARG;
+  return to_status(launch_pack_e2m1(x, n, scale_exp, out, (hipStream_t)stream));
+}
+
 int fp4kv_stream_copy(const void *src, void *dst, size_t bytes, void *stream) {
   if (!src || !dst || bytes == 0 || bytes % 4096 != 0) return FP4KV_ERR_INVALID_ARG;
   return to_status(launch_stream_copy(src, dst, bytes, (hipStream_t)stream));

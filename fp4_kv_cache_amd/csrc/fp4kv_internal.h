@@ -65,6 +65,7 @@ hipError_t launch_bf16_partials(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_bf16_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_cache_read(const DecodeArgs &a, uint32_t *sink, hipStream_t s);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_pack_e2m1(const float *x, size_t n, int scale_exp, uint8_t *out, hipStream_t s);
 hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
 
 }  // namespace fp4kv

@@ -1,6 +1,6 @@
 // Streaming-read kernel: the achievable HBM read bandwidth on this device, measured
 // next to the decode kernel (16-byte loads, a few KB in flight per wave).
-#include "fp4kv_internal.h"
+#include "decode_common.h"
 
 namespace fp4kv {
 
@@ -38,6 +38,22 @@ __global__ __launch_bounds__(256) void stream_read(const uint4 *src, size_t n16,
 __global__ __launch_bounds__(256) void stream_copy(const uint4 *src, uint4 *dst, size_t n16) {
   const size_t stride = (size_t)gridDim.x * 256;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// E2M1 codes of x / 2^e (the conversion divides by its scale operand) with the hardware conversion the decode kernels use for the
+// probabilities (v_cvt_scalef32_pk_fp4_f32, the same call sequence as their packing): thread i
+// converts x[8 i .. 8 i + 7] into one word, byte j = code(x[2 j]) | code(x[2 j + 1]) << 4.
+__global__ __launch_bounds__(256) void pack_e2m1(const float *x, size_t n8, float scale, uint32_t *out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const float *p = x + 8 * i;
+  out[i] = pack8(p, p + 4, scale);
+}
+
+hipError_t launch_pack_e2m1(const float *x, size_t n, int scale_exp, uint8_t *out, hipStream_t s) {
+  const size_t n8 = n / 8;
+  pack_e2m1<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(x, n8, ldexpf(1.0f, scale_exp), (uint32_t *)out);
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t s) {

@@ -67,6 +67,7 @@ _SIGS = {
     "bf16_decode_workspace_bytes": (_c_size, [ctypes.POINTER(BF16KVCache), _c_int, _c_int, _c_int]),
     "bf16_decode_attention": (_c_int, [ctypes.POINTER(BF16KVCache), _vp, _c_int, _c_int, _c_int, _vp, _c_int,
                                        _vp, ctypes.c_float, _vp, _vp, _c_size, _vp]),
+    "fp4kv_pack_e2m1": (_c_int, [_vp, _c_size, _c_int, _vp, _vp]),
     "fp4_decode_multi_workspace_bytes": (_c_size, [ctypes.POINTER(FP4KVCache), _c_int, _c_int, _c_int, _c_int]),
     "fp4_decode_attention_multi": (_c_int, [ctypes.POINTER(FP4KVCache), _vp, _c_int, _c_int, _c_int, _c_int, _vp,
                                             _c_int, _vp, ctypes.c_float, _vp, _vp, _c_size, _vp, _vp]),
@@ -201,6 +202,10 @@ def bf16_decode_attention(cache, q, q_dtype, batch, num_q_heads, block_table, ma
     return load().bf16_decode_attention(_ref(cache), q, q_dtype, batch, num_q_heads, block_table,
                                         max_pages_per_seq, seq_lens, softmax_scale, out, workspace,
                                         workspace_bytes, stream)
+
+
+def fp4kv_pack_e2m1(x, n, scale_exp, out, stream):
+    return load().fp4kv_pack_e2m1(x, n, scale_exp, out, stream)
 
 
 def fp4_decode_multi_workspace_bytes(cache, batch, q_len, num_q_heads, max_seq_len):

@@ -265,6 +265,14 @@ int fp4_decode_merge(const fp4kv_cache *c, int batch, int num_q_heads, int max_p
  * HBM read bandwidth next to the decode kernel. */
 int fp4kv_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
+/* Diagnostic: E2M1 codes of x[i] / 2^scale_exp (n a multiple of 8, f32 in, n / 2 packed
+ * bytes out, byte j = code(x[2j]) | code(x[2j+1]) << 4) computed with the hardware
+ * conversion the decode kernels use to quantize the probabilities to FP4 (the fused
+ * probability quantization of "BitDecoding-FP4: Native FP4 KV Cache Decoding via
+ * Algorithm-System Co-Design", Article Summary), so that its rounding can be checked
+ * against the format's definition.  scale_exp in [-126, 127]. */
+int fp4kv_pack_e2m1(const float *x, size_t n, int scale_exp, uint8_t *out, void *stream);
+
 /* Measurement helper: copies `bytes` (a multiple of 4096) from `src` to `dst`, the
  * known-size reference against which hardware traffic counters are scaled. */
 int fp4kv_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
