@@ -14,6 +14,61 @@ __device__ __forceinline__ v4f mfma4(const v8i &a, const v8i &b, v4f c, int sa, 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, OPA, sa, OPB, sb);
 }
 
+// An E4M3 scale S on the E8M0-scaled MFMA: S written as a sum of at most three signed powers
+// of two, each applied by one MFMA pass whose scale byte is that power (byte 0 = 2^-127 for an
+// absent term: its products fall below fp32 resolution).  Normal S = 2^E (8 + m) / 8 uses the
+// set bits of 8 + m, except m = 7, where 15 = 16 - 1; subnormal S = m 2^-9 uses the bits of m.
+// Bytes 0-2 hold the three passes' scale bytes; byte 3 is 0x88 when the third term is
+// negative (the pass then runs on operand codes with their sign bits flipped), else 0.
+// Codes 0x7F and above (NaN, negative) give no term.
+constexpr uint32_t e4m3_pass_word(int c) {
+  if (c < 0 || c >= 0x7F) return 0u;
+  const int ef = c >> 3, m = c & 7;
+  if (ef != 0 && m == 7) {
+    const int E = ef - 7;
+    return (uint32_t)(E + 1 + 127) | ((uint32_t)(E - 3 + 127) << 16) | 0x88000000u;
+  }
+  // digit k of (implicit bit, m2, m1, m0) has exponent top - k
+  const int top = ef != 0 ? ef - 7 : -6;
+  const int bits = (ef != 0 ? 8 : 0) | m;
+  uint32_t w = 0u;
+  int slot = 0;
+  for (int k = 0; k < 4; k++)
+    if (bits & (8 >> k)) w |= (uint32_t)(top - k + 127) << (8 * slot++);
+  return w;
+}
+
+// Sign-bit mask of the third pass of a pass word (0x88888888 or 0): byte 3 replicated.
+__device__ __forceinline__ uint32_t pass_neg_mask(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x03030303u); }
+
+namespace detail {
+constexpr double pow2c(int e) {
+  double r = 1.0;
+  for (; e > 0; e--) r *= 2.0;
+  for (; e < 0; e++) r *= 0.5;
+  return r;
+}
+// every finite non-negative E4M3 code: the signed sum of the word's terms is the scale itself
+constexpr bool pass_words_are_exact() {
+  for (int c = 0; c < 0x7F; c++) {
+    const uint32_t w = e4m3_pass_word(c);
+    double s = 0.0;
+    for (int k = 0; k < 3; k++) {
+      const int b = (int)((w >> (8 * k)) & 0xFFu);
+      if (b == 0) continue;
+      const double t = pow2c(b - 127);
+      s += (k == 2 && (w >> 24) == 0x88u) ? -t : t;
+    }
+    if ((w >> 24) != 0u && (w >> 24) != 0x88u) return false;
+    const int ef = c >> 3, m = c & 7;
+    const double want = ef != 0 ? pow2c(ef - 7) * (8 + m) / 8.0 : pow2c(-6) * m / 8.0;
+    if (s != want) return false;
+  }
+  return e4m3_pass_word(0x7F) == 0u && e4m3_pass_word(0x80) == 0u;
+}
+static_assert(pass_words_are_exact(), "E4M3 pass words must sum to the scale");
+}  // namespace detail
+
 // lane l <- lane (l ^ 8) inside each row of 16 (row_ror:8)
 __device__ __forceinline__ float xlane8(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));

@@ -29,15 +29,17 @@
 //    scales applied by the hardware.
 //  * NVFP4 latent (16 x 16 tiles, E4M3 scale S = 2^E (1 + m/8)): the E8M0-scaled MFMA takes
 //    one power of two per (row, 32-element lane group), so each K-step runs as two parity
-//    passes (A keeps one 16-channel half of every lane group, the other half zeroed: the
-//    16-channel block that the tile scale and the query block exponent belong to) times four
-//    binary-digit passes of S (A scale 2^(E - d) where bit d of (1, m2, m1, m0) is set,
-//    E8M0 byte 0 = 2^-127 where it is not, whose products vanish below fp32 resolution),
-//    accumulated by the MFMA: the exact products code_K * S * code_Q * 2^eQ summed in fp32.
+//    passes (the query operand keeps one 16-channel half of every lane group, the other half
+//    zeroed: the 16-channel block that the tile scale and the query block exponent belong to) times three
+//    signed-digit passes of S (S as a sum of at most three signed powers of two -- the set
+//    bits of 8 + m, or 16 - 1 for m = 7 -- each the A scale of one pass, E8M0 byte 0 = 2^-127
+//    for an absent term, whose products vanish below fp32 resolution; a negative term's pass
+//    takes the codes with flipped signs), accumulated by the MFMA: the exact products
+//    code_K * S * code_Q * 2^eQ summed in fp32.
 //  * P.V: the value operand (16 channels x 32 tokens per lane) is read transposed from the
 //    same token-major tile with the 4-bit transposed LDS read, so the cache holds the latent
-//    once; the NVFP4 tile scale goes through the same binary expansion (token parities on
-//    the P side).
+//    once; the NVFP4 tile scale goes through the same signed-digit passes (token parities on
+//    the P side, the negative term's sign flip on the value codes).
 //  * The merge kernel un-rotates and un-smooths the merged latent output:
 //    out = (o H / 512) * q_smooth.
 #include "decode_common.h"
@@ -100,19 +102,21 @@ __device__ __forceinline__ float bfly_x32(float x, bool upper) {
 __device__ __forceinline__ int swz_lat(int r) { return (r & 15) ^ (((r >> 5) & 3) << 2); }
 __device__ __forceinline__ int swz_rope(int r) { return ((r >> 1) & 1) | (((r >> 5) & 3) << 1); }
 
-// The four binary-digit passes of one NVFP4 Q.K^T parity pass, Q1 and Q2 interleaved (two
-// accumulator chains): A scale byte d of w (the tile scale's pass d), B scale byte 0 of e1 / e2
-// (the query block exponent).
-__device__ __forceinline__ void nv_qk_passes(const v8i &av, const v8i &b1, const v8i &b2, v4f &acc1, v4f &acc2,
-                                             int w, int e1, int e2) {
-  acc1 = mfma4<0, 0>(av, b1, acc1, w, e1);
-  acc2 = mfma4<0, 0>(av, b2, acc2, w, e2);
-  acc1 = mfma4<1, 0>(av, b1, acc1, w, e1);
-  acc2 = mfma4<1, 0>(av, b2, acc2, w, e2);
-  acc1 = mfma4<2, 0>(av, b1, acc1, w, e1);
-  acc2 = mfma4<2, 0>(av, b2, acc2, w, e2);
-  acc1 = mfma4<3, 0>(av, b1, acc1, w, e1);
-  acc2 = mfma4<3, 0>(av, b2, acc2, w, e2);
+// The three signed-digit passes of one NVFP4 Q.K^T parity pass PB, Q1 and Q2 interleaved (two
+// accumulator chains).  The query operands b1 / b2 hold only the parity's 16-channel half of
+// every lane group (the block that the tile scale and the query block exponent belong to), so
+// the key operand is the full staged row: A scale byte d of w (the tile scale's term d), the
+// third term on `avn`, the codes with their signs flipped where that term is negative; B scale
+// byte PB of e1 / e2 (the query block exponents of the two halves).
+template <int PB>
+__device__ __forceinline__ void nv_qk_passes(const v8i &av, const v8i &avn, const v8i &b1, const v8i &b2,
+                                             v4f &acc1, v4f &acc2, int w, int e1, int e2) {
+  acc1 = mfma4<0, PB>(av, b1, acc1, w, e1);
+  acc2 = mfma4<0, PB>(av, b2, acc2, w, e2);
+  acc1 = mfma4<1, PB>(av, b1, acc1, w, e1);
+  acc2 = mfma4<1, PB>(av, b2, acc2, w, e2);
+  acc1 = mfma4<2, PB>(avn, b1, acc1, w, e1);
+  acc2 = mfma4<2, PB>(avn, b2, acc2, w, e2);
 }
 
 // MLA partials.  Grid: one-dimensional; ids with equal residue mod 8 run on one XCD, and the
@@ -151,16 +155,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ int pgl[kMaxSplitPages];
 
   if constexpr (NV) {
-    // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale): byte d is E - d + 127
-    // when bit d of (implicit bit, m2, m1, m0) is set, else 0 (read after the first barrier)
-    if (tid < 256) {
-      const int c = tid;
-      const int ef = (c >> 3) & 15, m = c & 7;
-      const int E = (ef ? ef : 1) - 7 + 127;
-      const uint32_t w = (ef ? (uint32_t)E : 0u) | ((m & 4) ? (uint32_t)(E - 1) << 8 : 0u) |
-                         ((m & 2) ? (uint32_t)(E - 2) << 16 : 0u) | ((m & 1) ? (uint32_t)(E - 3) << 24 : 0u);
-      lut[c] = c < 0x7F ? w : 0u;
-    }
+    // E4M3 code -> its three signed-digit pass bytes (read after the first barrier)
+    if (tid < 256) lut[tid] = e4m3_pass_word(tid);
   }
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   const float gk = NV ? a.gk[0] : 1.0f;
@@ -250,8 +246,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // lane (n, q4) holds channels 128 st + 32 q4 + j (st = 0..3, j = 0..31) of head h0 + n.
     // Walsh-Hadamard stages on channel bits 0-4 and 7-8 stay in the lane, bits 5 and 6 pair
     // lanes l ^ 16 and l ^ 32 (the oracle's stage order, h = 1, 2, ..., 256).
-    v8i bq[2][4];            // [pass][K-step]: FP4 codes of the lane's 32 channels
-    int qsb[2][4][2];        // their E8M0 scale bytes: NVFP4 per 16-channel half, MXFP4 [.][.][0]
+    // [pass][K-step][half]: FP4 codes of the lane's 32 channels; NVFP4 keeps one 16-channel
+    // half per operand (the other half zero), MXFP4 all 32 in [.][.][0]
+    v8i bq[2][4][2];
+    int qsb[2][4];           // their E8M0 scale bytes: NVFP4 byte p = half p, MXFP4 byte 0
     float qg[2] = {0.0f, 0.0f};
     if (active) {
       const long q0 = ((long)b * a.hq + h0 + n) * (D + R) + 32 * q4;
@@ -319,6 +317,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int st = 0; st < 4; st++) {
             uint32_t w[4] = {0u, 0u, 0u, 0u};
+            int sb = 0;
 #pragma unroll
             for (int p = 0; p < 2; p++) {
               float bmax = 0.0f;
@@ -337,9 +336,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 w[ch / 8] |= c << (4 * (ch % 8));
                 y[st][ch] = x - (e2m1_dec(c) * S) * gq;
               }
-              qsb[k][st][p] = e + 127;
+              sb |= (e + 127) << (8 * p);
             }
-            bq[k][st] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+            bq[k][st][0] = v8i{(int)w[0], (int)w[1], 0, 0, 0, 0, 0, 0};
+            bq[k][st][1] = v8i{0, 0, (int)w[2], (int)w[3], 0, 0, 0, 0};
+            qsb[k][st] = sb;
           }
           qg[k] = gq;
         } else {
@@ -357,8 +358,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               w[j / 8] |= c << (4 * (j % 8));
               y[st][j] = y[st][j] - ldexpf(e2m1_dec(c), e);
             }
-            bq[k][st] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-            qsb[k][st][0] = qsb[k][st][1] = e + 127;
+            bq[k][st][0] = bq[k][st][1] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+            qsb[k][st] = e + 127;
           }
           qg[k] = 1.0f;
         }
@@ -368,8 +369,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int k = 0; k < 2; k++)
 #pragma unroll
         for (int st = 0; st < 4; st++) {
-          bq[k][st] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-          qsb[k][st][0] = qsb[k][st][1] = 0;
+          bq[k][st][0] = bq[k][st][1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          qsb[k][st] = 0;
         }
     }
     // rope query (bf16): K-step s, lane group q4, element j is rope channel 32 s + 8 q4 + j
@@ -448,17 +449,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int st = 0; st < 4; st++) {
             if constexpr (NV) {
-              const v8i alo = {(int)o[st].x, (int)o[st].y, 0, 0, 0, 0, 0, 0};
-              const v8i ahi = {0, 0, (int)o[st].z, (int)o[st].w, 0, 0, 0, 0};
-              nv_qk_passes(alo, bq[0][st], bq[1][st], acc1, acc2, (int)lw[i >> 2][st][0], qsb[0][st][0],
-                           qsb[1][st][0]);
-              nv_qk_passes(ahi, bq[0][st], bq[1][st], acc1, acc2, (int)lw[i >> 2][st][1], qsb[0][st][1],
-                           qsb[1][st][1]);
+              // one sign-flipped copy serves both halves: each pass sees only its own half
+              const uint32_t k0 = pass_neg_mask(lw[i >> 2][st][0]), k1 = pass_neg_mask(lw[i >> 2][st][1]);
+              const v8i av = {(int)o[st].x, (int)o[st].y, (int)o[st].z, (int)o[st].w, 0, 0, 0, 0};
+              const v8i avn = {(int)(o[st].x ^ k0), (int)(o[st].y ^ k0), (int)(o[st].z ^ k1),
+                               (int)(o[st].w ^ k1), 0, 0, 0, 0};
+              const int w0 = (int)lw[i >> 2][st][0], w1 = (int)lw[i >> 2][st][1];
+              nv_qk_passes<0>(av, avn, bq[0][st][0], bq[1][st][0], acc1, acc2, w0, qsb[0][st], qsb[1][st]);
+              nv_qk_passes<1>(av, avn, bq[0][st][1], bq[1][st][1], acc1, acc2, w1, qsb[0][st], qsb[1][st]);
             } else {
               const v8i av = {(int)o[st].x, (int)o[st].y, (int)o[st].z, (int)o[st].w, 0, 0, 0, 0};
               const int sa = (int)byte_of(scc, 4 * st + q4);
-              acc1 = mfma4<0, 0>(av, bq[0][st], acc1, sa, qsb[0][st][0]);
-              acc2 = mfma4<0, 0>(av, bq[1][st], acc2, sa, qsb[1][st][0]);
+              acc1 = mfma4<0, 0>(av, bq[0][st][0], acc1, sa, qsb[0][st]);
+              acc2 = mfma4<0, 0>(av, bq[1][st][0], acc2, sa, qsb[1][st]);
             }
           }
           accr = mfma_bf16(as_bh8(o[4]), bqr[0], accr);
@@ -575,10 +578,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // of channel groups 4 c .. 4 c + 3 are read while chunk c - 1 computes
         v2i vt[2][4][2];
         if constexpr (NV) {
-          int lt[2][4][2];
           const v8i p0 = {(int)hp.x, (int)hp.y, 0, 0, 0, 0, 0, 0};
           const v8i p1 = {0, 0, (int)hp.z, (int)hp.w, 0, 0, 0, 0};
           // tile scales of the lane's token tiles 2 q4 and 2 q4 + 1 (the two P parities)
+          int lt[2][4][2];
           const uint4 sa0 = *(const uint4 *)(St + (2 * q4) * 32), sa1 = *(const uint4 *)(St + (2 * q4) * 32 + 16);
           const uint4 sb0 = *(const uint4 *)(St + (2 * q4 + 1) * 32), sb1 = *(const uint4 *)(St + (2 * q4 + 1) * 32 + 16);
           auto read_vals = [&](int c, v2i (*o)[2], int (*l)[2]) {
@@ -602,14 +605,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const v2i lo = vt[c & 1][k][0], hi = vt[c & 1][k][1];
               const v8i av = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
               const int l0 = lt[c & 1][k][0], l1 = lt[c & 1][k][1];
+              // the third terms' passes take the values with flipped signs where the term is
+              // negative; P of one parity is zero in the other half, so one copy serves both
+              const uint32_t m0 = pass_neg_mask((uint32_t)l0), m1 = pass_neg_mask((uint32_t)l1);
+              const v8i avn = {(int)((uint32_t)lo[0] ^ m0), (int)((uint32_t)lo[1] ^ m0), (int)((uint32_t)hi[0] ^ m1),
+                               (int)((uint32_t)hi[1] ^ m1), 0, 0, 0, 0};
               v4f acc = mfma4<0, 0>(av, p0, o_run[cg], l0, pb0);
               acc = mfma4<1, 0>(av, p0, acc, l0, pb0);
-              acc = mfma4<2, 0>(av, p0, acc, l0, pb0);
-              acc = mfma4<3, 0>(av, p0, acc, l0, pb0);
+              acc = mfma4<2, 0>(avn, p0, acc, l0, pb0);
               acc = mfma4<0, 0>(av, p1, acc, l1, pb1);
               acc = mfma4<1, 0>(av, p1, acc, l1, pb1);
-              acc = mfma4<2, 0>(av, p1, acc, l1, pb1);
-              o_run[cg] = mfma4<3, 0>(av, p1, acc, l1, pb1);
+              o_run[cg] = mfma4<2, 0>(avn, p1, acc, l1, pb1);
             }
           }
         } else {
