@@ -89,15 +89,23 @@ long plan_shares(const fp4kv_cache *c, long units, int hq, long max_len) {
 long units_of(const fp4kv_cache *c, long batch) { return c->attn == FP4KV_MLA ? batch : batch * c->num_kv_heads; }
 
 // Workspace for `shares` shares: (shares + units) partial slots -- GQA `group * q_len` rows each,
-// MLA `hq` rows each -- of d + 2 floats, then the per-unit slot ranges (two int32 per unit).
+// MLA `hq` rows each -- of d + 2 floats, then the per-unit slot ranges (two int32 per unit);
+// MLA then holds the prepared query at the next multiple of 256 bytes (one record per
+// (sequence, query head)).
 size_t workspace_rows(const fp4kv_cache *c, long batch, int hq, long shares, int q_len) {
   const size_t units = (size_t)units_of(c, batch);
   const size_t per = c->attn == FP4KV_MLA ? (size_t)hq : (size_t)(hq / c->num_kv_heads) * (size_t)q_len;
   return ((size_t)shares + units) * per;
 }
-size_t workspace_size(const fp4kv_cache *c, long batch, int hq, long shares, int q_len) {
+size_t partials_bytes(const fp4kv_cache *c, long batch, int hq, long shares, int q_len) {
   const size_t rows = workspace_rows(c, batch, hq, shares, q_len);
   return rows * ((size_t)c->head_dim + 2) * sizeof(float) + (size_t)units_of(c, batch) * 2 * sizeof(int32_t);
+}
+size_t query_offset(size_t partials) { return (partials + 255) / 256 * 256; }
+size_t workspace_size(const fp4kv_cache *c, long batch, int hq, long shares, int q_len) {
+  const size_t part = partials_bytes(c, batch, hq, shares, q_len);
+  if (c->attn != FP4KV_MLA) return part;
+  return query_offset(part) + (size_t)batch * (size_t)hq * kMlaQRecord;
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP4KV_OK : FP4KV_ERR_HIP; }
@@ -177,6 +185,7 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.ws_o = (float *)ws;
   d.ws_ml = (float *)ws + rows * (size_t)c->head_dim;
   d.ws_meta = (int32_t *)(d.ws_ml + rows * 2);
+  d.ws_q = c->attn == FP4KV_MLA ? (uint8_t *)ws + query_offset(partials_bytes(c, batch, hq, shares, q_len)) : nullptr;
   d.out = out;
   d.zero_blocks = zero;
   return FP4KV_OK;

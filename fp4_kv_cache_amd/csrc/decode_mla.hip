@@ -242,128 +242,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   if (scorer) {
     // ---------------- score waves ----------------
-    // Prologue: smoothing, rotation and the dual-residual FP4 query in the B-operand layout:
-    // lane (n, q4) holds channels 128 st + 32 q4 + j (st = 0..3, j = 0..31) of head h0 + n.
-    // Walsh-Hadamard stages on channel bits 0-4 and 7-8 stay in the lane, bits 5 and 6 pair
-    // lanes l ^ 16 and l ^ 32 (the oracle's stage order, h = 1, 2, ..., 256).
+    // The prepared query (mla_qprep) in the B-operand layout: lane (n, q4) takes channels
+    // 128 st + 32 q4 .. + 31 (st = 0..3) of head h0 + n, both passes, their block scale bytes,
+    // the tensor scales and the rope query (K-step s, lane group q4: rope channels 32 s + 8 q4 ..).
     // [pass][K-step][half]: FP4 codes of the lane's 32 channels; NVFP4 keeps one 16-channel
     // half per operand (the other half zero), MXFP4 all 32 in [.][.][0]
     v8i bq[2][4][2];
     int qsb[2][4];           // their E8M0 scale bytes: NVFP4 byte p = half p, MXFP4 byte 0
     float qg[2] = {0.0f, 0.0f};
+    bh8 bqr[2];
     if (active) {
-      const long q0 = ((long)b * a.hq + h0 + n) * (D + R) + 32 * q4;
-      float y[4][32];
-#pragma unroll
-      for (int st = 0; st < 4; st++) {
-        if (a.q_bf16) {
-          const uint16_t *qp = (const uint16_t *)a.q + q0 + 128 * st;
-#pragma unroll
-          for (int j = 0; j < 32; j++) y[st][j] = bf16_to_f32(qp[j]);
-        } else {
-          const float *qp = (const float *)a.q + q0 + 128 * st;
-#pragma unroll
-          for (int j = 0; j < 32; j++) y[st][j] = qp[j];
-        }
-#pragma unroll
-        for (int j = 0; j < 32; j++) y[st][j] = y[st][j] * a.qs[128 * st + 32 * q4 + j];
-      }
-#pragma unroll
-      for (int h = 1; h < 32; h <<= 1)
-#pragma unroll
-        for (int st = 0; st < 4; st++)
-#pragma unroll
-          for (int j = 0; j < 32; j++)
-            if ((j & h) == 0) {
-              const float x0 = y[st][j], x1 = y[st][j + h];
-              y[st][j] = x0 + x1;
-              y[st][j + h] = x0 - x1;
-            }
-#pragma unroll
-      for (int st = 0; st < 4; st++)
-#pragma unroll
-        for (int j = 0; j < 32; j++) y[st][j] = bfly_x16(y[st][j], (lane & 16) != 0);
-#pragma unroll
-      for (int st = 0; st < 4; st++)
-#pragma unroll
-        for (int j = 0; j < 32; j++) y[st][j] = bfly_x32(y[st][j], (lane & 32) != 0);
-#pragma unroll
-      for (int hs = 1; hs < 4; hs <<= 1)
-#pragma unroll
-        for (int st = 0; st < 4; st++)
-          if ((st & hs) == 0) {
-#pragma unroll
-            for (int j = 0; j < 32; j++) {
-              const float x0 = y[st][j], x1 = y[st + hs][j];
-              y[st][j] = x0 + x1;
-              y[st + hs][j] = x0 - x1;
-            }
-          }
-      // pass k quantizes the residual left by pass k - 1
+      const uint8_t *rec = a.ws_q + ((long)b * a.hq + h0 + n) * kMlaQRecord;
 #pragma unroll
       for (int k = 0; k < 2; k++) {
-        if constexpr (NV) {
-          // NVFP4 with power-of-two block scales over 16 channels and G = row max / 1536
-          float rmax = 0.0f;
 #pragma unroll
-          for (int st = 0; st < 4; st++)
-#pragma unroll
-            for (int j = 0; j < 32; j++) rmax = fmaxf(rmax, fabsf(y[st][j]));
-          rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
-          rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-          const float gq = rmax / 1536.0f;
-          const float sixg = 6.0f * gq;
-          const float inv6g = sixg != 0.0f ? 1.0f / sixg : 0.0f;
-#pragma unroll
-          for (int st = 0; st < 4; st++) {
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
-            int sb = 0;
-#pragma unroll
-            for (int p = 0; p < 2; p++) {
-              float bmax = 0.0f;
-#pragma unroll
-              for (int j = 0; j < 16; j++) bmax = fmaxf(bmax, fabsf(y[st][16 * p + j]));
-              const bool valid = bmax > 0.0f && gq > 0.0f;
-              const int e = ceil_log2_clamp(bmax * inv6g, -9, 8);
-              const float S = pow2f(e);
-              const float sg = S * gq;
-              const float rr = (valid && sg != 0.0f) ? 1.0f / sg : 0.0f;   // invalid: every code 0
-#pragma unroll
-              for (int j = 0; j < 16; j++) {
-                const int ch = 16 * p + j;
-                const float x = y[st][ch];
-                const uint32_t c = e2m1_enc(x * rr);
-                w[ch / 8] |= c << (4 * (ch % 8));
-                y[st][ch] = x - (e2m1_dec(c) * S) * gq;
-              }
-              sb |= (e + 127) << (8 * p);
-            }
-            bq[k][st][0] = v8i{(int)w[0], (int)w[1], 0, 0, 0, 0, 0, 0};
-            bq[k][st][1] = v8i{0, 0, (int)w[2], (int)w[3], 0, 0, 0, 0};
-            qsb[k][st] = sb;
+        for (int st = 0; st < 4; st++) {
+          const uint4 w = *(const uint4 *)(rec + 256 * k + 4 * (16 * st + 4 * q4));
+          if constexpr (NV) {
+            bq[k][st][0] = v8i{(int)w.x, (int)w.y, 0, 0, 0, 0, 0, 0};
+            bq[k][st][1] = v8i{0, 0, (int)w.z, (int)w.w, 0, 0, 0, 0};
+            qsb[k][st] = *(const uint16_t *)(rec + 512 + 32 * k + 8 * st + 2 * q4);
+          } else {
+            bq[k][st][0] = bq[k][st][1] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+            qsb[k][st] = rec[512 + 32 * k + 4 * st + q4];
           }
-          qg[k] = gq;
-        } else {
-          // MXFP4: E8M0 per 32 channels (one lane's K-step slice), no tensor scale
-#pragma unroll
-          for (int st = 0; st < 4; st++) {
-            float bmax = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 32; j++) bmax = fmaxf(bmax, fabsf(y[st][j]));
-            const int e = mx_exp(bmax);
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int j = 0; j < 32; j++) {
-              const uint32_t c = e2m1_enc(ldexpf(y[st][j], -e));
-              w[j / 8] |= c << (4 * (j % 8));
-              y[st][j] = y[st][j] - ldexpf(e2m1_dec(c), e);
-            }
-            bq[k][st][0] = bq[k][st][1] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-            qsb[k][st] = e + 127;
-          }
-          qg[k] = 1.0f;
         }
+        qg[k] = *(const float *)(rec + 576 + 4 * k);
       }
+#pragma unroll
+      for (int st = 0; st < 2; st++) bqr[st] = as_bh8(*(const uint4 *)(rec + 640 + 2 * (32 * st + 8 * q4)));
     } else {
 #pragma unroll
       for (int k = 0; k < 2; k++)
@@ -372,26 +279,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           bq[k][st][0] = bq[k][st][1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
           qsb[k][st] = 0;
         }
-    }
-    // rope query (bf16): K-step s, lane group q4, element j is rope channel 32 s + 8 q4 + j
-    bh8 bqr[2];
-    {
-      const long qr = ((long)b * a.hq + h0 + n) * (D + R) + D + 8 * q4;
-#pragma unroll
-      for (int st = 0; st < 2; st++) {
-        uint16_t hb[8];
-        if (a.q_bf16) {
-#pragma unroll
-          for (int j = 0; j < 8; j++) hb[j] = ((const uint16_t *)a.q)[qr + 32 * st + j];
-        } else {  // fp32 rope query rounded to bf16 (nearest even)
-#pragma unroll
-          for (int j = 0; j < 8; j++) {
-            const uint32_t u = __float_as_uint(((const float *)a.q)[qr + 32 * st + j]);
-            hb[j] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-          }
-        }
-        __builtin_memcpy(&bqr[st], hb, 16);
-      }
+      bqr[0] = bqr[1] = as_bh8(uint4{0u, 0u, 0u, 0u});
     }
     // logit coefficients: s = fl32(a1 raw1) + fl32(a2 raw2) + fl32(c_r raw_rope)
     const float a1 = (qg[0] * gk) * a.coef, a2 = (qg[1] * gk) * a.coef, cr = a.coef_rope;
@@ -672,6 +560,116 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// Query preparation, once per (sequence, query head) row before the partials: smoothing,
+// rotation and the dual-residual FP4 query, written as a kMlaQRecord record.  One wave per row;
+// lane i holds latent channels 8 i .. 8 i + 7.  Walsh-Hadamard stages h = 1, 2, 4 stay in the
+// lane, h = 8 .. 256 pair lanes i ^ (h / 8) (the oracle's stage order); each butterfly keeps
+// (lower + upper, lower - upper).  The quantization takes the same fp32 steps per element as
+// the oracle: NVFP4 with power-of-two block scales over 16 channels and G = row max / 1536,
+// MXFP4 with E8M0 scales over 32 channels; pass 2 quantizes the residual of pass 1.
+template <int FMT>
+__global__ __launch_bounds__(256) void mla_qprep(DecodeArgs a) {
+  constexpr int D = kMlaD, R = kMlaR;
+  constexpr bool NV = FMT == kFmtNV;
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (long)a.batch * a.hq) return;
+  uint8_t *rec = a.ws_q + row * kMlaQRecord;
+  const long q0 = row * (D + R);
+  float y[8];
+  if (a.q_bf16) {
+    const uint4 u = *(const uint4 *)((const uint16_t *)a.q + q0 + 8 * lane);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 8; j++) y[j] = bf16_to_f32((uint16_t)(w[j / 2] >> (16 * (j & 1))));
+  } else {
+    const float4 u0 = *(const float4 *)((const float *)a.q + q0 + 8 * lane);
+    const float4 u1 = *(const float4 *)((const float *)a.q + q0 + 8 * lane + 4);
+    y[0] = u0.x; y[1] = u0.y; y[2] = u0.z; y[3] = u0.w;
+    y[4] = u1.x; y[5] = u1.y; y[6] = u1.z; y[7] = u1.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++) y[j] = y[j] * a.qs[8 * lane + j];
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if ((j & h) == 0) {
+        const float x0 = y[j], x1 = y[j + h];
+        y[j] = x0 + x1;
+        y[j + h] = x0 - x1;
+      }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const float x = __shfl_xor(y[j], m);
+      y[j] = upper ? x - y[j] : y[j] + x;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    float lmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) lmax = fmaxf(lmax, fabsf(y[j]));
+    uint32_t w = 0u;
+    if constexpr (NV) {
+      float rmax = lmax;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, m));
+      const float gq = rmax / 1536.0f;
+      const float sixg = 6.0f * gq;
+      const float inv6g = sixg != 0.0f ? 1.0f / sixg : 0.0f;
+      const float bmax = fmaxf(lmax, __shfl_xor(lmax, 1));   // 16-channel block: lanes 2 i, 2 i + 1
+      const bool valid = bmax > 0.0f && gq > 0.0f;
+      const int e = ceil_log2_clamp(bmax * inv6g, -9, 8);
+      const float S = pow2f(e);
+      const float sg = S * gq;
+      const float rr = (valid && sg != 0.0f) ? 1.0f / sg : 0.0f;   // invalid: every code 0
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float x = y[j];
+        const uint32_t c = e2m1_enc(x * rr);
+        w |= c << (4 * j);
+        y[j] = x - (e2m1_dec(c) * S) * gq;
+      }
+      if ((lane & 1) == 0) rec[512 + 32 * k + lane / 2] = (uint8_t)(e + 127);
+      if (lane == 0) *(float *)(rec + 576 + 4 * k) = gq;
+    } else {
+      float bmax = fmaxf(lmax, __shfl_xor(lmax, 1));   // 32-channel block: lanes 4 i .. 4 i + 3
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 2));
+      const int e = mx_exp(bmax);
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const uint32_t c = e2m1_enc(ldexpf(y[j], -e));
+        w |= c << (4 * j);
+        y[j] = y[j] - ldexpf(e2m1_dec(c), e);
+      }
+      if ((lane & 3) == 0) rec[512 + 32 * k + lane / 4] = (uint8_t)(e + 127);
+      if (lane == 0) *(float *)(rec + 576 + 4 * k) = 1.0f;
+    }
+    *(uint32_t *)(rec + 256 * k + 4 * lane) = w;
+  }
+  // rope query as bf16 (an fp32 query rounded to nearest even)
+  if (lane < R / 8) {
+    uint16_t hb[8];
+    if (a.q_bf16) {
+#pragma unroll
+      for (int j = 0; j < 8; j++) hb[j] = ((const uint16_t *)a.q)[q0 + D + 8 * lane + j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const uint32_t u = __float_as_uint(((const float *)a.q)[q0 + D + 8 * lane + j]);
+        hb[j] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+      }
+    }
+    uint4 v;
+    __builtin_memcpy(&v, hb, 16);
+    *(uint4 *)(rec + 640 + 16 * lane) = v;
+  }
+}
+
 // Merge of one (sequence, query head) row over the sequence's partials:
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, then un-rotated (Walsh-Hadamard over
 // the 512 channels, / 512) and un-smoothed (* q_smooth).  Lane l holds channels 8 l .. 8 l + 7.
@@ -780,10 +778,17 @@ static hipError_t launch_mla_fmt(const DecodeArgs &a, unsigned grid, hipStream_t
   return hipGetLastError();
 }
 
-// Grid: the planned shares rounded up to a multiple of 8 (one per XCD residue), times the
-// head-group quads; shares past the device-side count return at once.
+// The query preparation (one wave per row), then the partials.  Grid: the planned shares rounded
+// up to a multiple of 8 (one per XCD residue), times the head-group quads; shares past the
+// device-side count return at once.
 hipError_t launch_mla_partials(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
+  const unsigned qgrid = (unsigned)(((long)a.batch * a.hq + 3) / 4);
+  if (a.fmt == kFmtMX)
+    mla_qprep<kFmtMX><<<qgrid, 256, 0, s>>>(a);
+  else
+    mla_qprep<kFmtNV><<<qgrid, 256, 0, s>>>(a);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const int nhg = a.hq / kMlaHeads;
   const unsigned grid = (unsigned)(((a.n_waves + 7) / 8) * 8 * ((nhg + 3) / 4));
   return a.fmt == kFmtMX ? launch_mla_fmt<kFmtMX>(a, grid, s) : launch_mla_fmt<kFmtNV>(a, grid, s);

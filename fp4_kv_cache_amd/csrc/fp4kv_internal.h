@@ -52,6 +52,7 @@ struct DecodeArgs {
                          // rows = group * q_len; MLA units = batch, rows = hq
   float *ws_ml;          // same rows, [2] each
   int32_t *ws_meta;      // [units][2] = first partial slot of the unit, partial count
+  uint8_t *ws_q;         // MLA: the prepared query, kMlaQRecord bytes per (sequence, head)
   float *out;            // [batch * hq][d]
   int32_t *zero_blocks;  // nullable
 };
@@ -59,6 +60,11 @@ struct DecodeArgs {
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
+// MLA prepared query record of one (sequence, query head): the dual-residual FP4 codes of the
+// rotated, smoothed latent query (pass k, channels 8 i .. 8 i + 7 in dword k * 64 + i), their
+// block scale bytes (pass k at byte 512 + 32 k: NVFP4 per 16 channels, MXFP4 per 32), the two
+// tensor scales (float at 576 and 580) and the rope query as bf16 (at 640).
+constexpr int kMlaQRecord = 768;
 hipError_t launch_mla_partials(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_mla_merge(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_bf16_partials(const DecodeArgs &a, hipStream_t s);

@@ -205,7 +205,7 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
  * needs clearing between calls.
  * Returns FP4KV_ERR_WORKSPACE when fp4_decode_workspace_bytes() for this shape exceeds
  * FP4KV_NOALLOC_SCRATCH_BYTES (64 MiB: GQA up to about 30,000 (sequence, KV head) units at 4
- * query heads per KV head; MLA with 128 query heads up to 127 sequences), and
+ * query heads per KV head; MLA with 128 query heads up to 92 sequences), and
  * FP4KV_ERR_HIP when the scratch address cannot be obtained; otherwise exactly as
  * fp4_decode_attention, whose kernels it runs. */
 #define FP4KV_NOALLOC_SCRATCH_BYTES (64u << 20)
@@ -251,7 +251,11 @@ int fp4_decode_attention_multi(const fp4kv_cache *c, const void *q, int q_dtype,
  *   query head h).  MLA: U = batch (a sequence is a unit), R = num_q_heads.
  *   The tiles of all units are shared out equally among the W shares; the
  *   partials of unit u are the `count` consecutive slots from `first`.  Units
- *   of empty sequences have no partials (their range is not written). */
+ *   of empty sequences have no partials (their range is not written).  MLA then
+ *   holds, from the next multiple of 256 bytes, the prepared query: 768 bytes
+ *   per (sequence, query head), written by fp4_decode_partials before the
+ *   partials (rotated, smoothed dual-residual FP4 codes, their block scales and
+ *   tensor scales, and the rope query as bf16). */
 int fp4_decode_partials(const fp4kv_cache *c, const void *q, int q_dtype, int batch,
                         int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
                         const int32_t *seq_lens, float softmax_scale, void *workspace,

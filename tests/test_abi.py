@@ -119,9 +119,15 @@ def test_split_plan_sizes(lib):
     c2 = _desc(num_kv_heads=2)
     assert L.fp4_decode_workspace_bytes(c2, 1, 8, 4096) == (2048 + 2) * 4 * 130 * 4 + 2 * 8
     # MLA: at most 128 shares (256 workgroups of 64 query heads for 128 heads) + 32 sequences,
-    # 128 partial rows of 512 + 2 floats each, and 32 slot ranges
+    # 128 partial rows of 512 + 2 floats each, and 32 slot ranges; then, from the next multiple
+    # of 256 bytes, one 768-byte prepared query per (sequence, query head)
     cm = _desc(attn=1, num_kv_heads=1, head_dim=512, rope_dim=64, page_size=64)
-    assert L.fp4_decode_workspace_bytes(cm, 32, 128, 16384) == (128 + 32) * 128 * 514 * 4 + 32 * 8
+    part = (128 + 32) * 128 * 514 * 4 + 32 * 8
+    assert part % 256 == 0
+    assert L.fp4_decode_workspace_bytes(cm, 32, 128, 16384) == part + 32 * 128 * 768
+    part3 = (128 + 3) * 128 * 514 * 4 + 3 * 8
+    assert part3 % 256 != 0
+    assert L.fp4_decode_workspace_bytes(cm, 3, 128, 16384) == (part3 + 255) // 256 * 256 + 3 * 128 * 768
 
 
 @pytest.mark.parametrize("attn", [0, 1])
@@ -179,15 +185,15 @@ def test_host_entry_points_from_c(lib, tmp_path):
 
 def test_noalloc_limit_checked_on_the_host(lib):
     """fp4_decode_attention_noalloc refuses, before touching the device, a batch whose workspace
-    would not fit its 64 MiB scratch; the stated limits (GQA ~30,000 units at group 4, MLA 127
+    would not fit its 64 MiB scratch; the stated limits (GQA ~30,000 units at group 4, MLA 92
     sequences at 128 heads) follow from fp4_decode_workspace_bytes."""
     limit = 64 << 20
     c = _desc(num_kv_heads=8)
     assert L.fp4_decode_workspace_bytes(c, 3700, 32, 4096) <= limit        # 29,600 units
     assert L.fp4_decode_workspace_bytes(c, 3800, 32, 4096) > limit         # 30,400 units
     cm = _desc(attn=1, num_kv_heads=1, head_dim=512, rope_dim=64, page_size=64)
-    assert L.fp4_decode_workspace_bytes(cm, 127, 128, 4096) <= limit
-    assert L.fp4_decode_workspace_bytes(cm, 128, 128, 4096) > limit
+    assert L.fp4_decode_workspace_bytes(cm, 92, 128, 4096) <= limit
+    assert L.fp4_decode_workspace_bytes(cm, 93, 128, 4096) > limit
     for f in ("k_codes", "k_scales", "v_codes", "v_scales", "stage", "k_tensor_scale", "v_tensor_scale",
               "k_smooth_inv", "q_smooth"):
         setattr(c, f, 0x1000)
