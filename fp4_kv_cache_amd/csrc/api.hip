@@ -90,8 +90,8 @@ long units_of(const fp4kv_cache *c, long batch) { return c->attn == FP4KV_MLA ? 
 
 // Workspace for `shares` shares: (shares + units) partial slots -- GQA `group * q_len` rows each,
 // MLA `hq` rows each -- of d + 2 floats, then the per-unit slot ranges (two int32 per unit);
-// MLA then holds the prepared query at the next multiple of 256 bytes (one record per
-// (sequence, query head)).
+// MLA then holds the prepared query (one record per (sequence, query head)) from the next
+// multiple of 256 bytes after the partials of the most shares a launch may plan.
 size_t workspace_rows(const fp4kv_cache *c, long batch, int hq, long shares, int q_len) {
   const size_t units = (size_t)units_of(c, batch);
   const size_t per = c->attn == FP4KV_MLA ? (size_t)hq : (size_t)(hq / c->num_kv_heads) * (size_t)q_len;
@@ -185,7 +185,11 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.ws_o = (float *)ws;
   d.ws_ml = (float *)ws + rows * (size_t)c->head_dim;
   d.ws_meta = (int32_t *)(d.ws_ml + rows * 2);
-  d.ws_q = c->attn == FP4KV_MLA ? (uint8_t *)ws + query_offset(partials_bytes(c, batch, hq, shares, q_len)) : nullptr;
+  // the prepared query sits at a place the caller can find: the last batch * hq records of the
+  // size the workspace query reports
+  d.ws_q = c->attn == FP4KV_MLA
+               ? (uint8_t *)ws + query_offset(partials_bytes(c, batch, hq, max_shares(c, hq), q_len))
+               : nullptr;
   d.out = out;
   d.zero_blocks = zero;
   return FP4KV_OK;

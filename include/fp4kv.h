@@ -251,11 +251,15 @@ int fp4_decode_attention_multi(const fp4kv_cache *c, const void *q, int q_dtype,
  *   query head h).  MLA: U = batch (a sequence is a unit), R = num_q_heads.
  *   The tiles of all units are shared out equally among the W shares; the
  *   partials of unit u are the `count` consecutive slots from `first`.  Units
- *   of empty sequences have no partials (their range is not written).  MLA then
- *   holds, from the next multiple of 256 bytes, the prepared query: 768 bytes
- *   per (sequence, query head), written by fp4_decode_partials before the
- *   partials (rotated, smoothed dual-residual FP4 codes, their block scales and
- *   tensor scales, and the rope query as bf16). */
+ *   of empty sequences have no partials (their range is not written).  MLA
+ *   also holds the prepared query, written by fp4_decode_partials before the
+ *   partials, in the last batch * num_q_heads * 768 bytes of the size
+ *   fp4_decode_workspace_bytes reports: per (sequence, query head), row
+ *   b * num_q_heads + h, the rotated, smoothed dual-residual FP4 codes of pass k
+ *   at byte 256 k (channels 2i, 2i+1 in byte i, low nibble first), their block
+ *   scale bytes (E8M0 exponent + 127; NVFP4 per 16 channels, MXFP4 per 32) at
+ *   512 + 32 k, the tensor scales G1, G2 (f32) at 576 and 580, and the rope
+ *   query as bf16 at 640. */
 int fp4_decode_partials(const fp4kv_cache *c, const void *q, int q_dtype, int batch,
                         int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
                         const int32_t *seq_lens, float softmax_scale, void *workspace,

@@ -421,3 +421,45 @@ def test_workspace_from_a_bound_below_the_block_table(torch_dev, name):
         compare_gqa(built, tol=TOL)
     else:
         compare_mla(built, tol=TOL)
+
+
+@pytest.mark.parametrize("name,dtype", [("mla", "bf16"), ("mla_mxfp4", "bf16"), ("mla", "fp32"),
+                                        ("mla_mxfp4", "fp32")])
+def test_mla_prepared_query_is_the_oracles(torch_dev, name, dtype):
+    """The MLA query that the partial kernel consumes -- smoothed, rotated, dual-residual FP4 --
+    read back from the workspace (the last batch * heads records of the reported size): the
+    codes of both passes, the block scale bytes of valid blocks and the two tensor scales equal
+    the oracle's quantize_query bit for bit, and the rope query is the input rounded to bf16.
+    This is the query-code agreement measured directly, for every row of the batch."""
+    import torch
+    from oracle import query as QY
+    lens = np.array([300, 0, 1025], np.int32)
+    w = W.workload(name, batch=len(lens), hq=48, dtype=dtype)
+    say("prepared query", name, dtype, lens.tolist())
+    built = harness.build(w, lens=lens)
+    q = built.queries()
+    B, hq, D = len(lens), w["hq"], w["d"]
+    nb = built.cache.workspace_bytes(B, hq, built.bt.shape[1] * w["page"])
+    ws = torch.zeros(nb, dtype=torch.uint8, device=built.device)
+    built.cache.decode(q, built.bt, built.seq_lens, W.softmax_scale(w), workspace=ws)
+    torch.cuda.synchronize()
+    rec = ws[nb - B * hq * 768:].cpu().numpy().reshape(B, hq, 768)
+    qn = q.float().cpu().numpy()
+    qs = built.calib[1][0]
+    blk = 16 if w["fmt"] == W.NVFP4 else 32
+    for b in range(B):
+        qq = QY.quantize_query(qn[b, :, :D], qs, w["fmt"])
+        for k, (c, e, v, G) in enumerate(((qq.c1, qq.e1, qq.v1, qq.G1), (qq.c2, qq.e2, qq.v2, qq.G2))):
+            packed = rec[b, :, 256 * k:256 * (k + 1)]
+            got = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(hq, D)
+            bad = np.argwhere(got != c)
+            assert bad.size == 0, "seq %d pass %d: %d code mismatches, first (head, channel) %s" % (
+                b, k + 1, len(bad), bad[0].tolist())
+            sb = rec[b, :, 512 + 32 * k:512 + 32 * k + D // blk].astype(np.int32)
+            want = np.asarray(e, np.int32) + 127
+            assert np.array_equal(np.where(v, sb, 0), np.where(v, want, 0)), (b, k)
+            gs = rec[b, :, 576 + 4 * k:580 + 4 * k].copy().view(np.float32).ravel()
+            assert np.array_equal(gs.view(np.uint32), np.asarray(G, np.float32).view(np.uint32)), (b, k)
+        rope = rec[b, :, 640:768].copy().view(np.uint16)
+        assert np.array_equal(rope, W.bf16_bits(W.bf16_round(qn[b, :, D:]))), b
+    say("prepared query: %d rows, both passes bit-exact" % (B * hq))
