@@ -16,7 +16,8 @@
 // behind, taking the probabilities, their block exponents and the online-softmax rescale
 // factor from a small LDS handoff.  Each SIMD holds one wave of each kind.  Each tile --
 // latent codes (token-major), rope keys and scales -- is staged once per workgroup in LDS
-// with direct global -> LDS loads issued a whole tile ahead.
+// with direct global -> LDS loads, issued a whole tile ahead by the value waves.  The query is
+// prepared beforehand by its own kernel (mla_qprep), once per (sequence, query head).
 //
 // Both contractions run on v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 operands:
 //  * K index -> channel: in K-step st lane group q4 (lanes 16 q4 .. + 15) holds channels
@@ -191,33 +192,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int pg = pgl[(j % CAP) * NPT + (NPT == 1 ? 0 : r / P)];
     return (long)pg * P + ((tb + j) * 128 + r) % P;
   };
-  // stage relative tile j: 32 latent, 16 rope and the scale loads, spread over the waves
+  // stage relative tile j: 32 latent, 16 rope and the scale loads, issued by the value waves
+  // (the score waves carry the longer dependency chain per tile)
   auto stage_tile = [&](int j) {
+    if (wv < 4) return;
+    const int vw = wv - 4;
     uint8_t *Lt = lat + (j % 3) * LAT;
     uint8_t *Rt = rope + (j & 1) * ROPE;
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-      const int g = 4 * wv + m;
+    for (int m = 0; m < 8; m++) {
+      const int g = 8 * vw + m;
       const int r = 4 * g + (lane >> 4);
       const int c = (lane & 15) ^ swz_lat(r);
       lds_load16(a.k_codes + row_of(j, r) * (D / 2) + 16 * c, Lt + 1024 * g);
     }
 #pragma unroll
-    for (int m = 0; m < 2; m++) {
-      const int g = 2 * wv + m;
+    for (int m = 0; m < 4; m++) {
+      const int g = 4 * vw + m;
       const int r = 8 * g + (lane >> 3);
       const int c = (lane & 7) ^ swz_rope(r);
       lds_load16((const uint8_t *)a.k_rope + row_of(j, r) * (2 * R) + 16 * c, Rt + 1024 * g);
     }
     if constexpr (NV) {
-      if (wv == 0 && lane < 16) {
+      if (vw == 0 && lane < 16) {
         const int tr = lane >> 1;   // token tile (16 tokens): 32 scale bytes
         const int pg = pgl[(j % CAP) * NPT + (NPT == 1 ? 0 : 16 * tr / P)];
         const int off = (((tb + j) * 128 + 16 * tr) % P) / 16;
         lds_load16(a.k_scales + ((long)pg * (P / 16) + off) * 32 + 16 * (lane & 1), scl + (j % 3) * SCL);
       }
     } else {
-      if (wv == 0 && lane < 4) {
+      if (vw == 0 && lane < 4) {
         const int t = 32 * lane;   // token block (32 tokens): 16 scale bytes
         const int pg = pgl[(j % CAP) * NPT + (NPT == 1 ? 0 : t / P)];
         lds_load16(a.k_scales + ((long)pg * (P / 32) + (((tb + j) * 128 + t) % P) / 32) * 16, scl + (j % 3) * SCL);
