@@ -101,6 +101,16 @@ template <int SEL>
 __device__ __forceinline__ uint32_t cvt_pk(uint32_t old, float a, float b, float sc) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, sc, SEL);
 }
+// The two E2M1 codes of byte SEL of w, times the power of two `sc` (exact): hardware decode.
+typedef float v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2f dec_pk(uint32_t w, int sel, float sc) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+  }
+}
 __device__ __forceinline__ uint32_t pack8(const float *x0, const float *x1, float sc) {
   uint32_t w = 0u;
   w = cvt_pk<0>(w, x0[0], x0[1], sc);

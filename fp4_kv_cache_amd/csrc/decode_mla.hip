@@ -564,6 +564,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// Value of lane l ^ M (M = 1, 2, 4, 8): quad permutes and a row rotation by DPP, xor 4 by a
+// swizzle inside each 32-lane half.
+template <int M>
+__device__ __forceinline__ float xlane(float x) {
+  const int v = __float_as_int(x);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  if constexpr (M == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x101F));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+}
+// One Walsh-Hadamard stage across lane bit M of the values x[0..7]: the lane with the bit clear
+// keeps lower + upper, the other lower - upper (fma with +-1 rounds exactly like the add or
+// subtract).
+template <int M>
+__device__ __forceinline__ void fwht_lanes(float (&x)[8], int lane) {
+  const float sg = (lane & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    if constexpr (M <= 8) {
+      x[j] = fmaf(sg, x[j], xlane<M>(x[j]));
+    } else {
+      const uint32_t u = __float_as_uint(x[j]);
+      const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      x[j] = fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
+    }
+  }
+}
+// Maximum over lane bit M (M = 1 .. 32).
+template <int M>
+__device__ __forceinline__ float max_lanes(float x) {
+  if constexpr (M <= 8) {
+    return fmaxf(x, xlane<M>(x));
+  } else {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+
 // Query preparation, once per (sequence, query head) row before the partials: smoothing,
 // rotation and the dual-residual FP4 query, written as a kMlaQRecord record.  One wave per row;
 // lane i holds latent channels 8 i .. 8 i + 7.  Walsh-Hadamard stages h = 1, 2, 4 stay in the
@@ -603,15 +644,12 @@ __global__ __launch_bounds__(256) void mla_qprep(DecodeArgs a) {
         y[j] = x0 + x1;
         y[j + h] = x0 - x1;
       }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const float x = __shfl_xor(y[j], m);
-      y[j] = upper ? x - y[j] : y[j] + x;
-    }
-  }
+  fwht_lanes<1>(y, lane);
+  fwht_lanes<2>(y, lane);
+  fwht_lanes<4>(y, lane);
+  fwht_lanes<8>(y, lane);
+  fwht_lanes<16>(y, lane);
+  fwht_lanes<32>(y, lane);
 #pragma unroll
   for (int k = 0; k < 2; k++) {
     float lmax = 0.0f;
@@ -619,36 +657,45 @@ __global__ __launch_bounds__(256) void mla_qprep(DecodeArgs a) {
     for (int j = 0; j < 8; j++) lmax = fmaxf(lmax, fabsf(y[j]));
     uint32_t w = 0u;
     if constexpr (NV) {
-      float rmax = lmax;
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, m));
+      float rmax = max_lanes<1>(lmax);
+      rmax = max_lanes<32>(max_lanes<16>(max_lanes<8>(max_lanes<4>(max_lanes<2>(rmax)))));
       const float gq = rmax / 1536.0f;
       const float sixg = 6.0f * gq;
       const float inv6g = sixg != 0.0f ? 1.0f / sixg : 0.0f;
-      const float bmax = fmaxf(lmax, __shfl_xor(lmax, 1));   // 16-channel block: lanes 2 i, 2 i + 1
+      const float bmax = max_lanes<1>(lmax);   // 16-channel block: lanes 2 i, 2 i + 1
       const bool valid = bmax > 0.0f && gq > 0.0f;
       const int e = ceil_log2_clamp(bmax * inv6g, -9, 8);
       const float S = pow2f(e);
       const float sg = S * gq;
       const float rr = (valid && sg != 0.0f) ? 1.0f / sg : 0.0f;   // invalid: every code 0
+      // codes of x * rr by the hardware conversion (nearest even, saturating at 6); the residual
+      // takes dec(code) * S from the hardware decode (exact), then * G
+      w = cvt_pk<0>(w, y[0] * rr, y[1] * rr, 1.0f);
+      w = cvt_pk<1>(w, y[2] * rr, y[3] * rr, 1.0f);
+      w = cvt_pk<2>(w, y[4] * rr, y[5] * rr, 1.0f);
+      w = cvt_pk<3>(w, y[6] * rr, y[7] * rr, 1.0f);
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const float x = y[j];
-        const uint32_t c = e2m1_enc(x * rr);
-        w |= c << (4 * j);
-        y[j] = x - (e2m1_dec(c) * S) * gq;
+      for (int j = 0; j < 8; j += 2) {
+        const v2f d = dec_pk(w, j / 2, S);
+        y[j] = y[j] - d.x * gq;
+        y[j + 1] = y[j + 1] - d.y * gq;
       }
       if ((lane & 1) == 0) rec[512 + 32 * k + lane / 2] = (uint8_t)(e + 127);
       if (lane == 0) *(float *)(rec + 576 + 4 * k) = gq;
     } else {
-      float bmax = fmaxf(lmax, __shfl_xor(lmax, 1));   // 32-channel block: lanes 4 i .. 4 i + 3
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 2));
+      const float bmax = max_lanes<2>(max_lanes<1>(lmax));   // 32-channel block: lanes 4 i .. 4 i + 3
       const int e = mx_exp(bmax);
+      // codes of y / 2^e and the residual y - dec(code) 2^e, both by the hardware conversions
+      const float se = ldexpf(1.0f, e);
+      w = cvt_pk<0>(w, y[0], y[1], se);
+      w = cvt_pk<1>(w, y[2], y[3], se);
+      w = cvt_pk<2>(w, y[4], y[5], se);
+      w = cvt_pk<3>(w, y[6], y[7], se);
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const uint32_t c = e2m1_enc(ldexpf(y[j], -e));
-        w |= c << (4 * j);
-        y[j] = y[j] - ldexpf(e2m1_dec(c), e);
+      for (int j = 0; j < 8; j += 2) {
+        const v2f d = dec_pk(w, j / 2, se);
+        y[j] = y[j] - d.x;
+        y[j + 1] = y[j + 1] - d.y;
       }
       if ((lane & 3) == 0) rec[512 + 32 * k + lane / 4] = (uint8_t)(e + 127);
       if (lane == 0) *(float *)(rec + 576 + 4 * k) = 1.0f;
@@ -754,15 +801,12 @@ __global__ __launch_bounds__(64) void mla_merge(DecodeArgs a) {
         y[j] = x0 + x1;
         y[j + hh] = x0 - x1;
       }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const float x = __shfl_xor(y[j], m);
-      y[j] = upper ? x - y[j] : y[j] + x;
-    }
-  }
+  fwht_lanes<1>(y, lane);
+  fwht_lanes<2>(y, lane);
+  fwht_lanes<4>(y, lane);
+  fwht_lanes<8>(y, lane);
+  fwht_lanes<16>(y, lane);
+  fwht_lanes<32>(y, lane);
   const float *qs = a.qs + 8 * lane;
 #pragma unroll
   for (int j = 0; j < 8; j++) y[j] = y[j] * (1.0f / 512.0f) * qs[j];
