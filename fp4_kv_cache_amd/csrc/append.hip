@@ -35,8 +35,7 @@ __device__ __forceinline__ float nv_block_err(const float *x, uint32_t c, float 
   float err = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; i++) {
-    uint32_t q = e2m1_enc(x[i] * r);
-    float xh = (e2m1_dec(q) * S) * G;
+    float xh = (e2m1_round_hw(x[i] * r) * S) * G;
     float d = x[i] - xh;
     err = err + d * d;
   }
@@ -50,7 +49,7 @@ __device__ __forceinline__ void nv_block_codes(const float *x, uint32_t c, float
   float r = (sg != 0.0f) ? 1.0f / sg : 0.0f;
 #pragma unroll
   for (int i = 0; i < N; i += 2)
-    codes[i / 2] = (uint8_t)(e2m1_enc(x[i] * r) | (e2m1_enc(x[i + 1] * r) << 4));
+    codes[i / 2] = (uint8_t)e2m1_enc2_hw(x[i] * r, x[i + 1] * r);
 }
 
 __device__ __forceinline__ uint32_t nv_default_scale(float amax, float G) {
@@ -86,8 +85,7 @@ __device__ __forceinline__ float mx_block_err(const float *x, int e) {
   float err = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; i++) {
-    uint32_t q = e2m1_enc(ldexpf(x[i], -e));
-    float xh = ldexpf(e2m1_dec(q), e);
+    float xh = ldexpf(e2m1_round_hw(ldexpf(x[i], -e)), e);
     float d = x[i] - xh;
     err = err + d * d;
   }
@@ -98,7 +96,7 @@ template <int N>
 __device__ __forceinline__ void mx_block_codes(const float *x, int e, uint8_t *codes) {
 #pragma unroll
   for (int i = 0; i < N; i += 2)
-    codes[i / 2] = (uint8_t)(e2m1_enc(ldexpf(x[i], -e)) | (e2m1_enc(ldexpf(x[i + 1], -e)) << 4));
+    codes[i / 2] = (uint8_t)e2m1_enc2_hw(ldexpf(x[i], -e), ldexpf(x[i + 1], -e));
 }
 
 // MXFP4 exponent search (e0, e0+1, e0-1).
@@ -626,8 +624,8 @@ __global__ __launch_bounds__(kLatThreads) void latent_append(AppendArgs a) {
 #pragma unroll
       for (int kk = 0; kk < NC; kk++) {
         float dx;
-        if constexpr (FMT == kFmtNV) dx = x - (e2m1_dec(e2m1_enc(x * c_r[kk])) * c_s[kk]) * G;
-        else dx = x - ldexpf(e2m1_dec(e2m1_enc(ldexpf(x, -c_e[kk]))), c_e[kk]);
+        if constexpr (FMT == kFmtNV) dx = x - (e2m1_round_hw(x * c_r[kk]) * c_s[kk]) * G;
+        else dx = x - ldexpf(e2m1_round_hw(ldexpf(x, -c_e[kk])), c_e[kk]);
         dd[kk][st_ct][e] = dx * dx;
       }
     }
@@ -679,7 +677,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_append(AppendArgs a) {
 #pragma unroll
       for (int u = 0; u < 8; u++) {
         const float x = X(k, ct * B + 2 * j + u);
-        const uint32_t q = FMT == kFmtNV ? e2m1_enc(x * r) : e2m1_enc(ldexpf(x, -eb));
+        const uint32_t q = FMT == kFmtNV ? e2m1_enc_hw(x * r) : e2m1_enc_hw(ldexpf(x, -eb));
         w |= q << (4 * u);
       }
       *(uint32_t *)(dst + j) = w;

@@ -685,17 +685,17 @@ __global__ __launch_bounds__(256) void mla_qprep(DecodeArgs a) {
     } else {
       const float bmax = max_lanes<2>(max_lanes<1>(lmax));   // 32-channel block: lanes 4 i .. 4 i + 3
       const int e = mx_exp(bmax);
-      // codes of y / 2^e and the residual y - dec(code) 2^e, both by the hardware conversions
-      const float se = ldexpf(1.0f, e);
-      w = cvt_pk<0>(w, y[0], y[1], se);
-      w = cvt_pk<1>(w, y[2], y[3], se);
-      w = cvt_pk<2>(w, y[4], y[5], se);
-      w = cvt_pk<3>(w, y[6], y[7], se);
+      // codes of y 2^-e and the residual y - dec(code) 2^e, the conversions by the hardware
+      // with scale 1 (2^e itself can be subnormal: e reaches -127)
+      w = cvt_pk<0>(w, ldexpf(y[0], -e), ldexpf(y[1], -e), 1.0f);
+      w = cvt_pk<1>(w, ldexpf(y[2], -e), ldexpf(y[3], -e), 1.0f);
+      w = cvt_pk<2>(w, ldexpf(y[4], -e), ldexpf(y[5], -e), 1.0f);
+      w = cvt_pk<3>(w, ldexpf(y[6], -e), ldexpf(y[7], -e), 1.0f);
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const v2f d = dec_pk(w, j / 2, se);
-        y[j] = y[j] - d.x;
-        y[j + 1] = y[j + 1] - d.y;
+        const v2f d = dec_pk(w, j / 2, 1.0f);
+        y[j] = y[j] - ldexpf(d.x, e);
+        y[j + 1] = y[j + 1] - ldexpf(d.y, e);
       }
       if ((lane & 3) == 0) rec[512 + 32 * k + lane / 4] = (uint8_t)(e + 127);
       if (lane == 0) *(float *)(rec + 576 + 4 * k) = 1.0f;

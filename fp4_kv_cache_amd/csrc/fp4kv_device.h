@@ -44,6 +44,22 @@ __device__ __forceinline__ float e2m1_dec(uint32_t c) {
   return __uint_as_float(__float_as_uint(ldexpf(mant, ex)) | ((c & 8u) << 28));
 }
 
+// The same conversions by the hardware (v_cvt_scalef32_pk_fp4_f32 / v_cvt_scalef32_pk_f32_fp4
+// with scale 1): round to nearest with ties to the even code and saturation at +-6, so for
+// every finite input the code equals e2m1_enc's (checked on the GPU at every rounding
+// threshold, its fp32 neighbours, the grid, values past 6, zeros and subnormals, both signs);
+// the decode is exact.  One instruction each instead of a compare chain.
+__device__ __forceinline__ uint32_t e2m1_enc_hw(float y) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, y, 1.0f, 0) & 0xFu;
+}
+// byte = code(y0) | code(y1) << 4
+__device__ __forceinline__ uint32_t e2m1_enc2_hw(float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y0, y1, 1.0f, 0) & 0xFFu;
+}
+__device__ __forceinline__ float e2m1_dec_hw(uint32_t c) { return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0)[0]; }
+// dec(enc(y)): y rounded onto the E2M1 grid
+__device__ __forceinline__ float e2m1_round_hw(float y) { return e2m1_dec_hw(e2m1_enc_hw(y)); }
+
 // E4M3 byte -> fp32 (exact).  0x7F / 0xFF decode to NaN.
 __device__ __forceinline__ float e4m3_dec(uint32_t c) {
   uint32_t e = (c >> 3) & 15u, m = c & 7u;
