@@ -307,18 +307,18 @@ void gqa_partials(DecodeArgs a) {
       const float r = (valid && sg != 0.0f) ? 1.0f / sg : 0.0f;
 #pragma unroll
       for (int j = 0; j < EPL; j++) {
-        const uint32_t c = e2m1_enc(y[j] * r);
+        const uint32_t c = e2m1_enc_hw(y[j] * r);
         w[j / 8] |= c << (4 * (j % 8));
-        y[j] = y[j] - (e2m1_dec(c) * S) * gq;
+        y[j] = y[j] - (e2m1_dec_hw(c) * S) * gq;
       }
       if (!valid) e = -128;
     } else {
       e = mx_exp(bmax);
 #pragma unroll
       for (int j = 0; j < EPL; j++) {
-        const uint32_t c = e2m1_enc(ldexpf(y[j], -e));
+        const uint32_t c = e2m1_enc_hw(ldexpf(y[j], -e));
         w[j / 8] |= c << (4 * (j % 8));
-        y[j] = y[j] - ldexpf(e2m1_dec(c), e);
+        y[j] = y[j] - ldexpf(e2m1_dec_hw(c), e);
       }
     }
     // packed codes of channels c0 .. c0 + EPL - 1 (EPL / 2 bytes)

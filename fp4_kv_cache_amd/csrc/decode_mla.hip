@@ -153,6 +153,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __align__(16) uint8_t scl[3 * SCL];
   __shared__ __align__(16) uint4 hand[2][4][2][64];   // [tile & 1][group][part][lane]
   __shared__ uint32_t lut[256];
+  // NVFP4: pass words and sign masks of a tile's scales [tile & 1][token tile][channel block],
+  // written by the value waves one iteration before their P.V reads them
+  __shared__ __align__(16) uint2 pw[NV ? 2 * 8 * 32 : 2];
   __shared__ int pgl[kMaxSplitPages];
 
   if constexpr (NV) {
@@ -452,6 +455,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll 1
     for (int j = 0; j <= nt; j++) {
       next_loads(j);
+      if constexpr (NV) {
+        if (j < nt) {   // tile j's scales arrived before the last barrier
+          const int e = 64 * (wv - 4) + lane;   // token tile e / 32, channel block e % 32
+          const uint32_t w = lut[scl[(j % 3) * SCL + e]];
+          pw[(j & 1) * 256 + e] = uint2{w, pass_neg_mask(w)};
+        }
+      }
       if (active && j >= 1) {
         const int jp = j - 1;
         const uint8_t *Lt = lat + (jp % 3) * LAT;
@@ -472,21 +482,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (NV) {
           const v8i p0 = {(int)hp.x, (int)hp.y, 0, 0, 0, 0, 0, 0};
           const v8i p1 = {0, 0, (int)hp.z, (int)hp.w, 0, 0, 0, 0};
-          // tile scales of the lane's token tiles 2 q4 and 2 q4 + 1 (the two P parities)
-          int lt[2][4][2];
-          const uint4 sa0 = *(const uint4 *)(St + (2 * q4) * 32), sa1 = *(const uint4 *)(St + (2 * q4) * 32 + 16);
-          const uint4 sb0 = *(const uint4 *)(St + (2 * q4 + 1) * 32), sb1 = *(const uint4 *)(St + (2 * q4 + 1) * 32 + 16);
-          auto read_vals = [&](int c, v2i (*o)[2], int (*l)[2]) {
+          // pass words and sign masks of the lane's token tiles 2 q4 (P parity 0) and 2 q4 + 1
+          // (parity 1), two channel groups per 16-byte read
+          const uint2 *pa = pw + (jp & 1) * 256 + (2 * q4) * 32, *pb = pa + 32;
+          auto read_vals = [&](int c, v2i (*o)[2], uint4 (*l)[2]) {
 #pragma unroll
             for (int k = 0; k < 4; k++) {
               const int cg = 4 * c + k;
               const int off = 8 * (cg & 1);
               o[k][0] = lds_read_tr4(rowa + (((cg >> 1) ^ swa) << 4) + off);
               o[k][1] = lds_read_tr4(rowb + (((cg >> 1) ^ swb) << 4) + off);
-              l[k][0] = (int)lut[byte_of(cg < 16 ? sa0 : sa1, cg & 15)];
-              l[k][1] = (int)lut[byte_of(cg < 16 ? sb0 : sb1, cg & 15)];
+            }
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+              l[h][0] = *(const uint4 *)(pa + 4 * c + 2 * h);
+              l[h][1] = *(const uint4 *)(pb + 4 * c + 2 * h);
             }
           };
+          uint4 lt[2][2][2];
           read_vals(0, vt[0], lt[0]);
 #pragma unroll
           for (int c = 0; c < 8; c++) {
@@ -496,10 +509,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const int cg = 4 * c + k;
               const v2i lo = vt[c & 1][k][0], hi = vt[c & 1][k][1];
               const v8i av = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
-              const int l0 = lt[c & 1][k][0], l1 = lt[c & 1][k][1];
+              const uint4 wa = lt[c & 1][k >> 1][0], wb = lt[c & 1][k >> 1][1];
+              const int l0 = (int)((k & 1) ? wa.z : wa.x), l1 = (int)((k & 1) ? wb.z : wb.x);
+              const uint32_t m0 = (k & 1) ? wa.w : wa.y, m1 = (k & 1) ? wb.w : wb.y;
               // the third terms' passes take the values with flipped signs where the term is
               // negative; P of one parity is zero in the other half, so one copy serves both
-              const uint32_t m0 = pass_neg_mask((uint32_t)l0), m1 = pass_neg_mask((uint32_t)l1);
               const v8i avn = {(int)((uint32_t)lo[0] ^ m0), (int)((uint32_t)lo[1] ^ m0), (int)((uint32_t)hi[0] ^ m1),
                                (int)((uint32_t)hi[1] ^ m1), 0, 0, 0, 0};
               v4f acc = mfma4<0, 0>(av, p0, o_run[cg], l0, pb0);
