@@ -14,32 +14,35 @@ __device__ __forceinline__ v4f mfma4(const v8i &a, const v8i &b, v4f c, int sa, 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, OPA, sa, OPB, sb);
 }
 
-// An E4M3 scale S on the E8M0-scaled MFMA: S written as a sum of at most three signed powers
-// of two, each applied by one MFMA pass whose scale byte is that power (byte 0 = 2^-127 for an
-// absent term: its products fall below fp32 resolution).  Normal S = 2^E (8 + m) / 8 uses the
-// set bits of 8 + m, except m = 7, where 15 = 16 - 1; subnormal S = m 2^-9 uses the bits of m.
-// Bytes 0-2 hold the three passes' scale bytes; byte 3 is 0x88 when the third term is
-// negative (the pass then runs on operand codes with their sign bits flipped), else 0.
-// Codes 0x7F and above (NaN, negative) give no term.
+// An E4M3 scale S on the E8M0-scaled MFMA: S = t0 + t1 - t2 with t0, t1, t2 powers of two or
+// zero, each applied by one MFMA pass whose scale byte is that power (byte 0 = 2^-127 for an
+// absent term: its products fall below fp32 resolution).  The third term is always the
+// subtracted one, so its pass runs on operands with flipped sign bits for every row alike.
+// In units of 2^(E-3), a normal S = 2^E (8 + m) / 8 is
+//   8, 8+1, 8+2, 8+4-1, 8+4, 16+1-4, 16-2, 16-1   (m = 0 .. 7),
+// a subnormal S = m 2^-9 is 1, 2, 2+1, 4, 4+1, 4+2, 8-1.  Bytes 0 and 1 hold the added terms,
+// byte 2 the subtracted one (E8M0 exponent + 127).  Codes 0x7F and above give no term.
 constexpr uint32_t e4m3_pass_word(int c) {
   if (c < 0 || c >= 0x7F) return 0u;
   const int ef = c >> 3, m = c & 7;
-  if (ef != 0 && m == 7) {
-    const int E = ef - 7;
-    return (uint32_t)(E + 1 + 127) | ((uint32_t)(E - 3 + 127) << 16) | 0x88000000u;
+  // exponents (relative to the unit) of t0, t1, t2; -99 = absent
+  constexpr int kAbs = -99;
+  const int unit = ef != 0 ? ef - 7 - 3 : -9;
+  int e0 = kAbs, e1 = kAbs, e2 = kAbs;
+  if (ef != 0) {
+    constexpr int t0[8] = {3, 3, 3, 3, 3, 4, 4, 4};
+    constexpr int t1[8] = {kAbs, 0, 1, 2, 2, 0, kAbs, kAbs};
+    constexpr int t2[8] = {kAbs, kAbs, kAbs, 0, kAbs, 2, 1, 0};
+    e0 = t0[m], e1 = t1[m], e2 = t2[m];
+  } else {
+    constexpr int t0[8] = {kAbs, 0, 1, 1, 2, 2, 2, 3};
+    constexpr int t1[8] = {kAbs, kAbs, kAbs, 0, kAbs, 0, 1, kAbs};
+    constexpr int t2[8] = {kAbs, kAbs, kAbs, kAbs, kAbs, kAbs, kAbs, 0};
+    e0 = t0[m], e1 = t1[m], e2 = t2[m];
   }
-  // digit k of (implicit bit, m2, m1, m0) has exponent top - k
-  const int top = ef != 0 ? ef - 7 : -6;
-  const int bits = (ef != 0 ? 8 : 0) | m;
-  uint32_t w = 0u;
-  int slot = 0;
-  for (int k = 0; k < 4; k++)
-    if (bits & (8 >> k)) w |= (uint32_t)(top - k + 127) << (8 * slot++);
-  return w;
+  auto byte = [unit](int e) -> uint32_t { return e == kAbs ? 0u : (uint32_t)(unit + e + 127); };
+  return byte(e0) | (byte(e1) << 8) | (byte(e2) << 16);
 }
-
-// Sign-bit mask of the third pass of a pass word (0x88888888 or 0): byte 3 replicated.
-__device__ __forceinline__ uint32_t pass_neg_mask(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x03030303u); }
 
 namespace detail {
 constexpr double pow2c(int e) {
@@ -48,7 +51,7 @@ constexpr double pow2c(int e) {
   for (; e < 0; e++) r *= 0.5;
   return r;
 }
-// every finite non-negative E4M3 code: the signed sum of the word's terms is the scale itself
+// every finite non-negative E4M3 code: t0 + t1 - t2 is the scale itself
 constexpr bool pass_words_are_exact() {
   for (int c = 0; c < 0x7F; c++) {
     const uint32_t w = e4m3_pass_word(c);
@@ -56,10 +59,9 @@ constexpr bool pass_words_are_exact() {
     for (int k = 0; k < 3; k++) {
       const int b = (int)((w >> (8 * k)) & 0xFFu);
       if (b == 0) continue;
-      const double t = pow2c(b - 127);
-      s += (k == 2 && (w >> 24) == 0x88u) ? -t : t;
+      s += (k == 2 ? -1.0 : 1.0) * pow2c(b - 127);
     }
-    if ((w >> 24) != 0u && (w >> 24) != 0x88u) return false;
+    if ((w >> 24) != 0u) return false;
     const int ef = c >> 3, m = c & 7;
     const double want = ef != 0 ? pow2c(ef - 7) * (8 + m) / 8.0 : pow2c(-6) * m / 8.0;
     if (s != want) return false;
@@ -68,6 +70,9 @@ constexpr bool pass_words_are_exact() {
 }
 static_assert(pass_words_are_exact(), "E4M3 pass words must sum to the scale");
 }  // namespace detail
+
+// Sign bits of the eight E2M1 codes of a word: the operand of the subtracted term's pass.
+constexpr uint32_t kFp4SignBits = 0x88888888u;
 
 // lane l <- lane (l ^ 8) inside each row of 16 (row_ror:8)
 __device__ __forceinline__ float xlane8(float x) {

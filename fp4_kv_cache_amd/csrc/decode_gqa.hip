@@ -31,10 +31,11 @@
 //    over the tile-relative p = 2^(s - m_tile) (<= 1), converted with
 //    v_cvt_scalef32_pk_fp4_f32 (exact power-of-two scaling, RNE); MXFP4 with
 //    the MX exponent rule.
-//  * NVFP4 values: the E4M3 block scale S_V = sum_j bit_j 2^(E-j) is applied
-//    as up to four E8M0 passes (one per set bit; absent bits use scale byte 0,
-//    2^-127, which contributes nothing) and two parity passes (16-token
-//    blocks inside a 32-token lane group), accumulated in the MFMA.
+//  * NVFP4 values: the E4M3 block scale S_V = t0 + t1 - t2 (powers of two or
+//    zeros) is applied as three E8M0 passes (an absent term uses scale byte 0,
+//    2^-127, which contributes nothing; the subtracted one runs on P with
+//    flipped signs) and two parity passes (16-token blocks inside a 32-token
+//    lane group), accumulated in the MFMA.
 #include "decode_common.h"
 
 namespace fp4kv {
@@ -173,25 +174,17 @@ void gqa_partials(DecodeArgs a) {
   __shared__ uint32_t qc[2][GV][D / 8];
   __shared__ int qe[2][GV][NBLK];
   __shared__ float qg[2][GV];
-  __shared__ uint32_t lut[256];                // E4M3 value scale -> four E8M0 pass bytes
+  __shared__ uint32_t lut[256];                // E4M3 value scale -> its three pass bytes
   __shared__ float4 sk[128 * 2 + 8];           // NVFP4 key scales of the tile (sk_index)
   // physical page ids of the segment's tiles: entry ((tile - tb) % CAPG) * NPT + j is logical
   // page tile * 128 / P + j (clamped to the sequence), so per-tile lookups are LDS reads; a
   // segment longer than CAPG tiles re-stages the window every CAPG tiles
   __shared__ int pgl[kMaxSplitPages];
 
-  // E4M3 code -> four E8M0 pass bytes (binary expansion of the scale), for NVFP4 values:
-  // byte j is E - j + 127 when bit j of (implicit bit, m2, m1, m0) is set, else 0
-  // (read after the first segment's barrier below)
+  // E4M3 code -> its signed-digit pass bytes (t0 + t1 - t2), for NVFP4 values (read after the
+  // first segment's barrier below)
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int c = lane + 64 * i;
-    const int ef = (c >> 3) & 15, m = c & 7;
-    const int E = (ef ? ef : 1) - 7 + 127;
-    uint32_t w = (ef ? (uint32_t)E : 0u) | ((m & 4) ? (uint32_t)(E - 1) << 8 : 0u) |
-                 ((m & 2) ? (uint32_t)(E - 2) << 16 : 0u) | ((m & 1) ? (uint32_t)(E - 3) << 24 : 0u);
-    lut[c] = c < 0x7F ? w : 0u;
-  }
+  for (int i = 0; i < 4; i++) lut[lane + 64 * i] = e4m3_pass_word(lane + 64 * i);
   int nzero = 0;
   const bool count_zero = a.zero_blocks != nullptr;
   const int GQ = MQ ? a.group : GV, QL = MQ ? a.q_len : 1;   // query heads per KV head, tokens
@@ -560,6 +553,9 @@ void gqa_partials(DecodeArgs a) {
     if constexpr (FMT == kFmtNV) {
       const v8i p0 = {(int)pk[0], (int)pk[1], 0, 0, 0, 0, 0, 0};
       const v8i p1 = {0, 0, (int)pk[2], (int)pk[3], 0, 0, 0, 0};
+      // the subtracted term's passes take P with flipped signs
+      const v8i p0n = {(int)(pk[0] ^ kFp4SignBits), (int)(pk[1] ^ kFp4SignBits), 0, 0, 0, 0, 0, 0};
+      const v8i p1n = {0, 0, (int)(pk[2] ^ kFp4SignBits), (int)(pk[3] ^ kFp4SignBits), 0, 0, 0, 0};
 #pragma unroll
       for (int cg = 0; cg < 8; cg++) {
         const v8i av = {(int)vt.x[cg].x, (int)vt.x[cg].y, (int)vt.x[cg].z, (int)vt.x[cg].w, 0, 0, 0, 0};
@@ -569,12 +565,10 @@ void gqa_partials(DecodeArgs a) {
         const int l0 = (int)lut[b0], l1 = (int)lut[b1];
         v4f c = mfma4<0, 0>(av, p0, o_run[rs][cg], l0, pbyte[0]);
         c = mfma4<1, 0>(av, p0, c, l0, pbyte[0]);
-        c = mfma4<2, 0>(av, p0, c, l0, pbyte[0]);
-        c = mfma4<3, 0>(av, p0, c, l0, pbyte[0]);
+        c = mfma4<2, 0>(av, p0n, c, l0, pbyte[0]);
         c = mfma4<0, 0>(av, p1, c, l1, pbyte[1]);
         c = mfma4<1, 0>(av, p1, c, l1, pbyte[1]);
-        c = mfma4<2, 0>(av, p1, c, l1, pbyte[1]);
-        o_run[rs][cg] = mfma4<3, 0>(av, p1, c, l1, pbyte[1]);
+        o_run[rs][cg] = mfma4<2, 0>(av, p1n, c, l1, pbyte[1]);
       }
     } else {
       const v8i pv = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0};

@@ -31,16 +31,15 @@
 //  * NVFP4 latent (16 x 16 tiles, E4M3 scale S = 2^E (1 + m/8)): the E8M0-scaled MFMA takes
 //    one power of two per (row, 32-element lane group), so each K-step runs as two parity
 //    passes (the query operand keeps one 16-channel half of every lane group, the other half
-//    zeroed: the 16-channel block that the tile scale and the query block exponent belong to) times three
-//    signed-digit passes of S (S as a sum of at most three signed powers of two -- the set
-//    bits of 8 + m, or 16 - 1 for m = 7 -- each the A scale of one pass, E8M0 byte 0 = 2^-127
-//    for an absent term, whose products vanish below fp32 resolution; a negative term's pass
-//    takes the codes with flipped signs), accumulated by the MFMA: the exact products
-//    code_K * S * code_Q * 2^eQ summed in fp32.
+//    zeroed: the 16-channel block that the tile scale and the query block exponent belong to)
+//    times three signed-digit passes of S (S = t0 + t1 - t2 with powers of two or zeros, each
+//    the A scale of one pass, E8M0 byte 0 = 2^-127 for an absent term, whose products vanish
+//    below fp32 resolution; the subtracted term's pass takes the codes with flipped signs),
+//    accumulated by the MFMA: the exact products code_K * S * code_Q * 2^eQ summed in fp32.
 //  * P.V: the value operand (16 channels x 32 tokens per lane) is read transposed from the
 //    same token-major tile with the 4-bit transposed LDS read, so the cache holds the latent
-//    once; the NVFP4 tile scale goes through the same signed-digit passes (token parities on
-//    the P side, the negative term's sign flip on the value codes).
+//    once; the NVFP4 tile scale goes through the same signed-digit passes (token parities and
+//    the subtracted term's sign flip on the P side).
 //  * The merge kernel un-rotates and un-smooths the merged latent output:
 //    out = (o H / 512) * q_smooth.
 #include "decode_common.h"
@@ -107,8 +106,8 @@ __device__ __forceinline__ int swz_rope(int r) { return ((r >> 1) & 1) | (((r >>
 // accumulator chains).  The query operands b1 / b2 hold only the parity's 16-channel half of
 // every lane group (the block that the tile scale and the query block exponent belong to), so
 // the key operand is the full staged row: A scale byte d of w (the tile scale's term d), the
-// third term on `avn`, the codes with their signs flipped where that term is negative; B scale
-// byte PB of e1 / e2 (the query block exponents of the two halves).
+// subtracted third term on `avn`, the codes with flipped signs; B scale byte PB of e1 / e2 (the
+// query block exponents of the two halves).
 template <int PB>
 __device__ __forceinline__ void nv_qk_passes(const v8i &av, const v8i &avn, const v8i &b1, const v8i &b2,
                                              v4f &acc1, v4f &acc2, int w, int e1, int e2) {
@@ -153,9 +152,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __align__(16) uint8_t scl[3 * SCL];
   __shared__ __align__(16) uint4 hand[2][4][2][64];   // [tile & 1][group][part][lane]
   __shared__ uint32_t lut[256];
-  // NVFP4: pass words and sign masks of a tile's scales [tile & 1][token tile][channel block],
-  // written by the value waves one iteration before their P.V reads them
-  __shared__ __align__(16) uint2 pw[NV ? 2 * 8 * 32 : 2];
+  // NVFP4: pass words of a tile's scales [tile & 1][token tile][channel block], written by the
+  // value waves one iteration before their P.V reads them
+  __shared__ __align__(16) uint32_t pw[NV ? 2 * 8 * 32 : 4];
   __shared__ int pgl[kMaxSplitPages];
 
   if constexpr (NV) {
@@ -344,11 +343,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int st = 0; st < 4; st++) {
             if constexpr (NV) {
-              // one sign-flipped copy serves both halves: each pass sees only its own half
-              const uint32_t k0 = pass_neg_mask(lw[i >> 2][st][0]), k1 = pass_neg_mask(lw[i >> 2][st][1]);
+              // the subtracted term's pass takes the codes with flipped signs
               const v8i av = {(int)o[st].x, (int)o[st].y, (int)o[st].z, (int)o[st].w, 0, 0, 0, 0};
-              const v8i avn = {(int)(o[st].x ^ k0), (int)(o[st].y ^ k0), (int)(o[st].z ^ k1),
-                               (int)(o[st].w ^ k1), 0, 0, 0, 0};
+              const v8i avn = {(int)(o[st].x ^ kFp4SignBits), (int)(o[st].y ^ kFp4SignBits),
+                               (int)(o[st].z ^ kFp4SignBits), (int)(o[st].w ^ kFp4SignBits), 0, 0, 0, 0};
               const int w0 = (int)lw[i >> 2][st][0], w1 = (int)lw[i >> 2][st][1];
               nv_qk_passes<0>(av, avn, bq[0][st][0], bq[1][st][0], acc1, acc2, w0, qsb[0][st], qsb[1][st]);
               nv_qk_passes<1>(av, avn, bq[0][st][1], bq[1][st][1], acc1, acc2, w1, qsb[0][st], qsb[1][st]);
@@ -458,8 +456,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if constexpr (NV) {
         if (j < nt) {   // tile j's scales arrived before the last barrier
           const int e = 64 * (wv - 4) + lane;   // token tile e / 32, channel block e % 32
-          const uint32_t w = lut[scl[(j % 3) * SCL + e]];
-          pw[(j & 1) * 256 + e] = uint2{w, pass_neg_mask(w)};
+          pw[(j & 1) * 256 + e] = lut[scl[(j % 3) * SCL + e]];
         }
       }
       if (active && j >= 1) {
@@ -482,10 +479,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (NV) {
           const v8i p0 = {(int)hp.x, (int)hp.y, 0, 0, 0, 0, 0, 0};
           const v8i p1 = {0, 0, (int)hp.z, (int)hp.w, 0, 0, 0, 0};
-          // pass words and sign masks of the lane's token tiles 2 q4 (P parity 0) and 2 q4 + 1
-          // (parity 1), two channel groups per 16-byte read
-          const uint2 *pa = pw + (jp & 1) * 256 + (2 * q4) * 32, *pb = pa + 32;
-          auto read_vals = [&](int c, v2i (*o)[2], uint4 (*l)[2]) {
+          // the subtracted term's passes take P with flipped signs
+          const v8i p0n = {(int)(hp.x ^ kFp4SignBits), (int)(hp.y ^ kFp4SignBits), 0, 0, 0, 0, 0, 0};
+          const v8i p1n = {0, 0, (int)(hp.z ^ kFp4SignBits), (int)(hp.w ^ kFp4SignBits), 0, 0, 0, 0};
+          // pass words of the lane's token tiles 2 q4 (P parity 0) and 2 q4 + 1 (parity 1), four
+          // channel groups per 16-byte read
+          const uint32_t *pa = pw + (jp & 1) * 256 + (2 * q4) * 32, *pb = pa + 32;
+          auto read_vals = [&](int c, v2i (*o)[2], uint4 *l) {
 #pragma unroll
             for (int k = 0; k < 4; k++) {
               const int cg = 4 * c + k;
@@ -493,13 +493,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               o[k][0] = lds_read_tr4(rowa + (((cg >> 1) ^ swa) << 4) + off);
               o[k][1] = lds_read_tr4(rowb + (((cg >> 1) ^ swb) << 4) + off);
             }
-#pragma unroll
-            for (int h = 0; h < 2; h++) {
-              l[h][0] = *(const uint4 *)(pa + 4 * c + 2 * h);
-              l[h][1] = *(const uint4 *)(pb + 4 * c + 2 * h);
-            }
+            l[0] = *(const uint4 *)(pa + 4 * c);
+            l[1] = *(const uint4 *)(pb + 4 * c);
           };
-          uint4 lt[2][2][2];
+          uint4 lt[2][2];
           read_vals(0, vt[0], lt[0]);
 #pragma unroll
           for (int c = 0; c < 8; c++) {
@@ -509,19 +506,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const int cg = 4 * c + k;
               const v2i lo = vt[c & 1][k][0], hi = vt[c & 1][k][1];
               const v8i av = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
-              const uint4 wa = lt[c & 1][k >> 1][0], wb = lt[c & 1][k >> 1][1];
-              const int l0 = (int)((k & 1) ? wa.z : wa.x), l1 = (int)((k & 1) ? wb.z : wb.x);
-              const uint32_t m0 = (k & 1) ? wa.w : wa.y, m1 = (k & 1) ? wb.w : wb.y;
-              // the third terms' passes take the values with flipped signs where the term is
-              // negative; P of one parity is zero in the other half, so one copy serves both
-              const v8i avn = {(int)((uint32_t)lo[0] ^ m0), (int)((uint32_t)lo[1] ^ m0), (int)((uint32_t)hi[0] ^ m1),
-                               (int)((uint32_t)hi[1] ^ m1), 0, 0, 0, 0};
+              const int l0 = (int)lt[c & 1][0][k], l1 = (int)lt[c & 1][1][k];
               v4f acc = mfma4<0, 0>(av, p0, o_run[cg], l0, pb0);
               acc = mfma4<1, 0>(av, p0, acc, l0, pb0);
-              acc = mfma4<2, 0>(avn, p0, acc, l0, pb0);
+              acc = mfma4<2, 0>(av, p0n, acc, l0, pb0);
               acc = mfma4<0, 0>(av, p1, acc, l1, pb1);
               acc = mfma4<1, 0>(av, p1, acc, l1, pb1);
-              o_run[cg] = mfma4<2, 0>(avn, p1, acc, l1, pb1);
+              o_run[cg] = mfma4<2, 0>(av, p1n, acc, l1, pb1);
             }
           }
         } else {
