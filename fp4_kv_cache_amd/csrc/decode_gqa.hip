@@ -18,13 +18,14 @@
 //    as its B operand.  The softmax works on this transposed layout and the
 //    probabilities never leave registers.
 //  * NVFP4 keys carry E4M3 block scales (16 channels) whose mantissa the
-//    E8M0-scaled MFMA cannot take.  Each MFMA therefore sees one 16-channel
-//    block per output column (query rows masked to one block), giving the exact
-//    block dot 2^eQ * sum(code_q * code_k); the key scale multiplies it in fp32
-//    and the 8 block terms are added in fp32 (even-block sum + odd-block sum);
-//    every term is exact, so the logit differs from the exact dot rounded once
-//    only by those few roundings.  Columns: 8 * parity + stacked row
-//    (row = 2*head + {Q1, Q2}).
+//    E8M0-scaled MFMA cannot take, over blocks half the MFMA's 32-element scale
+//    group.  Each group of 16 tokens therefore runs as two parity passes (the
+//    query operand keeps one 16-channel half of every lane group, the block its
+//    exponent belongs to) times three signed-digit passes of the key scale
+//    (S = t0 + t1 - t2, each term the A scale of one pass, the subtracted one
+//    on sign-flipped key codes), six MFMAs on one accumulator: the exact
+//    products code_K * S * code_Q * 2^eQ summed by the matrix core in fp32.
+//    Columns: stacked row = 2 * virtual head + {Q1, Q2}, for both formats.
 //  * MXFP4 keys (32-channel E8M0 blocks = one lane group) use one native MFMA
 //    per 16 tokens with both scales in hardware.
 //  * Probabilities: NVFP4 with power-of-two block scales and tensor scale 2^-10
@@ -138,17 +139,16 @@ __device__ __forceinline__ void load_v(const DecodeArgs &a, Tile &v, const int *
 }
 
 
-// NVFP4 key scales of a tile, staged as fp32 float4 [token][parity] (blocks 2j + parity,
-// j = 0..3) with two float4 of padding after every 32 tokens (LDS bank spread).
-__device__ __forceinline__ int sk_index(int tok, int par) { return tok * 2 + par + 2 * (tok >> 5); }
+// NVFP4 key scales of a tile, staged as pass words [token][lane group] (uint2: blocks 2 q4 and
+// 2 q4 + 1) with two entries of padding after every 32 tokens (LDS bank spread).
+__device__ __forceinline__ int ksw_index(int tok, int q4) { return tok * 4 + q4 + 2 * (tok >> 5); }
 
 
 // Query rows of one KV head: GV "virtual heads" = (query token j, query head g) pairs,
-// v = j * group + g (one query token per sequence: v = g).  One 16-column MFMA holds VS of
-// them (Q1 and Q2 rows; NVFP4 also both block parities), so GV > VS runs RS row sets on
-// the same key/value tile registers.
+// v = j * group + g (one query token per sequence: v = g).  One 16-column MFMA holds 8 of
+// them (Q1 and Q2 rows), so GV > 8 runs RS row sets on the same key/value tile registers.
 template <int FMT, int GV>
-constexpr int row_sets() { return (GV + (FMT == kFmtNV ? 4 : 8) - 1) / (FMT == kFmtNV ? 4 : 8); }
+constexpr int row_sets() { return (GV + 7) / 8; }
 
 // MQ: several query tokens per sequence (causal rows); false compiles the one-token decode
 // with every row seeing the whole sequence.
@@ -156,7 +156,7 @@ template <int FMT, int GV, int P, bool MQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(row_sets<FMT, GV>() == 1 ? 2 : 1, 2)))
 void gqa_partials(DecodeArgs a) {
   constexpr int D = 128;
-  constexpr int VS = FMT == kFmtNV ? 4 : 8;    // virtual heads per row set
+  constexpr int VS = 8;                        // virtual heads per row set
   constexpr int RS = row_sets<FMT, GV>();      // row sets
   constexpr int NR = 2 * (GV < VS ? GV : VS);  // stacked rows per set: (virtual head, Q1/Q2)
   constexpr int B = FMT == kFmtNV ? 16 : 32;   // scale block
@@ -175,7 +175,7 @@ void gqa_partials(DecodeArgs a) {
   __shared__ int qe[2][GV][NBLK];
   __shared__ float qg[2][GV];
   __shared__ uint32_t lut[256];                // E4M3 value scale -> its three pass bytes
-  __shared__ float4 sk[128 * 2 + 8];           // NVFP4 key scales of the tile (sk_index)
+  __shared__ __align__(16) uint2 ksw[FMT == kFmtNV ? 128 * 4 + 8 : 2];   // NVFP4 key pass words
   // physical page ids of the segment's tiles: entry ((tile - tb) % CAPG) * NPT + j is logical
   // page tile * 128 / P + j (clamped to the sequence), so per-tile lookups are LDS reads; a
   // segment longer than CAPG tiles re-stages the window every CAPG tiles
@@ -335,50 +335,42 @@ void gqa_partials(DecodeArgs a) {
 
   const int q4 = lane >> 4;        // lane group: channel block (A/B operands) or token group (D)
   const int n = lane & 15;         // operand row / output column
-  // B operand (stacked query rows) and per-lane logit coefficients.  NVFP4: the lane
-  // holds its (row, block 2*q4 + parity) half of the 32 channels; MFMA j keeps only lane
-  // group j by giving every other lane group the E8M0 scale byte 0 (2^-127), whose
-  // products vanish below fp32 resolution.
-  // Per row set: column n holds stacked row r (NVFP4: r = n & 7, parity n >> 3), virtual
-  // head rs * VS + r / 2, query pass r & 1; its query token sees Lrow tokens.
-  v8i bq[RS];
+  // B operand (stacked query rows) and per-lane logit coefficients.  Per row set: column n
+  // holds stacked row n: virtual head rs * VS + n / 2, query pass n & 1; its query token sees
+  // Lrow tokens.  The lane holds the row's channels 32 q4 .. + 31.  NVFP4: one operand per
+  // 16-channel parity (the other half zero), each with its block exponent (B scale byte p);
+  // MXFP4: all 32 channels, one E8M0 scale.
+  v8i bq[RS][2];
   int qsb[RS];
-  int qsj[RS][4];
   float a_own[RS];
   int Lrow[RS];
   bool lrow[RS];                               // the column holds a row in use
-  const int ncol = FMT == kFmtNV ? (n & 7) : n;
+  const int ncol = n;
 #pragma unroll
   for (int rs = 0; rs < RS; rs++) {
-    bq[rs] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    qsb[rs] = 127;
+    bq[rs][0] = bq[rs][1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    qsb[rs] = 127 | (127 << 8);
     a_own[rs] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; j++) qsj[rs][j] = 0;
     const float gk = FMT == kFmtNV ? a.gk[kvh] : 1.0f;
     const int r = ncol;
     const int h = rs * VS + (r >> 1), k = r & 1;
     const bool live = r < NR && (!MQ || h < GVr);
     lrow[rs] = live;
     Lrow[rs] = MQ && live ? L - QL + 1 + h / GQ : L;
-    if constexpr (FMT == kFmtNV) {
-      const int par = n >> 3;
-      const int blk = 2 * q4 + par;
-      uint32_t c0 = live ? qc[k][h][2 * blk] : 0u, c1 = live ? qc[k][h][2 * blk + 1] : 0u;
-      int e = live ? qe[k][h][blk] : -128;
-      qsb[rs] = e == -128 ? 127 : e + 127;
-      if (par == 0) { bq[rs][0] = (int)c0; bq[rs][1] = (int)c1; }
-      else { bq[rs][2] = (int)c0; bq[rs][3] = (int)c1; }
-#pragma unroll
-      for (int j = 0; j < 4; j++) qsj[rs][j] = (j == q4) ? qsb[rs] : 0;
-    } else {
-      if (live) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) bq[rs][i] = (int)qc[k][h][4 * q4 + i];
+    if (live) {
+      const uint32_t c0 = qc[k][h][4 * q4], c1 = qc[k][h][4 * q4 + 1];
+      const uint32_t c2 = qc[k][h][4 * q4 + 2], c3 = qc[k][h][4 * q4 + 3];
+      if constexpr (FMT == kFmtNV) {
+        bq[rs][0] = v8i{(int)c0, (int)c1, 0, 0, 0, 0, 0, 0};
+        bq[rs][1] = v8i{0, 0, (int)c2, (int)c3, 0, 0, 0, 0};
+        const int e0 = qe[k][h][2 * q4], e1 = qe[k][h][2 * q4 + 1];   // -128: a block of zeros
+        qsb[rs] = (e0 == -128 ? 127 : e0 + 127) | ((e1 == -128 ? 127 : e1 + 127) << 8);
+      } else {
+        bq[rs][0] = v8i{(int)c0, (int)c1, (int)c2, (int)c3, 0, 0, 0, 0};
         qsb[rs] = qe[k][h][q4] + 127;
       }
+      a_own[rs] = (qg[k][h] * gk) * a.coef;
     }
-    if (live) a_own[rs] = (qg[k][h] * gk) * a.coef;
   }
   const int Lmin = MQ ? L - QL + 1 : L;       // the shortest row's length
 
@@ -412,18 +404,18 @@ void gqa_partials(DecodeArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FMT == kFmtNV) {
-      // stage the tile's key scales as fp32 [token][parity][j] = S(block 2j + parity); the
-      // E4M3 -> fp32 conversions are exact
+      // stage the tile's key scales as pass words: the lane holds the scale bytes of tokens
+      // 2 lane and 2 lane + 1 (blocks 0..7 each)
       const uint32_t wv[4] = {kt.x[8].x, kt.x[8].y, kt.x[8].z, kt.x[8].w};
 #pragma unroll
       for (int u = 0; u < 2; u++) {
-        const auto s01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[2 * u], false);
-        const auto s23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[2 * u], true);
-        const auto s45 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[2 * u + 1], false);
-        const auto s67 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[2 * u + 1], true);
         const int tok = 2 * lane + u;
-        sk[sk_index(tok, 0)] = float4{s01[0], s23[0], s45[0], s67[0]};
-        sk[sk_index(tok, 1)] = float4{s01[1], s23[1], s45[1], s67[1]};
+#pragma unroll
+        for (int hq = 0; hq < 2; hq++) {   // lane groups 2 hq, 2 hq + 1
+          const uint32_t w = wv[2 * u + hq];
+          *(uint4 *)&ksw[ksw_index(tok, 2 * hq)] =
+              uint4{lut[w & 0xFFu], lut[(w >> 8) & 0xFFu], lut[(w >> 16) & 0xFFu], lut[w >> 24]};
+        }
       }
       __syncthreads();
     }
@@ -437,23 +429,22 @@ void gqa_partials(DecodeArgs a) {
     for (int i = 0; i < 8; i++) {
       const v8i av = {(int)kt.x[i].x, (int)kt.x[i].y, (int)kt.x[i].z, (int)kt.x[i].w, 0, 0, 0, 0};
       if constexpr (FMT == kFmtNV) {
-        const v4f o0 = mfma4<0, 0>(av, bq[rs], zero, 127, qsj[rs][0]);
-        const v4f o1 = mfma4<0, 0>(av, bq[rs], zero, 127, qsj[rs][1]);
-        const v4f o2 = mfma4<0, 0>(av, bq[rs], zero, 127, qsj[rs][2]);
-        const v4f o3 = mfma4<0, 0>(av, bq[rs], zero, 127, qsj[rs][3]);
-        const int par = n >> 3;
+        // the key scales of the lane's row (token 32 (n / 4) + 4 i + n % 4), blocks 2 q4 + p,
+        // as three signed-digit passes per parity p on one accumulator; the subtracted term's
+        // passes take the key codes with flipped signs
+        const uint2 w = ksw[ksw_index(32 * (n >> 2) + 4 * i + (n & 3), q4)];
+        const v8i avn = {(int)(kt.x[i].x ^ kFp4SignBits), (int)(kt.x[i].y ^ kFp4SignBits),
+                         (int)(kt.x[i].z ^ kFp4SignBits), (int)(kt.x[i].w ^ kFp4SignBits), 0, 0, 0, 0};
+        v4f o = mfma4<0, 0>(av, bq[rs][0], zero, (int)w.x, qsb[rs]);
+        o = mfma4<1, 0>(av, bq[rs][0], o, (int)w.x, qsb[rs]);
+        o = mfma4<2, 0>(avn, bq[rs][0], o, (int)w.x, qsb[rs]);
+        o = mfma4<0, 1>(av, bq[rs][1], o, (int)w.y, qsb[rs]);
+        o = mfma4<1, 1>(av, bq[rs][1], o, (int)w.y, qsb[rs]);
+        o = mfma4<2, 1>(avn, bq[rs][1], o, (int)w.y, qsb[rs]);
 #pragma unroll
-        for (int rr = 0; rr < 4; rr++) {
-          // each block term o_j * S_j is exact in fp32, so fma(o, S, acc) == acc + o*S
-          const float4 S = sk[sk_index(32 * q4 + 4 * i + rr, par)];
-          float acc = o0[rr] * S.x;
-          acc = fmaf(o1[rr], S.y, acc);
-          acc = fmaf(o2[rr], S.z, acc);
-          acc = fmaf(o3[rr], S.w, acc);
-          s[i][rr] = acc + xlane8(acc);                  // even-block sum + odd-block sum
-        }
+        for (int rr = 0; rr < 4; rr++) s[i][rr] = o[rr];
       } else {
-        const v4f o = mfma4<0, 0>(av, bq[rs], zero, (int)byte_of(kt.x[8], i), qsb[rs]);
+        const v4f o = mfma4<0, 0>(av, bq[rs][0], zero, (int)byte_of(kt.x[8], i), qsb[rs]);
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) s[i][rr] = o[rr];
       }
@@ -519,7 +510,7 @@ void gqa_partials(DecodeArgs a) {
       for (int w = 0; w < 4; w++) pk[w] = pack8(s[2 * w], s[2 * w + 1], ps);
     }
     if (count_zero) {
-      const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (ncol & 1) == 0 && lrow[rs];
+      const bool rep = (ncol & 1) == 0 && lrow[rs];
       const int L = Lrow[rs];
       if (rep) {
         if constexpr (FMT == kFmtNV) {
@@ -601,7 +592,7 @@ void gqa_partials(DecodeArgs a) {
 #pragma unroll
   for (int rs = 0; rs < RS; rs++) {
     const float l_tot = sum_x32(sum_x16(l_run[rs]));
-    const bool rep = (FMT == kFmtNV ? (n < 8) : true) && (ncol & 1) == 0 && lrow[rs];
+    const bool rep = (ncol & 1) == 0 && lrow[rs];
     if (rep) {
       const long rowi = slot * GVr + rs * VS + (ncol >> 1);   // one slot holds GVr partial rows
       const float gv = (FMT == kFmtNV ? a.gv[kvh] : 1.0f) * f_run[rs];
