@@ -128,10 +128,10 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   int group = hq / c->num_kv_heads;
   if (q_len < 1) return FP4KV_ERR_INVALID_ARG;
   if (c->attn == FP4KV_GQA) {
-    bool ok = group == 1 || group == 2 || group == 4 || (c->format == FP4KV_MXFP4 && group == 8);
+    bool ok = group == 1 || group == 2 || group == 4 || group == 8;
     if (!ok) return FP4KV_ERR_UNSUPPORTED;
     // query tokens x query heads per KV head: up to two row sets of one MFMA's columns
-    if (q_len > 8 || group * q_len > (c->format == FP4KV_NVFP4 ? 8 : 16)) return FP4KV_ERR_UNSUPPORTED;
+    if (q_len > 8 || group * q_len > 16) return FP4KV_ERR_UNSUPPORTED;
     if (c->format == FP4KV_MXFP4 && c->page_size < 32) return FP4KV_ERR_UNSUPPORTED;
   } else {
     // MLA: query heads in groups of 16, pages of at least 32 tokens

@@ -799,9 +799,9 @@ static hipError_t launch_g(const DecodeArgs &a, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Virtual heads (query tokens x query heads per KV head) rounded up to a compiled size:
-// NVFP4 up to 8 (two row sets of 4), MXFP4 up to 16 (two row sets of 8); more row sets
-// would not fit the register file next to the resident key / value tiles.
+// Virtual heads (query tokens x query heads per KV head) rounded up to a compiled size: up
+// to 16 (two row sets of 8); more row sets would not fit the register file next to the
+// resident key / value tiles.
 hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   const dim3 grid((unsigned)a.n_waves);
@@ -811,6 +811,7 @@ hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s) {
         case 1: return launch_g<kFmtNV, 1, false>(a, grid, s);
         case 2: return launch_g<kFmtNV, 2, false>(a, grid, s);
         case 4: return launch_g<kFmtNV, 4, false>(a, grid, s);
+        case 8: return launch_g<kFmtNV, 8, false>(a, grid, s);
         default: return hipErrorInvalidValue;
       }
     }
@@ -827,6 +828,7 @@ hipError_t launch_decode_partials(const DecodeArgs &a, hipStream_t s) {
     if (gv <= 2) return launch_g<kFmtNV, 2, true>(a, grid, s);
     if (gv <= 4) return launch_g<kFmtNV, 4, true>(a, grid, s);
     if (gv <= 8) return launch_g<kFmtNV, 8, true>(a, grid, s);
+    if (gv <= 16) return launch_g<kFmtNV, 16, true>(a, grid, s);
     return hipErrorInvalidValue;
   }
   if (gv <= 2) return launch_g<kFmtMX, 2, true>(a, grid, s);

@@ -185,7 +185,7 @@ size_t fp4_decode_workspace_bytes(const fp4kv_cache *c, int batch, int num_q_hea
  *   zero_block_count  nullable i32 counter; when given, the number of
  *              probability blocks that held a valid token and quantized to all
  *              zeros is ADDED to it (the caller zeroes it)
- * GQA needs num_q_heads == group * Hkv with group <= 4 (NVFP4) or <= 8 (MXFP4).
+ * GQA needs num_q_heads == group * Hkv with group 1, 2, 4 or 8.
  * Launches the split-K partial kernel and the merge kernel on `stream`. */
 int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int batch,
                          int num_q_heads, const int32_t *block_table, int max_pages_per_seq,
@@ -224,8 +224,8 @@ int fp4_decode_attention_noalloc(const fp4kv_cache *c, const void *q, int q_dtyp
  *   q    [batch][q_len][num_q_heads][head_dim], dtype q_dtype
  *   out  f32 [batch][q_len][num_q_heads][head_dim]
  * Other arguments as fp4_decode_attention; seq_lens[b] must be 0 or >= q_len.
- * GQA only (MLA: q_len 1); q_len <= 8 and group * q_len <= 8 (NVFP4) or <= 16
- * (MXFP4), else FP4KV_ERR_UNSUPPORTED.  q_len == 1 is fp4_decode_attention. */
+ * GQA only (MLA: q_len 1); q_len <= 8 and group * q_len <= 16, else
+ * FP4KV_ERR_UNSUPPORTED.  q_len == 1 is fp4_decode_attention. */
 size_t fp4_decode_multi_workspace_bytes(const fp4kv_cache *c, int batch, int q_len, int num_q_heads,
                                         int max_seq_len);
 int fp4_decode_attention_multi(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int q_len,

@@ -88,7 +88,8 @@ def test_workspace_and_group_checks(lib):
     assert need > 0
     assert L.fp4_decode_attention(c, 1, 0, 3, 8, 1, 16, 1, 0.1, 1, 1, need - 1, None, None) == L.ERR_WORKSPACE
     assert L.fp4_decode_attention(c, 1, 0, 3, 7, 1, 16, 1, 0.1, 1, 1, need, None, None) == L.ERR_INVALID_ARG
-    assert L.fp4_decode_attention(c, 1, 0, 3, 16, 1, 16, 1, 0.1, 1, 1, 1 << 30, None, None) == L.ERR_UNSUPPORTED
+    # 32 query heads on 2 KV heads: group 16, beyond the supported 1, 2, 4, 8
+    assert L.fp4_decode_attention(c, 1, 0, 3, 32, 1, 16, 1, 0.1, 1, 1, 1 << 30, None, None) == L.ERR_UNSUPPORTED
     assert L.fp4_decode_attention(c, 1, 7, 3, 8, 1, 16, 1, 0.1, 1, 1, need, None, None) == L.ERR_INVALID_ARG
     assert L.kv_quant_append(c, 1, 1, 5, 4, 1, 1, 1, None, None) == L.ERR_INVALID_ARG
     assert L.kv_quant_append(c, 1, None, 0, 4, 1, 1, 1, None, None) == L.ERR_INVALID_ARG
@@ -105,7 +106,8 @@ def test_workspace_and_group_checks(lib):
     big = 1 << 30
     assert L.fp4_decode_attention_multi(c, 1, 0, 3, 0, 8, 1, 16, 1, 0.1, 1, 1, big, None, None) == L.ERR_INVALID_ARG
     assert L.fp4_decode_attention_multi(c, 1, 0, 3, 9, 2, 1, 16, 1, 0.1, 1, 1, big, None, None) == L.ERR_UNSUPPORTED
-    assert L.fp4_decode_attention_multi(c, 1, 0, 3, 4, 8, 1, 16, 1, 0.1, 1, 1, big, None, None) == L.ERR_UNSUPPORTED
+    # group 4 x q_len 8 = 32 stacked query rows per KV head: beyond two row sets of 8
+    assert L.fp4_decode_attention_multi(c, 1, 0, 3, 8, 8, 1, 16, 1, 0.1, 1, 1, big, None, None) == L.ERR_UNSUPPORTED
     need2 = L.fp4_decode_multi_workspace_bytes(c, 3, 2, 8, 1000)
     assert L.fp4_decode_attention_multi(c, 1, 0, 3, 2, 8, 1, 16, 1, 0.1, 1, 1, need2 - 1, None, None) == L.ERR_WORKSPACE
     assert L.fp4kv_status_string(3) == "workspace too small"

@@ -129,7 +129,7 @@ def test_decode_tiny_nvfp4(torch_dev):
         % (worst, worst_ref, zg, zo))
 
 
-@pytest.mark.parametrize("hq", [32, 16, 8])
+@pytest.mark.parametrize("hq", [64, 32, 16, 8])   # query heads per KV head 8, 4, 2, 1
 def test_decode_nvfp4_ragged(torch_dev, hq):
     w = W.workload("qwen3_4b", batch=5, hq=hq)
     lens = np.array([1, 129, 1000, 2500, 0], np.int32)
@@ -320,7 +320,9 @@ def test_decode_mla_head_counts(torch_dev, name, hq):
                                        # pages of 16, fp32 inputs; with 2 KV heads the partition
                                        # starts a share at the 129-token sequence's second tile,
                                        # which holds none of its first row's tokens
-                                       ("tiny", 8, 2), ("tiny", 4, 4)])
+                                       ("tiny", 8, 2), ("tiny", 4, 4),
+                                       # NVFP4 with 16 stacked query rows (two row sets of 8)
+                                       ("qwen3_4b", 32, 4), ("qwen3_4b", 64, 2), ("tiny", 16, 2)])
 def test_decode_multi_token(torch_dev, name, hq, n):
     """Several query tokens per sequence (causal), stacked on the same key / value tiles in
     one or two row sets; lengths put the shorter rows' last tile empty (129 = 128 + 1) and
