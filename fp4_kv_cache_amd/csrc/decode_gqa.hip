@@ -701,7 +701,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // over the partials of the head's (sequence, KV head) unit.  Lanes first take one partial
 // each for (m, l); the weights then go through LDS to the channel loop (lane = 2
 // channels), whose loads are independent.
-constexpr int kMergeFast = 32;   // partials per row that the merge loads all at once
+// Merge of one row whose nv <= N partials are all loaded at once (lane s also takes partial s's
+// (m, l)); the same operations in the same order as the general path of gqa_merge.
+template <int N>
+__device__ __forceinline__ void merge_row_fast(const float *ml, const float *o, long sm, long so, int nv, int lane,
+                                               float2 *dst) {
+  float2 mlv = float2{-INFINITY, 0.f};
+  if (lane < nv) mlv = *(const float2 *)(ml + sm * lane);
+  float2 v[N];
+#pragma unroll
+  for (int s = 0; s < N; s++) v[s] = s < nv ? *((const float2 *)(o + so * s) + lane) : float2{0.f, 0.f};
+  float M = mlv.x;
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
+  if (!(M > -INFINITY)) { *dst = float2{0.f, 0.f}; return; }   // a query row with no tokens
+  const float wl = lane < nv ? __builtin_amdgcn_exp2f(mlv.x - M) : 0.f;
+  float den = lane < nv ? fmaf(wl, mlv.y, 0.f) : 0.f;
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k);
+  float n0 = 0.f, n1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < N; s++) {
+    if (s < nv) {
+      const float w = __shfl(wl, s);
+      n0 = fmaf(w, v[s].x, n0);
+      n1 = fmaf(w, v[s].y, n1);
+    }
+  }
+  *dst = float2{n0 / den, n1 / den};
+}
 
 __global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
   const int row = blockIdx.x, lane = threadIdx.x;   // row = (b * q_len + j) * hq + h
@@ -720,34 +748,9 @@ __global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
   const float *ml = a.ws_ml + r0 * 2;
   const float *o = a.ws_o + r0 * 128;
   const long so = (long)GVr * 128, sm = 2L * GVr;  // strides between the unit's partials
-  if (nv <= kMergeFast) {
-    // every (m, l) pair and output partial of the row in flight at once; the same operations
-    // in the same order as the general path below
-    float2 mlv = float2{-INFINITY, 0.f};
-    if (lane < nv) mlv = *(const float2 *)(ml + sm * lane);
-    float2 v[kMergeFast];
-#pragma unroll
-    for (int s = 0; s < kMergeFast; s++) v[s] = s < nv ? *((const float2 *)(o + so * s) + lane) : float2{0.f, 0.f};
-    float M = mlv.x;
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
-    if (!(M > -INFINITY)) { *dst = float2{0.f, 0.f}; return; }   // a query row with no tokens
-    const float wl = lane < nv ? __builtin_amdgcn_exp2f(mlv.x - M) : 0.f;
-    float den = lane < nv ? fmaf(wl, mlv.y, 0.f) : 0.f;
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k);
-    float n0 = 0.f, n1 = 0.f;
-#pragma unroll
-    for (int s = 0; s < kMergeFast; s++) {
-      if (s < nv) {
-        const float w = __shfl(wl, s);
-        n0 = fmaf(w, v[s].x, n0);
-        n1 = fmaf(w, v[s].y, n1);
-      }
-    }
-    *dst = float2{n0 / den, n1 / den};
-    return;
-  }
+  // every (m, l) pair and output partial of the row in flight at once, in two size classes
+  if (nv <= 16) { merge_row_fast<16>(ml, o, sm, so, nv, lane, dst); return; }
+  if (nv <= 64) { merge_row_fast<64>(ml, o, sm, so, nv, lane, dst); return; }
   __shared__ float wsh[256];
   float M = -INFINITY;
   for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[sm * s]);
