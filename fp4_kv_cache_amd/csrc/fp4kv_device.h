@@ -22,33 +22,11 @@ __device__ __forceinline__ float load_elem(const void *p, long i, int bf16) {
   return bf16 ? bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
 }
 
-// E2M1 code of y: round to nearest, ties to the even code, saturating at 6; the
-// sign is y's sign bit (so -0.0 gives 8).  Each threshold is a midpoint of two
-// neighbouring grid points; '>' sends a tie down, '>=' sends it up, chosen so the
-// tie lands on the even code.
-__device__ __forceinline__ uint32_t e2m1_enc(float y) {
-  float a = fabsf(y);
-  uint32_t idx = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                 (uint32_t)(a > 5.0f);
-  return idx | ((__float_as_uint(y) >> 28) & 8u);
-}
-
-// Value of an E2M1 code (exact), without branches: magnitude m >= 2 is (2 + (m & 1)) *
-// 2^((m >> 1) - 2), m < 2 is m / 2; the sign is bit 3.
-__device__ __forceinline__ float e2m1_dec(uint32_t c) {
-  const uint32_t m = c & 7u;
-  const bool sub = m < 2u;
-  const float mant = (float)(sub ? m : 2u + (m & 1u));
-  const int ex = sub ? -1 : (int)(m >> 1) - 2;
-  return __uint_as_float(__float_as_uint(ldexpf(mant, ex)) | ((c & 8u) << 28));
-}
-
-// The same conversions by the hardware (v_cvt_scalef32_pk_fp4_f32 / v_cvt_scalef32_pk_f32_fp4
-// with scale 1): round to nearest with ties to the even code and saturation at +-6, so for
-// every finite input the code equals e2m1_enc's (checked on the GPU at every rounding
-// threshold, its fp32 neighbours, the grid, values past 6, zeros and subnormals, both signs);
-// the decode is exact.  One instruction each instead of a compare chain.
+// E2M1 conversions by the hardware (v_cvt_scalef32_pk_fp4_f32 / v_cvt_scalef32_pk_f32_fp4 with
+// scale 1).  Encode: round to nearest with ties to the even code, saturation at +-6, the sign
+// from y's sign bit (-0.0 gives code 8) -- the format's definition, which the GPU tests check
+// against the oracle's encoder at every rounding threshold, its fp32 neighbours, the grid,
+// values past 6, zeros and subnormals, both signs.  Decode: exact.
 __device__ __forceinline__ uint32_t e2m1_enc_hw(float y) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, y, 1.0f, 0) & 0xFu;
 }
