@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kTarget = 2048;   // GQA waves: 8 single-wave groups per CU on 256 CUs
 constexpr int kMlaWorkgroups = 256;   // MLA: one eight-wave workgroup per CU
-constexpr int kMinTilesPerSplit = 4;   // the partial kernels' minimum share (kMinTilesPerWave)
+constexpr int kMinTilesPerSplit = 1;   // the partial kernels' minimum share (kMinTilesPerWave)
 constexpr int kTile = 128;
 
 int block_of(int fmt) { return fmt == FP4KV_NVFP4 ? 16 : 32; }

@@ -162,8 +162,9 @@ __device__ __forceinline__ uint32_t byte_of(const uint4 &u, int k) {
 // (T tiles in all), so every wave streams the same number of tiles however ragged the
 // sequence lengths are.  A wave whose range crosses unit boundaries writes one partial
 // per unit it touches, into slot i + u: the ranges are ordered like the units, so no two
-// (wave, unit) pairs share a slot and the slots of one unit are consecutive.
-constexpr int kMinTilesPerWave = 4;
+// (wave, unit) pairs share a slot and the slots of one unit are consecutive.  A batch with
+// fewer tiles than planned waves gets one tile per wave (it is latency-bound).
+constexpr int kMinTilesPerWave = 1;
 
 // A sequence's tiles of 128 tokens.
 __device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int b) { return (seq_len_clamped(a, b) + 127) >> 7; }

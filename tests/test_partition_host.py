@@ -46,8 +46,8 @@ def planned_waves(lens, hkv, page):
 
 
 def device_waves(total, planned):
-    # the kernels shrink the plan to shares of at least four tiles
-    return min(planned, -(-total // 4))
+    # the kernels shrink the plan to no more shares than tiles
+    return min(planned, total)
 
 
 def check_partition(lens, hkv, page):
