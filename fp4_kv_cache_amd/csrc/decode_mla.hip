@@ -102,21 +102,21 @@ __device__ __forceinline__ float bfly_x32(float x, bool upper) {
 __device__ __forceinline__ int swz_lat(int r) { return (r & 15) ^ (((r >> 5) & 3) << 2); }
 __device__ __forceinline__ int swz_rope(int r) { return ((r >> 1) & 1) | (((r >> 5) & 3) << 1); }
 
-// The three signed-digit passes of one NVFP4 Q.K^T parity pass PB, Q1 and Q2 interleaved (two
-// accumulator chains).  The query operands b1 / b2 hold only the parity's 16-channel half of
-// every lane group (the block that the tile scale and the query block exponent belong to), so
-// the key operand is the full staged row: A scale byte d of w (the tile scale's term d), the
-// subtracted third term on `avn`, the codes with flipped signs; B scale byte PB of e1 / e2 (the
-// query block exponents of the two halves).
+// The three signed-digit passes of one NVFP4 Q.K^T parity pass PB, Q1 and Q2 interleaved.  The
+// query operands b1 / b2 hold only the parity's 16-channel half of every lane group (the block
+// that the tile scale and the query block exponent belong to), so the key operand is the full
+// staged row: A scale byte d of w (the tile scale's term d), B scale byte PB of e1 / e2 (the query
+// block exponents of the two halves).  The added terms t0, t1 accumulate in acc1 / acc2, the
+// subtracted term t2 in acc1n / acc2n; the logit takes the difference.
 template <int PB>
-__device__ __forceinline__ void nv_qk_passes(const v8i &av, const v8i &avn, const v8i &b1, const v8i &b2,
-                                             v4f &acc1, v4f &acc2, int w, int e1, int e2) {
+__device__ __forceinline__ void nv_qk_passes(const v8i &av, const v8i &b1, const v8i &b2, v4f &acc1, v4f &acc2,
+                                             v4f &acc1n, v4f &acc2n, int w, int e1, int e2) {
   acc1 = mfma4<0, PB>(av, b1, acc1, w, e1);
   acc2 = mfma4<0, PB>(av, b2, acc2, w, e2);
   acc1 = mfma4<1, PB>(av, b1, acc1, w, e1);
   acc2 = mfma4<1, PB>(av, b2, acc2, w, e2);
-  acc1 = mfma4<2, PB>(avn, b1, acc1, w, e1);
-  acc2 = mfma4<2, PB>(avn, b2, acc2, w, e2);
+  acc1n = mfma4<2, PB>(av, b1, acc1n, w, e1);
+  acc2n = mfma4<2, PB>(av, b2, acc2n, w, e2);
 }
 
 // MLA partials.  Grid: one-dimensional; ids with equal residue mod 8 run on one XCD, and the
@@ -287,11 +287,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       bqr[0] = bqr[1] = as_bh8(uint4{0u, 0u, 0u, 0u});
     }
-    // logit coefficients: s = fl32(a1 raw1) + fl32(a2 raw2) + fl32(c_r raw_rope)
+    // logit coefficients: s = fl32(a1 raw1) + fl32(a2 raw2) + fl32(c_r raw_rope); NVFP4 raw_k is
+    // the added minus the subtracted terms' sum (each sum exact in fp32 unless the tile scales of
+    // a row span more than the fp32 mantissa, so raw_k is the dot rounded once)
     const float a1 = (qg[0] * gk) * a.coef, a2 = (qg[1] * gk) * a.coef, cr = a.coef_rope;
     float m_run = -INFINITY, l_run = 0.0f, f_run = 1.0f;
     const float inv6gp = 1.0f / (6.0f * 0.0009765625f);   // fl32(1 / fl32(6 * 2^-10))
     const int trow = 32 * (n >> 2) + (n & 3);   // A-operand row: tile token trow + 4 i in group i
+    // Byte offsets inside a tile buffer of the lane's Q.K^T operand chunks.  Row trow + 4 i has
+    // latent swizzle (n & 3) + 4 ((i & 3) ^ (n / 4)) and rope swizzle ((n / 2) & 1) + 2 (n / 4),
+    // so latent chunk st of group i sits at lo[st ^ (i & 3)] + 1024 i and rope chunk k at
+    // ro[k] + 512 i: six per-lane bases, the rest immediate offsets.
+    int lo[4], ro[2];
+    {
+      const int n2 = n >> 2, sr = ((n >> 1) & 1) | (n2 << 1);
+#pragma unroll
+      for (int v = 0; v < 4; v++) lo[v] = trow * 256 + ((4 * (v ^ n2) + (q4 ^ (n & 3))) << 4);
+      ro[0] = trow * 128 + ((q4 ^ sr) << 4);
+      ro[1] = trow * 128 + (((4 + q4) ^ sr) << 4);
+    }
 
     wait_lds_loads();
     __syncthreads();
@@ -323,15 +337,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float s[8][4];
         uint4 opd[2][6];
         auto read_ops = [&](int i, uint4 *o) {
-          const int r = trow + 4 * i;
-          const uint8_t *row = Lt + r * 256;
-          const int sw = swz_lat(r);
 #pragma unroll
-          for (int st = 0; st < 4; st++) o[st] = *(const uint4 *)(row + (((4 * st + q4) ^ sw) << 4));
-          const uint8_t *rrow = Rt + r * 128;
-          const int swr = swz_rope(r);
-          o[4] = *(const uint4 *)(rrow + ((q4 ^ swr) << 4));
-          o[5] = *(const uint4 *)(rrow + (((4 + q4) ^ swr) << 4));
+          for (int st = 0; st < 4; st++) o[st] = *(const uint4 *)(Lt + lo[st ^ (i & 3)] + 1024 * i);
+          o[4] = *(const uint4 *)(Rt + ro[0] + 512 * i);
+          o[5] = *(const uint4 *)(Rt + ro[1] + 512 * i);
         };
         read_ops(0, opd[0]);
 #pragma unroll
@@ -339,17 +348,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           if (i < 7) read_ops(i + 1, opd[(i + 1) & 1]);
           __builtin_amdgcn_sched_barrier(0);
           const uint4 *o = opd[i & 1];
-          v4f acc1 = zero, acc2 = zero, accr = zero;
+          v4f acc1 = zero, acc2 = zero, acc1n = zero, acc2n = zero, accr = zero;
 #pragma unroll
           for (int st = 0; st < 4; st++) {
             if constexpr (NV) {
-              // the subtracted term's pass takes the codes with flipped signs
               const v8i av = {(int)o[st].x, (int)o[st].y, (int)o[st].z, (int)o[st].w, 0, 0, 0, 0};
-              const v8i avn = {(int)(o[st].x ^ kFp4SignBits), (int)(o[st].y ^ kFp4SignBits),
-                               (int)(o[st].z ^ kFp4SignBits), (int)(o[st].w ^ kFp4SignBits), 0, 0, 0, 0};
               const int w0 = (int)lw[i >> 2][st][0], w1 = (int)lw[i >> 2][st][1];
-              nv_qk_passes<0>(av, avn, bq[0][st][0], bq[1][st][0], acc1, acc2, w0, qsb[0][st], qsb[1][st]);
-              nv_qk_passes<1>(av, avn, bq[0][st][1], bq[1][st][1], acc1, acc2, w1, qsb[0][st], qsb[1][st]);
+              nv_qk_passes<0>(av, bq[0][st][0], bq[1][st][0], acc1, acc2, acc1n, acc2n, w0, qsb[0][st], qsb[1][st]);
+              nv_qk_passes<1>(av, bq[0][st][1], bq[1][st][1], acc1, acc2, acc1n, acc2n, w1, qsb[0][st], qsb[1][st]);
             } else {
               const v8i av = {(int)o[st].x, (int)o[st].y, (int)o[st].z, (int)o[st].w, 0, 0, 0, 0};
               const int sa = (int)byte_of(scc, 4 * st + q4);
@@ -361,7 +367,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           accr = mfma_bf16(as_bh8(o[5]), bqr[1], accr);
 #pragma unroll
           for (int rr = 0; rr < 4; rr++) {
-            const float t12 = a1 * acc1[rr] + a2 * acc2[rr];
+            const float raw1 = NV ? acc1[rr] - acc1n[rr] : acc1[rr];
+            const float raw2 = NV ? acc2[rr] - acc2n[rr] : acc2[rr];
+            const float t12 = a1 * raw1 + a2 * raw2;
             s[i][rr] = t12 + cr * accr[rr];
           }
         }
