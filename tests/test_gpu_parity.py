@@ -364,8 +364,8 @@ def test_decode_underflow_no_zero_blocks(torch_dev):
 @pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
 def test_decode_mla_ragged(torch_dev, name):
     """MLA: 128 query heads on one latent head (key and value) plus the bf16 rope part;
-    NVFP4 (16 x 16 E4M3 tiles, fp16 matrix cores for Q.K^T) and MXFP4 (32 x 32 E8M0 tiles,
-    FP4 matrix cores throughout)."""
+    NVFP4 (16 x 16 E4M3 tiles, FP4 matrix cores with signed-digit scale passes) and MXFP4
+    (32 x 32 E8M0 tiles, FP4 matrix cores with the tile scales applied natively)."""
     w = W.workload(name, batch=4)
     lens = np.array([1, 200, 777, 0], np.int32)
     say("decode %s ragged" % name, lens.tolist())
