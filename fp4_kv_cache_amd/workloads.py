@@ -135,6 +135,33 @@ def outlier_channels(w, h):
     return _rng(w, T_OUTL, h).choice(w["d"], size=w["n_outliers"], replace=False)
 
 
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
+
+
+def special_rows(w, x):
+    """With w["degenerate"], token rows of special values replace drawn rows of x [L, d], by
+    token index t % 8: 0 zeros, 1 negative zeros, 2 the constant 0.75, 3 E2M1 grid values
+    times powers of two 2^-2 .. 2^2 with mixed signs, 4 a drawn row with one element set to
+    1000; other rows stay as drawn.  Deterministic in (t, channel), so a slice of a sequence
+    regenerates on its own."""
+    if not w.get("degenerate"):
+        return x
+    x = np.array(x, dtype=np.float32, copy=True)
+    L, d = x.shape
+    t = np.arange(L)
+    c = np.arange(d)
+    r = t % 8
+    x[r == 0] = 0.0
+    x[r == 1] = -0.0
+    x[r == 2] = 0.75
+    t3 = t[r == 3][:, None]
+    sign = np.where((t3 + c[None, :]) % 3 == 0, -1.0, 1.0).astype(np.float32)
+    x[r == 3] = E2M1_GRID[(t3 + c[None, :]) % 8] * np.exp2((c % 5) - 2).astype(np.float32)[None, :] * sign
+    t4 = t[r == 4]
+    x[t4, (7 * t4) % d] = 1000.0
+    return x
+
+
 def keys(w, b, h, L):
     """K[b, :L, h, :] as float32 (bf16-rounded for bf16 workloads).  For MLA: the latent."""
     k = _rng(w, T_K, b, h).standard_normal((L, w["d"]), dtype=np.float32) * np.float32(w["k_std"])
@@ -143,14 +170,14 @@ def keys(w, b, h, L):
     ch = outlier_channels(w, h)
     if len(ch):
         k[:, ch] *= np.float32(w["outlier_scale"])
-    return _cast(w, k)
+    return _cast(w, special_rows(w, k))
 
 
 def values(w, b, h, L):
     v = _rng(w, T_V, b, h).standard_normal((L, w["d"]), dtype=np.float32)
     if w["lognormal"]:
         v *= np.exp(_rng(w, T_VMAG, b, h).normal(0.0, w["lognormal"], size=(L, 1))).astype(np.float32)
-    return _cast(w, v)
+    return _cast(w, special_rows(w, v))
 
 
 def queries(w, b):

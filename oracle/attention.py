@@ -37,6 +37,14 @@ Readings:
          kernel; p~ = fl32(2^fl32(s - m)) is taken correctly rounded here.
          The kernel's hardware exp2 may differ in the last bit, so a P code
          can differ where p~ sits within an ulp of an E2M1 rounding boundary.
+         The pages fix no precision for p~, so it takes the kernel's: an fp32
+         value in the normal range, a result below 2^-126 being 0 (the
+         hardware exp2 returns no subnormals).  Only MXFP4 P codes can tell
+         (NVFP4's power-of-two P block scales stop at 2^-19, below which every
+         p~ quantizes to 0 anyway): a block whose largest p~ lies in
+         (2^-129, 2^-126) keeps nonzero E8M0-scaled codes with subnormal p~ and
+         none without; its weight in the output is below 2^-126 of the tile
+         maximum's.
 * Merge  M = max_tau m_tau, out = sum 2^(m_tau - M) o_tau / sum 2^(m_tau - M) l_tau
          (float64 here).
 
@@ -146,6 +154,13 @@ def quantize_probs(pt, fmt, mode="tile"):
     return ph.reshape(R, Lt), codes
 
 
+def p_tilde_fp32(x):
+    """p~ = 2^x (x <= 0, or -inf) as fp32 in the normal range: correctly rounded, and 0 where
+    the result lies below 2^-126 (decision precision reading in the module header)."""
+    p = np.exp2(np.asarray(x, np.float64)).astype(F32)
+    return np.where(p < F32(2.0 ** -126), F32(0.0), p).astype(F32)
+
+
 def attend(s, vhat, L, fmt, tile=P_TILE, p_mode="tile", partials=False, row_len=None):
     """Tile-wise FP4 softmax.V emulation for rows s [R, L] (fp32 base-2 logits).
 
@@ -184,7 +199,7 @@ def attend(s, vhat, L, fmt, tile=P_TILE, p_mode="tile", partials=False, row_len=
     live = np.isfinite(m)                     # the tile holds a valid token of the row
     diff = np.where(live[..., None], sp.reshape(R, T, tile) - np.where(live, m, 0)[..., None],
                     -np.inf).astype(F32)
-    pt = np.exp2(diff.astype(np.float64)).astype(F32).reshape(R, Lt)
+    pt = p_tilde_fp32(diff).reshape(R, Lt)
     if p_mode == "exact":                     # identity codec on P (ablation / skeleton check)
         ph, codes, zero = pt.astype(np.float64), None, 0
     else:

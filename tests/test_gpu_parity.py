@@ -361,6 +361,30 @@ def test_decode_underflow_no_zero_blocks(torch_dev):
     assert zg == 0 and zo == 0
 
 
+@pytest.mark.parametrize("name,hq", [("tiny", 8), ("qwen3_30b_a3b", 16), ("mla", 16), ("mla_mxfp4", 16)])
+def test_special_values(torch_dev, name, hq):
+    """Keys, values and the MLA latent with token rows of zeros, negative zeros, one constant,
+    E2M1 grid values times powers of two (rounding ties) and single elements of 1000
+    (``special_rows``): all-zero blocks (scale 0, signed zero codes), tie-breaking in the
+    element rounding and the scale search, and large tensor scales.  The cache bytes equal the
+    oracle's and the decode matches it.  The 1000-valued elements set the tensor scales, so the
+    method's own error against fp64 attention is larger than on Gaussian data (the oracle's:
+    0.42 for the NVFP4 GQA case, 0.25 MXFP4, 0.13 and 0.08 for the two latents); the bound
+    against fp64 attention is 0.6 here."""
+    w = W.workload(name, batch=2, hq=hq, degenerate=True)
+    lens = np.array([300, 77], np.int32)
+    say("special values %s hq=%d" % (name, hq), lens.tolist())
+    built = harness.build(w, lens=lens)
+    if w["attn"] == W.MLA:
+        check_mla_cache(built)
+        worst, worst_ref, zg = compare_mla(built, tol=TOL, ref_bound=0.6)
+    else:
+        check_gqa_cache(built)
+        worst, worst_ref, zg, zo = compare_gqa(built, tol=TOL, ref_bound=0.6)
+        assert zg == zo
+    say("special values: max err vs oracle %.3g, vs fp64 attention %.3g" % (worst, worst_ref))
+
+
 @pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
 def test_decode_mla_ragged(torch_dev, name):
     """MLA: 128 query heads on one latent head (key and value) plus the bf16 rope part;

@@ -340,3 +340,27 @@ def test_mla_rotated_smoothed_exact_codecs_is_textbook_attention():
     wrong_smooth = res["out"] / qs.astype(np.float64) * ksi.astype(np.float64)
     assert np.max(A.row_rel_err(wrong_smooth, ref)) > 0.1                     # k_smooth_inv for q_smooth
     assert np.max(A.row_rel_err(res["out"] * D, ref)) > 0.1                   # missing / 512
+
+
+def test_p_tilde_is_fp32_normal():
+    """p~ = 2^(s - m) is an fp32 value in the normal range: 2^-126 and above stay (correctly
+    rounded), results below 2^-126 are 0.  In a one-tile MXFP4 row, a 32-token block whose
+    logits sit 125 below the tile maximum keeps p~ = 2^-125 and E8M0 scale 2^-127 (the MX rule
+    floor(log2 amax) - 2 at its clamp), so its codes are RNE(2^-125 / 2^-127) = 4, not zero;
+    a block 127.5 below (p~ would be 2^-127.5, subnormal) is all zero, and so is a block at
+    -inf; zero_blocks counts exactly those two of the row's four blocks."""
+    x = np.array([0.0, -1.0, -126.0, -125.5, -126.25, -127.0, -140.0, -np.inf])
+    p = A.p_tilde_fp32(x)
+    want = np.array([1.0, 0.5, 2.0 ** -126, F32(2.0 ** -125.5), 0.0, 0.0, 0.0, 0.0], F32)
+    assert p.dtype == F32 and np.array_equal(p, want)
+    s = np.full((1, 128), -np.inf, F32)
+    s[0, :32] = 0.0
+    s[0, 32:64] = -125.0
+    s[0, 64:96] = -127.5
+    vhat = np.ones((128, 4))
+    res = A.attend(s, vhat, 128, KQ.MXFP4, partials=True)
+    codes = res["p_codes"].reshape(4, 32)
+    assert np.all(codes[0] == 6)                      # p~ = 1 over MX scale 2^-2 is 4: code 6
+    assert np.all(codes[1] == 6)                      # 2^-125 / 2^-127 = 4: code 6
+    assert np.all((codes[2] & 7) == 0) and np.all((codes[3] & 7) == 0)
+    assert res["zero_blocks"] == 2
