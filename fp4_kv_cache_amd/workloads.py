@@ -138,12 +138,16 @@ def outlier_channels(w, h):
 E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
 
 
-def special_rows(w, x):
+def special_rows(w, x, b):
     """With w["degenerate"], token rows of special values replace drawn rows of x [L, d], by
     token index t % 8: 0 zeros, 1 negative zeros, 2 the constant 0.75, 3 E2M1 grid values
     times powers of two 2^-2 .. 2^2 with mixed signs, 4 a drawn row with one element set to
     1000; other rows stay as drawn.  Deterministic in (t, channel), so a slice of a sequence
-    regenerates on its own."""
+    regenerates on its own.  w["seq_scales"] (optional, one power of two per sequence)
+    multiplies sequence b's rows, e.g. far beyond the calibration statistics of sequence 0."""
+    sc = w.get("seq_scales")
+    if sc is not None:
+        x = x * np.float32(sc[b])
     if not w.get("degenerate"):
         return x
     x = np.array(x, dtype=np.float32, copy=True)
@@ -170,14 +174,14 @@ def keys(w, b, h, L):
     ch = outlier_channels(w, h)
     if len(ch):
         k[:, ch] *= np.float32(w["outlier_scale"])
-    return _cast(w, special_rows(w, k))
+    return _cast(w, special_rows(w, k, b))
 
 
 def values(w, b, h, L):
     v = _rng(w, T_V, b, h).standard_normal((L, w["d"]), dtype=np.float32)
     if w["lognormal"]:
         v *= np.exp(_rng(w, T_VMAG, b, h).normal(0.0, w["lognormal"], size=(L, 1))).astype(np.float32)
-    return _cast(w, special_rows(w, v))
+    return _cast(w, special_rows(w, v, b))
 
 
 def queries(w, b):

@@ -385,6 +385,27 @@ def test_special_values(torch_dev, name, hq):
     say("special values: max err vs oracle %.3g, vs fp64 attention %.3g" % (worst, worst_ref))
 
 
+@pytest.mark.parametrize("name,hq", [("tiny", 8), ("qwen3_30b_a3b", 16), ("mla", 16), ("mla_mxfp4", 16)])
+def test_scales_past_the_calibration(torch_dev, name, hq):
+    """The special-value rows with the second sequence's keys, values and latent 2^20 times
+    larger than the calibration sequence's: its NVFP4 block scales saturate at E4M3 448 (code
+    0x7E, the search candidates clamped to [1, 0x7E]) and its FP4 codes at 6, while MXFP4 only
+    shifts its E8M0 exponents.  Cache bytes equal the oracle's and the decode matches it; the
+    saturation is deliberate, so the error against fp64 attention is not bounded here."""
+    w = W.workload(name, batch=2, hq=hq, degenerate=True, seq_scales=(1.0, 2.0 ** 20))
+    lens = np.array([300, 77], np.int32)
+    say("scales past the calibration %s hq=%d" % (name, hq), lens.tolist())
+    built = harness.build(w, lens=lens)
+    if w["attn"] == W.MLA:
+        check_mla_cache(built)
+        worst, worst_ref, zg = compare_mla(built, tol=TOL, ref_bound=float("inf"))
+    else:
+        check_gqa_cache(built)
+        worst, worst_ref, zg, zo = compare_gqa(built, tol=TOL, ref_bound=float("inf"))
+        assert zg == zo
+    say("scales past the calibration: max err vs oracle %.3g" % worst)
+
+
 @pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
 def test_decode_mla_ragged(torch_dev, name):
     """MLA: 128 query heads on one latent head (key and value) plus the bf16 rope part;
