@@ -73,6 +73,13 @@ __device__ __forceinline__ void lds_load16(const void *g, const void *lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(__builtin_amdgcn_readfirstlane(base)), "v"(g) : "memory");
 }
+// The same load from a wave-uniform 64-bit base (in SGPRs) plus a 32-bit per-lane byte offset,
+// so that a wave's loads from one page need no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void lds_load16_so(const uint8_t *gbase, uint32_t off, const void *lds) {
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(base)), "v"(off), "s"(gbase) : "memory");
+}
 __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Transposed 4-bit LDS read: within each group of 16 lanes, lane 16 g + j receives nibble j of
@@ -189,32 +196,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int e = tid; e < cnt; e += 512)
       pgl[e] = phys_page(a, b, ((tb + j0 + e / NPT) * 128) / P + e % NPT, last_lp);
   };
-  // physical row (page * P + offset) of token r of relative tile j
-  auto row_of = [&](int j, int r) -> long {
-    const int pg = pgl[(j % CAP) * NPT + (NPT == 1 ? 0 : r / P)];
-    return (long)pg * P + ((tb + j) * 128 + r) % P;
-  };
   // stage relative tile j: 32 latent, 16 rope and the scale loads, issued by the value waves
-  // (the score waves carry the longer dependency chain per tile)
+  // (the score waves carry the longer dependency chain per tile).  Value wave vw loads tile
+  // rows 32 vw .. 32 vw + 31, which lie in one page (P is a multiple of 32): one page lookup and
+  // a wave-uniform base per tile.  Latent load m: lane (c, q) = (lane % 16, lane / 16) takes
+  // 16-byte chunk c ^ swz_lat(r) of row r = 32 vw + 4 m + q; rope load m: lane (c, q) =
+  // (lane % 8, lane / 8) takes chunk c ^ swz_rope(r) of row r = 32 vw + 8 m + q.  Since
+  // swz_lat(r) = (4 ((m ^ vw) & 3) + q) and swz_rope(r) = ((q / 2) & 1) + 2 (vw & 3) there, the
+  // lanes' byte offsets inside the wave's rows are fixed up to an xor of 64 ((m ^ vw) & 3).
   auto stage_tile = [&](int j) {
     if (wv < 4) return;
-    const int vw = wv - 4;
-    uint8_t *Lt = lat + (j % 3) * LAT;
-    uint8_t *Rt = rope + (j & 1) * ROPE;
+    const int vw = __builtin_amdgcn_readfirstlane(wv - 4);
+    const int pg = __builtin_amdgcn_readfirstlane(pgl[(j % CAP) * NPT + (NPT == 1 ? 0 : (32 * vw) / P)]);
+    const long row0 = (long)pg * P + ((tb + j) * 128 + 32 * vw) % P;
+    const uint8_t *lg = a.k_codes + row0 * (D / 2);
+    const uint8_t *rg = (const uint8_t *)a.k_rope + row0 * (2 * R);
+    uint8_t *Lt = lat + (j % 3) * LAT + 8192 * vw;
+    uint8_t *Rt = rope + (j & 1) * ROPE + 4096 * vw;
+    const uint32_t lq = lane >> 4, rq = lane >> 3;
+    const uint32_t lat_lane = 256 * lq + 16 * ((lane & 15) ^ lq);
+    const uint32_t rope_lane = 128 * rq + 16 * ((lane & 7) ^ ((rq >> 1) & 1) ^ (2 * (vw & 3)));
 #pragma unroll
-    for (int m = 0; m < 8; m++) {
-      const int g = 8 * vw + m;
-      const int r = 4 * g + (lane >> 4);
-      const int c = (lane & 15) ^ swz_lat(r);
-      lds_load16(a.k_codes + row_of(j, r) * (D / 2) + 16 * c, Lt + 1024 * g);
-    }
+    for (int m = 0; m < 8; m++)
+      lds_load16_so(lg + 1024 * m, lat_lane ^ (64u * ((m ^ vw) & 3)), Lt + 1024 * m);
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-      const int g = 4 * vw + m;
-      const int r = 8 * g + (lane >> 3);
-      const int c = (lane & 7) ^ swz_rope(r);
-      lds_load16((const uint8_t *)a.k_rope + row_of(j, r) * (2 * R) + 16 * c, Rt + 1024 * g);
-    }
+    for (int m = 0; m < 4; m++)
+      lds_load16_so(rg + 1024 * m, rope_lane, Rt + 1024 * m);
     if constexpr (NV) {
       if (vw == 0 && lane < 16) {
         const int tr = lane >> 1;   // token tile (16 tokens): 32 scale bytes
@@ -375,7 +382,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         // ---- transposed softmax (lane (n, q4) holds tokens 32 q4 .. + 31 of head n)
         const int tok0 = (tb + j) * 128;
-        if (tok0 + 128 > L) {
+        if (tok0 + 128 > L) {   // the last tile only: a branch, not selects on every tile
+          asm volatile("" ::: "memory");
 #pragma unroll
           for (int i = 0; i < 8; i++)
 #pragma unroll
