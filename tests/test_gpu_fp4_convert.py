@@ -66,3 +66,46 @@ def test_hardware_fp4_convert_matches_the_encoder(torch_dev, e):
     # every negative value that does not round to zero agrees
     nz = ~nonneg & ((want & 7) != 0)
     assert np.array_equal(got[nz], want[nz])
+
+
+
+def _verify_slice(start, n, codes, e):
+    """Oracle codes of the fp32 patterns start .. start + n - 1 divided by 2^e, against the
+    hardware's codes (one nibble per pattern); NaN patterns are skipped.  Returns
+    (patterns checked, first mismatches)."""
+    x = np.arange(start, start + n, dtype=np.uint32).view(np.float32)
+    with np.errstate(over="ignore", under="ignore", invalid="ignore"):
+        base = x * np.float32(2.0 ** -e)   # exact unless it overflows to infinity or underflows
+    want = C.e2m1_encode(base)
+    got = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(-1)
+    keep = ~np.isnan(x)
+    bad = np.nonzero((got != want) & keep)[0]
+    return int(keep.sum()), [(hex(start + int(i)), int(got[i]), int(want[i])) for i in bad[:4]]
+
+
+@pytest.mark.parametrize("e", [0, -10])
+def test_hardware_fp4_convert_exhaustive(torch_dev, e):
+    """Every fp32 bit pattern except the NaNs (a caller error for the encoder), both signs,
+    through the hardware conversion at scale 2^e: its code equals the oracle's encoder's code
+    of x / 2^e (a power-of-two division, rounded only where it overflows to infinity or
+    underflows, and those values land on the same code either way).  The patterns are made on
+    the GPU; the oracle checks them in slices on a thread pool."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    from fp4_kv_cache_amd import lib as L
+    CH, SL = 1 << 26, 1 << 22
+    stream = torch.cuda.current_stream().cuda_stream
+    out = torch.empty(CH // 2, dtype=torch.uint8, device="cuda")
+    checked, bad = 0, []
+    with ThreadPoolExecutor(8) as pool:
+        for start in range(0, 1 << 32, CH):
+            u = torch.arange(start, start + CH, dtype=torch.int64, device="cuda")
+            xt = torch.where(u >= (1 << 31), u - (1 << 32), u).to(torch.int32).view(torch.float32)
+            L.check(L.fp4kv_pack_e2m1(xt.data_ptr(), CH, e, out.data_ptr(), stream), "fp4kv_pack_e2m1")
+            o = out.cpu().numpy()
+            res = list(pool.map(lambda k: _verify_slice(start + k, SL, o[k // 2:(k + SL) // 2], e), range(0, CH, SL)))
+            checked += sum(r[0] for r in res)
+            bad += [b for r in res for b in r[1]]
+            assert not bad, ("scale 2^%d" % e, bad[:8])
+    say("scale 2^%d: all %d non-NaN fp32 patterns give the oracle's E2M1 code" % (e, checked))
+    assert checked == (1 << 32) - 2 * ((1 << 23) - 1)
