@@ -67,7 +67,9 @@ __device__ __forceinline__ bh8 as_bh8(const uint4 &u) {
 // would make every LDS read it cannot prove disjoint from a pending LDS load wait for it, which
 // defeats loading the next tile while the current one is read; the kernel waits for its own
 // loads (vmcnt) before the barrier that hands a tile to the other waves.  M0 holds the LDS base
-// (one wait state between writing M0 and the load).
+// (one wait state between writing M0 and the load).  M0 is a register the compiler reserves and
+// cannot take as a clobber; no compiler-generated instruction of these kernels reads or writes it
+// (their compiled code sets M0 only in these wrappers), so the wrappers disturb nothing.
 __device__ __forceinline__ void lds_load16(const void *g, const void *lds) {
   const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
