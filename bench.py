@@ -495,7 +495,7 @@ def main():
                                    "1 new token per sequence per step" if QN == 1 else
                                    "%d new tokens per sequence per step, all %d decoded (causal)" % (QN, QN))),
                    "global_batch": B, "seq_len": int(lens.max()), "kv_bytes_per_step": int(kv_bytes),
-                   "cache_copies_rotated": len(copies)},
+                   "cache_copies_rotated": nc},
         "roofline": roofline,
         "breakdown_us": {"decode_partials_kernel": round(k_us, 2), "split_merge_kernel": round(m_us, 2),
                          "kv_append_1_token": round(a_us, 2)},
