@@ -202,7 +202,9 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
  * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
  * different streams, or from several host threads) race and give undefined results; calls
  * ordered on one stream are safe.  The scratch keeps the last call's contents; nothing in it
- * needs clearing between calls.
+ * needs clearing between calls.  The first call on a GPU looks up the scratch's device address
+ * (hipGetSymbolAddress); a caller that captures this call in a HIP graph makes one call on that
+ * GPU before capturing.
  * Returns FP4KV_ERR_WORKSPACE when fp4_decode_workspace_bytes() for this shape exceeds
  * FP4KV_NOALLOC_SCRATCH_BYTES (64 MiB: GQA up to about 30,000 (sequence, KV head) units at 4
  * query heads per KV head; MLA with 128 query heads up to 92 sequences), and
