@@ -163,6 +163,8 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.q_len = q_len;
   d.abl = kAblation ? g_ablation : 0;
   if (d.abl && c->attn != FP4KV_GQA) return FP4KV_ERR_UNSUPPORTED;
+  // normalized P needs both passes of one fp4_decode_attention call, one query token
+  if ((d.abl & kAblVanillaP) && (q_len != 1 || !need_q || !need_out)) return FP4KV_ERR_UNSUPPORTED;
   d.n_waves = (int)shares;
   d.softmax_scale = softmax_scale;
   // 1/head_dim of the unnormalized rotation (1 when the rotation is switched off)
@@ -338,7 +340,7 @@ int bf16_decode_attention(const fp4kv_bf16_cache *c, const void *q, int q_dtype,
 // Ablation-study build only: technique switches (kAbl* bits) for the following GQA append
 // and decode calls of this process.
 int fp4kv_ablation_set(int flags) {
-  if (flags & ~(kAblSingleQ | kAblNoRotation | kAblNoSearch)) return FP4KV_ERR_INVALID_ARG;
+  if (flags & ~(kAblSingleQ | kAblNoRotation | kAblNoSearch | kAblVanillaP)) return FP4KV_ERR_INVALID_ARG;
   g_ablation = flags;
   return FP4KV_OK;
 }
@@ -460,6 +462,15 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
                        softmax_scale, out, workspace, workspace_bytes, zero_block_count, true, true, &a);
   if (st) return st;
   const bool mla = c->attn == FP4KV_MLA;
+  if (kAblation && (a.abl & kAblVanillaP)) {
+    // ablation study, normalized P: a first pass of the method gives each row's max and
+    // softmax denominator (written into out, which the second pass overwrites)
+    DecodeArgs a1 = a;
+    a1.abl = (a.abl & ~kAblVanillaP) | kAblRowStats;
+    a1.zero_blocks = nullptr;
+    if (launch_decode_partials(a1, (hipStream_t)stream) != hipSuccess) return FP4KV_ERR_HIP;
+    if (launch_decode_merge(a1, (hipStream_t)stream) != hipSuccess) return FP4KV_ERR_HIP;
+  }
   hipError_t e = mla ? launch_mla_partials(a, (hipStream_t)stream) : launch_decode_partials(a, (hipStream_t)stream);
   if (e != hipSuccess) return FP4KV_ERR_HIP;
   return to_status(mla ? launch_mla_merge(a, (hipStream_t)stream) : launch_decode_merge(a, (hipStream_t)stream));

@@ -150,6 +150,25 @@ __device__ __forceinline__ int ksw_index(int tok, int q4) { return tok * 4 + q4 
 template <int FMT, int GV>
 constexpr int row_sets() { return (GV + 7) / 8; }
 
+// Ablation study only (normalized P): P.V of one 16-token parity when the P block scale is a
+// general E4M3 value like the value scale -- both as signed-digit passes, 3 x 3 MFMAs; a term
+// takes the sign-flipped P when exactly one of its two digits is the subtracted one.
+template <int DV, int DP>
+__device__ __forceinline__ v4f pv_term(const v8i &av, const v8i &p, const v8i &pn, v4f c, int lv, int lp) {
+  return mfma4<DV, DP>(av, ((DV == 2) != (DP == 2)) ? pn : p, c, lv, lp);
+}
+__device__ __forceinline__ v4f pv_general(const v8i &av, const v8i &p, const v8i &pn, v4f c, int lv, int lp) {
+  c = pv_term<0, 0>(av, p, pn, c, lv, lp);
+  c = pv_term<0, 1>(av, p, pn, c, lv, lp);
+  c = pv_term<0, 2>(av, p, pn, c, lv, lp);
+  c = pv_term<1, 0>(av, p, pn, c, lv, lp);
+  c = pv_term<1, 1>(av, p, pn, c, lv, lp);
+  c = pv_term<1, 2>(av, p, pn, c, lv, lp);
+  c = pv_term<2, 0>(av, p, pn, c, lv, lp);
+  c = pv_term<2, 1>(av, p, pn, c, lv, lp);
+  return pv_term<2, 2>(av, p, pn, c, lv, lp);
+}
+
 // MQ: several query tokens per sequence (causal rows); false compiles the one-token decode
 // with every row seeing the whole sequence.
 template <int FMT, int GV, int P, bool MQ>
@@ -373,6 +392,18 @@ void gqa_partials(DecodeArgs a) {
     }
   }
   const int Lmin = MQ ? L - QL + 1 : L;       // the shortest row's length
+  // ablation study, normalized P: the row's max and softmax denominator from the first pass
+  float vst[RS][2];
+#pragma unroll
+  for (int rs = 0; rs < RS; rs++) {
+    vst[rs][0] = 0.0f;
+    vst[rs][1] = 1.0f;
+    if (kAblation && (a.abl & kAblVanillaP) && lrow[rs]) {
+      const long row = (long)b * a.hq + kvh * GQ + rs * VS + (ncol >> 1);   // one query token
+      vst[rs][0] = a.out[row * 128];
+      vst[rs][1] = a.out[row * 128 + 1];
+    }
+  }
 
   // ---------------- main loop over 128-token tiles ----------------
   float m_run[RS], l_run[RS], f_run[RS];
@@ -465,6 +496,64 @@ void gqa_partials(DecodeArgs a) {
         for (int rr = 0; rr < 4; rr++)
           if (tok0 + 32 * q4 + 4 * i + rr >= Lr) s[i][rr] = -INFINITY;
     }
+    uint32_t pk[4];
+    int pbyte[2];
+    uint32_t ppw[2] = {0u, 0u};   // normalized P, NVFP4: pass words of the P block scales
+    if (kAblation && (a.abl & kAblVanillaP)) {
+      // ablation study only: p = 2^(s - M) / den over the whole row (M, den from the first
+      // pass), quantized with tensor scale 1: NVFP4 default E4M3 scale per 16 tokens, MXFP4
+      // E8M0 per 32; the partial is the plain sum of P.V (the merge adds the unit's slots)
+      const float Mr = vst[rs][0], dr = vst[rs][1];
+      float am0 = 0.0f, am1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) {
+          const float p = s[i][rr] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[i][rr] - Mr) / dr;
+          s[i][rr] = p;
+          if (i < 4) am0 = fmaxf(am0, p);
+          else am1 = fmaxf(am1, p);
+        }
+      if constexpr (FMT == kFmtNV) {
+        const float am[2] = {am0, am1};
+#pragma unroll
+        for (int pb = 0; pb < 2; pb++) {
+          const uint32_t c = e4m3_enc_sat(am[pb] / 6.0f);
+          const float S = e4m3_dec(c);
+          const float r = S != 0.0f ? 1.0f / S : 0.0f;
+          float t[4][4];
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) t[j][rr] = s[4 * pb + j][rr] * r;
+          pk[2 * pb] = pack8(t[0], t[1], 1.0f);
+          pk[2 * pb + 1] = pack8(t[2], t[3], 1.0f);
+          ppw[pb] = lut[c];
+          pbyte[pb] = 127;
+        }
+      } else {
+        const int e = mx_exp(fmaxf(am0, am1));
+        const float ps = ldexpf(1.0f, e);
+        pbyte[0] = pbyte[1] = e + 127;
+#pragma unroll
+        for (int w = 0; w < 4; w++) pk[w] = pack8(s[2 * w], s[2 * w + 1], ps);
+      }
+      if (count_zero) {
+        const bool rep = (ncol & 1) == 0 && lrow[rs];
+        const int L = Lrow[rs];
+        if (rep) {
+          if constexpr (FMT == kFmtNV) {
+#pragma unroll
+            for (int pb = 0; pb < 2; pb++)
+              if (tok0 + 32 * q4 + 16 * pb < L && ((pk[2 * pb] | pk[2 * pb + 1]) & 0x77777777u) == 0u) nzero++;
+          } else {
+            if (tok0 + 32 * q4 < L && ((pk[0] | pk[1] | pk[2] | pk[3]) & 0x77777777u) == 0u) nzero++;
+          }
+        }
+      }
+      m_run[rs] = 0.0f;                                  // weight 1 in the merge
+      l_run[rs] = (tb == 0 && q4 == 0) ? 1.0f : 0.0f;    // the unit's first slot carries den = 1
+    } else {
     // ---- transposed softmax over the tile; block maxima of the logits give the
     // probability block maxima (exp2 is monotone)
     float bm0 = -INFINITY, bm1 = -INFINITY;
@@ -489,8 +578,6 @@ void gqa_partials(DecodeArgs a) {
         lt = lt + p;
       }
     // ---- fused probability quantization into the P.V B operand
-    uint32_t pk[4];
-    int pbyte[2];
     if constexpr (FMT == kFmtNV) {
       const float am[2] = {__builtin_amdgcn_exp2f(bm0 - mts), __builtin_amdgcn_exp2f(bm1 - mts)};
 #pragma unroll
@@ -540,6 +627,7 @@ void gqa_partials(DecodeArgs a) {
     for (int cg = 0; cg < 8; cg++)
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) o_run[rs][cg][rr] = o_run[rs][cg][rr] * gamma;
+    }   // method P
     // ---- P.V
     if constexpr (FMT == kFmtNV) {
       const v8i p0 = {(int)pk[0], (int)pk[1], 0, 0, 0, 0, 0, 0};
@@ -554,6 +642,11 @@ void gqa_partials(DecodeArgs a) {
         const uint32_t b0 = P >= 32 ? byte_of(vt.x[8], 2 * cg) : byte_of(vt.x[8], cg);
         const uint32_t b1 = P >= 32 ? byte_of(vt.x[8], 2 * cg + 1) : byte_of(vt.x[8], 8 + cg);
         const int l0 = (int)lut[b0], l1 = (int)lut[b1];
+        if (kAblation && (a.abl & kAblVanillaP)) {   // general E4M3 P block scales
+          const v4f c = pv_general(av, p0, p0n, o_run[rs][cg], l0, (int)ppw[0]);
+          o_run[rs][cg] = pv_general(av, p1, p1n, c, l1, (int)ppw[1]);
+          continue;
+        }
         v4f c = mfma4<0, 0>(av, p0, o_run[rs][cg], l0, pbyte[0]);
         c = mfma4<1, 0>(av, p0, c, l0, pbyte[0]);
         c = mfma4<2, 0>(av, p0n, c, l0, pbyte[0]);
@@ -748,6 +841,20 @@ __global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
   const float *ml = a.ws_ml + r0 * 2;
   const float *o = a.ws_o + r0 * 128;
   const long so = (long)GVr * 128, sm = 2L * GVr;  // strides between the unit's partials
+  if (kAblation && (a.abl & kAblRowStats)) {
+    // ablation study, first pass of normalized P: the row's max and softmax denominator
+    float M = -INFINITY;
+    for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[sm * s]);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
+    float den = 0.f;
+    if (M > -INFINITY)
+      for (int s = lane; s < nv; s += 64) den = fmaf(__builtin_amdgcn_exp2f(ml[sm * s] - M), ml[sm * s + 1], den);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k);
+    if (lane == 0) *(float2 *)(a.out + (long)row * 128) = float2{M, den};
+    return;
+  }
   // every (m, l) pair and output partial of the row in flight at once, in two size classes
   if (nv <= 16) { merge_row_fast<16>(ml, o, sm, so, nv, lane, dst); return; }
   if (nv <= 64) { merge_row_fast<64>(ml, o, sm, so, nv, lane, dst); return; }

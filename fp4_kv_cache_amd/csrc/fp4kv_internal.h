@@ -17,6 +17,11 @@ constexpr int kMaxSplitPages = 512;
 constexpr int kAblSingleQ = 1;      // no dual residual: the query's second FP4 pass is zero
 constexpr int kAblNoRotation = 2;   // no Hadamard rotation of keys and queries
 constexpr int kAblNoSearch = 4;     // every key block keeps its default scale
+constexpr int kAblVanillaP = 8;     // no underflow-aware P: P normalized over the whole row, NVFP4
+                                    // with tensor scale 1 and default E4M3 block scales (MXFP4:
+                                    // E8M0), from the row's max and denominator of a first pass
+constexpr int kAblRowStats = 16;    // internal: that first pass's merge writes the row's (max,
+                                    // denominator) into out[row][0..1] instead of the output
 #ifdef FP4KV_ABLATION
 constexpr bool kAblation = true;
 #else

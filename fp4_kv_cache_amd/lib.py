@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libfp4kv.so")
 # the ablation-study build (same sources with -DFP4KV_ABLATION): the product entry points plus
 # fp4kv_ablation_set, whose switches turn techniques of the method off (study only)
 LIB_ABLATION_PATH = os.path.join(HERE, "libfp4kv_ablate.so")
-ABL_SINGLE_Q, ABL_NO_ROTATION, ABL_NO_SEARCH = 1, 2, 4
+ABL_SINGLE_Q, ABL_NO_ROTATION, ABL_NO_SEARCH, ABL_NORMALIZED_P = 1, 2, 4, 8
 
 NVFP4, MXFP4 = 0, 1
 F32, BF16 = 0, 1
