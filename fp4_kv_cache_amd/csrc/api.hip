@@ -162,7 +162,7 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.q_bf16 = q_dtype == FP4KV_BF16;
   d.q_len = q_len;
   d.abl = kAblation ? g_ablation : 0;
-  if (d.abl && c->attn != FP4KV_GQA) return FP4KV_ERR_UNSUPPORTED;
+  if ((d.abl & kAblVanillaP) && c->attn != FP4KV_GQA) return FP4KV_ERR_UNSUPPORTED;
   // normalized P needs both passes of one fp4_decode_attention call, one query token
   if ((d.abl & kAblVanillaP) && (q_len != 1 || !need_q || !need_out)) return FP4KV_ERR_UNSUPPORTED;
   d.n_waves = (int)shares;
@@ -404,7 +404,6 @@ int kv_quant_append(const fp4kv_cache *c, const void *k_new, const void *v_new, 
   a.num_tokens = num_tokens;
   a.bf16 = dtype == FP4KV_BF16;
   a.abl = kAblation ? g_ablation : 0;
-  if (a.abl && c->attn != FP4KV_GQA) return FP4KV_ERR_UNSUPPORTED;
   a.k_codes = c->k_codes;
   a.k_scales = c->k_scales;
   a.v_codes = c->v_codes;

@@ -529,8 +529,10 @@ __global__ __launch_bounds__(kLatThreads) void latent_append(AppendArgs a) {
   }
   for (int e = (sp.first + sp.n_new) * D + tid; e < B * D; e += kLatThreads) X(e / D, e % D) = 0.0f;
   __syncthreads();
-  // FWHT over the rows of the new tokens (stages h = 1, 2, ..., 256)
-  for (int h = 1; h < D; h <<= 1) {
+  // FWHT over the rows of the new tokens (stages h = 1, 2, ..., 256; none when the ablation
+  // build switches the rotation off -- the barrier above already published the rows)
+  const int hend = kAblation && (a.abl & kAblNoRotation) ? 1 : D;
+  for (int h = 1; h < hend; h <<= 1) {
     for (int e = tid; e < sp.n_new * (D / 2); e += kLatThreads) {
       const int k = sp.first + e / (D / 2), w = e % (D / 2);
       int idx = (w / h) * 2 * h + (w % h);
@@ -595,6 +597,8 @@ __global__ __launch_bounds__(kLatThreads) void latent_append(AppendArgs a) {
       c = mx_exp(amax) + deltas[s_kk];
       valid = c >= -127 && c <= 127;
     }
+    // (the ablation build's no-search switch leaves only the default candidate)
+    if (kAblation && s_kk > 0 && (a.abl & kAblNoSearch)) valid = false;
     cand[s_kk][s_ct] = valid ? c : kNoCand;
   }
   __syncthreads();
@@ -694,7 +698,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_append(AppendArgs a) {
     X(k, ch) = load_elem(a.k_new, (long)(tail.i + k) * D + ch, a.bf16) * ksi[ch];
   }
   __syncthreads();
-  for (int h = 1; h < D; h <<= 1) {
+  for (int h = 1; h < hend; h <<= 1) {
     for (int e = tid; e < tail.n * (D / 2); e += kLatThreads) {
       const int k = e / (D / 2), w = e % (D / 2);
       const int idx = (w / h) * 2 * h + (w % h);

@@ -658,6 +658,7 @@ __global__ __launch_bounds__(256) void mla_qprep(DecodeArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < 8; j++) y[j] = y[j] * a.qs[8 * lane + j];
+  if (!(kAblation && (a.abl & kAblNoRotation))) {   // (the ablation build can switch it off)
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
@@ -673,8 +674,13 @@ __global__ __launch_bounds__(256) void mla_qprep(DecodeArgs a) {
   fwht_lanes<8>(y, lane);
   fwht_lanes<16>(y, lane);
   fwht_lanes<32>(y, lane);
+  }
 #pragma unroll
   for (int k = 0; k < 2; k++) {
+    if (kAblation && k == 1 && (a.abl & kAblSingleQ)) {   // single-pass query: the second pass sees zeros
+#pragma unroll
+      for (int j = 0; j < 8; j++) y[j] = 0.0f;
+    }
     float lmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; j++) lmax = fmaxf(lmax, fabsf(y[j]));
@@ -814,6 +820,11 @@ __global__ __launch_bounds__(64) void mla_merge(DecodeArgs a) {
   const float inv = 1.0f / den;
 #pragma unroll
   for (int j = 0; j < 8; j++) y[j] *= inv;
+  const float *qs = a.qs + 8 * lane;
+  if (kAblation && (a.abl & kAblNoRotation)) {   // ablation study: the latent was not rotated
+#pragma unroll
+    for (int j = 0; j < 8; j++) y[j] = y[j] * qs[j];
+  } else {
   // Walsh-Hadamard over 512 channels: stages 1, 2, 4 in the lane, 8 .. 256 across lanes
 #pragma unroll
   for (int hh = 1; hh < 8; hh <<= 1)
@@ -830,9 +841,9 @@ __global__ __launch_bounds__(64) void mla_merge(DecodeArgs a) {
   fwht_lanes<8>(y, lane);
   fwht_lanes<16>(y, lane);
   fwht_lanes<32>(y, lane);
-  const float *qs = a.qs + 8 * lane;
 #pragma unroll
   for (int j = 0; j < 8; j++) y[j] = y[j] * (1.0f / 512.0f) * qs[j];
+  }
   dst[0] = float4{y[0], y[1], y[2], y[3]};
   dst[1] = float4{y[4], y[5], y[6], y[7]};
 }

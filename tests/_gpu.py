@@ -87,7 +87,11 @@ def check_gqa_cache(built, seqs=None, pairs=None, opts=None):
                                         exp[tuple(bad[0])]))
 
 
-def check_mla_cache(built, seqs=None):
+def check_mla_cache(built, seqs=None, opts=None):
+    """Latent codes, tile scales and rope bytes of the given sequences == the oracle's one-shot
+    quantization (bit exact); ``opts`` carries the oracle's search / rotate switches."""
+    search = (opts or {}).get("search", True)
+    rotate = (opts or {}).get("rotate", True)
     w = built.w
     ksi, qs, gk, gv = built.calib
     views = cache_np(built)
@@ -95,7 +99,7 @@ def check_mla_cache(built, seqs=None):
     for b in seqs:
         L = int(built.lens[b])
         lc, ls, kr = LY.gather_mla(views, built.bt_np[b], L, w["fmt"])
-        olc, ols, _ = KQ.quantize_latent(W.keys(w, b, 0, L), ksi[0], gk[0], w["fmt"])
+        olc, ols, _ = KQ.quantize_latent(W.keys(w, b, 0, L), ksi[0], gk[0], w["fmt"], search, rotate)
         okr = W.bf16_bits(W.rope_keys(w, b, L))
         for name, got, exp in (("latent codes", lc, olc), ("tile scales", ls, ols),
                                ("rope", kr.view(np.uint16), okr)):
@@ -157,9 +161,10 @@ def compare_gqa(built, pairs=None, tol=1e-3, opts=None, ref_bound=None):
     return worst, worst_ref, zgpu, zor
 
 
-def compare_mla(built, seqs=None, tol=1e-3, ref_bound=None):
+def compare_mla(built, seqs=None, tol=1e-3, ref_bound=None, opts=None):
     """GPU MLA decode vs oracle on the given sequences; returns (max err, max err vs fp64 attention).
-    ``ref_bound`` overrides the aggregate bound against fp64 attention."""
+    ``ref_bound`` overrides the aggregate bound against fp64 attention; ``opts``: the oracle's
+    technique switches."""
     w = built.w
     ksi, qs, gk, gv = built.calib
     qn, out, zgpu = run_decode(built)
@@ -178,7 +183,7 @@ def compare_mla(built, seqs=None, tol=1e-3, ref_bound=None):
             continue
         K = W.keys(w, b, 0, L)
         kr = W.rope_keys(w, b, L)
-        res = A.mla_seq(qn[b, :, :D], qn[b, :, D:], K, kr, ksi[0], qs[0], gk[0], w["fmt"], sc, L=L)
+        res = A.mla_seq(qn[b, :, :D], qn[b, :, D:], K, kr, ksi[0], qs[0], gk[0], w["fmt"], sc, L=L, opts=opts)
         ref = A.reference_attention(qn[b, :, :D], K, K, sc, q_rope=qn[b, :, D:], k_rope=kr)
         er_rows = A.row_rel_err(got, res["out"])
         rows.append(er_rows)
@@ -188,7 +193,7 @@ def compare_mla(built, seqs=None, tol=1e-3, ref_bound=None):
         assert e <= tol, "seq %d: max row error %.3g > %.1g" % (b, e, tol)
         agg.add(got, ref)
     _flip_report("mla", np.concatenate(rows) if rows else [])
-    agg.check(w["fmt"], "mla", ref_bound)
+    compare_mla.last_agg = agg.check(w["fmt"], "mla", ref_bound)
     return worst, worst_ref, zgpu
 
 

@@ -12,7 +12,7 @@ import pytest
 
 from fp4_kv_cache_amd import workloads as W
 from fp4_kv_cache_amd import harness
-from _gpu import say, check_gqa_cache, compare_gqa, run_decode, gqa_oracle
+from _gpu import say, check_gqa_cache, check_mla_cache, compare_gqa, compare_mla, run_decode, gqa_oracle
 from oracle import attention as A
 
 pytestmark = pytest.mark.gpu
@@ -59,6 +59,27 @@ def test_ablation_switch_matches_oracle(torch_dev, name, label, flags, opts):
     # a P block scale decided on the other side of a rounding boundary (p from fp32 exp2 and a
     # differently ordered denominator) may change a block; the counts must agree otherwise
     assert abs(zg - zo) <= 2, (zg, zo)
+
+
+@pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
+@pytest.mark.parametrize("label,flags,opts", SETTINGS[:5], ids=[s[0].split(" (")[0] for s in SETTINGS[:5]])
+def test_ablation_switch_matches_oracle_mla(torch_dev, name, label, flags, opts):
+    """The same switches on the MLA path (query preparation, latent append, merge): the latent's
+    codes and tile scales bit-exact, outputs within 1e-3 of the oracle with the same switch."""
+    from fp4_kv_cache_amd import lib as L
+    lens = np.array([700, 129, 2100], np.int32)
+    w = W.workload(name, batch=len(lens))
+    calib = None
+    if not opts.get("smooth", True):
+        ksi, qs, gk, gv = W.calibration(w)
+        calib = (np.ones_like(ksi), np.ones_like(qs), gk, gv)
+    say("ablation %s: %s" % (name, label), lens.tolist())
+    with L.ablation(flags):
+        built = harness.build(w, lens=lens, calib=calib)
+        check_mla_cache(built, opts=opts)
+        worst, worst_ref, _ = compare_mla(built, tol=TOL, opts=opts, ref_bound=1.5)
+    say("ABLATION %s | %s | max err vs oracle %.3g | error vs fp64 attention over all rows %.4f"
+        % (name, label, worst, compare_mla.last_agg))
 
 
 def _zero_blocks(built, flags, opts):
