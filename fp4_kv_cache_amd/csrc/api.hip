@@ -162,7 +162,6 @@ int fill_decode(const fp4kv_cache *c, const void *q, int q_dtype, int batch, int
   d.q_bf16 = q_dtype == FP4KV_BF16;
   d.q_len = q_len;
   d.abl = kAblation ? g_ablation : 0;
-  if ((d.abl & kAblVanillaP) && c->attn != FP4KV_GQA) return FP4KV_ERR_UNSUPPORTED;
   // normalized P needs both passes of one fp4_decode_attention call, one query token
   if ((d.abl & kAblVanillaP) && (q_len != 1 || !need_q || !need_out)) return FP4KV_ERR_UNSUPPORTED;
   d.n_waves = (int)shares;
@@ -467,8 +466,11 @@ int fp4_decode_attention(const fp4kv_cache *c, const void *q, int q_dtype, int b
     DecodeArgs a1 = a;
     a1.abl = (a.abl & ~kAblVanillaP) | kAblRowStats;
     a1.zero_blocks = nullptr;
-    if (launch_decode_partials(a1, (hipStream_t)stream) != hipSuccess) return FP4KV_ERR_HIP;
-    if (launch_decode_merge(a1, (hipStream_t)stream) != hipSuccess) return FP4KV_ERR_HIP;
+    if ((mla ? launch_mla_partials(a1, (hipStream_t)stream) : launch_decode_partials(a1, (hipStream_t)stream)) !=
+        hipSuccess)
+      return FP4KV_ERR_HIP;
+    if ((mla ? launch_mla_merge(a1, (hipStream_t)stream) : launch_decode_merge(a1, (hipStream_t)stream)) != hipSuccess)
+      return FP4KV_ERR_HIP;
   }
   hipError_t e = mla ? launch_mla_partials(a, (hipStream_t)stream) : launch_decode_partials(a, (hipStream_t)stream);
   if (e != hipSuccess) return FP4KV_ERR_HIP;

@@ -74,6 +74,25 @@ static_assert(pass_words_are_exact(), "E4M3 pass words must sum to the scale");
 // Sign bits of the eight E2M1 codes of a word: the operand of the subtracted term's pass.
 constexpr uint32_t kFp4SignBits = 0x88888888u;
 
+// Ablation study only (normalized P): P.V of one 16-token parity when the P block scale is a
+// general E4M3 value like the value scale -- both as signed-digit passes, 3 x 3 MFMAs; a term
+// takes the sign-flipped P when exactly one of its two digits is the subtracted one.
+template <int DV, int DP>
+__device__ __forceinline__ v4f pv_term(const v8i &av, const v8i &p, const v8i &pn, v4f c, int lv, int lp) {
+  return mfma4<DV, DP>(av, ((DV == 2) != (DP == 2)) ? pn : p, c, lv, lp);
+}
+__device__ __forceinline__ v4f pv_general(const v8i &av, const v8i &p, const v8i &pn, v4f c, int lv, int lp) {
+  c = pv_term<0, 0>(av, p, pn, c, lv, lp);
+  c = pv_term<0, 1>(av, p, pn, c, lv, lp);
+  c = pv_term<0, 2>(av, p, pn, c, lv, lp);
+  c = pv_term<1, 0>(av, p, pn, c, lv, lp);
+  c = pv_term<1, 1>(av, p, pn, c, lv, lp);
+  c = pv_term<1, 2>(av, p, pn, c, lv, lp);
+  c = pv_term<2, 0>(av, p, pn, c, lv, lp);
+  c = pv_term<2, 1>(av, p, pn, c, lv, lp);
+  return pv_term<2, 2>(av, p, pn, c, lv, lp);
+}
+
 // lane l <- lane (l ^ 8) inside each row of 16 (row_ror:8)
 __device__ __forceinline__ float xlane8(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));

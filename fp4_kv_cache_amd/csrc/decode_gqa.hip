@@ -150,25 +150,6 @@ __device__ __forceinline__ int ksw_index(int tok, int q4) { return tok * 4 + q4 
 template <int FMT, int GV>
 constexpr int row_sets() { return (GV + 7) / 8; }
 
-// Ablation study only (normalized P): P.V of one 16-token parity when the P block scale is a
-// general E4M3 value like the value scale -- both as signed-digit passes, 3 x 3 MFMAs; a term
-// takes the sign-flipped P when exactly one of its two digits is the subtracted one.
-template <int DV, int DP>
-__device__ __forceinline__ v4f pv_term(const v8i &av, const v8i &p, const v8i &pn, v4f c, int lv, int lp) {
-  return mfma4<DV, DP>(av, ((DV == 2) != (DP == 2)) ? pn : p, c, lv, lp);
-}
-__device__ __forceinline__ v4f pv_general(const v8i &av, const v8i &p, const v8i &pn, v4f c, int lv, int lp) {
-  c = pv_term<0, 0>(av, p, pn, c, lv, lp);
-  c = pv_term<0, 1>(av, p, pn, c, lv, lp);
-  c = pv_term<0, 2>(av, p, pn, c, lv, lp);
-  c = pv_term<1, 0>(av, p, pn, c, lv, lp);
-  c = pv_term<1, 1>(av, p, pn, c, lv, lp);
-  c = pv_term<1, 2>(av, p, pn, c, lv, lp);
-  c = pv_term<2, 0>(av, p, pn, c, lv, lp);
-  c = pv_term<2, 1>(av, p, pn, c, lv, lp);
-  return pv_term<2, 2>(av, p, pn, c, lv, lp);
-}
-
 // MQ: several query tokens per sequence (causal rows); false compiles the one-token decode
 // with every row seeing the whole sequence.
 template <int FMT, int GV, int P, bool MQ>

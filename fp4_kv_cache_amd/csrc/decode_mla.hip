@@ -301,6 +301,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // a row span more than the fp32 mantissa, so raw_k is the dot rounded once)
     const float a1 = (qg[0] * gk) * a.coef, a2 = (qg[1] * gk) * a.coef, cr = a.coef_rope;
     float m_run = -INFINITY, l_run = 0.0f, f_run = 1.0f;
+    // ablation study, normalized P: the head's max and softmax denominator from a first pass
+    float vM = 0.0f, vD = 1.0f;
+    if (kAblation && (a.abl & kAblVanillaP) && active) {
+      const float *st = a.out + ((long)b * a.hq + h0 + n) * D;
+      vM = st[0];
+      vD = st[1];
+    }
     const float inv6gp = 1.0f / (6.0f * 0.0009765625f);   // fl32(1 / fl32(6 * 2^-10))
     const int trow = 32 * (n >> 2) + (n & 3);   // A-operand row: tile token trow + 4 i in group i
     // Byte offsets inside a tile buffer of the lane's Q.K^T operand chunks.  Row trow + 4 i has
@@ -392,6 +399,59 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int rr = 0; rr < 4; rr++)
               if (tok0 + 32 * q4 + 4 * i + rr >= L) s[i][rr] = -INFINITY;
         }
+        if (kAblation && (a.abl & kAblVanillaP)) {
+          // ablation study only: p = 2^(s - M) / den over the whole row (M, den of the head from
+          // a first pass), quantized with tensor scale 1 -- NVFP4 default E4M3 scale per 16
+          // tokens (its pass word goes to the value waves), MXFP4 E8M0 per 32; no rescale, the
+          // partials are summed by the merge
+          float am0 = 0.0f, am1 = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+              const float p = s[i][rr] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[i][rr] - vM) / vD;
+              s[i][rr] = p;
+              if (i < 4) am0 = fmaxf(am0, p);
+              else am1 = fmaxf(am1, p);
+            }
+          uint32_t pk[4], w0 = 0u, w1 = 0u;
+          if constexpr (NV) {
+            const float am[2] = {am0, am1};
+            uint32_t pwd[2];
+#pragma unroll
+            for (int pb = 0; pb < 2; pb++) {
+              const uint32_t c = e4m3_enc_sat(am[pb] / 6.0f);
+              const float S = e4m3_dec(c);
+              const float r = S != 0.0f ? 1.0f / S : 0.0f;
+              float t[4][4];
+#pragma unroll
+              for (int jj = 0; jj < 4; jj++)
+#pragma unroll
+                for (int rr = 0; rr < 4; rr++) t[jj][rr] = s[4 * pb + jj][rr] * r;
+              pk[2 * pb] = pack8(t[0], t[1], 1.0f);
+              pk[2 * pb + 1] = pack8(t[2], t[3], 1.0f);
+              pwd[pb] = lut[c];
+            }
+            if (count_zero) {
+#pragma unroll
+              for (int pb = 0; pb < 2; pb++)
+                if (tok0 + 32 * q4 + 16 * pb < L && ((pk[2 * pb] | pk[2 * pb + 1]) & 0x77777777u) == 0u) nzero++;
+            }
+            w0 = pwd[0];
+            w1 = pwd[1];
+          } else {
+            const int pe = mx_exp(fmaxf(am0, am1));
+            const float ps = ldexpf(1.0f, pe);
+#pragma unroll
+            for (int w = 0; w < 4; w++) pk[w] = pack8(s[2 * w], s[2 * w + 1], ps);
+            if (count_zero && tok0 + 32 * q4 < L && ((pk[0] | pk[1] | pk[2] | pk[3]) & 0x77777777u) == 0u) nzero++;
+            w0 = (uint32_t)(pe + 127) | ((uint32_t)(pe + 127) << 8);
+          }
+          m_run = 0.0f;                                  // weight 1 in the merge
+          l_run = (tb == 0 && q4 == 0) ? 1.0f : 0.0f;    // the sequence's first slot carries den = 1
+          hand[j & 1][hgl][0][lane] = uint4{pk[0], pk[1], pk[2], pk[3]};
+          hand[j & 1][hgl][1][lane] = uint4{w0, __float_as_uint(1.0f), __float_as_uint(1.0f), w1};
+        } else {
         float bm0 = -INFINITY, bm1 = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; i++)
@@ -450,6 +510,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         hand[j & 1][hgl][0][lane] = uint4{pk[0], pk[1], pk[2], pk[3]};
         hand[j & 1][hgl][1][lane] = uint4{(uint32_t)pbyte[0] | ((uint32_t)pbyte[1] << 8), __float_as_uint(gamma),
                                           __float_as_uint(f_run), 0u};
+        }   // method P
       }
       wait_lds_loads();
       __syncthreads();
@@ -525,6 +586,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               const v2i lo = vt[c & 1][k][0], hi = vt[c & 1][k][1];
               const v8i av = {lo[0], lo[1], hi[0], hi[1], 0, 0, 0, 0};
               const int l0 = (int)lt[c & 1][0][k], l1 = (int)lt[c & 1][1][k];
+              if (kAblation && (a.abl & kAblVanillaP)) {   // general E4M3 P block scales
+                const v4f g0 = pv_general(av, p0, p0n, o_run[cg], l0, (int)hs.x);
+                o_run[cg] = pv_general(av, p1, p1n, g0, l1, (int)hs.w);
+                continue;
+              }
               v4f acc = mfma4<0, 0>(av, p0, o_run[cg], l0, pb0);
               acc = mfma4<1, 0>(av, p0, acc, l0, pb0);
               acc = mfma4<2, 0>(av, p0n, acc, l0, pb0);
@@ -773,6 +839,20 @@ __global__ __launch_bounds__(64) void mla_merge(DecodeArgs a) {
   const float *ml = a.ws_ml + r0 * 2;
   const float *o = a.ws_o + r0 * D + 8 * lane;
   const long so = (long)a.hq * D, sm = 2L * a.hq;   // strides between the row's partials
+  if (kAblation && (a.abl & kAblRowStats)) {
+    // ablation study, first pass of normalized P: the row's max and softmax denominator
+    float M = -INFINITY;
+    for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[sm * s]);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k));
+    float dn = 0.f;
+    if (M > -INFINITY)
+      for (int s = lane; s < nv; s += 64) dn = fmaf(__builtin_amdgcn_exp2f(ml[sm * s] - M), ml[sm * s + 1], dn);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) dn += __shfl_xor(dn, k);
+    if (lane == 0) *(float2 *)(a.out + (long)row * D) = float2{M, dn};
+    return;
+  }
   float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (nv <= kMlaMergeFast) {

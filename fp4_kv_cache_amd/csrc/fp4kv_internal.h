@@ -13,8 +13,7 @@ namespace fp4kv {
 constexpr int kMaxSplitPages = 512;
 
 // Technique switches of the ablation-study build of the library (sources compiled with
-// -DFP4KV_ABLATION; the product build compiles every switch out).  GQA and MLA, except
-// normalized P (GQA only).
+// -DFP4KV_ABLATION; the product build compiles every switch out).  GQA and MLA.
 constexpr int kAblSingleQ = 1;      // no dual residual: the query's second FP4 pass is zero
 constexpr int kAblNoRotation = 2;   // no Hadamard rotation of keys and queries
 constexpr int kAblNoSearch = 4;     // every key block keeps its default scale

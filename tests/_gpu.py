@@ -174,6 +174,7 @@ def compare_mla(built, seqs=None, tol=1e-3, ref_bound=None, opts=None):
     D = w["d"]
     rows = []
     agg = _RefErr()
+    compare_mla.last_zero_oracle = 0
     for b in seqs:
         L = int(built.lens[b])
         got = out[b]
@@ -184,6 +185,7 @@ def compare_mla(built, seqs=None, tol=1e-3, ref_bound=None, opts=None):
         K = W.keys(w, b, 0, L)
         kr = W.rope_keys(w, b, L)
         res = A.mla_seq(qn[b, :, :D], qn[b, :, D:], K, kr, ksi[0], qs[0], gk[0], w["fmt"], sc, L=L, opts=opts)
+        compare_mla.last_zero_oracle += res["zero_blocks"]
         ref = A.reference_attention(qn[b, :, :D], K, K, sc, q_rope=qn[b, :, D:], k_rope=kr)
         er_rows = A.row_rel_err(got, res["out"])
         rows.append(er_rows)

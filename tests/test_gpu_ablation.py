@@ -62,10 +62,11 @@ def test_ablation_switch_matches_oracle(torch_dev, name, label, flags, opts):
 
 
 @pytest.mark.parametrize("name", ["mla", "mla_mxfp4"])
-@pytest.mark.parametrize("label,flags,opts", SETTINGS[:5], ids=[s[0].split(" (")[0] for s in SETTINGS[:5]])
+@pytest.mark.parametrize("label,flags,opts", SETTINGS, ids=[s[0].split(" (")[0] for s in SETTINGS])
 def test_ablation_switch_matches_oracle_mla(torch_dev, name, label, flags, opts):
-    """The same switches on the MLA path (query preparation, latent append, merge): the latent's
-    codes and tile scales bit-exact, outputs within 1e-3 of the oracle with the same switch."""
+    """The same switches on the MLA path (query preparation, latent append, merge; normalized P
+    through the two-pass decode): the latent's codes and tile scales bit-exact, outputs within
+    1e-3 of the oracle with the same switch, the same count of all-zero P blocks."""
     from fp4_kv_cache_amd import lib as L
     lens = np.array([700, 129, 2100], np.int32)
     w = W.workload(name, batch=len(lens))
@@ -77,9 +78,11 @@ def test_ablation_switch_matches_oracle_mla(torch_dev, name, label, flags, opts)
     with L.ablation(flags):
         built = harness.build(w, lens=lens, calib=calib)
         check_mla_cache(built, opts=opts)
-        worst, worst_ref, _ = compare_mla(built, tol=TOL, opts=opts, ref_bound=1.5)
-    say("ABLATION %s | %s | max err vs oracle %.3g | error vs fp64 attention over all rows %.4f"
-        % (name, label, worst, compare_mla.last_agg))
+        worst, worst_ref, zg = compare_mla(built, tol=TOL, opts=opts, ref_bound=1.5)
+    zo = compare_mla.last_zero_oracle
+    say("ABLATION %s | %s | max err vs oracle %.3g | error vs fp64 attention over all rows %.4f | "
+        "all-zero P blocks GPU %d oracle %d" % (name, label, worst, compare_mla.last_agg, zg, zo))
+    assert abs(zg - zo) <= 2, (zg, zo)
 
 
 def _zero_blocks(built, flags, opts):
