@@ -152,17 +152,37 @@ def test_workspace_does_not_depend_on_max_seq_len(lib, attn):
         assert len(words) == 1
 
 
-def test_header_is_plain_c():
-    """include/fp4kv.h compiles as C99 (no C++ or torch types at the boundary)."""
+@pytest.mark.parametrize("name", ["fp4kv.h", "fp4kv_ablation.h"])
+def test_header_is_plain_c(name):
+    """The public headers compile as C99 (no C++ or torch types at the boundary)."""
     import shutil
     import subprocess
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no C compiler")
-    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp4kv.h")
-    r = subprocess.run([cc, "-fsyntax-only", "-x", "c", "-std=c99", "-Wall", "-Werror", hdr],
-                       capture_output=True, text=True)
+    hdr = os.path.join(ROOT, "include", name)
+    r = subprocess.run([cc, "-fsyntax-only", "-x", "c", "-std=c99", "-Wall", "-Werror", "-I",
+                        os.path.join(ROOT, "include"), hdr], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_ablation_switches_agree_and_stay_out_of_the_product(lib):
+    """include/fp4kv_ablation.h's switch bits equal the kernels' constants and the binding's; the
+    study build exports fp4kv_ablation_set, the product library does not."""
+    hdr = open(os.path.join(ROOT, "include", "fp4kv_ablation.h")).read()
+    bits = {k: int(v) for k, v in re.findall(r"#define FP4KV_ABL_([A-Z_0-9]+) (\d+)", hdr)}
+    internal = open(os.path.join(ROOT, "fp4_kv_cache_amd", "csrc", "fp4kv_internal.h")).read()
+    kern = {k: int(v) for k, v in re.findall(r"constexpr int kAbl([A-Za-z]+) = (\d+);", internal)}
+    assert bits == {"SINGLE_Q": kern["SingleQ"], "NO_ROTATION": kern["NoRotation"],
+                    "NO_SEARCH": kern["NoSearch"], "NORMALIZED_P": kern["VanillaP"]}, (bits, kern)
+    assert (L.ABL_SINGLE_Q, L.ABL_NO_ROTATION, L.ABL_NO_SEARCH, L.ABL_NORMALIZED_P) == \
+        (bits["SINGLE_Q"], bits["NO_ROTATION"], bits["NO_SEARCH"], bits["NORMALIZED_P"])
+    assert not hasattr(lib, "fp4kv_ablation_set")
+    if not os.path.exists(L.LIB_ABLATION_PATH):
+        pytest.skip("study build not built")
+    abl = L.load_ablation()
+    assert abl.fp4kv_ablation_set(1 << 8) == L.ERR_INVALID_ARG   # an unknown bit
+    assert abl.fp4kv_ablation_set(0) == 0
 
 
 def test_host_entry_points_from_c(lib, tmp_path):
