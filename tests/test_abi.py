@@ -221,3 +221,21 @@ def test_noalloc_limit_checked_on_the_host(lib):
         setattr(c, f, 0x1000)
     assert L.fp4_decode_attention_noalloc(c, 1, 0, 3800, 32, 1, 16, 1, 0.1, 1, None, None) == L.ERR_WORKSPACE
     assert L.fp4_decode_attention_noalloc(c, 1, 0, -1, 32, 1, 16, 1, 0.1, 1, None, None) == L.ERR_INVALID_ARG
+
+
+def test_normalized_p_only_through_the_full_decode(lib):
+    """In the study build, normalized P (FP4KV_ABL_NORMALIZED_P) needs both passes of one
+    fp4_decode_attention call: the partial-only, merge-only and multi-token entry points refuse
+    it on the host, before anything is launched (fake non-null pointers, ample workspace)."""
+    if not os.path.exists(L.LIB_ABLATION_PATH):
+        pytest.skip("study build not built")
+    c = _desc()
+    for f in ("k_codes", "k_scales", "v_codes", "v_scales", "stage", "k_tensor_scale", "v_tensor_scale",
+              "k_smooth_inv", "q_smooth"):
+        setattr(c, f, 0x1000)
+    ws = 1 << 30
+    with L.ablation(L.ABL_NORMALIZED_P):
+        assert L.fp4_decode_partials(c, 1, 0, 3, 8, 1, 16, 1, 0.1, 1, ws, None, None) == L.ERR_UNSUPPORTED
+        assert L.fp4_decode_merge(c, 3, 8, 16, 1, 1, 1, ws, None) == L.ERR_UNSUPPORTED
+        assert L.fp4_decode_attention_multi(c, 1, 0, 3, 2, 8, 1, 16, 1, 0.1, 1, 1, ws, None, None) == \
+            L.ERR_UNSUPPORTED
