@@ -152,3 +152,38 @@ def test_noalloc_decode_graph_replay(torch_dev, name):
                                                None, torch.cuda.current_stream().cuda_stream),
                 "fp4_decode_attention_noalloc")
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_30b_a3b"])
+def test_multi_token_decode_graph_replay(torch_dev, name):
+    """fp4_decode_attention_multi (two query tokens per sequence, causal) captured in a HIP
+    graph: two eager calls give the same bytes and every replay equals them."""
+    torch = torch_dev
+    lens = np.array([700, 129, 0, 1500, 64], np.int32)
+    w = W.workload(name, batch=len(lens))
+    print("graph multi", name, lens.tolist(), flush=True)
+    built = harness.build(w, lens=lens)
+    cache = built.cache
+    q = built.queries_multi(2)
+    scale = W.softmax_scale(w)
+    from fp4_kv_cache_amd import lib as L
+    nb = L.fp4_decode_multi_workspace_bytes(cache.desc, q.shape[0], 2, q.shape[2], built.bt.shape[1] * w["page"])
+    ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=built.device)
+    out_e = cache.decode_multi(q, built.bt, built.seq_lens, scale, workspace=ws)
+    out_e2 = cache.decode_multi(q, built.bt, built.seq_lens, scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_e, out_e2)
+    assert torch.isfinite(out_e).all()
+    out_g = torch.empty_like(out_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cache.decode_multi(q, built.bt, built.seq_lens, scale, out=out_g, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), "replay %d: max diff %g" % (r, float((out_g - out_e).abs().max()))
+        cache.decode(q[:, -1].contiguous(), built.bt, built.seq_lens, scale, workspace=ws)   # eager work between
+        torch.cuda.synchronize()
