@@ -836,8 +836,9 @@ __global__ __launch_bounds__(64) void gqa_merge(DecodeArgs a) {
     if (lane == 0) *(float2 *)(a.out + (long)row * 128) = float2{M, den};
     return;
   }
-  // every (m, l) pair and output partial of the row in flight at once, in two size classes
+  // every (m, l) pair and output partial of the row in flight at once, in three size classes (16, 32, 64)
   if (nv <= 16) { merge_row_fast<16>(ml, o, sm, so, nv, lane, dst); return; }
+  if (nv <= 32) { merge_row_fast<32>(ml, o, sm, so, nv, lane, dst); return; }
   if (nv <= 64) { merge_row_fast<64>(ml, o, sm, so, nv, lane, dst); return; }
   __shared__ float wsh[256];
   float M = -INFINITY;
